@@ -1,0 +1,250 @@
+"""Benchmark: linear-attention layer tokens/s per packed pass on one MI355X.
+
+One step = one packed pass through la_scan_packed (all three launches) over
+one batch of synthetic input already resident in HBM.  The default workload
+is one 7,400-token view with 8 branches of 48 tokens, H = 16, d = 64, bf16
+(the pass size of the page "Serving 0.88M TPS from Two RTXs and Mac Minis",
+section "Kernels", paragraph "One scan per pass").
+
+Timing: W warm-up passes, then exactly K passes, both replayed as HIP graphs
+on one stream and bracketed by torch.cuda.synchronize().  Inputs rotate over
+enough copies (>= 1 GiB in total) that each pass reads its q/k/v from HBM
+rather than from the 256 MB Infinity Cache.  The dominant kernel (launch 3,
+the chunk outputs) is timed alone with HIP events on the same stream for the
+roofline line.  The fp64 CPU oracle is timed on the host cores on the same
+workload (cpu_baseline).
+
+Prints one JSON line.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+DEFAULT_WORKLOAD = "view7400_br8x48_h16_d64_bf16"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--block-chunks", type=int, default=None)
+    ap.add_argument("--rotate-gib", type=float, default=1.0,
+                    help="total size of the rotated input copies")
+    ap.add_argument("--eager", action="store_true",
+                    help="plain stream launches instead of HIP graphs (for profilers)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target CPU work of the oracle baseline")
+    return ap.parse_args()
+
+
+def _oracle_task(args):
+    q, k, v, so, bp = args
+    import oracle
+    t = time.perf_counter()
+    oracle.scan_recurrence(q, k, v, so, bp)
+    return time.perf_counter() - t
+
+
+def cpu_baseline(w, so, bp, target_s):
+    """The fp64 oracle, unmodified, over the whole pass; heads are split across
+    a process pool (heads are independent).  Repeated until about target_s
+    seconds of CPU work; median wall time of the repeats."""
+    import numpy as np
+    import torch
+    from concurrent.futures import ProcessPoolExecutor
+    cores = min(len(os.sched_getaffinity(0)), 16, w.H)
+    q, k, v = (x.to(torch.float32).numpy() for x in (w.q, w.k, w.v))
+    bounds = np.linspace(0, w.H, cores + 1).astype(int)
+    tasks = [(q[:, a:b], k[:, a:b], v[:, a:b], so, bp) for a, b in zip(bounds[:-1], bounds[1:])]
+    walls, cpu = [], 0.0
+    with ProcessPoolExecutor(max_workers=cores) as ex:
+        while cpu < target_s or len(walls) < 3:
+            t = time.perf_counter()
+            parts = list(ex.map(_oracle_task, tasks))
+            walls.append(time.perf_counter() - t)
+            cpu += sum(parts)
+            if len(walls) >= 20:
+                break
+    wall = float(np.median(walls))
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": w.n_tokens / wall, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"whole pass ({w.n_tokens} tokens x {w.H} heads), {len(walls)} repeats, "
+                      f"median wall {wall:.3f} s, {cpu:.1f} s CPU work, {model}"}
+
+
+def traffic_from_profiles(kernel_tag, workload, src_hash):
+    """HBM bytes per launch of the dominant kernel from committed rocprofv3
+    --pmc summaries, only if they were taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel_tag}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256") != src_hash:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    a = parse()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this scan runs on a single MI355X and has no "
+              "multi-GPU path (requests shard across GPUs with no exchange; see DESIGN.md). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import chunked_linear_attention_packed_amd as la
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    la.load_library()
+    dev = torch.device("cuda:0")
+    w = synth.workload(a.workload)
+    plan = la.pack(w.view_len, w.branch_count, w.branch_len, heads=w.H,
+                   block_chunks=a.block_chunks)
+    info = plan.info
+    T, H, d = w.n_tokens, w.H, w.d
+    s_el = 2 if w.dtype == "bf16" else 4
+    set_bytes = 4 * T * H * d * s_el
+    n_sets = max(2, int(np.ceil(a.rotate_gib * 2**30 / set_bytes)))
+    n_sets = min(n_sets, 64)
+    q0, k0, v0 = (x.to(dev) for x in (w.q, w.k, w.v))
+    sets = []
+    for i in range(n_sets):
+        sets.append(dict(q=q0.clone(), k=k0.clone(), v=v0.clone(), out=torch.empty_like(v0)))
+    del q0, k0, v0
+    fin = torch.empty((info.n_views, H, d, d), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(la.workspace_size(plan, H, d, w.q.dtype), 1), dtype=torch.uint8,
+                     device=dev)
+    plan.device_plan(dev)
+    stream = torch.cuda.Stream(dev)
+
+    def step(i, stages=la.STAGE_ALL):
+        s = sets[i % n_sets]
+        la.scan_packed(s["q"], s["k"], s["v"], plan, out=s["out"], final_state=fin,
+                       workspace=ws, stream=stream, stages=stages)
+
+    # first pass eagerly (also validates arguments)
+    with torch.cuda.stream(stream):
+        for i in range(n_sets):
+            step(i)
+    torch.cuda.synchronize()
+
+    def make_graph(n, stages=la.STAGE_ALL):
+        if a.eager:
+            return lambda: [step(i, stages) for i in range(n)]
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(n):
+                step(i, stages)
+        return g.replay
+
+    warm = make_graph(a.warmup)
+    timed = make_graph(a.steps)
+    with torch.cuda.stream(stream):
+        warm()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        ev0.record(stream)
+        timed()
+        ev1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall_ms = (t1 - t0) * 1e3
+    gpu_ms = ev0.elapsed_time(ev1)
+    ms_per_step = wall_ms / a.steps
+
+    # launch 3 alone (reads what the last full pass left in ws / final_state)
+    out_only = make_graph(a.steps, la.STAGE_OUTPUT)
+    with torch.cuda.stream(stream):
+        out_only()
+    torch.cuda.synchronize()
+    e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e2.record(stream)
+        out_only()
+        e3.record(stream)
+    torch.cuda.synchronize()
+    l3_us = e2.elapsed_time(e3) * 1e3 / a.steps
+
+    # algorithmic bytes: q, k, v read once and out written once per token-head;
+    # final states written once per view and head
+    per_token_head = d * (3 * s_el + s_el)
+    l3_bytes = T * H * per_token_head
+    pass_bytes = l3_bytes + info.n_views * H * d * d * 4
+    achieved = l3_bytes / (l3_us * 1e-6) / 1e9
+    src = os.path.join(ROOT, "chunked_linear_attention_packed_amd", "csrc", "scan.hip")
+    with open(src, "rb") as f:
+        src_hash = hashlib.sha256(f.read()).hexdigest()
+    traffic = traffic_from_profiles("output_kernel", a.workload, src_hash)
+    pass_us = gpu_ms * 1e3 / a.steps
+
+    cpu = None
+    if not a.no_cpu_baseline:
+        cpu = cpu_baseline(w, plan.seg_offsets, plan.branch_parent, a.cpu_seconds)
+
+    rec = {
+        "metric": "linear-attn layer tokens/s per packed pass on 1 GPU + % of roofline",
+        "value": T / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": a.workload,
+            "tokens": T, "heads": H, "d": d, "segments": info.n_segments,
+            "views": info.n_views, "branches": info.n_branches,
+            "chunk": info.chunk, "block_chunks": info.block_chunks,
+            "work_blocks": info.n_blocks, "delta_blocks": info.n_delta,
+            "launch": "eager" if a.eager else "hip_graph",
+            "rotating_input_sets": n_sets,
+            "gpu_us_per_pass": pass_us,
+            "pass_algorithmic_bytes": pass_bytes,
+            "pass_roofline_frac": pass_bytes / (pass_us * 1e-6) / (HBM_PEAK_GBS * 1e9),
+            "output_kernel_us": l3_us,
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+            "kernel": "output_kernel (launch 3)",
+            "bytes_per_launch": l3_bytes,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,281 @@
+"""Python binding of liblinattn.so: the packed chunked causal linear-attention
+scan for MI355X (gfx950).
+
+Argument marshalling only.  Every step of the scan runs in the HIP library;
+PyTorch supplies device memory and the stream.  There is no fallback: if the
+library is missing or was built without the GPU code, calls raise.
+
+Source of the method: "Serving 0.88M TPS from Two RTXs and Mac Minis",
+sections "The Workload", "Kernels" and "Long Requests".
+
+    plan = pack(view_len, branch_count, branch_len, heads=H)
+    out, final_state = scan_packed(q, k, v, plan)
+    export_view_state(final_state, view_row, dst)
+"""
+import ctypes
+import os
+from dataclasses import dataclass, field
+
+import numpy as np
+
+__all__ = ["LinAttnError", "PassInfo", "PassPlan", "pack", "plan_segments",
+           "choose_block_chunks", "workspace_size", "scan_packed",
+           "export_view_state", "library_path", "load_library", "CHUNK"]
+
+CHUNK = 64
+LA_OK, LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED, LA_ERR_WORKSPACE, LA_ERR_HIP = range(5)
+LA_F32, LA_BF16 = 0, 1
+STAGE_STATES, STAGE_PREFIX, STAGE_OUTPUT, STAGE_ALL = 1, 2, 4, 7
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def library_path():
+    return os.path.join(_HERE, "liblinattn.so")
+
+
+class LinAttnError(RuntimeError):
+    def __init__(self, fn, status, msg):
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+        self.status = status
+
+
+class PassInfo(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "n_requests", "n_segments", "n_views", "n_branches", "n_ext", "n_tokens", "chunk",
+        "block_chunks", "n_chunks", "n_view_chunks", "n_blocks", "n_delta", "n_scan",
+        "plan_words", "max_seg_tokens")] + [("reserved", ctypes.c_int32 * 9)]
+
+    def as_dict(self):
+        return {n: getattr(self, n) for n, _ in self._fields_ if n != "reserved"}
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I32P = ctypes.POINTER(ctypes.c_int32)
+
+
+def load_library():
+    """Load liblinattn.so once.  Raises if it is absent: nothing here runs
+    the scan any other way."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} is missing: build it with "
+            "`python -m chunked_linear_attention_packed_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(path)
+    lib.la_pack_pass.argtypes = [ctypes.c_int32, _I32P, _I32P, _I32P, ctypes.c_int32,
+                                 ctypes.c_int32, _I32P, _I32P, _I32P, _I32P,
+                                 ctypes.POINTER(PassInfo)]
+    lib.la_plan_segments.argtypes = [ctypes.c_int32, _I32P, _I32P, ctypes.c_int32,
+                                     ctypes.c_int32, _I32P, _I32P, ctypes.POINTER(PassInfo)]
+    lib.la_scan_workspace_size.argtypes = [ctypes.POINTER(PassInfo), ctypes.c_int32,
+                                           ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.POINTER(ctypes.c_size_t)]
+    lib.la_scan_packed.argtypes = [_P, _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                   ctypes.c_int32, ctypes.POINTER(PassInfo), _P, _P,
+                                   ctypes.c_int32, _P, _P, _P, ctypes.c_size_t, _P]
+    lib.la_scan_packed_stages.argtypes = [ctypes.c_int32] + lib.la_scan_packed.argtypes
+    lib.la_export_view_state.argtypes = [_P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                         ctypes.c_int32, ctypes.c_int32, _P, _P]
+    lib.la_status_string.argtypes = [ctypes.c_int32]
+    lib.la_status_string.restype = ctypes.c_char_p
+    for fn in ("la_pack_pass", "la_plan_segments", "la_scan_workspace_size",
+               "la_scan_packed", "la_scan_packed_stages", "la_export_view_state"):
+        getattr(lib, fn).restype = ctypes.c_int32
+    _lib = lib
+    return lib
+
+
+def _check(fn, status):
+    if status != LA_OK:
+        msg = load_library().la_status_string(status).decode()
+        raise LinAttnError(fn, status, msg)
+
+
+def _i32(a):
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def _ptr(a):
+    return a.ctypes.data_as(_I32P) if a is not None and a.size else None
+
+
+@dataclass
+class PassPlan:
+    """Host result of packing: segment table, info and the device plan."""
+    info: PassInfo
+    seg_offsets: np.ndarray
+    branch_parent: np.ndarray
+    view_ordinal: np.ndarray
+    plan: np.ndarray
+    _dev: dict = field(default_factory=dict, repr=False)
+
+    def device_plan(self, device):
+        """The plan as an int32 tensor on `device`, uploaded once."""
+        import torch
+        key = str(torch.device(device))
+        if key not in self._dev:
+            self._dev[key] = torch.from_numpy(self.plan).to(device)
+        return self._dev[key]
+
+
+def choose_block_chunks(chunks_per_segment, heads, target_groups=2048, max_g=8):
+    """Chunks per work block: the largest power of two (<= max_g) whose block
+    count times `heads` still reaches `target_groups` workgroups; 1 if none.
+    Larger blocks carry the state in registers longer (less state traffic);
+    smaller ones give more workgroups to fill 256 compute units."""
+    cps = np.asarray(chunks_per_segment, dtype=np.int64)
+    g = max_g
+    while g > 1:
+        nb = int(np.sum((cps + g - 1) // g))
+        if nb * heads >= target_groups:
+            return g
+        g //= 2
+    return 1
+
+
+def _auto_g(lengths, heads):
+    lengths = np.asarray(lengths, dtype=np.int64)
+    return choose_block_chunks((lengths + CHUNK - 1) // CHUNK, heads)
+
+
+def pack(view_len, branch_count, branch_len, heads=16, block_chunks=None, chunk=CHUNK):
+    """Request shapes -> PassPlan via la_pack_pass (view then branches per
+    request; view length 0 marks a shard request seeded from ext_state)."""
+    lib = load_library()
+    vl, bc, bl = _i32(view_len), _i32(branch_count), _i32(branch_len)
+    if block_chunks is None:
+        block_chunks = _auto_g(np.concatenate([vl[vl > 0], bl]), heads)
+    info = PassInfo()
+    _check("la_pack_pass", lib.la_pack_pass(len(vl), _ptr(vl), _ptr(bc), _ptr(bl), chunk,
+                                            block_chunks, None, None, None, None,
+                                            ctypes.byref(info)))
+    so = np.zeros(info.n_segments + 1, dtype=np.int32)
+    bp = np.zeros(info.n_segments, dtype=np.int32)
+    vo = np.zeros(info.n_segments, dtype=np.int32)
+    plan = np.zeros(info.plan_words, dtype=np.int32)
+    _check("la_pack_pass", lib.la_pack_pass(len(vl), _ptr(vl), _ptr(bc), _ptr(bl), chunk,
+                                            block_chunks, so.ctypes.data_as(_I32P),
+                                            _ptr(bp), _ptr(vo), _ptr(plan),
+                                            ctypes.byref(info)))
+    return PassPlan(info, so, bp, vo, plan)
+
+
+def plan_segments(seg_offsets, branch_parent, heads=16, block_chunks=None, chunk=CHUNK):
+    """Segment table (any order whose parents are views) -> PassPlan."""
+    lib = load_library()
+    so, bp = _i32(seg_offsets), _i32(branch_parent)
+    if block_chunks is None:
+        block_chunks = _auto_g(np.diff(so), heads) if len(bp) else 1
+    info = PassInfo()
+    _check("la_plan_segments", lib.la_plan_segments(len(bp), _ptr(so), _ptr(bp), chunk,
+                                                    block_chunks, None, None,
+                                                    ctypes.byref(info)))
+    vo = np.zeros(info.n_segments, dtype=np.int32)
+    plan = np.zeros(info.plan_words, dtype=np.int32)
+    _check("la_plan_segments", lib.la_plan_segments(len(bp), _ptr(so), _ptr(bp), chunk,
+                                                    block_chunks, _ptr(vo), _ptr(plan),
+                                                    ctypes.byref(info)))
+    return PassPlan(info, so, bp, vo, plan)
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return LA_BF16
+    if t.dtype == torch.float32:
+        return LA_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def workspace_size(plan, heads, d, dtype):
+    lib = load_library()
+    n = ctypes.c_size_t()
+    code = dtype if isinstance(dtype, int) else _dtype_code_from_torch(dtype)
+    _check("la_scan_workspace_size",
+           lib.la_scan_workspace_size(ctypes.byref(plan.info), heads, d, d, code,
+                                      ctypes.byref(n)))
+    return n.value
+
+
+def _dtype_code_from_torch(dt):
+    import torch
+    return {torch.bfloat16: LA_BF16, torch.float32: LA_F32}[dt]
+
+
+def _stream_ptr(stream, device):
+    import torch
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def scan_packed(q, k, v, plan, ext_state=None, out=None, final_state=None, workspace=None,
+                stream=None, stages=STAGE_ALL):
+    """Run the three-launch scan on `stream` (default: torch's current stream).
+
+    q, k: [T, H, d] and v: [T, H, d] contiguous CUDA tensors, bf16 or fp32.
+    Returns (out [T, H, d] in the input dtype, final_state [n_views, H, d, d]
+    fp32).  Pre-allocated out / final_state / workspace tensors are used as
+    given (no allocation then).  `stages` selects launches (STAGE_* bits, see
+    la_scan_packed_stages) for profiling; the default runs all three."""
+    import torch
+    lib = load_library()
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k, v must be device tensors")
+    if q.dim() != 3 or k.shape != q.shape or v.dim() != 3 or v.shape[:2] != q.shape[:2]:
+        raise ValueError("q, k: [T, H, d_k]; v: [T, H, d_v]")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share a dtype")
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    info = plan.info
+    if T != info.n_tokens:
+        raise ValueError(f"q has {T} tokens, the plan {info.n_tokens}")
+    code = _dtype_code(q)
+    dev = q.device
+    if out is None:
+        out = torch.empty((T, H, dv), dtype=q.dtype, device=dev)
+    if final_state is None:
+        final_state = torch.empty((info.n_views, H, dk, dv), dtype=torch.float32, device=dev)
+    need = workspace_size(plan, H, dk, code)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    n_ext = 0
+    ext_ptr = None
+    if ext_state is not None:
+        if ext_state.dtype != torch.float32 or not ext_state.is_contiguous():
+            raise TypeError("ext_state must be contiguous float32 [n_ext, H, d, d]")
+        n_ext = ext_state.shape[0]
+        ext_ptr = ctypes.c_void_p(ext_state.data_ptr())
+    dplan = plan.device_plan(dev)
+    st = lib.la_scan_packed_stages(stages, ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
+                            ctypes.c_void_p(v.data_ptr()), code, H, dk, dv,
+                            ctypes.byref(info), ctypes.c_void_p(dplan.data_ptr()), ext_ptr,
+                            n_ext, ctypes.c_void_p(out.data_ptr()),
+                            ctypes.c_void_p(final_state.data_ptr()) if final_state.numel() else None,
+                            ctypes.c_void_p(workspace.data_ptr()), ws_bytes,
+                            _stream_ptr(stream, dev))
+    _check("la_scan_packed", st)
+    return out, final_state
+
+
+def export_view_state(final_state, view_row, dst=None, stream=None):
+    """Copy final_state[view_row] ([H, d, d] fp32) into dst (allocated if
+    None) on the device, for a branch shard seeded from the cached view."""
+    import torch
+    lib = load_library()
+    nv, H, dk, dv = final_state.shape
+    if dst is None:
+        dst = torch.empty((H, dk, dv), dtype=torch.float32, device=final_state.device)
+    _check("la_export_view_state",
+           lib.la_export_view_state(ctypes.c_void_p(final_state.data_ptr()), view_row, nv, H,
+                                    dk, dv, ctypes.c_void_p(dst.data_ptr()),
+                                    _stream_ptr(stream, final_state.device)))
+    return dst

@@ -1,0 +1,65 @@
+"""Compile the HIP library liblinattn.so in-tree for gfx950.
+
+    python -m chunked_linear_attention_packed_amd.build
+
+The host packer (pack.cpp) is compiled with g++; the kernels and the scan's
+host entry points (scan.hip) with hipcc; both are linked into one shared
+library next to this file.  Always recompiles.
+"""
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "liblinattn.so")
+
+HIP_FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+    # keep the compiler from forming packed fp32 VALU instructions
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+]
+
+
+def _hipcc():
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build liblinattn.so)")
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(l for l in res.stdout.splitlines()
+                    if "packed-fp32-ops' is not a recognized feature" not in l)
+    if res.returncode != 0:
+        raise RuntimeError(f"build step failed ({res.returncode}): {' '.join(cmd)}\n{out}")
+    if verbose and out.strip():
+        print(out, flush=True)
+
+
+def build(verbose=False):
+    hipcc = _hipcc()
+    with tempfile.TemporaryDirectory(prefix="linattn_build_") as tmp:
+        pack_o = os.path.join(tmp, "pack.o")
+        scan_o = os.path.join(tmp, "scan.o")
+        _run(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", INCLUDE, "-c",
+              os.path.join(CSRC, "pack.cpp"), "-o", pack_o], verbose)
+        _run([hipcc] + HIP_FLAGS + ["-I", INCLUDE, "-c", os.path.join(CSRC, "scan.hip"),
+                                    "-o", scan_o], verbose)
+        tmp_lib = LIB + ".tmp"
+        _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", pack_o, scan_o,
+              "-o", tmp_lib], verbose)
+        os.replace(tmp_lib, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

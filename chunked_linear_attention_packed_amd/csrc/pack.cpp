@@ -1,0 +1,258 @@
+// Host-side packing and work planning for the packed linear-attention scan.
+//
+// Section "The Workload" of "Serving 0.88M TPS from Two RTXs and Mac Minis":
+// a request is one long view plus short branches that attend to the view and
+// never to each other.  Paragraph "Shared branch passes" (section "Kernels"):
+// the branches of every request in a pass go through one packed forward.
+// Section "Long Requests": a branch shard starts from the view's cached state.
+//
+// Everything here is integer bookkeeping on the host.  The output plan is the
+// only metadata the device kernels read: one descriptor per work block, per
+// delta block and per scanned segment.
+#include <cstdint>
+#include <cstring>
+#include <vector>
+
+#include "linattn.h"
+
+namespace {
+
+constexpr int32_t kPlanVersion = 1;
+
+struct Seg {
+    int32_t off, len, parent;
+};
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Validates a segment table and fills `info` and, when asked, the plan.
+la_status plan_impl(int32_t n_seg, const int32_t* seg_offsets, const int32_t* branch_parent,
+                    int32_t chunk, int32_t block_chunks, int32_t* view_ordinal, int32_t* plan,
+                    la_pass_info* info) {
+    if (!info) return LA_ERR_INVALID_ARG;
+    if (chunk != LA_CHUNK) return LA_ERR_UNSUPPORTED;
+    if (n_seg < 0 || block_chunks < 1 || block_chunks > (1 << 20)) return LA_ERR_INVALID_ARG;
+    if (n_seg > 0 && (!seg_offsets || !branch_parent)) return LA_ERR_INVALID_ARG;
+    if (n_seg == 0 && seg_offsets && seg_offsets[0] != 0) return LA_ERR_INVALID_ARG;
+
+    const int64_t blk_tok = int64_t(block_chunks) * chunk;
+    if (blk_tok > INT32_MAX) return LA_ERR_INVALID_ARG;
+
+    std::vector<int32_t> ord(size_t(n_seg), -1);
+    int32_t n_views = 0, n_branches = 0, n_ext = 0, max_len = 0;
+    int64_t n_chunks = 0, n_view_chunks = 0;
+    if (n_seg > 0 && seg_offsets[0] != 0) return LA_ERR_INVALID_ARG;
+    for (int32_t s = 0; s < n_seg; ++s) {
+        const int64_t len = int64_t(seg_offsets[s + 1]) - seg_offsets[s];
+        if (len < 1) return LA_ERR_INVALID_ARG;
+        if (len > max_len) max_len = int32_t(len);
+        const int32_t p = branch_parent[s];
+        if (p == -1) {
+            ord[size_t(s)] = n_views++;
+            n_view_chunks += ceil_div(len, chunk);
+        } else {
+            ++n_branches;
+        }
+        n_chunks += ceil_div(len, chunk);
+    }
+    // Parents are checked after all views are known: any order is accepted.
+    for (int32_t s = 0; s < n_seg; ++s) {
+        const int32_t p = branch_parent[s];
+        if (p == -1) continue;
+        if (p >= 0) {
+            if (p >= n_seg || branch_parent[p] != -1) return LA_ERR_INVALID_ARG;
+        } else {
+            if (p < -2 - (INT32_MAX - 2)) return LA_ERR_INVALID_ARG;
+            const int32_t e = -p - 2;
+            if (e + 1 > n_ext) n_ext = e + 1;
+        }
+    }
+
+    // Work blocks: views first (their blocks are the longest), then branches.
+    int64_t n_blocks = 0, n_delta = 0, n_scan = 0;
+    for (int pass = 0; pass < 2; ++pass) {
+        for (int32_t s = 0; s < n_seg; ++s) {
+            const bool is_view = branch_parent[s] == -1;
+            if (is_view != (pass == 0)) continue;
+            const int64_t len = int64_t(seg_offsets[s + 1]) - seg_offsets[s];
+            const int64_t nb = ceil_div(len, blk_tok);
+            n_blocks += nb;
+            // A view needs every block's state (its total is final_state);
+            // a branch needs all but its last block's.
+            const int64_t nslots = is_view ? nb : nb - 1;
+            n_delta += nslots;
+            if (is_view || nslots >= 2) ++n_scan;
+        }
+    }
+    const int64_t words = int64_t(LA_PLAN_HEADER_WORDS) + n_blocks * LA_PLAN_BLOCK_WORDS +
+                          n_delta * LA_PLAN_DELTA_WORDS + n_scan * LA_PLAN_SCAN_WORDS;
+    if (words > INT32_MAX || n_chunks > INT32_MAX) return LA_ERR_INVALID_ARG;
+
+    la_pass_info inf;
+    std::memset(&inf, 0, sizeof(inf));
+    inf.n_requests = 0;
+    inf.n_segments = n_seg;
+    inf.n_views = n_views;
+    inf.n_branches = n_branches;
+    inf.n_ext = n_ext;
+    inf.n_tokens = n_seg > 0 ? seg_offsets[n_seg] : 0;
+    inf.chunk = chunk;
+    inf.block_chunks = block_chunks;
+    inf.n_chunks = int32_t(n_chunks);
+    inf.n_view_chunks = int32_t(n_view_chunks);
+    inf.n_blocks = int32_t(n_blocks);
+    inf.n_delta = int32_t(n_delta);
+    inf.n_scan = int32_t(n_scan);
+    inf.plan_words = int32_t(words);
+    inf.max_seg_tokens = max_len;
+
+    if (view_ordinal)
+        for (int32_t s = 0; s < n_seg; ++s) view_ordinal[s] = ord[size_t(s)];
+
+    if (plan) {
+        const int32_t off_blocks = LA_PLAN_HEADER_WORDS;
+        const int32_t off_delta = off_blocks + int32_t(n_blocks) * LA_PLAN_BLOCK_WORDS;
+        const int32_t off_scan = off_delta + int32_t(n_delta) * LA_PLAN_DELTA_WORDS;
+        int32_t* h = plan;
+        std::memset(h, 0, sizeof(int32_t) * LA_PLAN_HEADER_WORDS);
+        h[0] = LA_PLAN_MAGIC;
+        h[1] = kPlanVersion;
+        h[2] = int32_t(n_blocks);
+        h[3] = int32_t(n_delta);
+        h[4] = int32_t(n_scan);
+        h[5] = chunk;
+        h[6] = block_chunks;
+        h[7] = inf.n_tokens;
+        h[8] = off_blocks;
+        h[9] = off_delta;
+        h[10] = off_scan;
+        h[11] = n_ext;
+        h[12] = n_views;
+        int32_t* blk = plan + off_blocks;
+        int32_t* del = plan + off_delta;
+        int32_t* scn = plan + off_scan;
+        int32_t slot = 0;
+        for (int pass = 0; pass < 2; ++pass) {
+            for (int32_t s = 0; s < n_seg; ++s) {
+                const int32_t p = branch_parent[s];
+                const bool is_view = p == -1;
+                if (is_view != (pass == 0)) continue;
+                const int32_t off = seg_offsets[s];
+                const int32_t len = seg_offsets[s + 1] - off;
+                const int32_t nb = int32_t(ceil_div(len, blk_tok));
+                const int32_t nslots = is_view ? nb : nb - 1;
+                const int32_t seed = is_view ? -1 : (p >= 0 ? ord[size_t(p)] : p);
+                for (int32_t j = 0; j < nb; ++j) {
+                    const int32_t tok0 = off + int32_t(j * blk_tok);
+                    const int32_t ntok = int32_t(len - j * blk_tok < blk_tok ? len - j * blk_tok
+                                                                             : blk_tok);
+                    blk[0] = tok0;
+                    blk[1] = ntok;
+                    blk[2] = j >= 1 ? slot + j - 1 : -1;
+                    blk[3] = j < nslots ? slot + j : -1;
+                    blk[4] = seed;
+                    blk[5] = s;
+                    blk[6] = 0;
+                    blk[7] = 0;
+                    blk += LA_PLAN_BLOCK_WORDS;
+                    if (j < nslots) {
+                        del[0] = tok0;
+                        del[1] = ntok;
+                        del[2] = slot + j;
+                        del[3] = s;
+                        del += LA_PLAN_DELTA_WORDS;
+                    }
+                }
+                if (is_view || nslots >= 2) {
+                    scn[0] = slot;
+                    scn[1] = nslots;
+                    scn[2] = is_view ? ord[size_t(s)] : -1;
+                    scn[3] = s;
+                    scn += LA_PLAN_SCAN_WORDS;
+                }
+                slot += nslots;
+            }
+        }
+    }
+    *info = inf;
+    return LA_OK;
+}
+
+}  // namespace
+
+extern "C" la_status la_plan_segments(int32_t n_segments, const int32_t* seg_offsets,
+                                      const int32_t* branch_parent, int32_t chunk,
+                                      int32_t block_chunks, int32_t* view_ordinal,
+                                      int32_t* plan, la_pass_info* info) {
+    return plan_impl(n_segments, seg_offsets, branch_parent, chunk, block_chunks, view_ordinal,
+                     plan, info);
+}
+
+extern "C" la_status la_pack_pass(int32_t n_requests, const int32_t* view_len,
+                                  const int32_t* branch_count, const int32_t* branch_len,
+                                  int32_t chunk, int32_t block_chunks, int32_t* seg_offsets,
+                                  int32_t* branch_parent, int32_t* view_ordinal, int32_t* plan,
+                                  la_pass_info* info) {
+    if (!info || n_requests < 0) return LA_ERR_INVALID_ARG;
+    if (n_requests > 0 && (!view_len || !branch_count)) return LA_ERR_INVALID_ARG;
+    if (chunk != LA_CHUNK) return LA_ERR_UNSUPPORTED;
+    int64_t n_br = 0;
+    for (int32_t r = 0; r < n_requests; ++r) {
+        if (view_len[r] < 0 || branch_count[r] < 0) return LA_ERR_INVALID_ARG;
+        if (view_len[r] == 0 && branch_count[r] == 0) return LA_ERR_INVALID_ARG;
+        n_br += branch_count[r];
+    }
+    if (n_br > 0 && !branch_len) return LA_ERR_INVALID_ARG;
+    if (n_br > INT32_MAX / 2) return LA_ERR_INVALID_ARG;
+
+    // Build the segment table: request by request, view then branches.
+    std::vector<int32_t> off;
+    std::vector<int32_t> par;
+    off.reserve(size_t(n_requests + n_br + 1));
+    par.reserve(size_t(n_requests + n_br));
+    off.push_back(0);
+    int64_t tok = 0;
+    int32_t n_ext = 0;
+    int64_t b = 0;
+    for (int32_t r = 0; r < n_requests; ++r) {
+        int32_t seed;
+        if (view_len[r] > 0) {
+            seed = int32_t(par.size());
+            par.push_back(-1);
+            tok += view_len[r];
+            if (tok > INT32_MAX) return LA_ERR_INVALID_ARG;
+            off.push_back(int32_t(tok));
+        } else {
+            seed = -2 - n_ext;
+            ++n_ext;
+        }
+        for (int32_t i = 0; i < branch_count[r]; ++i, ++b) {
+            if (branch_len[b] < 1) return LA_ERR_INVALID_ARG;
+            par.push_back(seed);
+            tok += branch_len[b];
+            if (tok > INT32_MAX) return LA_ERR_INVALID_ARG;
+            off.push_back(int32_t(tok));
+        }
+    }
+    const int32_t n_seg = int32_t(par.size());
+    la_pass_info inf;
+    la_status st = plan_impl(n_seg, off.data(), par.data(), chunk, block_chunks, view_ordinal,
+                             plan, &inf);
+    if (st != LA_OK) return st;
+    inf.n_requests = n_requests;
+    if (seg_offsets) std::memcpy(seg_offsets, off.data(), sizeof(int32_t) * off.size());
+    if (branch_parent && n_seg > 0) std::memcpy(branch_parent, par.data(), sizeof(int32_t) * par.size());
+    *info = inf;
+    return LA_OK;
+}
+
+extern "C" const char* la_status_string(la_status status) {
+    switch (status) {
+        case LA_OK: return "ok";
+        case LA_ERR_INVALID_ARG: return "invalid argument";
+        case LA_ERR_UNSUPPORTED: return "unsupported dtype, head dim or chunk size";
+        case LA_ERR_WORKSPACE: return "workspace missing or too small";
+        case LA_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}

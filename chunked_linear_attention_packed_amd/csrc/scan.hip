@@ -1,0 +1,817 @@
+// Packed chunked causal linear-attention scan for gfx950 (MI355X).
+//
+// Source: "Serving 0.88M TPS from Two RTXs and Mac Minis", section "Kernels":
+// linear attention is evaluated in 64-token chunks with a few 64x64 matrix
+// products each (paragraph "Tensor cores for linear attention"), and one scan
+// covers every view of a pass in three launches (paragraph "One scan per
+// pass"); branches of all requests share the packed pass (paragraph "Shared
+// branch passes") and start from their view's state (section "Long
+// Requests").  Per head, with an fp32 state S of shape d x d:
+//     S_t = S_{t-1} + k_t^T v_t,   o_t = q_t S_t.
+// Chunked over a block of chunks c with S_in the state before the chunk:
+//     O_c = Q_c S_in + tril(Q_c K_c^T) V_c,   S_in(next) = S_in + K_c^T V_c.
+//
+// The three launches:
+//   delta_kernel   one workgroup per (delta block, head): sum over the block's
+//                  chunks of K_c^T V_c, written to a workspace slot
+//   prefix_kernel  one thread per (scanned segment, head, state element):
+//                  inclusive prefix over the segment's slots, in place; the
+//                  total of a view goes to final_state
+//   output_kernel  one workgroup per (work block, head): chunk by chunk,
+//                  O^T = S^T Q^T + V^T P^T with P = tril(Q K^T), carrying S in
+//                  registers across the block's chunks
+//
+// MFMA use (v_mfma_f32_16x16x32_bf16 for bf16, v_mfma_f32_16x16x4_f32 for
+// fp32).  Accumulator layout of a 16x16 tile: lane l = 16 g + c holds rows
+// 4 g + j (j = 0..3) of column c.  An A operand gives each lane one row
+// (l % 16), a B operand one column (l % 16); the lane's group g = l / 16 and
+// element index select k-slots.  The contraction sums over all k-slots, so
+// any bijection from (g, element) to the contracted index is valid as long as
+// A and B use the same one.  That freedom lets accumulator registers feed the
+// next product directly: a tile's 4 rows 4g + j become the k-slots of lane
+// group g, two row-tiles making the 8 bf16 elements of one K=32 step.
+//
+// Register ownership inside a workgroup of 4 waves: wave w owns d_v blocks
+// w*VBW .. w*VBW+VBW-1 (16 columns each, VBW = d/64) of S for all d_k, and
+// computes the matching rows of O^T for all 64 tokens of a chunk.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "linattn.h"
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kThreads = 256;   // 4 waves of 64
+constexpr int kChunk = LA_CHUNK;
+
+__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// fp32 -> bf16 bits, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint32_t f2bf(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
+    return f2bf(lo) | (f2bf(hi) << 16);
+}
+__device__ __forceinline__ float bf2f(uint32_t h) { return __uint_as_float(h << 16); }
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// Workspace slot layout: element e of a d x d state is stored at
+//   e = ((vb * NKB + kb) * 4 + j) * 64 + lane,   lane = 16 g + c
+// holding S[kb*16 + 4g + j][vb*16 + c]: one coalesced 256-byte row per
+// (tile, j) for the lane order of the accumulator layout.
+template <int D>
+__device__ __forceinline__ void slot_to_rc(int e, int& row, int& col) {
+    constexpr int NKB = D / 16;
+    const int lane = e & 63;
+    const int j = (e >> 6) & 3;
+    const int kb = (e >> 8) % NKB;
+    const int vb = (e >> 8) / NKB;
+    row = kb * 16 + 4 * (lane >> 4) + j;
+    col = vb * 16 + (lane & 15);
+}
+
+// ---------------------------------------------------------------------------
+// bf16 tile staging.  A 64 x D tile is cut into 8x8 blocks; one lane loads a
+// block as 8 row pieces of 16 bytes (8 consecutive lanes cover one 128-byte
+// row piece, so every load instruction reads whole cache lines), then writes
+// it to LDS row-major and/or transposed (the transpose is done in registers).
+// ---------------------------------------------------------------------------
+template <int D>
+struct Bf16Tiles {
+    static constexpr int NCG = D / 8;           // 8-column groups per row
+    static constexpr int NBLK = 8 * NCG;        // 8x8 blocks per tile
+    static constexpr int LDR = D + 8;           // row-major stride (elements)
+    static constexpr int LDT = kChunk + 8;      // transposed stride (elements)
+};
+
+struct Block8 {
+    u32x4 r[8];  // r[i] = row i of the 8x8 block, 8 bf16
+};
+
+__device__ __forceinline__ void load_block8(Block8& b, const uint16_t* __restrict__ base,
+                                            int64_t tok0, int rows, int rg, int cg, int H,
+                                            int h, int D) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int row = rg * 8 + i;
+        if (row < rows) {
+            const uint16_t* p = base + ((tok0 + row) * H + h) * (int64_t)D + cg * 8;
+            b.r[i] = *reinterpret_cast<const u32x4*>(p);
+        } else {
+            b.r[i] = u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+}
+
+// Row-major store: dst[(rg*8+i)*ld + cg*8 .. +7] = row i.
+__device__ __forceinline__ void store_rows(uint16_t* dst, const Block8& b, int rg, int cg,
+                                           int ld) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        *reinterpret_cast<u32x4*>(dst + (rg * 8 + i) * ld + cg * 8) = b.r[i];
+}
+
+// Transposed store: dst[(cg*8+c)*ld + rg*8 .. +7] = column c of the block.
+__device__ __forceinline__ void store_cols(uint16_t* dst, const Block8& b, int rg, int cg,
+                                           int ld) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {       // columns 2m and 2m+1 live in dword m
+        u32x4 ev, od;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const uint32_t a = b.r[2 * jj][m];
+            const uint32_t c = b.r[2 * jj + 1][m];
+            ev[jj] = (a & 0xffffu) | (c << 16);
+            od[jj] = (a >> 16) | (c & 0xffff0000u);
+        }
+        *reinterpret_cast<u32x4*>(dst + (cg * 8 + 2 * m) * ld + rg * 8) = ev;
+        *reinterpret_cast<u32x4*>(dst + (cg * 8 + 2 * m + 1) * ld + rg * 8) = od;
+    }
+}
+
+__device__ __forceinline__ u32x2 lds_u32x2(const uint16_t* p) {
+    return *reinterpret_cast<const u32x2*>(p);
+}
+__device__ __forceinline__ u32x4 lds_u32x4(const uint16_t* p) {
+    return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ u32x4 cat2(u32x2 a, u32x2 b) { return u32x4{a[0], a[1], b[0], b[1]}; }
+
+// ---------------------------------------------------------------------------
+// Plan descriptors (see linattn.h).
+// ---------------------------------------------------------------------------
+struct BlockDesc {
+    int tok0, ntok, sin_slot, delta_slot, seed, seg, pad0, pad1;
+};
+struct DeltaDesc {
+    int tok0, ntok, slot, seg;
+};
+struct ScanDesc {
+    int first_slot, n_slots, final_row, seg;
+};
+
+// ===========================================================================
+// Launch 1: per delta block and head, sum over chunks of K_c^T V_c.
+// ===========================================================================
+template <int D>
+__global__ __launch_bounds__(kThreads) void delta_kernel_bf16(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const DeltaDesc* __restrict__ deltas, float* __restrict__ ws, int H) {
+    using TL = Bf16Tiles<D>;
+    constexpr int NKB = D / 16, VBW = D / 64, DD = D * D;
+    __shared__ __attribute__((aligned(16))) uint16_t sKt[D * TL::LDT];
+    __shared__ __attribute__((aligned(16))) uint16_t sVt[D * TL::LDT];
+
+    const int h = blockIdx.x % H;
+    const DeltaDesc dd = deltas[blockIdx.x / H];
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+
+    f32x4 S[VBW][NKB];
+#pragma unroll
+    for (int x = 0; x < VBW; ++x)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) S[x][kb] = zero4();
+
+    // Staging: blocks [0, NBLK) of K then [NBLK, 2 NBLK) of V; 2 NBLK <= 256.
+    const bool loader = tid < 2 * TL::NBLK;
+    const bool is_v = tid >= TL::NBLK;
+    const int within = is_v ? tid - TL::NBLK : tid;
+    const int rg = within / TL::NCG, cg = within % TL::NCG;
+    const uint16_t* src = is_v ? v : k;
+
+    const int nch = (dd.ntok + kChunk - 1) / kChunk;
+    Block8 pre;
+    if (loader) load_block8(pre, src, dd.tok0, min(kChunk, dd.ntok), rg, cg, H, h, D);
+    for (int c = 0; c < nch; ++c) {
+        if (loader) store_cols(is_v ? sVt : sKt, pre, rg, cg, TL::LDT);
+        __syncthreads();
+        if (c + 1 < nch && loader)
+            load_block8(pre, src, (int64_t)dd.tok0 + (c + 1) * kChunk,
+                        min(kChunk, dd.ntok - (c + 1) * kChunk), rg, cg, H, h, D);
+#pragma unroll
+        for (int ks = 0; ks < kChunk / 32; ++ks) {
+#pragma unroll
+            for (int x = 0; x < VBW; ++x) {
+                const int vb = w * VBW + x;
+                const u32x4 bv = lds_u32x4(sVt + (vb * 16 + c16) * TL::LDT + ks * 32 + 8 * g);
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) {
+                    const u32x4 ak = lds_u32x4(sKt + (kb * 16 + c16) * TL::LDT + ks * 32 + 8 * g);
+                    S[x][kb] = mfma_bf16(ak, bv, S[x][kb]);
+                }
+            }
+        }
+        __syncthreads();
+    }
+    float* dst = ws + ((int64_t)dd.slot * H + h) * DD;
+#pragma unroll
+    for (int x = 0; x < VBW; ++x)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                dst[(((w * VBW + x) * NKB + kb) * 4 + j) * 64 + lane] = S[x][kb][j];
+}
+
+// fp32 tiles: row-major [64][D+4] floats in LDS, loaded as 16-byte pieces.
+template <int D>
+struct F32Tiles {
+    static constexpr int LD = D + 4;
+    static constexpr int PIECES = kChunk * D / 4;      // 16-byte pieces per tile
+    static constexpr int PER = PIECES / kThreads;       // per thread per tile
+};
+
+template <int D>
+__device__ __forceinline__ void load_f32_tile(f32x4* regs, const float* __restrict__ base,
+                                              int64_t tok0, int rows, int H, int h) {
+    using TL = F32Tiles<D>;
+    constexpr int PPR = D / 4;   // pieces per row
+#pragma unroll
+    for (int i = 0; i < TL::PER; ++i) {
+        const int p = threadIdx.x + i * kThreads;
+        const int row = p / PPR, col = (p % PPR) * 4;
+        if (row < rows)
+            regs[i] = *reinterpret_cast<const f32x4*>(base + ((tok0 + row) * H + h) * (int64_t)D + col);
+        else
+            regs[i] = zero4();
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void store_f32_tile(float* dst, const f32x4* regs) {
+    using TL = F32Tiles<D>;
+    constexpr int PPR = D / 4;
+#pragma unroll
+    for (int i = 0; i < TL::PER; ++i) {
+        const int p = threadIdx.x + i * kThreads;
+        const int row = p / PPR, col = (p % PPR) * 4;
+        *reinterpret_cast<f32x4*>(dst + row * TL::LD + col) = regs[i];
+    }
+}
+
+// S[x][kb] += K^T V over one chunk, fp32 operands from row-major tiles.
+template <int D>
+__device__ __forceinline__ void f32_state_update(f32x4 (&S)[D / 64][D / 16], const float* sK,
+                                                 const float* sV, int w, int g, int c16) {
+    using TL = F32Tiles<D>;
+    constexpr int NKB = D / 16, VBW = D / 64;
+#pragma unroll 4
+    for (int ks = 0; ks < kChunk / 4; ++ks) {
+        const int u = ks * 4 + g;
+#pragma unroll
+        for (int x = 0; x < VBW; ++x) {
+            const float bv = sV[u * TL::LD + (w * VBW + x) * 16 + c16];
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+                S[x][kb] = mfma_f32(sK[u * TL::LD + kb * 16 + c16], bv, S[x][kb]);
+        }
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void delta_kernel_f32(
+    const float* __restrict__ k, const float* __restrict__ v,
+    const DeltaDesc* __restrict__ deltas, float* __restrict__ ws, int H) {
+    using TL = F32Tiles<D>;
+    constexpr int NKB = D / 16, VBW = D / 64, DD = D * D;
+    __shared__ __attribute__((aligned(16))) float sK[kChunk * TL::LD];
+    __shared__ __attribute__((aligned(16))) float sV[kChunk * TL::LD];
+
+    const int h = blockIdx.x % H;
+    const DeltaDesc dd = deltas[blockIdx.x / H];
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+
+    f32x4 S[VBW][NKB];
+#pragma unroll
+    for (int x = 0; x < VBW; ++x)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) S[x][kb] = zero4();
+
+    const int nch = (dd.ntok + kChunk - 1) / kChunk;
+    f32x4 pk[TL::PER], pv[TL::PER];
+    load_f32_tile<D>(pk, k, dd.tok0, min(kChunk, dd.ntok), H, h);
+    load_f32_tile<D>(pv, v, dd.tok0, min(kChunk, dd.ntok), H, h);
+    for (int c = 0; c < nch; ++c) {
+        store_f32_tile<D>(sK, pk);
+        store_f32_tile<D>(sV, pv);
+        __syncthreads();
+        if (c + 1 < nch) {
+            const int64_t t0 = (int64_t)dd.tok0 + (c + 1) * kChunk;
+            const int rows = min(kChunk, dd.ntok - (c + 1) * kChunk);
+            load_f32_tile<D>(pk, k, t0, rows, H, h);
+            load_f32_tile<D>(pv, v, t0, rows, H, h);
+        }
+        f32_state_update<D>(S, sK, sV, w, g, c16);
+        __syncthreads();
+    }
+    float* dst = ws + ((int64_t)dd.slot * H + h) * DD;
+#pragma unroll
+    for (int x = 0; x < VBW; ++x)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                dst[(((w * VBW + x) * NKB + kb) * 4 + j) * 64 + lane] = S[x][kb][j];
+}
+
+// ===========================================================================
+// Launch 2: segmented inclusive prefix over each scanned segment's slots.
+// Thread = one state element of one (segment, head).  Slot j >= 1 is
+// rewritten with the sum of slots 0..j (a view skips its last slot, whose
+// sum is the view's final state and goes to final_state instead).
+// ===========================================================================
+template <int D>
+__global__ __launch_bounds__(kThreads) void prefix_kernel(const ScanDesc* __restrict__ scans,
+                                                          float* __restrict__ ws,
+                                                          float* __restrict__ final_state,
+                                                          int H) {
+    constexpr int DD = D * D, WPS = DD / kThreads;
+    const int per_seg = H * WPS;
+    const ScanDesc sd = scans[blockIdx.x / per_seg];
+    const int rem = blockIdx.x % per_seg;
+    const int h = rem / WPS;
+    const int e = (rem % WPS) * kThreads + threadIdx.x;
+    const int64_t stride = (int64_t)H * DD;
+    float* p = ws + ((int64_t)sd.first_slot * H + h) * DD + e;
+    const int n = sd.n_slots;
+    const int last_store = sd.final_row >= 0 ? n - 1 : n;   // exclusive bound
+    float acc = 0.f;
+    constexpr int B = 8;
+    for (int j0 = 0; j0 < n; j0 += B) {
+        float x[B];
+#pragma unroll
+        for (int i = 0; i < B; ++i) x[i] = (j0 + i < n) ? p[(j0 + i) * stride] : 0.f;
+#pragma unroll
+        for (int i = 0; i < B; ++i) {
+            const int j = j0 + i;
+            acc += x[i];
+            if (j >= 1 && j < last_store) p[j * stride] = acc;
+        }
+    }
+    if (sd.final_row >= 0) {
+        int row, col;
+        slot_to_rc<D>(e, row, col);
+        final_state[(((int64_t)sd.final_row * H + h) * D + row) * D + col] = acc;
+    }
+}
+
+// ===========================================================================
+// Launch 3: outputs.  Per work block and head, chunk by chunk.
+// ===========================================================================
+
+// Initial state of a block: seed (zero, a view's final state, or an external
+// state) plus the segment-local prefix of the earlier blocks.
+template <int D>
+__device__ __forceinline__ void init_state(f32x4 (&S)[D / 64][D / 16], const BlockDesc& bd,
+                                           const float* __restrict__ ws,
+                                           const float* __restrict__ final_state,
+                                           const float* __restrict__ ext_state, int H, int h,
+                                           int w, int lane) {
+    constexpr int NKB = D / 16, VBW = D / 64, DD = D * D;
+    const int g = lane >> 4, c16 = lane & 15;
+#pragma unroll
+    for (int x = 0; x < VBW; ++x)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) S[x][kb] = zero4();
+    const float* seed = nullptr;
+    if (bd.seed >= 0)
+        seed = final_state + ((int64_t)bd.seed * H + h) * DD;
+    else if (bd.seed <= -2)
+        seed = ext_state + ((int64_t)(-bd.seed - 2) * H + h) * DD;
+    if (seed) {
+#pragma unroll
+        for (int x = 0; x < VBW; ++x)
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    S[x][kb][j] = seed[(kb * 16 + 4 * g + j) * D + (w * VBW + x) * 16 + c16];
+    }
+    if (bd.sin_slot >= 0) {
+        const float* src = ws + ((int64_t)bd.sin_slot * H + h) * DD;
+#pragma unroll
+        for (int x = 0; x < VBW; ++x)
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    S[x][kb][j] += src[(((w * VBW + x) * NKB + kb) * 4 + j) * 64 + lane];
+    }
+}
+
+// Global -> registers for one chunk of q, k and v (block b = tid + i*256 over
+// the concatenated [Q | K | V] block lists; each tile is handled by whole
+// waves, so the tile choice is wave-uniform).
+template <int D, int NPER>
+__device__ __forceinline__ void issue_qkv_bf16(Block8 (&pre)[NPER], const uint16_t* __restrict__ q,
+                                               const uint16_t* __restrict__ k,
+                                               const uint16_t* __restrict__ v, int64_t t0,
+                                               int rows, int H, int h) {
+    using TL = Bf16Tiles<D>;
+#pragma unroll
+    for (int i = 0; i < NPER; ++i) {
+        const int b = threadIdx.x + i * kThreads;
+        if (b < 3 * TL::NBLK) {
+            const int tile = b / TL::NBLK, within = b % TL::NBLK;
+            const uint16_t* src = tile == 0 ? q : (tile == 1 ? k : v);
+            load_block8(pre[i], src, t0, rows, within / TL::NCG, within % TL::NCG, H, h, D);
+        }
+    }
+}
+
+// Registers -> LDS: Q row-major, K row-major and transposed, V transposed.
+template <int D, int NPER>
+__device__ __forceinline__ void stage_qkv_bf16(const Block8 (&pre)[NPER], uint16_t* sQ,
+                                               uint16_t* sK, uint16_t* sKt, uint16_t* sVt) {
+    using TL = Bf16Tiles<D>;
+#pragma unroll
+    for (int i = 0; i < NPER; ++i) {
+        const int b = threadIdx.x + i * kThreads;
+        if (b < 3 * TL::NBLK) {
+            const int tile = b / TL::NBLK, within = b % TL::NBLK;
+            const int rg = within / TL::NCG, cg = within % TL::NCG;
+            if (tile == 0) {
+                store_rows(sQ, pre[i], rg, cg, TL::LDR);
+            } else if (tile == 1) {
+                store_rows(sK, pre[i], rg, cg, TL::LDR);
+                store_cols(sKt, pre[i], rg, cg, TL::LDT);
+            } else {
+                store_cols(sVt, pre[i], rg, cg, TL::LDT);
+            }
+        }
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void output_kernel_bf16(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const BlockDesc* __restrict__ blocks,
+    const float* __restrict__ ws, const float* __restrict__ final_state,
+    const float* __restrict__ ext_state, uint16_t* __restrict__ out, int H) {
+    using TL = Bf16Tiles<D>;
+    constexpr int NKB = D / 16, VBW = D / 64, NKS = D / 32;
+    constexpr int NPER = (3 * TL::NBLK + kThreads - 1) / kThreads;
+    __shared__ __attribute__((aligned(16))) uint16_t sQ[kChunk * TL::LDR];
+    __shared__ __attribute__((aligned(16))) uint16_t sK[kChunk * TL::LDR];
+    __shared__ __attribute__((aligned(16))) uint16_t sKt[D * TL::LDT];
+    __shared__ __attribute__((aligned(16))) uint16_t sVt[D * TL::LDT];
+
+    const int h = blockIdx.x % H;
+    const BlockDesc bd = blocks[blockIdx.x / H];
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+
+    f32x4 S[VBW][NKB];
+    init_state<D>(S, bd, ws, final_state, ext_state, H, h, w, lane);
+
+    // Staging assignment: block index b = tid + i*256 over [Q | K | V].
+    Block8 pre[NPER];
+    const int nch = (bd.ntok + kChunk - 1) / kChunk;
+    issue_qkv_bf16<D, NPER>(pre, q, k, v, bd.tok0, min(kChunk, bd.ntok), H, h);
+    for (int c = 0; c < nch; ++c) {
+        stage_qkv_bf16<D, NPER>(pre, sQ, sK, sKt, sVt);
+        __syncthreads();
+        if (c + 1 < nch)
+            issue_qkv_bf16<D, NPER>(pre, q, k, v, (int64_t)bd.tok0 + (c + 1) * kChunk,
+                                    min(kChunk, bd.ntok - (c + 1) * kChunk), H, h);
+        const int rows = min(kChunk, bd.ntok - c * kChunk);
+        const int64_t t0 = (int64_t)bd.tok0 + c * kChunk;
+
+        // hi/lo bf16 split of S as A operands of O^T += S^T Q^T:
+        // k-slots (g, i) -> d_k = kb_{i/4}*16 + 4g + i%4 for the pair
+        // (kb0, kb1) = (2kp, 2kp+1).
+        u32x4 Shi[VBW][NKB / 2], Slo[VBW][NKB / 2];
+#pragma unroll
+        for (int x = 0; x < VBW; ++x)
+#pragma unroll
+            for (int kp = 0; kp < NKB / 2; ++kp) {
+                float s[8];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    s[j] = S[x][2 * kp][j];
+                    s[4 + j] = S[x][2 * kp + 1][j];
+                }
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const uint32_t h0 = f2bf(s[2 * m]), h1 = f2bf(s[2 * m + 1]);
+                    Shi[x][kp][m] = h0 | (h1 << 16);
+                    Slo[x][kp][m] = pack_bf2(s[2 * m] - bf2f(h0), s[2 * m + 1] - bf2f(h1));
+                }
+            }
+
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+            // P^T tiles (ub, tb) for ub <= tb: P^T[u][t] = sum_d K[u][d] Q[t][d].
+            u32x4 qf[NKS];
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+                qf[ks] = lds_u32x4(sQ + (tb * 16 + c16) * TL::LDR + ks * 32 + 8 * g);
+            u32x2 pb[4];
+#pragma unroll
+            for (int ub = 0; ub < 4; ++ub) {
+                if (ub > tb) {
+                    pb[ub] = u32x2{0u, 0u};
+                    continue;
+                }
+                f32x4 p = zero4();
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks)
+                    p = mfma_bf16(lds_u32x4(sK + (ub * 16 + c16) * TL::LDR + ks * 32 + 8 * g),
+                                  qf[ks], p);
+                if (ub == tb) {   // causal mask inside the diagonal tile: u <= t
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        if (4 * g + j > c16) p[j] = 0.f;
+                }
+                pb[ub] = u32x2{pack_bf2(p[0], p[1]), pack_bf2(p[2], p[3])};
+            }
+            const int trow = tb * 16 + c16;
+#pragma unroll
+            for (int x = 0; x < VBW; ++x) {
+                const int vb = w * VBW + x;
+                f32x4 acc = zero4();
+                // inter-chunk: O^T += S^T Q^T
+#pragma unroll
+                for (int kp = 0; kp < NKB / 2; ++kp) {
+                    const u32x4 bq = cat2(lds_u32x2(sQ + trow * TL::LDR + (2 * kp) * 16 + 4 * g),
+                                          lds_u32x2(sQ + trow * TL::LDR + (2 * kp + 1) * 16 + 4 * g));
+                    acc = mfma_bf16(Shi[x][kp], bq, acc);
+                    acc = mfma_bf16(Slo[x][kp], bq, acc);
+                }
+                // intra-chunk: O^T += V^T P^T, k-slots (g, i) -> u = ub_{i/4}*16 + 4g + i%4
+#pragma unroll
+                for (int pp = 0; pp < 2; ++pp) {
+                    if (2 * pp > tb) continue;
+                    const uint16_t* vr = sVt + (vb * 16 + c16) * TL::LDT;
+                    const u32x4 av = cat2(lds_u32x2(vr + (2 * pp) * 16 + 4 * g),
+                                          lds_u32x2(vr + (2 * pp + 1) * 16 + 4 * g));
+                    acc = mfma_bf16(av, cat2(pb[2 * pp], pb[2 * pp + 1]), acc);
+                }
+                // lane holds O^T[vb*16 + 4g + j][t = tb*16 + c16]
+                if (trow < rows) {
+                    uint16_t* o = out + ((t0 + trow) * H + h) * (int64_t)D + vb * 16 + 4 * g;
+                    *reinterpret_cast<u32x2*>(o) =
+                        u32x2{pack_bf2(acc[0], acc[1]), pack_bf2(acc[2], acc[3])};
+                }
+            }
+        }
+        // carry: S += K^T V (not needed after the block's last chunk)
+        if (c + 1 < nch) {
+#pragma unroll
+            for (int ks = 0; ks < kChunk / 32; ++ks)
+#pragma unroll
+                for (int x = 0; x < VBW; ++x) {
+                    const int vb = w * VBW + x;
+                    const u32x4 bv = lds_u32x4(sVt + (vb * 16 + c16) * TL::LDT + ks * 32 + 8 * g);
+#pragma unroll
+                    for (int kb = 0; kb < NKB; ++kb)
+                        S[x][kb] = mfma_bf16(
+                            lds_u32x4(sKt + (kb * 16 + c16) * TL::LDT + ks * 32 + 8 * g), bv,
+                            S[x][kb]);
+                }
+        }
+        __syncthreads();
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void output_kernel_f32(
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+    const BlockDesc* __restrict__ blocks, const float* __restrict__ ws,
+    const float* __restrict__ final_state, const float* __restrict__ ext_state,
+    float* __restrict__ out, int H) {
+    using TL = F32Tiles<D>;
+    constexpr int NKB = D / 16, VBW = D / 64;
+    __shared__ __attribute__((aligned(16))) float sQ[kChunk * TL::LD];
+    __shared__ __attribute__((aligned(16))) float sK[kChunk * TL::LD];
+    __shared__ __attribute__((aligned(16))) float sV[kChunk * TL::LD];
+
+    const int h = blockIdx.x % H;
+    const BlockDesc bd = blocks[blockIdx.x / H];
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+
+    f32x4 S[VBW][NKB];
+    init_state<D>(S, bd, ws, final_state, ext_state, H, h, w, lane);
+
+    const int nch = (bd.ntok + kChunk - 1) / kChunk;
+    f32x4 pq[TL::PER], pk[TL::PER], pv[TL::PER];
+    {
+        const int rows = min(kChunk, bd.ntok);
+        load_f32_tile<D>(pq, q, bd.tok0, rows, H, h);
+        load_f32_tile<D>(pk, k, bd.tok0, rows, H, h);
+        load_f32_tile<D>(pv, v, bd.tok0, rows, H, h);
+    }
+    for (int c = 0; c < nch; ++c) {
+        store_f32_tile<D>(sQ, pq);
+        store_f32_tile<D>(sK, pk);
+        store_f32_tile<D>(sV, pv);
+        __syncthreads();
+        if (c + 1 < nch) {
+            const int64_t tn = (int64_t)bd.tok0 + (c + 1) * kChunk;
+            const int rn = min(kChunk, bd.ntok - (c + 1) * kChunk);
+            load_f32_tile<D>(pq, q, tn, rn, H, h);
+            load_f32_tile<D>(pk, k, tn, rn, H, h);
+            load_f32_tile<D>(pv, v, tn, rn, H, h);
+        }
+        const int rows = min(kChunk, bd.ntok - c * kChunk);
+        const int64_t t0 = (int64_t)bd.tok0 + c * kChunk;
+#pragma unroll 1
+        for (int tb = 0; tb < 4; ++tb) {
+            f32x4 p[4];
+#pragma unroll
+            for (int ub = 0; ub < 4; ++ub) {
+                p[ub] = zero4();
+                if (ub > tb) continue;
+#pragma unroll 4
+                for (int ks = 0; ks < D / 4; ++ks)
+                    p[ub] = mfma_f32(sK[(ub * 16 + c16) * TL::LD + ks * 4 + g],
+                                     sQ[(tb * 16 + c16) * TL::LD + ks * 4 + g], p[ub]);
+                if (ub == tb) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        if (4 * g + j > c16) p[ub][j] = 0.f;
+                }
+            }
+            const int trow = tb * 16 + c16;
+#pragma unroll
+            for (int x = 0; x < VBW; ++x) {
+                const int vb = w * VBW + x;
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        acc = mfma_f32(S[x][kb][j], sQ[trow * TL::LD + kb * 16 + 4 * g + j], acc);
+#pragma unroll
+                for (int ub = 0; ub < 4; ++ub) {
+                    if (ub > tb) continue;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        acc = mfma_f32(sV[(ub * 16 + 4 * g + j) * TL::LD + vb * 16 + c16],
+                                       p[ub][j], acc);
+                }
+                if (trow < rows) {
+                    float* o = out + ((t0 + trow) * H + h) * (int64_t)D + vb * 16 + 4 * g;
+                    *reinterpret_cast<f32x4*>(o) = acc;
+                }
+            }
+        }
+        if (c + 1 < nch) f32_state_update<D>(S, sK, sV, w, g, c16);
+        __syncthreads();
+    }
+}
+
+// ===========================================================================
+// View-state export: plain vectorised copy of H*d_k*d_v floats.
+// ===========================================================================
+__global__ __launch_bounds__(kThreads) void copy_kernel(const f32x4* __restrict__ src,
+                                                        f32x4* __restrict__ dst, int64_t n4) {
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i < n4) dst[i] = src[i];
+}
+
+// ---------------------------------------------------------------------------
+// Host side.
+// ---------------------------------------------------------------------------
+bool supported_dims(int32_t d_k, int32_t d_v) {
+    return d_k == d_v && (d_k == 64 || d_k == 128);
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+template <int D>
+la_status launch_all(int32_t stages, const void* q, const void* k, const void* v, la_dtype dtype, int32_t H,
+                     const la_pass_info& info, const int32_t* plan, const float* ext_state,
+                     void* out, float* final_state, float* ws, hipStream_t st) {
+    const int32_t off_blocks = LA_PLAN_HEADER_WORDS;
+    const int32_t off_delta = off_blocks + info.n_blocks * LA_PLAN_BLOCK_WORDS;
+    const int32_t off_scan = off_delta + info.n_delta * LA_PLAN_DELTA_WORDS;
+    const auto* blocks = reinterpret_cast<const BlockDesc*>(plan + off_blocks);
+    const auto* deltas = reinterpret_cast<const DeltaDesc*>(plan + off_delta);
+    const auto* scans = reinterpret_cast<const ScanDesc*>(plan + off_scan);
+    const dim3 blk(kThreads);
+    if ((stages & LA_STAGE_STATES) && info.n_delta > 0) {
+        const dim3 grid(unsigned(int64_t(info.n_delta) * H));
+        if (dtype == LA_BF16)
+            hipLaunchKernelGGL(delta_kernel_bf16<D>, grid, blk, 0, st,
+                               static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+                               deltas, ws, H);
+        else
+            hipLaunchKernelGGL(delta_kernel_f32<D>, grid, blk, 0, st,
+                               static_cast<const float*>(k), static_cast<const float*>(v), deltas,
+                               ws, H);
+        if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
+    }
+    if ((stages & LA_STAGE_PREFIX) && info.n_scan > 0) {
+        const dim3 grid(unsigned(int64_t(info.n_scan) * H * (D * D / kThreads)));
+        hipLaunchKernelGGL(prefix_kernel<D>, grid, blk, 0, st, scans, ws, final_state, H);
+        if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
+    }
+    if ((stages & LA_STAGE_OUTPUT) && info.n_blocks > 0) {
+        const dim3 grid(unsigned(int64_t(info.n_blocks) * H));
+        if (dtype == LA_BF16)
+            hipLaunchKernelGGL(output_kernel_bf16<D>, grid, blk, 0, st,
+                               static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                               static_cast<const uint16_t*>(v), blocks, ws, final_state,
+                               ext_state, static_cast<uint16_t*>(out), H);
+        else
+            hipLaunchKernelGGL(output_kernel_f32<D>, grid, blk, 0, st,
+                               static_cast<const float*>(q), static_cast<const float*>(k),
+                               static_cast<const float*>(v), blocks, ws, final_state, ext_state,
+                               static_cast<float*>(out), H);
+        if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
+    }
+    return LA_OK;
+}
+
+}  // namespace
+
+extern "C" la_status la_scan_workspace_size(const la_pass_info* info, int32_t H, int32_t d_k,
+                                            int32_t d_v, la_dtype dtype, size_t* bytes) {
+    if (!info || !bytes || H < 1 || info->n_delta < 0) return LA_ERR_INVALID_ARG;
+    if (!supported_dims(d_k, d_v) || (dtype != LA_F32 && dtype != LA_BF16))
+        return LA_ERR_UNSUPPORTED;
+    *bytes = size_t(info->n_delta) * size_t(H) * size_t(d_k) * size_t(d_v) * sizeof(float);
+    return LA_OK;
+}
+
+extern "C" la_status la_scan_packed_stages(int32_t stages, const void* q, const void* k,
+                                           const void* v, la_dtype dtype, int32_t H,
+                                           int32_t d_k, int32_t d_v, const la_pass_info* info,
+                                           const int32_t* plan, const float* ext_state,
+                                           int32_t n_ext, void* out, float* final_state,
+                                           void* workspace, size_t workspace_bytes,
+                                           void* stream) {
+    if (!info || stages < 1 || stages > LA_STAGE_ALL) return LA_ERR_INVALID_ARG;
+    if (dtype != LA_F32 && dtype != LA_BF16) return LA_ERR_UNSUPPORTED;
+    if (!supported_dims(d_k, d_v) || info->chunk != LA_CHUNK) return LA_ERR_UNSUPPORTED;
+    if (H < 1 || info->n_tokens < 0 || info->n_blocks < 0 || info->n_delta < 0 ||
+        info->n_scan < 0 || info->n_views < 0 || info->n_ext < 0 || n_ext < 0)
+        return LA_ERR_INVALID_ARG;
+    if (info->n_tokens == 0) return LA_OK;
+    if (int64_t(info->n_tokens) * H * d_k >= (int64_t(1) << 40)) return LA_ERR_INVALID_ARG;
+    if (int64_t(info->n_blocks) * H >= (int64_t(1) << 31) ||
+        int64_t(info->n_delta) * H >= (int64_t(1) << 31) ||
+        int64_t(info->n_scan) * H * (int64_t(d_k) * d_k / kThreads) >= (int64_t(1) << 31))
+        return LA_ERR_INVALID_ARG;
+    if (!q || !k || !v || !out || !plan) return LA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return LA_ERR_INVALID_ARG;
+    if (info->n_views > 0 && !final_state) return LA_ERR_INVALID_ARG;
+    if (info->n_ext > 0 && (!ext_state || n_ext < info->n_ext)) return LA_ERR_INVALID_ARG;
+    size_t need = 0;
+    la_status stw = la_scan_workspace_size(info, H, d_k, d_v, dtype, &need);
+    if (stw != LA_OK) return stw;
+    if (need > 0 && (!workspace || workspace_bytes < need)) return LA_ERR_WORKSPACE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    float* ws = static_cast<float*>(workspace);
+    if (d_k == 64)
+        return launch_all<64>(stages, q, k, v, dtype, H, *info, plan, ext_state, out, final_state, ws, st);
+    return launch_all<128>(stages, q, k, v, dtype, H, *info, plan, ext_state, out, final_state, ws, st);
+}
+
+extern "C" la_status la_scan_packed(const void* q, const void* k, const void* v, la_dtype dtype,
+                                    int32_t H, int32_t d_k, int32_t d_v,
+                                    const la_pass_info* info, const int32_t* plan,
+                                    const float* ext_state, int32_t n_ext, void* out,
+                                    float* final_state, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+    return la_scan_packed_stages(LA_STAGE_ALL, q, k, v, dtype, H, d_k, d_v, info, plan, ext_state,
+                                 n_ext, out, final_state, workspace, workspace_bytes, stream);
+}
+
+extern "C" la_status la_export_view_state(const float* final_state, int32_t view_row,
+                                          int32_t n_views, int32_t H, int32_t d_k, int32_t d_v,
+                                          float* dst, void* stream) {
+    if (!final_state || !dst || H < 1 || n_views < 1 || view_row < 0 || view_row >= n_views)
+        return LA_ERR_INVALID_ARG;
+    if (!supported_dims(d_k, d_v)) return LA_ERR_UNSUPPORTED;
+    if (!aligned16(final_state) || !aligned16(dst)) return LA_ERR_INVALID_ARG;
+    const int64_t n = int64_t(H) * d_k * d_v;
+    const float* src = final_state + int64_t(view_row) * n;
+    if (dst < src + n && src < dst + n) return LA_ERR_INVALID_ARG;
+    const int64_t n4 = n / 4;
+    const unsigned grid = unsigned((n4 + kThreads - 1) / kThreads);
+    hipLaunchKernelGGL(copy_kernel, dim3(grid), dim3(kThreads), 0,
+                       static_cast<hipStream_t>(stream), reinterpret_cast<const f32x4*>(src),
+                       reinterpret_cast<f32x4*>(dst), n4);
+    if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
+    return LA_OK;
+}

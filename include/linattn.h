@@ -1,0 +1,256 @@
+/*
+ * linattn.h -- C ABI of the packed chunked causal linear-attention scan
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes.  The page "Serving 0.88M TPS from Two RTXs and
+ * Mac Minis" describes a scoring pass in which each request is one long view
+ * followed by many short branches; branches attend to their own view but never
+ * to each other (section "The Workload").  Most layers are linear attention,
+ * evaluated in 64-token chunks with a few 64x64 matrix products each, and one
+ * scan covers every view of a pass in three launches (section "Kernels",
+ * paragraphs "Tensor cores for linear attention" and "One scan per pass").
+ * The branches of all requests share one packed forward (paragraph "Shared
+ * branch passes").  A branch shard can start from the view's cached
+ * linear-attention state instead of the view's tokens (section "Long
+ * Requests").  The page writes no equation; this library computes, per head,
+ * the plain unnormalised causal form
+ *
+ *     S_t = S_{t-1} + k_t^T v_t,      o_t = q_t S_t        (fp32 state)
+ *
+ * with S = 0 at the start of each view and S = the final state of the parent
+ * view (or a caller-supplied state) at the start of each branch.
+ *
+ * Conventions common to every call
+ *   - All integers are int32 unless stated.  Tokens are packed segment after
+ *     segment; q, k, v and out are dense, token-major [T][H][d] arrays.
+ *   - "host" pointers are ordinary CPU memory; "device" pointers are HIP device
+ *     memory of the current device.  The caller owns every buffer; the library
+ *     allocates nothing and keeps no state between calls.
+ *   - stream is a hipStream_t passed as void* (NULL = the null stream).
+ *     Device calls only enqueue work and return; results are ready when the
+ *     stream is synchronised.  Calls on different streams may overlap.
+ *   - Every call returns an la_status.  Argument, shape and dtype errors are
+ *     found on the host before anything is enqueued and leave every output
+ *     untouched.  Device-side metadata (the plan) is trusted: build it with
+ *     la_pack_pass or la_plan_segments.  A failed launch returns LA_ERR_HIP;
+ *     an asynchronous device fault surfaces at the caller's next
+ *     synchronisation.
+ */
+#ifndef LINATTN_H
+#define LINATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t la_status;
+enum {
+    LA_OK = 0,
+    LA_ERR_INVALID_ARG = 1,   /* NULL pointer, bad length, bad parent, ... */
+    LA_ERR_UNSUPPORTED = 2,   /* dtype, head dim or chunk size not built   */
+    LA_ERR_WORKSPACE = 3,     /* workspace missing or too small            */
+    LA_ERR_HIP = 4            /* a HIP runtime call or launch failed       */
+};
+
+typedef int32_t la_dtype;
+enum {
+    LA_F32 = 0,               /* fp32 q/k/v/out                            */
+    LA_BF16 = 1               /* bf16 q/k/v/out, fp32 state and accumulate */
+};
+
+/* Chunk size of the scan (tokens per chunk tile).  Section "Kernels" of the
+ * page evaluates linear attention in 64-token chunks; only 64 is built. */
+#define LA_CHUNK 64
+
+/* Magic word at plan[0]. */
+#define LA_PLAN_MAGIC 0x4C41504E
+#define LA_PLAN_HEADER_WORDS 16
+#define LA_PLAN_BLOCK_WORDS 8
+#define LA_PLAN_DELTA_WORDS 4
+#define LA_PLAN_SCAN_WORDS 4
+
+/* Shape summary of one packed pass, filled by la_pack_pass or
+ * la_plan_segments and read by la_scan_workspace_size and la_scan_packed. */
+typedef struct {
+    int32_t n_requests;       /* requests given to la_pack_pass (0 for la_plan_segments) */
+    int32_t n_segments;       /* views + branches                              */
+    int32_t n_views;          /* rows of final_state                           */
+    int32_t n_branches;
+    int32_t n_ext;            /* rows of ext_state the pass reads              */
+    int32_t n_tokens;         /* T                                             */
+    int32_t chunk;            /* C, tokens per chunk (LA_CHUNK)                */
+    int32_t block_chunks;     /* G, chunks per work block                      */
+    int32_t n_chunks;         /* sum over segments of ceil(len / C)            */
+    int32_t n_view_chunks;    /* the same over views only                      */
+    int32_t n_blocks;         /* work blocks (launch 3 runs blocks x H groups) */
+    int32_t n_delta;          /* blocks whose state launch 1 computes          */
+    int32_t n_scan;           /* segments launch 2 scans                       */
+    int32_t plan_words;       /* int32 words of the plan                       */
+    int32_t max_seg_tokens;   /* longest segment                               */
+    int32_t reserved[9];
+} la_pass_info;
+
+/*
+ * la_plan_segments -- build the device work plan of a pass from its segment
+ * table (any segment order whose parents are views).
+ *
+ *   n_segments       number of segments (>= 0)
+ *   seg_offsets      host [n_segments + 1]: token offset of each segment;
+ *                    seg_offsets[0] == 0, strictly increasing (every segment
+ *                    holds >= 1 token), total < 2^31
+ *   branch_parent    host [n_segments]: -1 for a view; for a branch either the
+ *                    segment index of its view (a segment whose parent is -1)
+ *                    or -2 - e to start from row e of ext_state (shard pass,
+ *                    section "Long Requests")
+ *   chunk            tokens per chunk; must be LA_CHUNK
+ *   block_chunks     G >= 1: chunks per work block.  A block is scanned by one
+ *                    workgroup per head carrying the state in registers;
+ *                    larger G means less state traffic, fewer workgroups
+ *   view_ordinal     host [n_segments] or NULL: row of final_state of a view,
+ *                    -1 for a branch
+ *   plan             host [info->plan_words] or NULL: the plan to upload to
+ *                    the device as int32 (layout below)
+ *   info             host, required: filled on success
+ * Call with view_ordinal = plan = NULL to learn info->plan_words first.
+ * Errors: LA_ERR_INVALID_ARG (bad table), LA_ERR_UNSUPPORTED (chunk).
+ *
+ * Plan layout (int32 words):
+ *   [0..15]   header: magic, version 1, n_blocks, n_delta, n_scan, chunk,
+ *             block_chunks, n_tokens, off_blocks, off_delta, off_scan, n_ext,
+ *             n_views, 0, 0, 0
+ *   blocks    n_blocks x 8: {tok0, ntok, sin_slot, delta_slot, seed, seg, 0, 0}
+ *             sin_slot   workspace slot holding the segment-local state before
+ *                        the block, -1 for a segment's first block
+ *             delta_slot slot that launch 1 fills with the block's own
+ *                        sum of k_t^T v_t, -1 if no later block needs it
+ *             seed       -1: start from zero (view); v >= 0: start from
+ *                        final_state row v; <= -2: ext_state row -seed-2
+ *   delta     n_delta x 4: {tok0, ntok, slot, seg}
+ *   scan      n_scan x 4:  {first_slot, n_slots, final_row (-1: branch), seg}
+ * View blocks come first (longest work first), then branch blocks.
+ */
+la_status la_plan_segments(int32_t n_segments, const int32_t* seg_offsets,
+                           const int32_t* branch_parent, int32_t chunk,
+                           int32_t block_chunks, int32_t* view_ordinal,
+                           int32_t* plan, la_pass_info* info);
+
+/*
+ * la_pack_pass -- pack request shapes into segments and build the plan
+ * (section "The Workload": one view, then that request's branches;
+ * paragraph "Shared branch passes": all requests of a pass in one forward).
+ *
+ *   n_requests     >= 0
+ *   view_len       host [n_requests]: view tokens; 0 marks a shard request
+ *                  whose view was scored earlier: its branches start from
+ *                  ext_state row e, e counting shard requests in order
+ *   branch_count   host [n_requests]: branches of each request (>= 0; a
+ *                  request needs a view or at least one branch)
+ *   branch_len     host [sum(branch_count)]: branch lengths (>= 1) in request
+ *                  order
+ *   chunk, block_chunks   as for la_plan_segments
+ *   seg_offsets    host [n_segments + 1] or NULL
+ *   branch_parent  host [n_segments] or NULL
+ *   view_ordinal   host [n_segments] or NULL
+ *   plan           host [plan_words] or NULL
+ *   info           host, required
+ * Segment order: request by request, the view then its branches.  Call with
+ * all outputs NULL to learn the sizes (info->n_segments, info->plan_words).
+ * Errors: LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED.  Outputs are written only
+ * on success.
+ */
+la_status la_pack_pass(int32_t n_requests, const int32_t* view_len,
+                       const int32_t* branch_count, const int32_t* branch_len,
+                       int32_t chunk, int32_t block_chunks, int32_t* seg_offsets,
+                       int32_t* branch_parent, int32_t* view_ordinal,
+                       int32_t* plan, la_pass_info* info);
+
+/*
+ * la_scan_workspace_size -- bytes of device workspace la_scan_packed needs:
+ * one fp32 d_k x d_v state per (delta block, head).
+ * Errors: LA_ERR_INVALID_ARG (NULL), LA_ERR_UNSUPPORTED (shape/dtype).
+ */
+la_status la_scan_workspace_size(const la_pass_info* info, int32_t H, int32_t d_k,
+                                 int32_t d_v, la_dtype dtype, size_t* bytes);
+
+/*
+ * la_scan_packed -- the scan of one packed pass, in three launches on
+ * `stream` (section "Kernels", paragraph "One scan per pass"):
+ *   1. per work block and head, the block's state sum_t k_t^T v_t (MFMA);
+ *   2. per segment, head and state element, the prefix of those block
+ *      states; writes final_state for every view;
+ *   3. per work block and head, chunk by chunk: o = q S_in + (causal
+ *      (q k^T)) v, carrying S in registers; branch blocks start from
+ *      final_state of their view or from ext_state.
+ *
+ *   q, k           device [T][H][d_k], dtype
+ *   v              device [T][H][d_v], dtype
+ *   dtype          LA_F32 or LA_BF16
+ *   H              heads >= 1
+ *   d_k, d_v       head dims; d_k == d_v, 64 or 128
+ *   info           host, from the planner that built `plan`
+ *   plan           device [info->plan_words] int32, a copy of the plan
+ *   ext_state      device [n_ext][H][d_k][d_v] fp32 or NULL when the pass has
+ *                  no shard branches (info->n_ext == 0)
+ *   n_ext          rows of ext_state (>= info->n_ext)
+ *   out            device [T][H][d_v], dtype: fully overwritten
+ *   final_state    device [info->n_views][H][d_k][d_v] fp32, row-major
+ *                  (d_v fastest): fully overwritten; NULL iff n_views == 0
+ *   workspace      device, >= la_scan_workspace_size bytes (NULL if 0)
+ *   stream         hipStream_t as void*
+ * Accumulation is fp32; bf16 outputs are rounded to nearest even.  A pass is
+ * idempotent: it reads only its inputs and overwrites all outputs.  Calls
+ * that share a workspace must be ordered on one stream.
+ */
+la_status la_scan_packed(const void* q, const void* k, const void* v, la_dtype dtype,
+                         int32_t H, int32_t d_k, int32_t d_v, const la_pass_info* info,
+                         const int32_t* plan, const float* ext_state, int32_t n_ext,
+                         void* out, float* final_state, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* Launch selection bits for la_scan_packed_stages. */
+#define LA_STAGE_STATES 1     /* launch 1: per-block states          */
+#define LA_STAGE_PREFIX 2     /* launch 2: segmented prefix          */
+#define LA_STAGE_OUTPUT 4     /* launch 3: chunk outputs             */
+#define LA_STAGE_ALL 7
+
+/*
+ * la_scan_packed_stages -- la_scan_packed restricted to the launches whose
+ * bits are set in `stages` (LA_STAGE_*), with the same arguments and checks.
+ * For profiling one launch in isolation.  Launch 2 rewrites the workspace in
+ * place, so it must follow a launch 1 on the same buffers; launch 3 only
+ * reads the workspace and final_state, so after one complete pass it may be
+ * repeated alone and produces the same out.  la_scan_packed(...) is
+ * la_scan_packed_stages(LA_STAGE_ALL, ...).
+ * Errors: as la_scan_packed, plus LA_ERR_INVALID_ARG for stages outside 1..7.
+ */
+la_status la_scan_packed_stages(int32_t stages, const void* q, const void* k, const void* v,
+                                la_dtype dtype, int32_t H, int32_t d_k, int32_t d_v,
+                                const la_pass_info* info, const int32_t* plan,
+                                const float* ext_state, int32_t n_ext, void* out,
+                                float* final_state, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/*
+ * la_export_view_state -- copy one view's final state, for a branch shard
+ * that starts from the cached view (section "Long Requests").
+ *   final_state  device [n_views][H][d_k][d_v] fp32
+ *   view_row     0 <= view_row < n_views
+ *   dst          device [H][d_k][d_v] fp32 (may be a row of an ext_state
+ *                array); must not overlap the source row
+ * Errors: LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED, LA_ERR_HIP.
+ */
+la_status la_export_view_state(const float* final_state, int32_t view_row,
+                               int32_t n_views, int32_t H, int32_t d_k, int32_t d_v,
+                               float* dst, void* stream);
+
+/* Static text for a status code. */
+const char* la_status_string(la_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LINATTN_H */

@@ -20,11 +20,12 @@ Contents:
   scan.scan_bruteforce   -- O(T^2) tree-masked (QK^T)V; pins the recurrence
   scan.scan_chunked      -- chunked fp64 evaluator; pins chunk-size invariance
   scan.sample_rows       -- closed form for selected tokens (large passes)
+  scan.view_states       -- final states of selected views (large passes)
   metrics.row_rel_err    -- row-normalised max relative error
 """
 from .pack import pack_segments, view_ordinals
-from .scan import scan_recurrence, scan_bruteforce, scan_chunked, sample_rows
+from .scan import scan_recurrence, scan_bruteforce, scan_chunked, sample_rows, view_states
 from .metrics import row_rel_err, state_rel_err
 
 __all__ = ["pack_segments", "view_ordinals", "scan_recurrence", "scan_bruteforce",
-           "scan_chunked", "sample_rows", "row_rel_err", "state_rel_err"]
+           "scan_chunked", "sample_rows", "view_states", "row_rel_err", "state_rel_err"]

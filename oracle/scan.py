@@ -185,12 +185,27 @@ def sample_rows(q, k, v, seg_offsets, branch_parent, rows, heads=None, ext_state
         if p >= 0:
             spans.append((int(seg_offsets[p]), int(seg_offsets[p + 1])))
         qt = _f64(q[int(t)])[heads]                      # [h, dk]
-        acc = np.zeros((len(heads), k.shape[2], v.shape[2]))
-        for (u0, u1) in spans:
-            ku = _f64(k[u0:u1])[:, heads, :]
-            vu = _f64(v[u0:u1])[:, heads, :]
-            acc += np.einsum("uhk,uhv->hkv", ku, vu)
-        if p <= -2:
-            acc += _f64(ext_state[-p - 2])[heads]
-        res[i] = np.einsum("hk,hkv->hv", qt, acc)
+        for hi, h in enumerate(heads):
+            S = np.zeros((k.shape[2], v.shape[2]))
+            for (u0, u1) in spans:
+                S += _f64(k[u0:u1, h]).T @ _f64(v[u0:u1, h])
+            if p <= -2:
+                S += _f64(ext_state[-p - 2, h])
+            res[i, hi] = qt[hi] @ S
+    return res
+
+
+def view_states(k, v, seg_offsets, branch_parent, views, heads=None):
+    """Final state of selected view segments: sum over the view's tokens of
+    k_u^T v_u, float64, [len(views), len(heads), d_k, d_v]."""
+    seg_offsets = np.asarray(seg_offsets)
+    H = k.shape[1]
+    heads = list(range(H)) if heads is None else list(heads)
+    res = np.zeros((len(views), len(heads), k.shape[2], v.shape[2]))
+    for i, s in enumerate(views):
+        if int(branch_parent[s]) != -1:
+            raise ValueError("segment %d is not a view" % s)
+        a, b = int(seg_offsets[s]), int(seg_offsets[s + 1])
+        for hi, h in enumerate(heads):
+            res[i, hi] = _f64(k[a:b, h]).T @ _f64(v[a:b, h])
     return res

@@ -297,3 +297,12 @@ def test_pins_catch_planted_mistakes(kind):
     good = np.asarray(g["out"], dtype=np.float64)
     assert not (np.array_equal(out[:, 0], good)
                 and np.array_equal(fin[:, 0], np.asarray(g["final_state"], dtype=np.float64)))
+
+
+def test_view_states_matches_recurrence():
+    rng = np.random.default_rng(6)
+    _, (so, bp, _), (q, k, v) = _rand_pass(rng, 3, 40, 2, 9, 2, 3, 5)
+    _, fin = oracle.scan_recurrence(q, k, v, so, bp)
+    views = [s for s in range(len(bp)) if bp[s] == -1]
+    st = oracle.view_states(k, v, so, bp, views, heads=[1])
+    assert oracle.state_rel_err(st, fin[:, [1]]) <= 1e-12

@@ -1,0 +1,204 @@
+"""Host-side tests of the C ABI (no GPU needed): the library loads and exports
+every symbol the header declares; la_pack_pass reproduces the oracle's own
+packer bit for bit on every workload; malformed shapes are rejected with the
+documented status before anything is written; the work plan covers every
+token exactly once with consistent state slots."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+import chunked_linear_attention_packed_amd as la
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_symbols():
+    with open(os.path.join(ROOT, "include", "linattn.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"\b(la_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = la.load_library()
+    names = _declared_symbols()
+    assert {"la_pack_pass", "la_plan_segments", "la_scan_workspace_size", "la_scan_packed",
+            "la_export_view_state", "la_status_string"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_pack_matches_oracle_packer(name):
+    vl, bc, bl = synth.shapes(name)
+    plan = la.pack(vl, bc, bl, heads=synth.WORKLOADS[name][1])
+    so, bp, vo = oracle.pack_segments(vl, bc, bl)
+    assert np.array_equal(plan.seg_offsets, so)
+    assert np.array_equal(plan.branch_parent, bp)
+    assert np.array_equal(plan.view_ordinal, vo)
+    info = plan.info
+    assert info.n_tokens == int(so[-1]) and info.n_segments == len(bp)
+    assert info.n_views == int((bp == -1).sum())
+    _check_plan(plan, so, bp, vo)
+
+
+def _check_plan(plan, so, bp, vo):
+    """Every token in exactly one block; blocks never cross segments; slots of
+    a segment are contiguous, the delta list matches the blocks, and the scan
+    list covers views plus branches with >= 2 slots."""
+    info, P = plan.info, plan.plan
+    G, C = info.block_chunks, info.chunk
+    assert P[0] == 0x4C41504E and P[1] == 1
+    assert (P[2], P[3], P[4]) == (info.n_blocks, info.n_delta, info.n_scan)
+    ob, od, osc = P[8], P[9], P[10]
+    blocks = P[ob:ob + 8 * info.n_blocks].reshape(-1, 8)
+    deltas = P[od:od + 4 * info.n_delta].reshape(-1, 4)
+    scans = P[osc:osc + 4 * info.n_scan].reshape(-1, 4)
+    assert osc + 4 * info.n_scan == info.plan_words
+    cover = np.zeros(info.n_tokens, dtype=np.int64)
+    seg_blocks = {}
+    for tok0, ntok, sin, dsl, seed, seg, _, _ in blocks:
+        assert 1 <= ntok <= G * C
+        assert so[seg] <= tok0 and tok0 + ntok <= so[seg + 1]
+        cover[tok0:tok0 + ntok] += 1
+        seg_blocks.setdefault(seg, []).append((tok0, sin, dsl, seed))
+        p = bp[seg]
+        assert seed == (-1 if p == -1 else (vo[p] if p >= 0 else p))
+    assert np.all(cover == 1)
+    dl = {int(r[2]): r for r in deltas}
+    seen_views = 0
+    for seg, bl in seg_blocks.items():
+        bl.sort()
+        first = None
+        for j, (tok0, sin, dsl, seed) in enumerate(bl):
+            assert tok0 == so[seg] + j * G * C
+            if j == 0:
+                assert sin == -1
+            else:
+                assert sin == bl[j - 1][2]
+            if dsl >= 0:
+                first = dsl - j if first is None else first
+                assert dsl == first + j and dl[dsl][0] == tok0
+        if bp[seg] == -1:
+            seen_views += 1
+            assert all(b[2] >= 0 for b in bl)
+        else:
+            assert bl[-1][2] == -1
+    assert seen_views == info.n_views
+    for first, n, frow, seg in scans:
+        if frow >= 0:
+            assert bp[seg] == -1 and vo[seg] == frow
+        else:
+            assert bp[seg] != -1 and n >= 2
+
+
+@pytest.mark.parametrize("G", [1, 2, 3, 8])
+def test_plan_random_structures(G):
+    rng = np.random.default_rng(G)
+    for _ in range(20):
+        R = int(rng.integers(1, 6))
+        vl = rng.integers(0, 700, size=R)
+        bc = rng.integers(0, 5, size=R)
+        bc[vl == 0] = np.maximum(bc[vl == 0], 1)
+        bl = rng.integers(1, 300, size=int(bc.sum()))
+        plan = la.pack(vl, bc, bl, block_chunks=G)
+        so, bp, vo = oracle.pack_segments(vl, bc, bl)
+        assert np.array_equal(plan.seg_offsets, so) and np.array_equal(plan.branch_parent, bp)
+        assert plan.info.n_ext == int((vl == 0).sum())
+        _check_plan(plan, so, bp, vo)
+
+
+def test_plan_segments_any_order():
+    # branches listed before their view; two views
+    so = [0, 5, 9, 109, 110, 250]
+    bp = [2, 2, -1, -1, 3]
+    plan = la.plan_segments(so, bp, block_chunks=1)
+    assert plan.view_ordinal.tolist() == [-1, -1, 0, 1, -1]
+    _check_plan(plan, np.asarray(so), np.asarray(bp), plan.view_ordinal)
+
+
+@pytest.mark.parametrize("vl,bc,bl", [
+    ([3], [1], [0]),            # empty branch
+    ([0], [0], []),             # empty request
+    ([-1], [1], [2]),           # negative view
+    ([3], [-1], []),            # negative count
+    ([2**31 - 10], [1], [20]),  # token count overflows int32
+])
+def test_pack_rejects_bad_shapes(vl, bc, bl):
+    with pytest.raises(la.LinAttnError) as e:
+        la.pack(vl, bc, bl, block_chunks=1)
+    assert e.value.status == la.LA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("so,bp", [
+    ([0, 5, 5], [-1, 0]),       # zero-length segment
+    ([0, 5, 9], [-1, 1]),       # parent is a branch (itself)
+    ([0, 5, 9], [-1, 7]),       # parent out of range
+    ([1, 5, 9], [-1, 0]),       # offsets do not start at 0
+    ([0, 5, 9], [0, -1]),       # view's parent points at a view... segment 0 parent 0 is a view? no: 0 -> itself
+])
+def test_plan_segments_rejects_bad_tables(so, bp):
+    with pytest.raises(la.LinAttnError) as e:
+        la.plan_segments(so, bp, block_chunks=1)
+    assert e.value.status == la.LA_ERR_INVALID_ARG
+
+
+def test_unsupported_chunk_and_dims():
+    lib = la.load_library()
+    info = la.PassInfo()
+    vl = np.array([10], dtype=np.int32)
+    bc = np.array([0], dtype=np.int32)
+    st = lib.la_pack_pass(1, vl.ctypes.data_as(la._I32P), bc.ctypes.data_as(la._I32P), None,
+                          32, 1, None, None, None, None, ctypes.byref(info))
+    assert st == la.LA_ERR_UNSUPPORTED
+    plan = la.pack([10], [0], [], block_chunks=1)
+    n = ctypes.c_size_t()
+    assert lib.la_scan_workspace_size(ctypes.byref(plan.info), 2, 96, 96, la.LA_BF16,
+                                      ctypes.byref(n)) == la.LA_ERR_UNSUPPORTED
+    assert lib.la_scan_workspace_size(ctypes.byref(plan.info), 2, 64, 128, la.LA_BF16,
+                                      ctypes.byref(n)) == la.LA_ERR_UNSUPPORTED
+    assert lib.la_scan_workspace_size(ctypes.byref(plan.info), 2, 64, 64, 7,
+                                      ctypes.byref(n)) == la.LA_ERR_UNSUPPORTED
+    assert lib.la_scan_workspace_size(ctypes.byref(plan.info), 2, 64, 64, la.LA_BF16,
+                                      ctypes.byref(n)) == la.LA_OK
+    assert n.value == plan.info.n_delta * 2 * 64 * 64 * 4
+
+
+def test_scan_rejects_bad_arguments_before_launch():
+    """Host-side validation returns an error without touching the device, so
+    it runs without a GPU: NULL pointers, unsupported shapes, a missing or too
+    small workspace, missing ext_state for a shard pass."""
+    lib = la.load_library()
+    plan = la.pack([100], [2], [10, 20], block_chunks=1)
+    info = plan.info
+    fake = ctypes.c_void_p(4096)   # never dereferenced: every case fails validation first
+    need = ctypes.c_size_t()
+    lib.la_scan_workspace_size(ctypes.byref(info), 2, 64, 64, la.LA_BF16, ctypes.byref(need))
+    args = dict(q=fake, k=fake, v=fake, dtype=la.LA_BF16, H=2, dk=64, dv=64, plan=fake,
+                ext=None, n_ext=0, out=fake, fin=fake, ws=fake, wsb=need.value)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return lib.la_scan_packed(a["q"], a["k"], a["v"], a["dtype"], a["H"], a["dk"], a["dv"],
+                                  ctypes.byref(info), a["plan"], a["ext"], a["n_ext"], a["out"],
+                                  a["fin"], a["ws"], a["wsb"], None)
+    assert call(q=None) == la.LA_ERR_INVALID_ARG
+    assert call(out=None) == la.LA_ERR_INVALID_ARG
+    assert call(fin=None) == la.LA_ERR_INVALID_ARG
+    assert call(plan=None) == la.LA_ERR_INVALID_ARG
+    assert call(H=0) == la.LA_ERR_INVALID_ARG
+    assert call(dk=96, dv=96) == la.LA_ERR_UNSUPPORTED
+    assert call(dtype=5) == la.LA_ERR_UNSUPPORTED
+    assert call(ws=None) == la.LA_ERR_WORKSPACE
+    assert call(wsb=need.value - 1) == la.LA_ERR_WORKSPACE
+    assert call(q=ctypes.c_void_p(4098)) == la.LA_ERR_INVALID_ARG   # misaligned
+    shard = la.pack([0], [2], [10, 20], block_chunks=1)
+    st = lib.la_scan_packed(fake, fake, fake, la.LA_BF16, 2, 64, 64, ctypes.byref(shard.info),
+                            fake, None, 0, fake, None, fake, 1 << 20, None)
+    assert st == la.LA_ERR_INVALID_ARG
+    assert lib.la_export_view_state(fake, 3, 2, 2, 64, 64, fake, None) == la.LA_ERR_INVALID_ARG
+    assert lib.la_export_view_state(fake, 0, 2, 2, 96, 96, fake, None) == la.LA_ERR_UNSUPPORTED
