@@ -45,7 +45,68 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU work of the oracle baseline")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB, --steps times "
+                         "(reference for scaling FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--launch-floor", action="store_true",
+                    help="only time three chained near-empty launches per step")
     return ap.parse_args()
+
+
+def calibrate_copy(mib, steps):
+    """A plain copy kernel of known size (torch elementwise add: reads mib MiB,
+    writes mib MiB per launch), timed with HIP events over `steps` launches
+    rotating over enough buffers (>= 1 GiB) to miss the Infinity Cache.  The
+    same command under rocprofv3 --pmc gives the FETCH_SIZE / WRITE_SIZE
+    readings of a known byte count."""
+    import torch
+    n = mib * 2**20 // 4
+    nbuf = max(2, -(-2**30 // (2 * n * 4)))
+    bufs = [(torch.ones(n, dtype=torch.float32, device="cuda:0"),
+             torch.empty(n, dtype=torch.float32, device="cuda:0")) for _ in range(nbuf)]
+    for a, b in bufs:
+        torch.add(a, 1.0, out=b)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        a, b = bufs[i % nbuf]
+        torch.add(a, 1.0, out=b)      # one elementwise kernel: reads a, writes b
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    print(json.dumps({"calibration": "device copy", "bytes_read_per_launch": n * 4,
+                      "bytes_written_per_launch": n * 4, "launches": steps,
+                      "us_per_launch": us, "GBps": 2 * n * 4 / (us * 1e-6) / 1e9}), flush=True)
+
+
+def launch_floor(steps):
+    """Three dependent launches of the library's smallest kernel (a 64 KiB
+    state export) per step, replayed as a HIP graph: the fixed cost of a
+    three-launch pass with no work in it."""
+    import torch
+    import chunked_linear_attention_packed_amd as la
+    src = torch.zeros((1, 1, 64, 64), dtype=torch.float32, device="cuda:0")
+    dst = torch.zeros((1, 64, 64), dtype=torch.float32, device="cuda:0")
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        la.export_view_state(src, 0, dst, stream=st)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=st):
+        for _ in range(steps):
+            for _ in range(3):
+                la.export_view_state(src, 0, dst, stream=st)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(st):
+        e0.record(st)
+        g.replay()
+        e1.record(st)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "launch floor", "launches_per_step": 3,
+                      "us_per_step": e0.elapsed_time(e1) * 1e3 / steps}), flush=True)
 
 
 def _oracle_task(args):
@@ -120,6 +181,12 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if a.calibrate_copy_mib:
+        calibrate_copy(a.calibrate_copy_mib, a.steps)
+        return
+    if a.launch_floor:
+        launch_floor(a.steps)
+        return
     la.load_library()
     dev = torch.device("cuda:0")
     w = synth.workload(a.workload)

@@ -123,7 +123,7 @@ class PassPlan:
         return self._dev[key]
 
 
-def choose_block_chunks(chunks_per_segment, heads, target_groups=2048, max_g=8):
+def choose_block_chunks(chunks_per_segment, heads, target_groups=512, max_g=8):
     """Chunks per work block: the largest power of two (<= max_g) whose block
     count times `heads` still reaches `target_groups` workgroups; 1 if none.
     Larger blocks carry the state in registers longer (less state traffic);

@@ -31,9 +31,11 @@
 // next product directly: a tile's 4 rows 4g + j become the k-slots of lane
 // group g, two row-tiles making the 8 bf16 elements of one K=32 step.
 //
-// Register ownership inside a workgroup of 4 waves: wave w owns d_v blocks
-// w*VBW .. w*VBW+VBW-1 (16 columns each, VBW = d/64) of S for all d_k, and
-// computes the matching rows of O^T for all 64 tokens of a chunk.
+// Work split inside a workgroup of 4 waves (bf16 path): wave w owns the state
+// columns w*VBW*16 .. (w+1)*VBW*16-1 (VBW = d/64) for the carry S += K^T V,
+// and the 16 tokens w*16 .. w*16+15 of each chunk for the outputs.  Each chunk
+// the waves publish S^T as two bf16 terms (hi + lo) in LDS for the inter-chunk
+// product.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -43,9 +45,13 @@
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;   // 4 waves of 64
 constexpr int kChunk = LA_CHUNK;
@@ -59,19 +65,21 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// fp32 -> bf16 bits, round to nearest even (NaN kept quiet).
-__device__ __forceinline__ uint32_t f2bf(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
+// Two fp32 -> packed bf16 (low half = a), round to nearest even
+// (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t cvt_bf2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2_t));
 }
-__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
-    return f2bf(lo) | (f2bf(hi) << 16);
-}
-__device__ __forceinline__ float bf2f(uint32_t h) { return __uint_as_float(h << 16); }
+__device__ __forceinline__ float bf_lo(uint32_t p) { return __uint_as_float(p << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t p) { return __uint_as_float(p & 0xffff0000u); }
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// Wave index as a wave-uniform (scalar) value, so that branches and buffer
+// resources chosen by it stay scalar.
+__device__ __forceinline__ int wave_id() {
+    return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x)) >> 6;
+}
 
 // Workspace slot layout: element e of a d x d state is stored at
 //   e = ((vb * NKB + kb) * 4 + j) * 64 + lane,   lane = 16 g + c
@@ -89,61 +97,83 @@ __device__ __forceinline__ void slot_to_rc(int e, int& row, int& col) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16 tile staging.  A 64 x D tile is cut into 8x8 blocks; one lane loads a
-// block as 8 row pieces of 16 bytes (8 consecutive lanes cover one 128-byte
-// row piece, so every load instruction reads whole cache lines), then writes
-// it to LDS row-major and/or transposed (the transpose is done in registers).
+// Range-checked chunk windows.  A chunk of `rows` tokens of a [T][H][D]
+// tensor is addressed through a raw buffer resource whose size is
+// rows*H*D*elem bytes from the chunk's first token: a token row r >= rows
+// lies entirely past the end (its offset is at least rows*H*D*elem), so the
+// hardware returns zeros for such loads and drops such stores.  Ragged last
+// chunks need no branches.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rsrc(const void* base, int64_t first_elem,
+                                                             int elem_bytes, int rows, int H,
+                                                             int D) {
+    const char* p = static_cast<const char*>(base) + first_elem * elem_bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p), (short)0,
+                                             rows * H * D * elem_bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ void buf_store8(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x2 x) {
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, x), r, off, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// bf16 tile staging.  A 64 x D tile is cut into 4x8 blocks (4 tokens x 8
+// features); one lane loads a block as 4 row pieces of 16 bytes (8 lanes
+// cover one D*2-byte row, so each load instruction reads whole cache lines)
+// and writes it to LDS row-major and/or transposed.  The transpose is done in
+// registers with v_perm_b32: column c of the block becomes 4 consecutive
+// tokens, one 8-byte LDS store.
 // ---------------------------------------------------------------------------
 template <int D>
-struct Bf16Tiles {
-    static constexpr int NCG = D / 8;           // 8-column groups per row
-    static constexpr int NBLK = 8 * NCG;        // 8x8 blocks per tile
+struct Stage {
+    static constexpr int NCG = D / 8;           // 8-feature groups per row
+    static constexpr int NB = 16 * NCG;         // 4x8 blocks per 64-token tile
     static constexpr int LDR = D + 8;           // row-major stride (elements)
     static constexpr int LDT = kChunk + 8;      // transposed stride (elements)
 };
 
-struct Block8 {
-    u32x4 r[8];  // r[i] = row i of the 8x8 block, 8 bf16
+struct Blk4 {
+    u32x4 r[4];  // r[i] = token i of the block, 8 bf16 features
 };
 
-__device__ __forceinline__ void load_block8(Block8& b, const uint16_t* __restrict__ base,
-                                            int64_t tok0, int rows, int rg, int cg, int H,
-                                            int h, int D) {
+__device__ __forceinline__ void load_blk4(Blk4& b, __amdgpu_buffer_rsrc_t rs, int rg4, int cg,
+                                          int H, int h, int D) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int row = rg * 8 + i;
-        if (row < rows) {
-            const uint16_t* p = base + ((tok0 + row) * H + h) * (int64_t)D + cg * 8;
-            b.r[i] = *reinterpret_cast<const u32x4*>(p);
-        } else {
-            b.r[i] = u32x4{0u, 0u, 0u, 0u};
-        }
-    }
+    for (int i = 0; i < 4; ++i)
+        b.r[i] = buf_load16(rs, uint32_t((((rg4 * 4 + i) * H + h) * D + cg * 8) * 2));
 }
 
-// Row-major store: dst[(rg*8+i)*ld + cg*8 .. +7] = row i.
-__device__ __forceinline__ void store_rows(uint16_t* dst, const Block8& b, int rg, int cg,
-                                           int ld) {
+__device__ __forceinline__ void store_rows4(uint16_t* dst, const Blk4& b, int rg4, int cg,
+                                            int ld) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-        *reinterpret_cast<u32x4*>(dst + (rg * 8 + i) * ld + cg * 8) = b.r[i];
+    for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<u32x4*>(dst + (rg4 * 4 + i) * ld + cg * 8) = b.r[i];
 }
 
-// Transposed store: dst[(cg*8+c)*ld + rg*8 .. +7] = column c of the block.
-__device__ __forceinline__ void store_cols(uint16_t* dst, const Block8& b, int rg, int cg,
-                                           int ld) {
+// Transposed tiles [feature][token] are stored with a swizzle: in feature
+// rows whose bit 4 is set, tokens t and t ^ 32 trade places.  The 8-byte
+// column stores of one instruction then cover all 64 LDS banks (rows 8 apart
+// start on the same or the opposite bank with 16-byte aligned rows), while
+// every read of 4 or 8 consecutive tokens (never crossing a 32-token half)
+// stays contiguous and keeps its alignment.
+__device__ __forceinline__ int tswz(int feature, int token) {
+    return token ^ ((feature & 16) << 1);
+}
+
+// dst[(cg*8 + c) * ld + tswz(cg*8 + c, rg4*4) .. +3] = column c of the block.
+__device__ __forceinline__ void store_cols4(uint16_t* dst, const Blk4& b, int rg4, int cg,
+                                            int ld) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {       // columns 2m and 2m+1 live in dword m
-        u32x4 ev, od;
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            const uint32_t a = b.r[2 * jj][m];
-            const uint32_t c = b.r[2 * jj + 1][m];
-            ev[jj] = (a & 0xffffu) | (c << 16);
-            od[jj] = (a >> 16) | (c & 0xffff0000u);
-        }
-        *reinterpret_cast<u32x4*>(dst + (cg * 8 + 2 * m) * ld + rg * 8) = ev;
-        *reinterpret_cast<u32x4*>(dst + (cg * 8 + 2 * m + 1) * ld + rg * 8) = od;
+    for (int m = 0; m < 4; ++m) {   // features 2m (low halves) and 2m+1 (high halves)
+        const u32x2 ev{__builtin_amdgcn_perm(b.r[1][m], b.r[0][m], 0x05040100u),
+                       __builtin_amdgcn_perm(b.r[3][m], b.r[2][m], 0x05040100u)};
+        const u32x2 od{__builtin_amdgcn_perm(b.r[1][m], b.r[0][m], 0x07060302u),
+                       __builtin_amdgcn_perm(b.r[3][m], b.r[2][m], 0x07060302u)};
+        const int f0 = cg * 8 + 2 * m;   // f0 and f0 + 1 share bit 4
+        *reinterpret_cast<u32x2*>(dst + f0 * ld + tswz(f0, rg4 * 4)) = ev;
+        *reinterpret_cast<u32x2*>(dst + (f0 + 1) * ld + tswz(f0, rg4 * 4)) = od;
     }
 }
 
@@ -154,6 +184,44 @@ __device__ __forceinline__ u32x4 lds_u32x4(const uint16_t* p) {
     return *reinterpret_cast<const u32x4*>(p);
 }
 __device__ __forceinline__ u32x4 cat2(u32x2 a, u32x2 b) { return u32x4{a[0], a[1], b[0], b[1]}; }
+
+// K and V blocks of one chunk: block index b = tid + i*256 over [K | V]
+// (2*NB blocks; each half is a whole number of waves, so the tile choice is
+// wave-uniform).
+template <int D, int NPER>
+__device__ __forceinline__ void load_kv(Blk4 (&pre)[NPER], __amdgpu_buffer_rsrc_t rk,
+                                        __amdgpu_buffer_rsrc_t rv, int H, int h) {
+    using ST = Stage<D>;
+    const int wbase = wave_id() * 64;
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < NPER; ++i) {
+        const bool is_v = wbase + i * kThreads >= ST::NB;   // wave-uniform
+        const int within = wbase + i * kThreads + lane - (is_v ? ST::NB : 0);
+        load_blk4(pre[i], is_v ? rv : rk, within / ST::NCG, within % ST::NCG, H, h, D);
+    }
+}
+
+// Registers -> LDS: K transposed (and row-major if sK is given), V transposed.
+template <int D, int NPER>
+__device__ __forceinline__ void stage_kv(const Blk4 (&pre)[NPER], uint16_t* sK, uint16_t* sKt,
+                                         uint16_t* sVt) {
+    using ST = Stage<D>;
+    const int wbase = wave_id() * 64;
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < NPER; ++i) {
+        const bool is_v = wbase + i * kThreads >= ST::NB;   // wave-uniform
+        const int within = wbase + i * kThreads + lane - (is_v ? ST::NB : 0);
+        const int rg4 = within / ST::NCG, cg = within % ST::NCG;
+        if (is_v) {
+            store_cols4(sVt, pre[i], rg4, cg, ST::LDT);
+        } else {
+            if (sK) store_rows4(sK, pre[i], rg4, cg, ST::LDR);
+            store_cols4(sKt, pre[i], rg4, cg, ST::LDT);
+        }
+    }
+}
 
 // ---------------------------------------------------------------------------
 // Plan descriptors (see linattn.h).
@@ -175,14 +243,15 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void delta_kernel_bf16(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const DeltaDesc* __restrict__ deltas, float* __restrict__ ws, int H) {
-    using TL = Bf16Tiles<D>;
+    using ST = Stage<D>;
     constexpr int NKB = D / 16, VBW = D / 64, DD = D * D;
-    __shared__ __attribute__((aligned(16))) uint16_t sKt[D * TL::LDT];
-    __shared__ __attribute__((aligned(16))) uint16_t sVt[D * TL::LDT];
+    constexpr int NPER = 2 * ST::NB / kThreads;
+    __shared__ __attribute__((aligned(16))) uint16_t sKt[D * ST::LDT];
+    __shared__ __attribute__((aligned(16))) uint16_t sVt[D * ST::LDT];
 
     const int h = blockIdx.x % H;
     const DeltaDesc dd = deltas[blockIdx.x / H];
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+    const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, g = lane >> 4, c16 = lane & 15;
 
     f32x4 S[VBW][NKB];
 #pragma unroll
@@ -190,36 +259,42 @@ __global__ __launch_bounds__(kThreads) void delta_kernel_bf16(
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) S[x][kb] = zero4();
 
-    // Staging: blocks [0, NBLK) of K then [NBLK, 2 NBLK) of V; 2 NBLK <= 256.
-    const bool loader = tid < 2 * TL::NBLK;
-    const bool is_v = tid >= TL::NBLK;
-    const int within = is_v ? tid - TL::NBLK : tid;
-    const int rg = within / TL::NCG, cg = within % TL::NCG;
-    const uint16_t* src = is_v ? v : k;
-
     const int nch = (dd.ntok + kChunk - 1) / kChunk;
-    Block8 pre;
-    if (loader) load_block8(pre, src, dd.tok0, min(kChunk, dd.ntok), rg, cg, H, h, D);
-    for (int c = 0; c < nch; ++c) {
-        if (loader) store_cols(is_v ? sVt : sKt, pre, rg, cg, TL::LDT);
+    const int64_t row_elems = int64_t(H) * D;
+    // two chunks in flight: registers A hold chunk c, B chunk c + 1
+    Blk4 pa[NPER], pb[NPER];
+    auto load = [&](Blk4 (&dst)[NPER], int c) {
+        const int64_t first = (int64_t(dd.tok0) + c * kChunk) * row_elems;
+        const int rows = min(kChunk, dd.ntok - c * kChunk);
+        load_kv<D, NPER>(dst, chunk_rsrc(k, first, 2, rows, H, D),
+                         chunk_rsrc(v, first, 2, rows, H, D), H, h);
+    };
+    auto step = [&](Blk4 (&cur)[NPER], int c) {
+        stage_kv<D, NPER>(cur, nullptr, sKt, sVt);
         __syncthreads();
-        if (c + 1 < nch && loader)
-            load_block8(pre, src, (int64_t)dd.tok0 + (c + 1) * kChunk,
-                        min(kChunk, dd.ntok - (c + 1) * kChunk), rg, cg, H, h, D);
+        if (c + 2 < nch) load(cur, c + 2);
 #pragma unroll
         for (int ks = 0; ks < kChunk / 32; ++ks) {
 #pragma unroll
             for (int x = 0; x < VBW; ++x) {
                 const int vb = w * VBW + x;
-                const u32x4 bv = lds_u32x4(sVt + (vb * 16 + c16) * TL::LDT + ks * 32 + 8 * g);
+                const u32x4 bv = lds_u32x4(sVt + (vb * 16 + c16) * ST::LDT +
+                                           tswz(vb * 16, ks * 32 + 8 * g));
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb) {
-                    const u32x4 ak = lds_u32x4(sKt + (kb * 16 + c16) * TL::LDT + ks * 32 + 8 * g);
+                    const u32x4 ak = lds_u32x4(sKt + (kb * 16 + c16) * ST::LDT +
+                                               tswz(kb * 16, ks * 32 + 8 * g));
                     S[x][kb] = mfma_bf16(ak, bv, S[x][kb]);
                 }
             }
         }
         __syncthreads();
+    };
+    load(pa, 0);
+    if (nch > 1) load(pb, 1);
+    for (int c = 0; c < nch; c += 2) {
+        step(pa, c);
+        if (c + 1 < nch) step(pb, c + 1);
     }
     float* dst = ws + ((int64_t)dd.slot * H + h) * DD;
 #pragma unroll
@@ -297,7 +372,7 @@ __global__ __launch_bounds__(kThreads) void delta_kernel_f32(
 
     const int h = blockIdx.x % H;
     const DeltaDesc dd = deltas[blockIdx.x / H];
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+    const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, g = lane >> 4, c16 = lane & 15;
 
     f32x4 S[VBW][NKB];
 #pragma unroll
@@ -334,10 +409,15 @@ __global__ __launch_bounds__(kThreads) void delta_kernel_f32(
 
 // ===========================================================================
 // Launch 2: segmented inclusive prefix over each scanned segment's slots.
-// Thread = one state element of one (segment, head).  Slot j >= 1 is
-// rewritten with the sum of slots 0..j (a view skips its last slot, whose
-// sum is the view's final state and goes to final_state instead).
+// One thread per state element of one (segment, head); consecutive threads
+// take consecutive elements, so every slot access is a coalesced row.  Up to
+// kPrefixBatch slot loads per thread are in flight at once (one memory round
+// trip for segments of up to that many slots).  Slot j >= 1 is rewritten
+// with the sum of slots 0..j; a view skips its last slot, whose sum is the
+// view's final state and goes to final_state instead.
 // ===========================================================================
+constexpr int kPrefixBatch = 32;
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void prefix_kernel(const ScanDesc* __restrict__ scans,
                                                           float* __restrict__ ws,
@@ -354,13 +434,13 @@ __global__ __launch_bounds__(kThreads) void prefix_kernel(const ScanDesc* __rest
     const int n = sd.n_slots;
     const int last_store = sd.final_row >= 0 ? n - 1 : n;   // exclusive bound
     float acc = 0.f;
-    constexpr int B = 8;
-    for (int j0 = 0; j0 < n; j0 += B) {
-        float x[B];
+    for (int j0 = 0; j0 < n; j0 += kPrefixBatch) {
+        float x[kPrefixBatch];
 #pragma unroll
-        for (int i = 0; i < B; ++i) x[i] = (j0 + i < n) ? p[(j0 + i) * stride] : 0.f;
+        for (int i = 0; i < kPrefixBatch; ++i)
+            x[i] = (j0 + i < n) ? p[(j0 + i) * stride] : 0.f;
 #pragma unroll
-        for (int i = 0; i < B; ++i) {
+        for (int i = 0; i < kPrefixBatch; ++i) {
             const int j = j0 + i;
             acc += x[i];
             if (j >= 1 && j < last_store) p[j * stride] = acc;
@@ -417,48 +497,6 @@ __device__ __forceinline__ void init_state(f32x4 (&S)[D / 64][D / 16], const Blo
     }
 }
 
-// Global -> registers for one chunk of q, k and v (block b = tid + i*256 over
-// the concatenated [Q | K | V] block lists; each tile is handled by whole
-// waves, so the tile choice is wave-uniform).
-template <int D, int NPER>
-__device__ __forceinline__ void issue_qkv_bf16(Block8 (&pre)[NPER], const uint16_t* __restrict__ q,
-                                               const uint16_t* __restrict__ k,
-                                               const uint16_t* __restrict__ v, int64_t t0,
-                                               int rows, int H, int h) {
-    using TL = Bf16Tiles<D>;
-#pragma unroll
-    for (int i = 0; i < NPER; ++i) {
-        const int b = threadIdx.x + i * kThreads;
-        if (b < 3 * TL::NBLK) {
-            const int tile = b / TL::NBLK, within = b % TL::NBLK;
-            const uint16_t* src = tile == 0 ? q : (tile == 1 ? k : v);
-            load_block8(pre[i], src, t0, rows, within / TL::NCG, within % TL::NCG, H, h, D);
-        }
-    }
-}
-
-// Registers -> LDS: Q row-major, K row-major and transposed, V transposed.
-template <int D, int NPER>
-__device__ __forceinline__ void stage_qkv_bf16(const Block8 (&pre)[NPER], uint16_t* sQ,
-                                               uint16_t* sK, uint16_t* sKt, uint16_t* sVt) {
-    using TL = Bf16Tiles<D>;
-#pragma unroll
-    for (int i = 0; i < NPER; ++i) {
-        const int b = threadIdx.x + i * kThreads;
-        if (b < 3 * TL::NBLK) {
-            const int tile = b / TL::NBLK, within = b % TL::NBLK;
-            const int rg = within / TL::NCG, cg = within % TL::NCG;
-            if (tile == 0) {
-                store_rows(sQ, pre[i], rg, cg, TL::LDR);
-            } else if (tile == 1) {
-                store_rows(sK, pre[i], rg, cg, TL::LDR);
-                store_cols(sKt, pre[i], rg, cg, TL::LDT);
-            } else {
-                store_cols(sVt, pre[i], rg, cg, TL::LDT);
-            }
-        }
-    }
-}
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void output_kernel_bf16(
@@ -466,128 +504,140 @@ __global__ __launch_bounds__(kThreads) void output_kernel_bf16(
     const uint16_t* __restrict__ v, const BlockDesc* __restrict__ blocks,
     const float* __restrict__ ws, const float* __restrict__ final_state,
     const float* __restrict__ ext_state, uint16_t* __restrict__ out, int H) {
-    using TL = Bf16Tiles<D>;
-    constexpr int NKB = D / 16, VBW = D / 64, NKS = D / 32;
-    constexpr int NPER = (3 * TL::NBLK + kThreads - 1) / kThreads;
-    __shared__ __attribute__((aligned(16))) uint16_t sQ[kChunk * TL::LDR];
-    __shared__ __attribute__((aligned(16))) uint16_t sK[kChunk * TL::LDR];
-    __shared__ __attribute__((aligned(16))) uint16_t sKt[D * TL::LDT];
-    __shared__ __attribute__((aligned(16))) uint16_t sVt[D * TL::LDT];
+    using ST = Stage<D>;
+    constexpr int NKB = D / 16, NVB = D / 16, VBW = D / 64, NKS = D / 32;
+    constexpr int NPER = 2 * ST::NB / kThreads;
+    constexpr int LDR = ST::LDR, LDT = ST::LDT;
+    __shared__ __attribute__((aligned(16))) uint16_t sK[kChunk * LDR];
+    __shared__ __attribute__((aligned(16))) uint16_t sKt[D * LDT];
+    __shared__ __attribute__((aligned(16))) uint16_t sVt[D * LDT];
+    __shared__ __attribute__((aligned(16))) uint16_t sSh[D * LDR];   // S^T, bf16 high term
+    __shared__ __attribute__((aligned(16))) uint16_t sSl[D * LDR];   // S^T, bf16 low term
 
     const int h = blockIdx.x % H;
     const BlockDesc bd = blocks[blockIdx.x / H];
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+    const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, g = lane >> 4, c16 = lane & 15;
 
     f32x4 S[VBW][NKB];
     init_state<D>(S, bd, ws, final_state, ext_state, H, h, w, lane);
 
-    // Staging assignment: block index b = tid + i*256 over [Q | K | V].
-    Block8 pre[NPER];
     const int nch = (bd.ntok + kChunk - 1) / kChunk;
-    issue_qkv_bf16<D, NPER>(pre, q, k, v, bd.tok0, min(kChunk, bd.ntok), H, h);
-    for (int c = 0; c < nch; ++c) {
-        stage_qkv_bf16<D, NPER>(pre, sQ, sK, sKt, sVt);
-        __syncthreads();
-        if (c + 1 < nch)
-            issue_qkv_bf16<D, NPER>(pre, q, k, v, (int64_t)bd.tok0 + (c + 1) * kChunk,
-                                    min(kChunk, bd.ntok - (c + 1) * kChunk), H, h);
-        const int rows = min(kChunk, bd.ntok - c * kChunk);
-        const int64_t t0 = (int64_t)bd.tok0 + c * kChunk;
+    const int64_t row_elems = int64_t(H) * D;
+    // this lane's token within the chunk (its wave's 16-token block) and the
+    // byte offset of its q/out row piece inside a chunk window
+    const int trow = w * 16 + c16;
+    const uint32_t qoff = uint32_t(((trow * H + h) * D + 8 * g) * 2);
+    const uint32_t ooff = uint32_t(((trow * H + h) * D + 4 * g) * 2);
 
-        // hi/lo bf16 split of S as A operands of O^T += S^T Q^T:
-        // k-slots (g, i) -> d_k = kb_{i/4}*16 + 4g + i%4 for the pair
-        // (kb0, kb1) = (2kp, 2kp+1).
-        u32x4 Shi[VBW][NKB / 2], Slo[VBW][NKB / 2];
+    // two chunks in flight: register sets A and B alternate
+    Blk4 kva[NPER], kvb[NPER];
+    u32x4 qa[NKS], qb[NKS];
+    auto load = [&](Blk4 (&kv)[NPER], u32x4 (&qf)[NKS], int c) {
+        const int64_t first = (int64_t(bd.tok0) + c * kChunk) * row_elems;
+        const int rows = min(kChunk, bd.ntok - c * kChunk);
+        load_kv<D, NPER>(kv, chunk_rsrc(k, first, 2, rows, H, D),
+                         chunk_rsrc(v, first, 2, rows, H, D), H, h);
+        const auto rq = chunk_rsrc(q, first, 2, rows, H, D);
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) qf[ks] = buf_load16(rq, qoff + ks * 64);
+    };
+    auto step = [&](Blk4 (&kv)[NPER], u32x4 (&qf)[NKS], int c) {
+        // publish S^T = S_hi + S_lo (bf16 terms) for the inter-chunk product;
+        // lane holds S[kb*16 + 4g + j][vb*16 + c16], i.e. 4 consecutive d_k
+        // of row vb*16 + c16 of S^T
 #pragma unroll
         for (int x = 0; x < VBW; ++x)
 #pragma unroll
-            for (int kp = 0; kp < NKB / 2; ++kp) {
-                float s[8];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    s[j] = S[x][2 * kp][j];
-                    s[4 + j] = S[x][2 * kp + 1][j];
-                }
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const uint32_t h0 = f2bf(s[2 * m]), h1 = f2bf(s[2 * m + 1]);
-                    Shi[x][kp][m] = h0 | (h1 << 16);
-                    Slo[x][kp][m] = pack_bf2(s[2 * m] - bf2f(h0), s[2 * m + 1] - bf2f(h1));
-                }
+            for (int kb = 0; kb < NKB; ++kb) {
+                const f32x4 s = S[x][kb];
+                const uint32_t h01 = cvt_bf2(s[0], s[1]), h23 = cvt_bf2(s[2], s[3]);
+                const uint32_t l01 = cvt_bf2(s[0] - bf_lo(h01), s[1] - bf_hi(h01));
+                const uint32_t l23 = cvt_bf2(s[2] - bf_lo(h23), s[3] - bf_hi(h23));
+                const int off = ((w * VBW + x) * 16 + c16) * LDR + kb * 16 + 4 * g;
+                *reinterpret_cast<u32x2*>(sSh + off) = u32x2{h01, h23};
+                *reinterpret_cast<u32x2*>(sSl + off) = u32x2{l01, l23};
             }
+        stage_kv<D, NPER>(kv, sK, sKt, sVt);
+        __syncthreads();
 
+        const int rows = min(kChunk, bd.ntok - c * kChunk);
+        const int64_t first = (int64_t(bd.tok0) + c * kChunk) * row_elems;
+
+        // P^T tiles (ub, w), ub <= w: P^T[u][t] = sum_d K[u][d] Q[t][d]
+        u32x2 pb[4];
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-            // P^T tiles (ub, tb) for ub <= tb: P^T[u][t] = sum_d K[u][d] Q[t][d].
-            u32x4 qf[NKS];
+        for (int ub = 0; ub < 4; ++ub) {
+            pb[ub] = u32x2{0u, 0u};
+            if (ub > w) continue;
+            f32x4 p = zero4();
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks)
-                qf[ks] = lds_u32x4(sQ + (tb * 16 + c16) * TL::LDR + ks * 32 + 8 * g);
-            u32x2 pb[4];
+                p = mfma_bf16(lds_u32x4(sK + (ub * 16 + c16) * LDR + ks * 32 + 8 * g), qf[ks], p);
+            if (ub == w) {   // causal mask inside the diagonal tile: u <= t
 #pragma unroll
-            for (int ub = 0; ub < 4; ++ub) {
-                if (ub > tb) {
-                    pb[ub] = u32x2{0u, 0u};
-                    continue;
-                }
-                f32x4 p = zero4();
-#pragma unroll
-                for (int ks = 0; ks < NKS; ++ks)
-                    p = mfma_bf16(lds_u32x4(sK + (ub * 16 + c16) * TL::LDR + ks * 32 + 8 * g),
-                                  qf[ks], p);
-                if (ub == tb) {   // causal mask inside the diagonal tile: u <= t
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        if (4 * g + j > c16) p[j] = 0.f;
-                }
-                pb[ub] = u32x2{pack_bf2(p[0], p[1]), pack_bf2(p[2], p[3])};
+                for (int j = 0; j < 4; ++j)
+                    if (4 * g + j > c16) p[j] = 0.f;
             }
-            const int trow = tb * 16 + c16;
-#pragma unroll
-            for (int x = 0; x < VBW; ++x) {
-                const int vb = w * VBW + x;
-                f32x4 acc = zero4();
-                // inter-chunk: O^T += S^T Q^T
-#pragma unroll
-                for (int kp = 0; kp < NKB / 2; ++kp) {
-                    const u32x4 bq = cat2(lds_u32x2(sQ + trow * TL::LDR + (2 * kp) * 16 + 4 * g),
-                                          lds_u32x2(sQ + trow * TL::LDR + (2 * kp + 1) * 16 + 4 * g));
-                    acc = mfma_bf16(Shi[x][kp], bq, acc);
-                    acc = mfma_bf16(Slo[x][kp], bq, acc);
-                }
-                // intra-chunk: O^T += V^T P^T, k-slots (g, i) -> u = ub_{i/4}*16 + 4g + i%4
-#pragma unroll
-                for (int pp = 0; pp < 2; ++pp) {
-                    if (2 * pp > tb) continue;
-                    const uint16_t* vr = sVt + (vb * 16 + c16) * TL::LDT;
-                    const u32x4 av = cat2(lds_u32x2(vr + (2 * pp) * 16 + 4 * g),
-                                          lds_u32x2(vr + (2 * pp + 1) * 16 + 4 * g));
-                    acc = mfma_bf16(av, cat2(pb[2 * pp], pb[2 * pp + 1]), acc);
-                }
-                // lane holds O^T[vb*16 + 4g + j][t = tb*16 + c16]
-                if (trow < rows) {
-                    uint16_t* o = out + ((t0 + trow) * H + h) * (int64_t)D + vb * 16 + 4 * g;
-                    *reinterpret_cast<u32x2*>(o) =
-                        u32x2{pack_bf2(acc[0], acc[1]), pack_bf2(acc[2], acc[3])};
-                }
-            }
+            pb[ub] = u32x2{cvt_bf2(p[0], p[1]), cvt_bf2(p[2], p[3])};
         }
-        // carry: S += K^T V (not needed after the block's last chunk)
+
+        // O^T tiles for this wave's 16 tokens, all features
+        f32x4 acc[NVB];
+#pragma unroll
+        for (int vb = 0; vb < NVB; ++vb) {
+            const int f = vb * 16 + c16;   // A-operand row (feature) of this lane
+            f32x4 a = zero4();
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                a = mfma_bf16(lds_u32x4(sSh + f * LDR + ks * 32 + 8 * g), qf[ks], a);
+                a = mfma_bf16(lds_u32x4(sSl + f * LDR + ks * 32 + 8 * g), qf[ks], a);
+            }
+            // intra-chunk: k-slots (g, i) -> u = ub_{i/4}*16 + 4g + i%4
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp) {
+                if (2 * pp > w) continue;
+                const uint16_t* vr = sVt + f * LDT;
+                const u32x4 av = cat2(lds_u32x2(vr + tswz(vb * 16, (2 * pp) * 16 + 4 * g)),
+                                      lds_u32x2(vr + tswz(vb * 16, (2 * pp + 1) * 16 + 4 * g)));
+                a = mfma_bf16(av, cat2(pb[2 * pp], pb[2 * pp + 1]), a);
+            }
+            acc[vb] = a;
+        }
+        // lane holds O[t = w*16 + c16][vb*16 + 4g + j], j = 0..3, per tile vb
+        {
+            const auto ro = chunk_rsrc(out, first, 2, rows, H, D);
+#pragma unroll
+            for (int vb = 0; vb < NVB; ++vb)
+                buf_store8(ro, ooff + vb * 32,
+                           u32x2{cvt_bf2(acc[vb][0], acc[vb][1]), cvt_bf2(acc[vb][2], acc[vb][3])});
+        }
+        // the registers of this chunk are free: fetch chunk c + 2 into them
+        if (c + 2 < nch) load(kv, qf, c + 2);
+
+        // carry: S += K^T V for this wave's state columns (not needed after
+        // the block's last chunk)
         if (c + 1 < nch) {
 #pragma unroll
             for (int ks = 0; ks < kChunk / 32; ++ks)
 #pragma unroll
                 for (int x = 0; x < VBW; ++x) {
                     const int vb = w * VBW + x;
-                    const u32x4 bv = lds_u32x4(sVt + (vb * 16 + c16) * TL::LDT + ks * 32 + 8 * g);
+                    const u32x4 bv = lds_u32x4(sVt + (vb * 16 + c16) * LDT +
+                                               tswz(vb * 16, ks * 32 + 8 * g));
 #pragma unroll
                     for (int kb = 0; kb < NKB; ++kb)
-                        S[x][kb] = mfma_bf16(
-                            lds_u32x4(sKt + (kb * 16 + c16) * TL::LDT + ks * 32 + 8 * g), bv,
-                            S[x][kb]);
+                        S[x][kb] = mfma_bf16(lds_u32x4(sKt + (kb * 16 + c16) * LDT +
+                                                       tswz(kb * 16, ks * 32 + 8 * g)),
+                                             bv, S[x][kb]);
                 }
         }
         __syncthreads();
+    };
+    load(kva, qa, 0);
+    if (nch > 1) load(kvb, qb, 1);
+    for (int c = 0; c < nch; c += 2) {
+        step(kva, qa, c);
+        if (c + 1 < nch) step(kvb, qb, c + 1);
     }
 }
 
@@ -605,7 +655,7 @@ __global__ __launch_bounds__(kThreads) void output_kernel_f32(
 
     const int h = blockIdx.x % H;
     const BlockDesc bd = blocks[blockIdx.x / H];
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+    const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, g = lane >> 4, c16 = lane & 15;
 
     f32x4 S[VBW][NKB];
     init_state<D>(S, bd, ws, final_state, ext_state, H, h, w, lane);
@@ -767,6 +817,8 @@ extern "C" la_status la_scan_packed_stages(int32_t stages, const void* q, const 
         return LA_ERR_INVALID_ARG;
     if (info->n_tokens == 0) return LA_OK;
     if (int64_t(info->n_tokens) * H * d_k >= (int64_t(1) << 40)) return LA_ERR_INVALID_ARG;
+    // a chunk window (64 token rows of all heads) must fit a 32-bit buffer range
+    if (int64_t(kChunk) * H * d_k * 4 >= (int64_t(1) << 31)) return LA_ERR_INVALID_ARG;
     if (int64_t(info->n_blocks) * H >= (int64_t(1) << 31) ||
         int64_t(info->n_delta) * H >= (int64_t(1) << 31) ||
         int64_t(info->n_scan) * H * (int64_t(d_k) * d_k / kThreads) >= (int64_t(1) << 31))

@@ -155,7 +155,7 @@ def test_exact_indexing_probe(G):
         f_exp = np.zeros((d,))
         f_exp[(0 // d ** digit) % d] = int(so[1])
         assert np.array_equal(fin[0, 0, 0].double().numpy(), f_exp)
-        assert np.all(fin[0, :, 1:] == 0)
+        assert bool(torch.all(fin[0, :, 1:] == 0))
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
