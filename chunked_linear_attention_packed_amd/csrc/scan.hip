@@ -104,12 +104,17 @@ __device__ __forceinline__ void slot_to_rc(int e, int& row, int& col) {
 // hardware returns zeros for such loads and drops such stores.  Ragged last
 // chunks need no branches.
 // ---------------------------------------------------------------------------
+// A window with rows <= 0 is empty: every load through it returns zeros
+// without touching memory, so a prefetch past the last chunk can be issued
+// unconditionally (no branch, hence no register merge that would force the
+// compiler to wait for the loads).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rsrc(const void* base, int64_t first_elem,
                                                              int elem_bytes, int rows, int H,
                                                              int D) {
-    const char* p = static_cast<const char*>(base) + first_elem * elem_bytes;
+    const char* p = static_cast<const char*>(base) + (rows > 0 ? first_elem * elem_bytes : 0);
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p), (short)0,
-                                             rows * H * D * elem_bytes, 0x00020000);
+                                             rows > 0 ? rows * H * D * elem_bytes : 0,
+                                             0x00020000);
 }
 __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
@@ -119,42 +124,45 @@ __device__ __forceinline__ void buf_store8(__amdgpu_buffer_rsrc_t r, uint32_t of
 }
 
 // ---------------------------------------------------------------------------
-// bf16 tile staging.  A 64 x D tile is cut into 4x8 blocks (4 tokens x 8
-// features); one lane loads a block as 4 row pieces of 16 bytes (8 lanes
-// cover one D*2-byte row, so each load instruction reads whole cache lines)
-// and writes it to LDS row-major and/or transposed.  The transpose is done in
-// registers with v_perm_b32: column c of the block becomes 4 consecutive
-// tokens, one 8-byte LDS store.
+// bf16 tile staging.  A 64 x D tile is cut into R x 8 blocks (R tokens x 8
+// features, R = 4 or 2); one lane loads a block as R row pieces of 16 bytes
+// (8 lanes cover one D*2-byte row, so each load instruction reads whole cache
+// lines) and writes it to LDS row-major and/or transposed.  The transpose is
+// done in registers with v_perm_b32: column c of the block becomes R
+// consecutive tokens, one R*2-byte LDS store.
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, int R>
 struct Stage {
     static constexpr int NCG = D / 8;           // 8-feature groups per row
-    static constexpr int NB = 16 * NCG;         // 4x8 blocks per 64-token tile
+    static constexpr int NB = (kChunk / R) * NCG;   // R x 8 blocks per 64-token tile
     static constexpr int LDR = D + 8;           // row-major stride (elements)
     static constexpr int LDT = kChunk + 8;      // transposed stride (elements)
 };
 
-struct Blk4 {
-    u32x4 r[4];  // r[i] = token i of the block, 8 bf16 features
+template <int R>
+struct BlkR {
+    u32x4 r[R];  // r[i] = token i of the block, 8 bf16 features
 };
 
-__device__ __forceinline__ void load_blk4(Blk4& b, __amdgpu_buffer_rsrc_t rs, int rg4, int cg,
-                                          int H, int h, int D) {
+template <int R>
+__device__ __forceinline__ void load_blk(BlkR<R>& b, __amdgpu_buffer_rsrc_t rs, int rg, int cg,
+                                         int H, int h, int D) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        b.r[i] = buf_load16(rs, uint32_t((((rg4 * 4 + i) * H + h) * D + cg * 8) * 2));
+    for (int i = 0; i < R; ++i)
+        b.r[i] = buf_load16(rs, uint32_t((((rg * R + i) * H + h) * D + cg * 8) * 2));
 }
 
-__device__ __forceinline__ void store_rows4(uint16_t* dst, const Blk4& b, int rg4, int cg,
-                                            int ld) {
+template <int R>
+__device__ __forceinline__ void store_rows(uint16_t* dst, const BlkR<R>& b, int rg, int cg,
+                                           int ld) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<u32x4*>(dst + (rg4 * 4 + i) * ld + cg * 8) = b.r[i];
+    for (int i = 0; i < R; ++i)
+        *reinterpret_cast<u32x4*>(dst + (rg * R + i) * ld + cg * 8) = b.r[i];
 }
 
 // Transposed tiles [feature][token] are stored with a swizzle: in feature
-// rows whose bit 4 is set, tokens t and t ^ 32 trade places.  The 8-byte
-// column stores of one instruction then cover all 64 LDS banks (rows 8 apart
+// rows whose bit 4 is set, tokens t and t ^ 32 trade places.  The column
+// stores of one instruction then spread over the LDS banks (rows 8 apart
 // start on the same or the opposite bank with 16-byte aligned rows), while
 // every read of 4 or 8 consecutive tokens (never crossing a 32-token half)
 // stays contiguous and keeps its alignment.
@@ -162,18 +170,28 @@ __device__ __forceinline__ int tswz(int feature, int token) {
     return token ^ ((feature & 16) << 1);
 }
 
-// dst[(cg*8 + c) * ld + tswz(cg*8 + c, rg4*4) .. +3] = column c of the block.
-__device__ __forceinline__ void store_cols4(uint16_t* dst, const Blk4& b, int rg4, int cg,
-                                            int ld) {
+// dst[(cg*8 + c) * ld + tswz(cg*8 + c, rg*R) .. + R-1] = column c of the block.
+template <int R>
+__device__ __forceinline__ void store_cols(uint16_t* dst, const BlkR<R>& b, int rg, int cg,
+                                           int ld) {
 #pragma unroll
     for (int m = 0; m < 4; ++m) {   // features 2m (low halves) and 2m+1 (high halves)
-        const u32x2 ev{__builtin_amdgcn_perm(b.r[1][m], b.r[0][m], 0x05040100u),
-                       __builtin_amdgcn_perm(b.r[3][m], b.r[2][m], 0x05040100u)};
-        const u32x2 od{__builtin_amdgcn_perm(b.r[1][m], b.r[0][m], 0x07060302u),
-                       __builtin_amdgcn_perm(b.r[3][m], b.r[2][m], 0x07060302u)};
         const int f0 = cg * 8 + 2 * m;   // f0 and f0 + 1 share bit 4
-        *reinterpret_cast<u32x2*>(dst + f0 * ld + tswz(f0, rg4 * 4)) = ev;
-        *reinterpret_cast<u32x2*>(dst + (f0 + 1) * ld + tswz(f0, rg4 * 4)) = od;
+        const int t0 = tswz(f0, rg * R);
+        if constexpr (R == 4) {
+            const u32x2 ev{__builtin_amdgcn_perm(b.r[1][m], b.r[0][m], 0x05040100u),
+                           __builtin_amdgcn_perm(b.r[3][m], b.r[2][m], 0x05040100u)};
+            const u32x2 od{__builtin_amdgcn_perm(b.r[1][m], b.r[0][m], 0x07060302u),
+                           __builtin_amdgcn_perm(b.r[3][m], b.r[2][m], 0x07060302u)};
+            *reinterpret_cast<u32x2*>(dst + f0 * ld + t0) = ev;
+            *reinterpret_cast<u32x2*>(dst + (f0 + 1) * ld + t0) = od;
+        } else {
+            static_assert(R == 2, "blocks of 2 or 4 tokens");
+            *reinterpret_cast<uint32_t*>(dst + f0 * ld + t0) =
+                __builtin_amdgcn_perm(b.r[1][m], b.r[0][m], 0x05040100u);
+            *reinterpret_cast<uint32_t*>(dst + (f0 + 1) * ld + t0) =
+                __builtin_amdgcn_perm(b.r[1][m], b.r[0][m], 0x07060302u);
+        }
     }
 }
 
@@ -185,40 +203,49 @@ __device__ __forceinline__ u32x4 lds_u32x4(const uint16_t* p) {
 }
 __device__ __forceinline__ u32x4 cat2(u32x2 a, u32x2 b) { return u32x4{a[0], a[1], b[0], b[1]}; }
 
-// K and V blocks of one chunk: block index b = tid + i*256 over [K | V]
-// (2*NB blocks; each half is a whole number of waves, so the tile choice is
-// wave-uniform).
-template <int D, int NPER>
-__device__ __forceinline__ void load_kv(Blk4 (&pre)[NPER], __amdgpu_buffer_rsrc_t rk,
+// K and V blocks of one chunk: block index b = tid + i*NT over [K | V]
+// (2*NB blocks; each half is a whole number of waves, so the tile choice and
+// whether a wave loads at all are wave-uniform).
+template <int D, int R, int NT>
+struct KVSplit {
+    static constexpr int NPER = (2 * Stage<D, R>::NB + NT - 1) / NT;
+};
+
+template <int D, int R, int NT, int NPER>
+__device__ __forceinline__ void load_kv(BlkR<R> (&pre)[NPER], __amdgpu_buffer_rsrc_t rk,
                                         __amdgpu_buffer_rsrc_t rv, int H, int h) {
-    using ST = Stage<D>;
+    using ST = Stage<D, R>;
     const int wbase = wave_id() * 64;
     const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int i = 0; i < NPER; ++i) {
-        const bool is_v = wbase + i * kThreads >= ST::NB;   // wave-uniform
-        const int within = wbase + i * kThreads + lane - (is_v ? ST::NB : 0);
-        load_blk4(pre[i], is_v ? rv : rk, within / ST::NCG, within % ST::NCG, H, h, D);
+        if constexpr (NPER * NT > 2 * ST::NB)
+            if (wbase + i * NT >= 2 * ST::NB) break;           // wave-uniform
+        const bool is_v = wbase + i * NT >= ST::NB;             // wave-uniform
+        const int within = wbase + i * NT + lane - (is_v ? ST::NB : 0);
+        load_blk<R>(pre[i], is_v ? rv : rk, within / ST::NCG, within % ST::NCG, H, h, D);
     }
 }
 
 // Registers -> LDS: K transposed (and row-major if sK is given), V transposed.
-template <int D, int NPER>
-__device__ __forceinline__ void stage_kv(const Blk4 (&pre)[NPER], uint16_t* sK, uint16_t* sKt,
-                                         uint16_t* sVt) {
-    using ST = Stage<D>;
+template <int D, int R, int NT, int NPER>
+__device__ __forceinline__ void stage_kv(const BlkR<R> (&pre)[NPER], uint16_t* sK,
+                                         uint16_t* sKt, uint16_t* sVt) {
+    using ST = Stage<D, R>;
     const int wbase = wave_id() * 64;
     const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int i = 0; i < NPER; ++i) {
-        const bool is_v = wbase + i * kThreads >= ST::NB;   // wave-uniform
-        const int within = wbase + i * kThreads + lane - (is_v ? ST::NB : 0);
-        const int rg4 = within / ST::NCG, cg = within % ST::NCG;
+        if constexpr (NPER * NT > 2 * ST::NB)
+            if (wbase + i * NT >= 2 * ST::NB) break;           // wave-uniform
+        const bool is_v = wbase + i * NT >= ST::NB;             // wave-uniform
+        const int within = wbase + i * NT + lane - (is_v ? ST::NB : 0);
+        const int rg = within / ST::NCG, cg = within % ST::NCG;
         if (is_v) {
-            store_cols4(sVt, pre[i], rg4, cg, ST::LDT);
+            store_cols<R>(sVt, pre[i], rg, cg, ST::LDT);
         } else {
-            if (sK) store_rows4(sK, pre[i], rg4, cg, ST::LDR);
-            store_cols4(sKt, pre[i], rg4, cg, ST::LDT);
+            if (sK) store_rows<R>(sK, pre[i], rg, cg, ST::LDR);
+            store_cols<R>(sKt, pre[i], rg, cg, ST::LDT);
         }
     }
 }
@@ -243,9 +270,10 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void delta_kernel_bf16(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const DeltaDesc* __restrict__ deltas, float* __restrict__ ws, int H) {
-    using ST = Stage<D>;
+    constexpr int R = 4;
+    using ST = Stage<D, R>;
     constexpr int NKB = D / 16, VBW = D / 64, DD = D * D;
-    constexpr int NPER = 2 * ST::NB / kThreads;
+    constexpr int NPER = KVSplit<D, R, kThreads>::NPER;
     __shared__ __attribute__((aligned(16))) uint16_t sKt[D * ST::LDT];
     __shared__ __attribute__((aligned(16))) uint16_t sVt[D * ST::LDT];
 
@@ -262,17 +290,17 @@ __global__ __launch_bounds__(kThreads) void delta_kernel_bf16(
     const int nch = (dd.ntok + kChunk - 1) / kChunk;
     const int64_t row_elems = int64_t(H) * D;
     // two chunks in flight: registers A hold chunk c, B chunk c + 1
-    Blk4 pa[NPER], pb[NPER];
-    auto load = [&](Blk4 (&dst)[NPER], int c) {
+    BlkR<R> pa[NPER], pb[NPER];
+    auto load = [&](BlkR<R> (&dst)[NPER], int c) {
         const int64_t first = (int64_t(dd.tok0) + c * kChunk) * row_elems;
-        const int rows = min(kChunk, dd.ntok - c * kChunk);
-        load_kv<D, NPER>(dst, chunk_rsrc(k, first, 2, rows, H, D),
-                         chunk_rsrc(v, first, 2, rows, H, D), H, h);
+        const int rows = min(kChunk, dd.ntok - c * kChunk);   // <= 0: empty window
+        load_kv<D, R, kThreads, NPER>(dst, chunk_rsrc(k, first, 2, rows, H, D),
+                                      chunk_rsrc(v, first, 2, rows, H, D), H, h);
     };
-    auto step = [&](Blk4 (&cur)[NPER], int c) {
-        stage_kv<D, NPER>(cur, nullptr, sKt, sVt);
+    auto step = [&](BlkR<R> (&cur)[NPER], int c) {
+        stage_kv<D, R, kThreads, NPER>(cur, nullptr, sKt, sVt);
         __syncthreads();
-        if (c + 2 < nch) load(cur, c + 2);
+        load(cur, c + 2);   // empty window past the last chunk
 #pragma unroll
         for (int ks = 0; ks < kChunk / 32; ++ks) {
 #pragma unroll
@@ -291,10 +319,11 @@ __global__ __launch_bounds__(kThreads) void delta_kernel_bf16(
         __syncthreads();
     };
     load(pa, 0);
-    if (nch > 1) load(pb, 1);
+    load(pb, 1);
     for (int c = 0; c < nch; c += 2) {
         step(pa, c);
-        if (c + 1 < nch) step(pb, c + 1);
+        if (c + 1 >= nch) break;
+        step(pb, c + 1);
     }
     float* dst = ws + ((int64_t)dd.slot * H + h) * DD;
 #pragma unroll
@@ -498,15 +527,102 @@ __device__ __forceinline__ void init_state(f32x4 (&S)[D / 64][D / 16], const Blo
 }
 
 
+// Launch 3 (bf16) runs NW = 4 (d = 64) or 8 (d = 128) waves per workgroup.
+// Wave w = 4 hv + tb computes the outputs of tokens tb*16 .. tb*16+15 for the
+// output features of part hv (all features with 4 waves, half with 8), and
+// owns TPW state tiles (vb_own, kb0 .. kb0+TPW-1) for the carry.
 template <int D>
-__global__ __launch_bounds__(kThreads) void output_kernel_bf16(
+struct Out3 {
+    static constexpr int NW = D == 64 ? 4 : 8;        // waves per workgroup
+    static constexpr int NT = 64 * NW;
+    static constexpr int R = 4;                       // tokens per staging block
+    static constexpr int NKB = D / 16, NVB = D / 16, NKS = D / 32;
+    static constexpr int VBH = NVB * 4 / NW;          // output tiles per wave
+    static constexpr int TPW = NVB * NKB / NW;        // carry tiles per wave
+    __device__ static int vb_own(int w) { return w % NVB; }
+    __device__ static int kb0(int w) { return (w / NVB) * TPW; }
+};
+
+// The outputs of one wave for one chunk: its 16 tokens (token block TB) and
+// VBH feature tiles starting at vb0.  Specialised per TB so that the causal
+// structure (TB + 1 score tiles, TB / 2 + 1 intra-chunk steps) is known at
+// compile time and every loop runs over independent accumulators with its
+// LDS fragments loaded in batches.
+template <int D, int TB, int VBH>
+__device__ __forceinline__ void out_tiles(const uint16_t* sK, const uint16_t* sVt,
+                                          const uint16_t* sSh, const uint16_t* sSl,
+                                          const u32x4 (&qf)[D / 32], int vb0, int g, int c16,
+                                          f32x4 (&acc)[VBH]) {
+    constexpr int NKS = D / 32;
+    constexpr int LDR = Stage<D, 4>::LDR, LDT = Stage<D, 4>::LDT;
+    // P^T tiles (ub, TB), ub <= TB: P^T[u][t] = sum_d K[u][d] Q[t][d]
+    f32x4 p[TB + 1];
+#pragma unroll
+    for (int ub = 0; ub <= TB; ++ub) p[ub] = zero4();
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+        u32x4 kf[TB + 1];
+#pragma unroll
+        for (int ub = 0; ub <= TB; ++ub)
+            kf[ub] = lds_u32x4(sK + (ub * 16 + c16) * LDR + ks * 32 + 8 * g);
+#pragma unroll
+        for (int ub = 0; ub <= TB; ++ub) p[ub] = mfma_bf16(kf[ub], qf[ks], p[ub]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)   // causal mask inside the diagonal tile: u <= t
+        if (4 * g + j > c16) p[TB][j] = 0.f;
+    u32x2 pb[4];
+#pragma unroll
+    for (int ub = 0; ub < 4; ++ub)
+        pb[ub] = ub <= TB ? u32x2{cvt_bf2(p[ub][0], p[ub][1]), cvt_bf2(p[ub][2], p[ub][3])}
+                          : u32x2{0u, 0u};
+
+    // inter-chunk: O^T += S_hi^T Q^T + S_lo^T Q^T
+#pragma unroll
+    for (int x = 0; x < VBH; ++x) acc[x] = zero4();
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+        u32x4 ah[VBH], al[VBH];
+#pragma unroll
+        for (int x = 0; x < VBH; ++x) {
+            const int f = (vb0 + x) * 16 + c16;
+            ah[x] = lds_u32x4(sSh + f * LDR + ks * 32 + 8 * g);
+            al[x] = lds_u32x4(sSl + f * LDR + ks * 32 + 8 * g);
+        }
+#pragma unroll
+        for (int x = 0; x < VBH; ++x) acc[x] = mfma_bf16(ah[x], qf[ks], acc[x]);
+#pragma unroll
+        for (int x = 0; x < VBH; ++x) acc[x] = mfma_bf16(al[x], qf[ks], acc[x]);
+    }
+    // intra-chunk: O^T += V^T P^T, k-slots (g, i) -> u = ub_{i/4}*16 + 4g + i%4
+#pragma unroll
+    for (int pp = 0; pp <= TB / 2; ++pp) {
+        const u32x4 bp = cat2(pb[2 * pp], pb[2 * pp + 1]);
+        u32x4 av[VBH];
+#pragma unroll
+        for (int x = 0; x < VBH; ++x) {
+            const int vb = vb0 + x;
+            const uint16_t* vr = sVt + (vb * 16 + c16) * LDT;
+            av[x] = cat2(lds_u32x2(vr + tswz(vb * 16, (2 * pp) * 16 + 4 * g)),
+                         lds_u32x2(vr + tswz(vb * 16, (2 * pp + 1) * 16 + 4 * g)));
+        }
+#pragma unroll
+        for (int x = 0; x < VBH; ++x) acc[x] = mfma_bf16(av[x], bp, acc[x]);
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(Out3<D>::NT) void output_kernel_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const BlockDesc* __restrict__ blocks,
     const float* __restrict__ ws, const float* __restrict__ final_state,
     const float* __restrict__ ext_state, uint16_t* __restrict__ out, int H) {
-    using ST = Stage<D>;
-    constexpr int NKB = D / 16, NVB = D / 16, VBW = D / 64, NKS = D / 32;
-    constexpr int NPER = 2 * ST::NB / kThreads;
+    using O3 = Out3<D>;
+    constexpr int R = O3::R, NT = O3::NT;
+    using ST = Stage<D, R>;
+    constexpr int NKB = O3::NKB, NKS = O3::NKS, VBH = O3::VBH, TPW = O3::TPW;
+    constexpr int DD = D * D;
+    constexpr int NPER = KVSplit<D, R, NT>::NPER;
     constexpr int LDR = ST::LDR, LDT = ST::LDT;
     __shared__ __attribute__((aligned(16))) uint16_t sK[kChunk * LDR];
     __shared__ __attribute__((aligned(16))) uint16_t sKt[D * LDT];
@@ -517,127 +633,111 @@ __global__ __launch_bounds__(kThreads) void output_kernel_bf16(
     const int h = blockIdx.x % H;
     const BlockDesc bd = blocks[blockIdx.x / H];
     const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+    const int tb = w & 3, hv = w >> 2;
+    const int vbo = O3::vb_own(w), kbo = O3::kb0(w);
 
-    f32x4 S[VBW][NKB];
-    init_state<D>(S, bd, ws, final_state, ext_state, H, h, w, lane);
+    // carry state: tiles (vbo, kbo + i); lane holds S[kb*16 + 4g + j][vbo*16 + c16]
+    f32x4 S[TPW];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) S[i] = zero4();
+    {
+        const float* seed = nullptr;
+        if (bd.seed >= 0)
+            seed = final_state + ((int64_t)bd.seed * H + h) * DD;
+        else if (bd.seed <= -2)
+            seed = ext_state + ((int64_t)(-bd.seed - 2) * H + h) * DD;
+        if (seed) {
+#pragma unroll
+            for (int i = 0; i < TPW; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    S[i][j] = seed[((kbo + i) * 16 + 4 * g + j) * D + vbo * 16 + c16];
+        }
+        if (bd.sin_slot >= 0) {
+            const float* src = ws + ((int64_t)bd.sin_slot * H + h) * DD;
+#pragma unroll
+            for (int i = 0; i < TPW; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    S[i][j] += src[((vbo * NKB + kbo + i) * 4 + j) * 64 + lane];
+        }
+    }
 
     const int nch = (bd.ntok + kChunk - 1) / kChunk;
     const int64_t row_elems = int64_t(H) * D;
-    // this lane's token within the chunk (its wave's 16-token block) and the
-    // byte offset of its q/out row piece inside a chunk window
-    const int trow = w * 16 + c16;
+    // this lane's token within the chunk and the byte offsets of its q / out
+    // row pieces inside a chunk window
+    const int trow = tb * 16 + c16;
     const uint32_t qoff = uint32_t(((trow * H + h) * D + 8 * g) * 2);
-    const uint32_t ooff = uint32_t(((trow * H + h) * D + 4 * g) * 2);
+    const uint32_t ooff = uint32_t(((trow * H + h) * D + hv * VBH * 16 + 4 * g) * 2);
 
-    // two chunks in flight: register sets A and B alternate
-    Blk4 kva[NPER], kvb[NPER];
-    u32x4 qa[NKS], qb[NKS];
-    auto load = [&](Blk4 (&kv)[NPER], u32x4 (&qf)[NKS], int c) {
+    // one chunk in flight: kv / qn hold chunk c + 1 while chunk c is computed
+    BlkR<R> kv[NPER];
+    u32x4 qf[NKS], qn[NKS];
+    auto load = [&](int c) {
         const int64_t first = (int64_t(bd.tok0) + c * kChunk) * row_elems;
-        const int rows = min(kChunk, bd.ntok - c * kChunk);
-        load_kv<D, NPER>(kv, chunk_rsrc(k, first, 2, rows, H, D),
-                         chunk_rsrc(v, first, 2, rows, H, D), H, h);
+        const int rows = min(kChunk, bd.ntok - c * kChunk);   // <= 0: empty window
+        load_kv<D, R, NT, NPER>(kv, chunk_rsrc(k, first, 2, rows, H, D),
+                                chunk_rsrc(v, first, 2, rows, H, D), H, h);
         const auto rq = chunk_rsrc(q, first, 2, rows, H, D);
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) qf[ks] = buf_load16(rq, qoff + ks * 64);
+        for (int ks = 0; ks < NKS; ++ks) qn[ks] = buf_load16(rq, qoff + ks * 64);
     };
-    auto step = [&](Blk4 (&kv)[NPER], u32x4 (&qf)[NKS], int c) {
+    load(0);
+    for (int c = 0; c < nch; ++c) {
         // publish S^T = S_hi + S_lo (bf16 terms) for the inter-chunk product;
-        // lane holds S[kb*16 + 4g + j][vb*16 + c16], i.e. 4 consecutive d_k
-        // of row vb*16 + c16 of S^T
+        // lane holds 4 consecutive d_k of row vbo*16 + c16 of S^T per tile
 #pragma unroll
-        for (int x = 0; x < VBW; ++x)
+        for (int i = 0; i < TPW; ++i) {
+            const f32x4 s = S[i];
+            const uint32_t h01 = cvt_bf2(s[0], s[1]), h23 = cvt_bf2(s[2], s[3]);
+            const uint32_t l01 = cvt_bf2(s[0] - bf_lo(h01), s[1] - bf_hi(h01));
+            const uint32_t l23 = cvt_bf2(s[2] - bf_lo(h23), s[3] - bf_hi(h23));
+            const int off = (vbo * 16 + c16) * LDR + (kbo + i) * 16 + 4 * g;
+            *reinterpret_cast<u32x2*>(sSh + off) = u32x2{h01, h23};
+            *reinterpret_cast<u32x2*>(sSl + off) = u32x2{l01, l23};
+        }
+        stage_kv<D, R, NT, NPER>(kv, sK, sKt, sVt);
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
-                const f32x4 s = S[x][kb];
-                const uint32_t h01 = cvt_bf2(s[0], s[1]), h23 = cvt_bf2(s[2], s[3]);
-                const uint32_t l01 = cvt_bf2(s[0] - bf_lo(h01), s[1] - bf_hi(h01));
-                const uint32_t l23 = cvt_bf2(s[2] - bf_lo(h23), s[3] - bf_hi(h23));
-                const int off = ((w * VBW + x) * 16 + c16) * LDR + kb * 16 + 4 * g;
-                *reinterpret_cast<u32x2*>(sSh + off) = u32x2{h01, h23};
-                *reinterpret_cast<u32x2*>(sSl + off) = u32x2{l01, l23};
-            }
-        stage_kv<D, NPER>(kv, sK, sKt, sVt);
+        for (int ks = 0; ks < NKS; ++ks) qf[ks] = qn[ks];
         __syncthreads();
+        // fetch the next chunk (an empty window past the last one)
+        load(c + 1);
 
         const int rows = min(kChunk, bd.ntok - c * kChunk);
         const int64_t first = (int64_t(bd.tok0) + c * kChunk) * row_elems;
 
-        // P^T tiles (ub, w), ub <= w: P^T[u][t] = sum_d K[u][d] Q[t][d]
-        u32x2 pb[4];
-#pragma unroll
-        for (int ub = 0; ub < 4; ++ub) {
-            pb[ub] = u32x2{0u, 0u};
-            if (ub > w) continue;
-            f32x4 p = zero4();
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks)
-                p = mfma_bf16(lds_u32x4(sK + (ub * 16 + c16) * LDR + ks * 32 + 8 * g), qf[ks], p);
-            if (ub == w) {   // causal mask inside the diagonal tile: u <= t
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    if (4 * g + j > c16) p[j] = 0.f;
-            }
-            pb[ub] = u32x2{cvt_bf2(p[0], p[1]), cvt_bf2(p[2], p[3])};
+        // O^T tiles: this wave's 16 tokens, features hv*VBH*16 .. +VBH*16-1
+        f32x4 acc[VBH];
+        switch (tb) {
+            case 0: out_tiles<D, 0, VBH>(sK, sVt, sSh, sSl, qf, hv * VBH, g, c16, acc); break;
+            case 1: out_tiles<D, 1, VBH>(sK, sVt, sSh, sSl, qf, hv * VBH, g, c16, acc); break;
+            case 2: out_tiles<D, 2, VBH>(sK, sVt, sSh, sSl, qf, hv * VBH, g, c16, acc); break;
+            default: out_tiles<D, 3, VBH>(sK, sVt, sSh, sSl, qf, hv * VBH, g, c16, acc); break;
         }
-
-        // O^T tiles for this wave's 16 tokens, all features
-        f32x4 acc[NVB];
-#pragma unroll
-        for (int vb = 0; vb < NVB; ++vb) {
-            const int f = vb * 16 + c16;   // A-operand row (feature) of this lane
-            f32x4 a = zero4();
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                a = mfma_bf16(lds_u32x4(sSh + f * LDR + ks * 32 + 8 * g), qf[ks], a);
-                a = mfma_bf16(lds_u32x4(sSl + f * LDR + ks * 32 + 8 * g), qf[ks], a);
-            }
-            // intra-chunk: k-slots (g, i) -> u = ub_{i/4}*16 + 4g + i%4
-#pragma unroll
-            for (int pp = 0; pp < 2; ++pp) {
-                if (2 * pp > w) continue;
-                const uint16_t* vr = sVt + f * LDT;
-                const u32x4 av = cat2(lds_u32x2(vr + tswz(vb * 16, (2 * pp) * 16 + 4 * g)),
-                                      lds_u32x2(vr + tswz(vb * 16, (2 * pp + 1) * 16 + 4 * g)));
-                a = mfma_bf16(av, cat2(pb[2 * pp], pb[2 * pp + 1]), a);
-            }
-            acc[vb] = a;
-        }
-        // lane holds O[t = w*16 + c16][vb*16 + 4g + j], j = 0..3, per tile vb
+        // lane holds O[t = tb*16 + c16][(hv*VBH + x)*16 + 4g + j], j = 0..3
         {
             const auto ro = chunk_rsrc(out, first, 2, rows, H, D);
 #pragma unroll
-            for (int vb = 0; vb < NVB; ++vb)
-                buf_store8(ro, ooff + vb * 32,
-                           u32x2{cvt_bf2(acc[vb][0], acc[vb][1]), cvt_bf2(acc[vb][2], acc[vb][3])});
+            for (int x = 0; x < VBH; ++x)
+                buf_store8(ro, ooff + x * 32,
+                           u32x2{cvt_bf2(acc[x][0], acc[x][1]), cvt_bf2(acc[x][2], acc[x][3])});
         }
-        // the registers of this chunk are free: fetch chunk c + 2 into them
-        if (c + 2 < nch) load(kv, qf, c + 2);
-
-        // carry: S += K^T V for this wave's state columns (not needed after
-        // the block's last chunk)
+        // carry: S += K^T V for this wave's tiles (not needed after the
+        // block's last chunk)
         if (c + 1 < nch) {
 #pragma unroll
-            for (int ks = 0; ks < kChunk / 32; ++ks)
+            for (int ks = 0; ks < kChunk / 32; ++ks) {
+                const u32x4 bv = lds_u32x4(sVt + (vbo * 16 + c16) * LDT +
+                                           tswz(vbo * 16, ks * 32 + 8 * g));
 #pragma unroll
-                for (int x = 0; x < VBW; ++x) {
-                    const int vb = w * VBW + x;
-                    const u32x4 bv = lds_u32x4(sVt + (vb * 16 + c16) * LDT +
-                                               tswz(vb * 16, ks * 32 + 8 * g));
-#pragma unroll
-                    for (int kb = 0; kb < NKB; ++kb)
-                        S[x][kb] = mfma_bf16(lds_u32x4(sKt + (kb * 16 + c16) * LDT +
-                                                       tswz(kb * 16, ks * 32 + 8 * g)),
-                                             bv, S[x][kb]);
-                }
+                for (int i = 0; i < TPW; ++i)
+                    S[i] = mfma_bf16(lds_u32x4(sKt + ((kbo + i) * 16 + c16) * LDT +
+                                               tswz((kbo + i) * 16, ks * 32 + 8 * g)),
+                                     bv, S[i]);
+            }
         }
         __syncthreads();
-    };
-    load(kva, qa, 0);
-    if (nch > 1) load(kvb, qb, 1);
-    for (int c = 0; c < nch; c += 2) {
-        step(kva, qa, c);
-        if (c + 1 < nch) step(kvb, qb, c + 1);
     }
 }
 
@@ -777,7 +877,7 @@ la_status launch_all(int32_t stages, const void* q, const void* k, const void* v
     if ((stages & LA_STAGE_OUTPUT) && info.n_blocks > 0) {
         const dim3 grid(unsigned(int64_t(info.n_blocks) * H));
         if (dtype == LA_BF16)
-            hipLaunchKernelGGL(output_kernel_bf16<D>, grid, blk, 0, st,
+            hipLaunchKernelGGL(output_kernel_bf16<D>, grid, dim3(Out3<D>::NT), 0, st,
                                static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                static_cast<const uint16_t*>(v), blocks, ws, final_state,
                                ext_state, static_cast<uint16_t*>(out), H);
