@@ -24,6 +24,8 @@ HIP_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # MFMA results in VGPRs: avoids AGPR->VGPR copies before the bf16 packing
     "-mllvm", "-amdgpu-mfma-vgpr-form",
+    # the first kernel arguments arrive in SGPRs at wave launch (no load)
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-Wall", "-Wno-unused-function",
 ]
 

@@ -160,24 +160,32 @@ __device__ __forceinline__ void store_rows(uint16_t* dst, const BlkR<R>& b, int 
         *reinterpret_cast<u32x4*>(dst + (rg * R + i) * ld + cg * 8) = b.r[i];
 }
 
-// Transposed tiles [feature][token] are stored with a swizzle: in feature
-// rows whose bit 4 is set, tokens t and t ^ 32 trade places.  The column
-// stores of one instruction then spread over the LDS banks (rows 8 apart
-// start on the same or the opposite bank with 16-byte aligned rows), while
-// every read of 4 or 8 consecutive tokens (never crossing a 32-token half)
-// stays contiguous and keeps its alignment.
-__device__ __forceinline__ int tswz(int feature, int token) {
-    return token ^ ((feature & 16) << 1);
+// Transposed tiles [feature][token] hold the 64 tokens of a row in the order
+//   position(u) = 32 a + 8 c + 4 b + d   for   u = 32 a + 16 b + 4 c + d,
+// so that the 8 tokens {32a + 16b + 4c + d : b, d} (two 4-token groups 16
+// apart: the k-slots of lane group c in a K = 32 step whose two halves come
+// from 16-row tiles 2a and 2a + 1) are 16 contiguous bytes.  Every consumer
+// reads such 8-token groups: the carry K^T V (both operands in this order,
+// so the contraction is unchanged) and the intra-chunk V^T P^T (whose P^T
+// operand comes from accumulator tiles in exactly this slot order).  On top,
+// rows whose feature index has bit 4 set swap their two 32-token halves, so
+// the 8-byte column stores of one instruction spread over all LDS banks
+// (16-byte aligned rows 8 apart otherwise start on the same or the opposite
+// bank).
+__device__ __forceinline__ int tpos(int feature, int token) {
+    const int pos = (token & 32) | ((token & 12) << 1) | ((token & 16) >> 2) | (token & 3);
+    return pos ^ ((feature & 16) << 1);
 }
 
-// dst[(cg*8 + c) * ld + tswz(cg*8 + c, rg*R) .. + R-1] = column c of the block.
+// dst[(cg*8 + c) * ld + tpos(cg*8 + c, rg*R) .. + R-1] = column c of the block
+// (R = 2 or 4 consecutive tokens stay contiguous under tpos).
 template <int R>
 __device__ __forceinline__ void store_cols(uint16_t* dst, const BlkR<R>& b, int rg, int cg,
                                            int ld) {
 #pragma unroll
     for (int m = 0; m < 4; ++m) {   // features 2m (low halves) and 2m+1 (high halves)
         const int f0 = cg * 8 + 2 * m;   // f0 and f0 + 1 share bit 4
-        const int t0 = tswz(f0, rg * R);
+        const int t0 = tpos(f0, rg * R);
         if constexpr (R == 4) {
             const u32x2 ev{__builtin_amdgcn_perm(b.r[1][m], b.r[0][m], 0x05040100u),
                            __builtin_amdgcn_perm(b.r[3][m], b.r[2][m], 0x05040100u)};
@@ -307,11 +315,11 @@ __global__ __launch_bounds__(kThreads) void delta_kernel_bf16(
             for (int x = 0; x < VBW; ++x) {
                 const int vb = w * VBW + x;
                 const u32x4 bv = lds_u32x4(sVt + (vb * 16 + c16) * ST::LDT +
-                                           tswz(vb * 16, ks * 32 + 8 * g));
+                                           tpos(vb * 16, ks * 32 + 4 * g));
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb) {
                     const u32x4 ak = lds_u32x4(sKt + (kb * 16 + c16) * ST::LDT +
-                                               tswz(kb * 16, ks * 32 + 8 * g));
+                                               tpos(kb * 16, ks * 32 + 4 * g));
                     S[x][kb] = mfma_bf16(ak, bv, S[x][kb]);
                 }
             }
@@ -539,6 +547,7 @@ struct Out3 {
     static constexpr int NKB = D / 16, NVB = D / 16, NKS = D / 32;
     static constexpr int VBH = NVB * 4 / NW;          // output tiles per wave
     static constexpr int TPW = NVB * NKB / NW;        // carry tiles per wave
+    static_assert(NKB % TPW == 0, "a wave's carry tiles share one state column block");
     __device__ static int vb_own(int w) { return w % NVB; }
     __device__ static int kb0(int w) { return (w / NVB) * TPW; }
 };
@@ -602,9 +611,7 @@ __device__ __forceinline__ void out_tiles(const uint16_t* sK, const uint16_t* sV
 #pragma unroll
         for (int x = 0; x < VBH; ++x) {
             const int vb = vb0 + x;
-            const uint16_t* vr = sVt + (vb * 16 + c16) * LDT;
-            av[x] = cat2(lds_u32x2(vr + tswz(vb * 16, (2 * pp) * 16 + 4 * g)),
-                         lds_u32x2(vr + tswz(vb * 16, (2 * pp + 1) * 16 + 4 * g)));
+            av[x] = lds_u32x4(sVt + (vb * 16 + c16) * LDT + tpos(vb * 16, pp * 32 + 4 * g));
         }
 #pragma unroll
         for (int x = 0; x < VBH; ++x) acc[x] = mfma_bf16(av[x], bp, acc[x]);
@@ -729,11 +736,11 @@ __global__ __launch_bounds__(Out3<D>::NT) void output_kernel_bf16(
 #pragma unroll
             for (int ks = 0; ks < kChunk / 32; ++ks) {
                 const u32x4 bv = lds_u32x4(sVt + (vbo * 16 + c16) * LDT +
-                                           tswz(vbo * 16, ks * 32 + 8 * g));
+                                           tpos(vbo * 16, ks * 32 + 4 * g));
 #pragma unroll
                 for (int i = 0; i < TPW; ++i)
                     S[i] = mfma_bf16(lds_u32x4(sKt + ((kbo + i) * 16 + c16) * LDT +
-                                               tswz((kbo + i) * 16, ks * 32 + 8 * g)),
+                                               tpos((kbo + i) * 16, ks * 32 + 4 * g)),
                                      bv, S[i]);
             }
         }
