@@ -123,11 +123,12 @@ class PassPlan:
         return self._dev[key]
 
 
-def choose_block_chunks(chunks_per_segment, heads, target_groups=512, max_g=8):
+def choose_block_chunks(chunks_per_segment, heads, target_groups=300, max_g=16):
     """Chunks per work block: the largest power of two (<= max_g) whose block
-    count times `heads` still reaches `target_groups` workgroups; 1 if none.
-    Larger blocks carry the state in registers longer (less state traffic);
-    smaller ones give more workgroups to fill 256 compute units."""
+    count times `heads` still reaches `target_groups` workgroups (about one
+    per compute unit); 1 if none.  Larger blocks carry the state in registers
+    longer (less state traffic, fewer workgroup prologues); smaller ones give
+    more workgroups to fill 256 compute units and shorter serial chains."""
     cps = np.asarray(chunks_per_segment, dtype=np.int64)
     g = max_g
     while g > 1:
