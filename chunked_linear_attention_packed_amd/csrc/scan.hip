@@ -31,11 +31,12 @@
 // next product directly: a tile's 4 rows 4g + j become the k-slots of lane
 // group g, two row-tiles making the 8 bf16 elements of one K=32 step.
 //
-// Work split inside a workgroup of 4 waves (bf16 path): wave w owns the state
-// columns w*VBW*16 .. (w+1)*VBW*16-1 (VBW = d/64) for the carry S += K^T V,
-// and the 16 tokens w*16 .. w*16+15 of each chunk for the outputs.  Each chunk
-// the waves publish S^T as two bf16 terms (hi + lo) in LDS for the inter-chunk
-// product.
+// Work split of launch 3 (bf16 path): NP workgroups share a (work block,
+// head), each computing D / NP output features (NP = 1 at d = 64, 2 at
+// d = 128; the parts of one item run on one XCD).  Inside a workgroup each
+// wave owns 16 tokens of every chunk for the outputs and a few state tiles
+// for the carry S += K^T V; each chunk the waves publish S^T as two bf16
+// terms (hi + lo) in LDS for the inter-chunk product.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -211,51 +212,82 @@ __device__ __forceinline__ u32x4 lds_u32x4(const uint16_t* p) {
 }
 __device__ __forceinline__ u32x4 cat2(u32x2 a, u32x2 b) { return u32x4{a[0], a[1], b[0], b[1]}; }
 
-// K and V blocks of one chunk: block index b = tid + i*NT over [K | V]
-// (2*NB blocks; each half is a whole number of waves, so the tile choice and
-// whether a wave loads at all are wave-uniform).
-template <int D, int R, int NT>
-struct KVSplit {
-    static constexpr int NPER = (2 * Stage<D, R>::NB + NT - 1) / NT;
+// K and V blocks of one chunk: all D features of K, and the DVW features of V
+// starting at feature vcg0 * 8 (a workgroup that computes only part of the
+// output features needs only that part of V).  Block index b = tid + i*NT
+// over [K | V]; each half is a whole number of waves, so the tile choice and
+// whether a wave loads at all are wave-uniform.
+template <int D, int DVW, int R, int NT>
+struct KVStage {
+    static constexpr int NCGK = D / 8, NCGV = DVW / 8;   // 8-feature groups per row
+    static constexpr int NBK = (kChunk / R) * NCGK;     // K blocks
+    static constexpr int NBV = (kChunk / R) * NCGV;     // V blocks
+    static constexpr int NPER = (NBK + NBV + NT - 1) / NT;
+    static_assert(NBK % 64 == 0 && NBV % 64 == 0, "K and V parts are whole waves");
 };
 
-template <int D, int R, int NT, int NPER>
+template <int D, int DVW, int R, int NT, int NPER>
 __device__ __forceinline__ void load_kv(BlkR<R> (&pre)[NPER], __amdgpu_buffer_rsrc_t rk,
-                                        __amdgpu_buffer_rsrc_t rv, int H, int h) {
-    using ST = Stage<D, R>;
+                                        __amdgpu_buffer_rsrc_t rv, int vcg0, int H, int h) {
+    using KS = KVStage<D, DVW, R, NT>;
     const int wbase = wave_id() * 64;
     const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int i = 0; i < NPER; ++i) {
-        if constexpr (NPER * NT > 2 * ST::NB)
-            if (wbase + i * NT >= 2 * ST::NB) break;           // wave-uniform
-        const bool is_v = wbase + i * NT >= ST::NB;             // wave-uniform
-        const int within = wbase + i * NT + lane - (is_v ? ST::NB : 0);
-        load_blk<R>(pre[i], is_v ? rv : rk, within / ST::NCG, within % ST::NCG, H, h, D);
+        const int b0 = wbase + i * NT;                      // wave-uniform
+        if constexpr (NPER * NT > KS::NBK + KS::NBV)
+            if (b0 >= KS::NBK + KS::NBV) break;
+        const bool is_v = b0 >= KS::NBK;
+        const int wk = b0 + lane, wv = b0 - KS::NBK + lane;
+        // selects, not branches: the loads stay unconditional
+        const int rg = is_v ? wv / KS::NCGV : wk / KS::NCGK;
+        const int cg = is_v ? vcg0 + wv % KS::NCGV : wk % KS::NCGK;
+        load_blk<R>(pre[i], is_v ? rv : rk, rg, cg, H, h, D);
     }
 }
 
-// Registers -> LDS: K transposed (and row-major if sK is given), V transposed.
-template <int D, int R, int NT, int NPER>
+// Registers -> LDS: K transposed (and row-major if sK is given), V transposed
+// (rows are the workgroup's own V features, 0 .. DVW-1).
+template <int D, int DVW, int R, int NT, int NPER>
 __device__ __forceinline__ void stage_kv(const BlkR<R> (&pre)[NPER], uint16_t* sK,
                                          uint16_t* sKt, uint16_t* sVt) {
+    using KS = KVStage<D, DVW, R, NT>;
     using ST = Stage<D, R>;
     const int wbase = wave_id() * 64;
     const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int i = 0; i < NPER; ++i) {
-        if constexpr (NPER * NT > 2 * ST::NB)
-            if (wbase + i * NT >= 2 * ST::NB) break;           // wave-uniform
-        const bool is_v = wbase + i * NT >= ST::NB;             // wave-uniform
-        const int within = wbase + i * NT + lane - (is_v ? ST::NB : 0);
-        const int rg = within / ST::NCG, cg = within % ST::NCG;
-        if (is_v) {
-            store_cols<R>(sVt, pre[i], rg, cg, ST::LDT);
+        const int b0 = wbase + i * NT;                      // wave-uniform
+        if constexpr (NPER * NT > KS::NBK + KS::NBV)
+            if (b0 >= KS::NBK + KS::NBV) break;
+        if (b0 >= KS::NBK) {
+            const int wv = b0 - KS::NBK + lane;
+            store_cols<R>(sVt, pre[i], wv / KS::NCGV, wv % KS::NCGV, ST::LDT);
         } else {
-            if (sK) store_rows<R>(sK, pre[i], rg, cg, ST::LDR);
-            store_cols<R>(sKt, pre[i], rg, cg, ST::LDT);
+            const int wk = b0 + lane;
+            if (sK) store_rows<R>(sK, pre[i], wk / KS::NCGK, wk % KS::NCGK, ST::LDR);
+            store_cols<R>(sKt, pre[i], wk / KS::NCGK, wk % KS::NCGK, ST::LDT);
         }
     }
+}
+
+// Work items (one per block or delta block and head) split over NP
+// workgroups by output feature.  Workgroups go to the 8 XCDs round-robin by
+// id, so the NP parts of one item get ids 8 apart: they run on one XCD at
+// about the same time and their common q / k reads meet in its L2.
+template <int NP>
+__device__ __forceinline__ void split_id(int bid, int& item, int& part) {
+    if constexpr (NP == 1) {
+        item = bid;
+        part = 0;
+    } else {
+        item = (bid / (8 * NP)) * 8 + bid % 8;
+        part = (bid / 8) % NP;
+    }
+}
+template <int NP>
+inline int64_t split_grid(int64_t items) {
+    return NP == 1 ? items : (items + 7) / 8 * 8 * NP;
 }
 
 // ---------------------------------------------------------------------------
@@ -272,55 +304,78 @@ struct ScanDesc {
 };
 
 // ===========================================================================
-// Launch 1: per delta block and head, sum over chunks of K_c^T V_c.
+// Launch 1: per delta block and head, sum over chunks of K_c^T V_c.  NP
+// workgroups share a (delta block, head) item, each summing the state
+// columns of D / NP value features (it reads all of K and its part of V).
 // ===========================================================================
-template <int D>
+template <int D, int NP>
+struct Delta1 {
+    static constexpr int NW = 4;                       // waves per workgroup
+    static constexpr int R = 4;                        // tokens per staging block
+    static constexpr int DVW = D / NP;                 // value features per workgroup
+    static constexpr int NKB = D / 16, NVB = DVW / 16;
+    // a wave owns VBW column blocks x KBW row blocks of the state
+    static constexpr int VBW = NVB >= NW ? NVB / NW : 1;
+    static constexpr int KBW = NVB >= NW ? NKB : NKB * NVB / NW;
+    static_assert(NVB % NW == 0 || NW % NVB == 0, "state tiles split evenly over the waves");
+    __device__ static int vb0(int w) { return NVB >= NW ? w * VBW : w % NVB; }
+    __device__ static int kb0(int w) { return NVB >= NW ? 0 : (w / NVB) * KBW; }
+};
+
+template <int D, int NP>
 __global__ __launch_bounds__(kThreads) void delta_kernel_bf16(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const DeltaDesc* __restrict__ deltas, float* __restrict__ ws, int H) {
-    constexpr int R = 4;
+    const DeltaDesc* __restrict__ deltas, float* __restrict__ ws, int H, int n_items) {
+    using D1 = Delta1<D, NP>;
+    constexpr int R = D1::R, DVW = D1::DVW, NKB = D1::NKB, NVB = D1::NVB;
+    constexpr int VBW = D1::VBW, KBW = D1::KBW, DD = D * D;
     using ST = Stage<D, R>;
-    constexpr int NKB = D / 16, VBW = D / 64, DD = D * D;
-    constexpr int NPER = KVSplit<D, R, kThreads>::NPER;
+    constexpr int NPER = KVStage<D, DVW, R, kThreads>::NPER;
     __shared__ __attribute__((aligned(16))) uint16_t sKt[D * ST::LDT];
-    __shared__ __attribute__((aligned(16))) uint16_t sVt[D * ST::LDT];
+    __shared__ __attribute__((aligned(16))) uint16_t sVt[DVW * ST::LDT];
 
-    const int h = blockIdx.x % H;
-    const DeltaDesc dd = deltas[blockIdx.x / H];
+    int item, part;
+    split_id<NP>(blockIdx.x, item, part);
+    if (item >= n_items) return;   // whole workgroup: padding of the split grid
+    const int h = item % H;
+    const DeltaDesc dd = deltas[item / H];
     const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+    const int vbw = D1::vb0(w), kbw = D1::kb0(w);
 
-    f32x4 S[VBW][NKB];
+    f32x4 S[VBW][KBW];
 #pragma unroll
     for (int x = 0; x < VBW; ++x)
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) S[x][kb] = zero4();
+        for (int i = 0; i < KBW; ++i) S[x][i] = zero4();
 
     const int nch = (dd.ntok + kChunk - 1) / kChunk;
     const int64_t row_elems = int64_t(H) * D;
+    const int vcg0 = part * (DVW / 8);
     // two chunks in flight: registers A hold chunk c, B chunk c + 1
     BlkR<R> pa[NPER], pb[NPER];
     auto load = [&](BlkR<R> (&dst)[NPER], int c) {
         const int64_t first = (int64_t(dd.tok0) + c * kChunk) * row_elems;
         const int rows = min(kChunk, dd.ntok - c * kChunk);   // <= 0: empty window
-        load_kv<D, R, kThreads, NPER>(dst, chunk_rsrc(k, first, 2, rows, H, D),
-                                      chunk_rsrc(v, first, 2, rows, H, D), H, h);
+        load_kv<D, DVW, R, kThreads, NPER>(dst, chunk_rsrc(k, first, 2, rows, H, D),
+                                           chunk_rsrc(v, first, 2, rows, H, D), vcg0, H, h);
     };
     auto step = [&](BlkR<R> (&cur)[NPER], int c) {
-        stage_kv<D, R, kThreads, NPER>(cur, nullptr, sKt, sVt);
+        stage_kv<D, DVW, R, kThreads, NPER>(cur, nullptr, sKt, sVt);
         __syncthreads();
         load(cur, c + 2);   // empty window past the last chunk
 #pragma unroll
         for (int ks = 0; ks < kChunk / 32; ++ks) {
 #pragma unroll
             for (int x = 0; x < VBW; ++x) {
-                const int vb = w * VBW + x;
+                const int vb = vbw + x;
                 const u32x4 bv = lds_u32x4(sVt + (vb * 16 + c16) * ST::LDT +
                                            tpos(vb * 16, ks * 32 + 4 * g));
 #pragma unroll
-                for (int kb = 0; kb < NKB; ++kb) {
+                for (int i = 0; i < KBW; ++i) {
+                    const int kb = kbw + i;
                     const u32x4 ak = lds_u32x4(sKt + (kb * 16 + c16) * ST::LDT +
                                                tpos(kb * 16, ks * 32 + 4 * g));
-                    S[x][kb] = mfma_bf16(ak, bv, S[x][kb]);
+                    S[x][i] = mfma_bf16(ak, bv, S[x][i]);
                 }
             }
         }
@@ -337,10 +392,10 @@ __global__ __launch_bounds__(kThreads) void delta_kernel_bf16(
 #pragma unroll
     for (int x = 0; x < VBW; ++x)
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
+        for (int i = 0; i < KBW; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                dst[(((w * VBW + x) * NKB + kb) * 4 + j) * 64 + lane] = S[x][kb][j];
+                dst[(((part * NVB + vbw + x) * NKB + kbw + i) * 4 + j) * 64 + lane] = S[x][i][j];
 }
 
 // fp32 tiles: row-major [64][D+4] floats in LDS, loaded as 16-byte pieces.
@@ -535,21 +590,62 @@ __device__ __forceinline__ void init_state(f32x4 (&S)[D / 64][D / 16], const Blo
 }
 
 
-// Launch 3 (bf16) runs NW = 4 (d = 64) or 8 (d = 128) waves per workgroup.
-// Wave w = 4 hv + tb computes the outputs of tokens tb*16 .. tb*16+15 for the
-// output features of part hv (all features with 4 waves, half with 8), and
-// owns TPW state tiles (vb_own, kb0 .. kb0+TPW-1) for the carry.
-template <int D>
+// Launch 3 (bf16): NP workgroups share a (work block, head) item, each
+// computing the DV = D / NP output features starting at part * DV and
+// carrying the matching state columns.  NW waves per workgroup: wave
+// w = 4 hv + tb computes the outputs of tokens tb*16 .. tb*16+15 for VBH
+// feature tiles (feature part hv of the workgroup's DV features), and owns
+// TPW state tiles (vb_own, kb0 .. kb0+TPW-1; vb_own local to the part) for
+// the carry.
+template <int D, int NP, int NW_>
 struct Out3 {
-    static constexpr int NW = D == 64 ? 4 : 8;        // waves per workgroup
+    static constexpr int NP_ = NP, NW = NW_;
     static constexpr int NT = 64 * NW;
     static constexpr int R = 4;                       // tokens per staging block
-    static constexpr int NKB = D / 16, NVB = D / 16, NKS = D / 32;
-    static constexpr int VBH = NVB * 4 / NW;          // output tiles per wave
+    static constexpr int DV = D / NP;                 // output features per workgroup
+    static constexpr int NKB = D / 16, NVB = DV / 16, NKS = D / 32;
+    static constexpr int NHV = NW / 4;                // feature parts per workgroup
+    static constexpr int VBH = NVB / NHV;             // output tiles per wave
     static constexpr int TPW = NVB * NKB / NW;        // carry tiles per wave
-    static_assert(NKB % TPW == 0, "a wave's carry tiles share one state column block");
+    static_assert(NW % 4 == 0 && NVB % NHV == 0, "waves cover 4 token blocks x feature parts");
+    static_assert(NW % NVB == 0 && NKB % TPW == 0,
+                  "a wave's carry tiles share one state column block");
     __device__ static int vb_own(int w) { return w % NVB; }
     __device__ static int kb0(int w) { return (w / NVB) * TPW; }
+};
+
+// Launch configurations, chosen by measurement on MI355X: launch 1 splits
+// each item over DELTA_NP workgroups, launch 3 over OUT_NP workgroups of
+// OUT_NW waves.
+#ifndef LA_DELTA_NP_64
+#define LA_DELTA_NP_64 1
+#endif
+#ifndef LA_DELTA_NP_128
+#define LA_DELTA_NP_128 1
+#endif
+#ifndef LA_OUT_NP_64
+#define LA_OUT_NP_64 1
+#endif
+#ifndef LA_OUT_NW_64
+#define LA_OUT_NW_64 4
+#endif
+#ifndef LA_OUT_NP_128
+#define LA_OUT_NP_128 2
+#endif
+#ifndef LA_OUT_NW_128
+#define LA_OUT_NW_128 4
+#endif
+template <int D>
+struct LaunchCfg;
+template <>
+struct LaunchCfg<64> {
+    static constexpr int DELTA_NP = LA_DELTA_NP_64;
+    using O3 = Out3<64, LA_OUT_NP_64, LA_OUT_NW_64>;
+};
+template <>
+struct LaunchCfg<128> {
+    static constexpr int DELTA_NP = LA_DELTA_NP_128;
+    using O3 = Out3<128, LA_OUT_NP_128, LA_OUT_NW_128>;
 };
 
 // The outputs of one wave for one chunk: its 16 tokens (token block TB) and
@@ -618,32 +714,35 @@ __device__ __forceinline__ void out_tiles(const uint16_t* sK, const uint16_t* sV
     }
 }
 
-template <int D>
-__global__ __launch_bounds__(Out3<D>::NT) void output_kernel_bf16(
+template <int D, class O3>
+__global__ __launch_bounds__(O3::NT) void output_kernel_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const BlockDesc* __restrict__ blocks,
     const float* __restrict__ ws, const float* __restrict__ final_state,
-    const float* __restrict__ ext_state, uint16_t* __restrict__ out, int H) {
-    using O3 = Out3<D>;
-    constexpr int R = O3::R, NT = O3::NT;
+    const float* __restrict__ ext_state, uint16_t* __restrict__ out, int H, int n_items) {
+    constexpr int R = O3::R, NT = O3::NT, NP = O3::NP_, DV = O3::DV;
     using ST = Stage<D, R>;
-    constexpr int NKB = O3::NKB, NKS = O3::NKS, VBH = O3::VBH, TPW = O3::TPW;
+    constexpr int NKB = O3::NKB, NVB = O3::NVB, NKS = O3::NKS, VBH = O3::VBH, TPW = O3::TPW;
     constexpr int DD = D * D;
-    constexpr int NPER = KVSplit<D, R, NT>::NPER;
+    constexpr int NPER = KVStage<D, DV, R, NT>::NPER;
     constexpr int LDR = ST::LDR, LDT = ST::LDT;
     __shared__ __attribute__((aligned(16))) uint16_t sK[kChunk * LDR];
     __shared__ __attribute__((aligned(16))) uint16_t sKt[D * LDT];
-    __shared__ __attribute__((aligned(16))) uint16_t sVt[D * LDT];
-    __shared__ __attribute__((aligned(16))) uint16_t sSh[D * LDR];   // S^T, bf16 high term
-    __shared__ __attribute__((aligned(16))) uint16_t sSl[D * LDR];   // S^T, bf16 low term
+    __shared__ __attribute__((aligned(16))) uint16_t sVt[DV * LDT];
+    __shared__ __attribute__((aligned(16))) uint16_t sSh[DV * LDR];   // S^T, bf16 high term
+    __shared__ __attribute__((aligned(16))) uint16_t sSl[DV * LDR];   // S^T, bf16 low term
 
-    const int h = blockIdx.x % H;
-    const BlockDesc bd = blocks[blockIdx.x / H];
+    int item, part;
+    split_id<NP>(blockIdx.x, item, part);
+    if (item >= n_items) return;   // whole workgroup: padding of the split grid
+    const int h = item % H;
+    const BlockDesc bd = blocks[item / H];
     const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, g = lane >> 4, c16 = lane & 15;
     const int tb = w & 3, hv = w >> 2;
-    const int vbo = O3::vb_own(w), kbo = O3::kb0(w);
+    const int vbo = O3::vb_own(w), kbo = O3::kb0(w);   // vbo local to the part
+    const int vbg = part * NVB + vbo;                   // global column block
 
-    // carry state: tiles (vbo, kbo + i); lane holds S[kb*16 + 4g + j][vbo*16 + c16]
+    // carry state: tiles (vbg, kbo + i); lane holds S[kb*16 + 4g + j][vbg*16 + c16]
     f32x4 S[TPW];
 #pragma unroll
     for (int i = 0; i < TPW; ++i) S[i] = zero4();
@@ -658,7 +757,7 @@ __global__ __launch_bounds__(Out3<D>::NT) void output_kernel_bf16(
             for (int i = 0; i < TPW; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    S[i][j] = seed[((kbo + i) * 16 + 4 * g + j) * D + vbo * 16 + c16];
+                    S[i][j] = seed[((kbo + i) * 16 + 4 * g + j) * D + vbg * 16 + c16];
         }
         if (bd.sin_slot >= 0) {
             const float* src = ws + ((int64_t)bd.sin_slot * H + h) * DD;
@@ -666,7 +765,7 @@ __global__ __launch_bounds__(Out3<D>::NT) void output_kernel_bf16(
             for (int i = 0; i < TPW; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    S[i][j] += src[((vbo * NKB + kbo + i) * 4 + j) * 64 + lane];
+                    S[i][j] += src[((vbg * NKB + kbo + i) * 4 + j) * 64 + lane];
         }
     }
 
@@ -676,7 +775,9 @@ __global__ __launch_bounds__(Out3<D>::NT) void output_kernel_bf16(
     // row pieces inside a chunk window
     const int trow = tb * 16 + c16;
     const uint32_t qoff = uint32_t(((trow * H + h) * D + 8 * g) * 2);
-    const uint32_t ooff = uint32_t(((trow * H + h) * D + hv * VBH * 16 + 4 * g) * 2);
+    const uint32_t ooff =
+        uint32_t(((trow * H + h) * D + part * DV + hv * VBH * 16 + 4 * g) * 2);
+    const int vcg0 = part * (DV / 8);
 
     // one chunk in flight: kv / qn hold chunk c + 1 while chunk c is computed
     BlkR<R> kv[NPER];
@@ -684,8 +785,8 @@ __global__ __launch_bounds__(Out3<D>::NT) void output_kernel_bf16(
     auto load = [&](int c) {
         const int64_t first = (int64_t(bd.tok0) + c * kChunk) * row_elems;
         const int rows = min(kChunk, bd.ntok - c * kChunk);   // <= 0: empty window
-        load_kv<D, R, NT, NPER>(kv, chunk_rsrc(k, first, 2, rows, H, D),
-                                chunk_rsrc(v, first, 2, rows, H, D), H, h);
+        load_kv<D, DV, R, NT, NPER>(kv, chunk_rsrc(k, first, 2, rows, H, D),
+                                    chunk_rsrc(v, first, 2, rows, H, D), vcg0, H, h);
         const auto rq = chunk_rsrc(q, first, 2, rows, H, D);
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) qn[ks] = buf_load16(rq, qoff + ks * 64);
@@ -693,7 +794,7 @@ __global__ __launch_bounds__(Out3<D>::NT) void output_kernel_bf16(
     load(0);
     for (int c = 0; c < nch; ++c) {
         // publish S^T = S_hi + S_lo (bf16 terms) for the inter-chunk product;
-        // lane holds 4 consecutive d_k of row vbo*16 + c16 of S^T per tile
+        // lane holds 4 consecutive d_k of row vbo*16 + c16 of the part's S^T
 #pragma unroll
         for (int i = 0; i < TPW; ++i) {
             const f32x4 s = S[i];
@@ -704,7 +805,7 @@ __global__ __launch_bounds__(Out3<D>::NT) void output_kernel_bf16(
             *reinterpret_cast<u32x2*>(sSh + off) = u32x2{h01, h23};
             *reinterpret_cast<u32x2*>(sSl + off) = u32x2{l01, l23};
         }
-        stage_kv<D, R, NT, NPER>(kv, sK, sKt, sVt);
+        stage_kv<D, DV, R, NT, NPER>(kv, sK, sKt, sVt);
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) qf[ks] = qn[ks];
         __syncthreads();
@@ -714,7 +815,7 @@ __global__ __launch_bounds__(Out3<D>::NT) void output_kernel_bf16(
         const int rows = min(kChunk, bd.ntok - c * kChunk);
         const int64_t first = (int64_t(bd.tok0) + c * kChunk) * row_elems;
 
-        // O^T tiles: this wave's 16 tokens, features hv*VBH*16 .. +VBH*16-1
+        // O^T tiles: this wave's 16 tokens, local feature tiles hv*VBH .. +VBH-1
         f32x4 acc[VBH];
         switch (tb) {
             case 0: out_tiles<D, 0, VBH>(sK, sVt, sSh, sSl, qf, hv * VBH, g, c16, acc); break;
@@ -722,7 +823,7 @@ __global__ __launch_bounds__(Out3<D>::NT) void output_kernel_bf16(
             case 2: out_tiles<D, 2, VBH>(sK, sVt, sSh, sSl, qf, hv * VBH, g, c16, acc); break;
             default: out_tiles<D, 3, VBH>(sK, sVt, sSh, sSl, qf, hv * VBH, g, c16, acc); break;
         }
-        // lane holds O[t = tb*16 + c16][(hv*VBH + x)*16 + 4g + j], j = 0..3
+        // lane holds O[t = tb*16 + c16][part*DV + (hv*VBH + x)*16 + 4g + j], j = 0..3
         {
             const auto ro = chunk_rsrc(out, first, 2, rows, H, D);
 #pragma unroll
@@ -853,6 +954,18 @@ bool supported_dims(int32_t d_k, int32_t d_v) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Every launch's grid, in work-items, must fit the 32-bit dispatch size.
+template <int D>
+bool grids_fit(const la_pass_info& info, int32_t H) {
+    constexpr int64_t kMax = (int64_t(1) << 32) - 1;
+    using O3 = typename LaunchCfg<D>::O3;
+    const int64_t l1 = split_grid<LaunchCfg<D>::DELTA_NP>(int64_t(info.n_delta) * H) * kThreads;
+    const int64_t l2 = int64_t(info.n_scan) * H * (D * D);
+    const int64_t l3 = split_grid<O3::NP_>(int64_t(info.n_blocks) * H) *
+                       (O3::NT > kThreads ? O3::NT : kThreads);
+    return l1 <= kMax && l2 <= kMax && l3 <= kMax;
+}
+
 template <int D>
 la_status launch_all(int32_t stages, const void* q, const void* k, const void* v, la_dtype dtype, int32_t H,
                      const la_pass_info& info, const int32_t* plan, const float* ext_state,
@@ -865,13 +978,14 @@ la_status launch_all(int32_t stages, const void* q, const void* k, const void* v
     const auto* scans = reinterpret_cast<const ScanDesc*>(plan + off_scan);
     const dim3 blk(kThreads);
     if ((stages & LA_STAGE_STATES) && info.n_delta > 0) {
-        const dim3 grid(unsigned(int64_t(info.n_delta) * H));
+        const int items = info.n_delta * H;
+        constexpr int NP = LaunchCfg<D>::DELTA_NP;
         if (dtype == LA_BF16)
-            hipLaunchKernelGGL(delta_kernel_bf16<D>, grid, blk, 0, st,
-                               static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
-                               deltas, ws, H);
+            hipLaunchKernelGGL((delta_kernel_bf16<D, NP>), dim3(unsigned(split_grid<NP>(items))),
+                               blk, 0, st, static_cast<const uint16_t*>(k),
+                               static_cast<const uint16_t*>(v), deltas, ws, H, items);
         else
-            hipLaunchKernelGGL(delta_kernel_f32<D>, grid, blk, 0, st,
+            hipLaunchKernelGGL(delta_kernel_f32<D>, dim3(unsigned(items)), blk, 0, st,
                                static_cast<const float*>(k), static_cast<const float*>(v), deltas,
                                ws, H);
         if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
@@ -882,14 +996,16 @@ la_status launch_all(int32_t stages, const void* q, const void* k, const void* v
         if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
     }
     if ((stages & LA_STAGE_OUTPUT) && info.n_blocks > 0) {
-        const dim3 grid(unsigned(int64_t(info.n_blocks) * H));
+        const int items = info.n_blocks * H;
+        using O3 = typename LaunchCfg<D>::O3;
         if (dtype == LA_BF16)
-            hipLaunchKernelGGL(output_kernel_bf16<D>, grid, dim3(Out3<D>::NT), 0, st,
+            hipLaunchKernelGGL((output_kernel_bf16<D, O3>),
+                               dim3(unsigned(split_grid<O3::NP_>(items))), dim3(O3::NT), 0, st,
                                static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                static_cast<const uint16_t*>(v), blocks, ws, final_state,
-                               ext_state, static_cast<uint16_t*>(out), H);
+                               ext_state, static_cast<uint16_t*>(out), H, items);
         else
-            hipLaunchKernelGGL(output_kernel_f32<D>, grid, blk, 0, st,
+            hipLaunchKernelGGL(output_kernel_f32<D>, dim3(unsigned(items)), blk, 0, st,
                                static_cast<const float*>(q), static_cast<const float*>(k),
                                static_cast<const float*>(v), blocks, ws, final_state, ext_state,
                                static_cast<float*>(out), H);
@@ -926,9 +1042,7 @@ extern "C" la_status la_scan_packed_stages(int32_t stages, const void* q, const 
     if (int64_t(info->n_tokens) * H * d_k >= (int64_t(1) << 40)) return LA_ERR_INVALID_ARG;
     // a chunk window (64 token rows of all heads) must fit a 32-bit buffer range
     if (int64_t(kChunk) * H * d_k * 4 >= (int64_t(1) << 31)) return LA_ERR_INVALID_ARG;
-    if (int64_t(info->n_blocks) * H >= (int64_t(1) << 31) ||
-        int64_t(info->n_delta) * H >= (int64_t(1) << 31) ||
-        int64_t(info->n_scan) * H * (int64_t(d_k) * d_k / kThreads) >= (int64_t(1) << 31))
+    if (!(d_k == 64 ? grids_fit<64>(*info, H) : grids_fit<128>(*info, H)))
         return LA_ERR_INVALID_ARG;
     if (!q || !k || !v || !out || !plan) return LA_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
