@@ -50,6 +50,13 @@ def parse():
                          "(reference for scaling FETCH_SIZE / WRITE_SIZE counters)")
     ap.add_argument("--launch-floor", action="store_true",
                     help="only time three chained near-empty launches per step")
+    ap.add_argument("--shards", type=int, default=0,
+                    help="instead of the headline: split the workload's one request "
+                         "into this many branch shards and time them with and without "
+                         "the view-state cache against the unsplit pass")
+    ap.add_argument("--cost-model", type=int, default=0,
+                    help="instead of the headline: time this many random pass shapes and "
+                         "fit the three-term cost model t = c0 + c1*sum(view) + c2*branches")
     return ap.parse_args()
 
 
@@ -152,6 +159,197 @@ def cpu_baseline(w, so, bp, target_s):
                       f"median wall {wall:.3f} s, {cpu:.1f} s CPU work, {model}"}
 
 
+def _graph_us(fn, steps, warmup, stream, eager=False):
+    """Mean device time of fn() over `steps` calls replayed as one HIP graph
+    (eager stream launches with eager=True), after `warmup` calls."""
+    import torch
+    with torch.cuda.stream(stream):
+        for _ in range(max(warmup, 1)):
+            fn()
+    torch.cuda.synchronize()
+    if eager:
+        run = lambda: [fn() for _ in range(steps)]
+    else:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for _ in range(steps):
+                fn()
+        run = g.replay
+        with torch.cuda.stream(stream):
+            run()
+        torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        run()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / steps
+
+
+def shard_bench(a):
+    """Branch shards of one long request on one GPU (section "Long Requests":
+    shards each need the full view; cached view states avoid recomputing it).
+
+    The workload's single request (view V, branches b_1..b_n) is scored three
+    ways, each as one step of the graph-replayed timing:
+      unsplit   one pass over the view and all branches;
+      cached    shard 0 = view + its branches, its view state stored in a
+                ViewStateCache, then shards 1..S-1 as branch-only passes
+                seeded from the cache pool;
+      uncached  every shard = view + its branches (the view recomputed S times).
+    All passes use the unsplit pass's block size, so the shard outputs equal
+    the unsplit ones bit for bit (checked here).  Inputs are already in HBM."""
+    import numpy as np
+    import torch
+    import chunked_linear_attention_packed_amd as la
+    import synth
+    w = synth.workload(a.workload)
+    if len(w.view_len) != 1 or w.view_len[0] < 1:
+        raise SystemExit("--shards needs a workload with one request that has a view")
+    V, lens, H, d = int(w.view_len[0]), np.asarray(w.branch_len), w.H, w.d
+    n, S = len(lens), a.shards
+    if not 1 <= S <= n:
+        raise SystemExit(f"--shards must be between 1 and the {n} branches")
+    dev = torch.device("cuda:0")
+    q, k, v = (x.to(dev) for x in (w.q, w.k, w.v))
+    off = np.concatenate([[0], np.cumsum(np.concatenate([[V], lens]))]).astype(np.int64)
+    plan_u = la.pack([V], [n], lens, heads=H, block_chunks=a.block_chunks)
+    G = plan_u.info.block_chunks
+    stream = torch.cuda.Stream(dev)
+
+    def make(plan, qq, kk, vv, ext=None):
+        qq, kk, vv = qq.contiguous(), kk.contiguous(), vv.contiguous()
+        out = torch.empty_like(vv)
+        fin = torch.empty((plan.info.n_views, H, d, d), dtype=torch.float32, device=dev)
+        ws = torch.empty(max(la.workspace_size(plan, H, d, qq.dtype), 1), dtype=torch.uint8,
+                         device=dev)
+        plan.device_plan(dev)
+        return dict(plan=plan, q=qq, k=kk, v=vv, out=out, fin=fin, ws=ws, ext=ext)
+
+    def run(p):
+        la.scan_packed(p["q"], p["k"], p["v"], p["plan"], ext_state=p["ext"], out=p["out"],
+                       final_state=p["fin"], workspace=p["ws"], stream=stream)
+
+    unsplit = make(plan_u, q, k, v)
+    cache = la.ViewStateCache(1, H, d, dev)
+    row, _ = cache.reserve(0)
+    parts = np.array_split(np.arange(n), S)
+    cached, uncached = [], []
+    for s, idx in enumerate(parts):
+        b0, b1 = int(idx[0]), int(idx[-1]) + 1
+        t0, t1 = int(off[1 + b0]), int(off[1 + b1])
+        sel = torch.cat([torch.arange(0, V), torch.arange(t0, t1)]).to(dev)
+        full = make(la.pack([V], [b1 - b0], lens[b0:b1], heads=H, block_chunks=G),
+                    q[sel], k[sel], v[sel])
+        uncached.append(full)
+        if s == 0:
+            cached.append(full)
+        else:
+            cached.append(make(la.pack([0], [b1 - b0], lens[b0:b1], heads=H, block_chunks=G,
+                                       ext_row=[row]),
+                               q[t0:t1], k[t0:t1], v[t0:t1], ext=cache.pool))
+
+    def step_unsplit():
+        run(unsplit)
+
+    def step_cached():
+        run(cached[0])
+        la.export_view_state(cached[0]["fin"], 0, cache.pool[row], stream=stream)
+        for p in cached[1:]:
+            run(p)
+
+    def step_uncached():
+        for p in uncached:
+            run(p)
+
+    us_u = _graph_us(step_unsplit, a.steps, a.warmup, stream, a.eager)
+    us_c = _graph_us(step_cached, a.steps, a.warmup, stream, a.eager)
+    us_n = _graph_us(step_uncached, a.steps, a.warmup, stream, a.eager)
+    # the shard outputs are the unsplit outputs, bit for bit
+    match = True
+    for s, idx in enumerate(parts):
+        t0, t1 = int(off[1 + idx[0]]), int(off[1 + idx[-1] + 1])
+        got = cached[s]["out"][V:] if s == 0 else cached[s]["out"]
+        match &= bool(torch.equal(got, unsplit["out"][t0:t1]))
+    T = int(off[-1])
+    print(json.dumps({
+        "experiment": "branch shards from a cached view state, one GPU",
+        "workload": a.workload, "tokens": T, "view_tokens": V, "branches": n, "shards": S,
+        "heads": H, "d": d, "dtype": w.dtype, "block_chunks": G,
+        "launch": "eager" if a.eager else "hip_graph", "steps": a.steps,
+        "unsplit_us": us_u, "cached_shards_us": us_c, "uncached_shards_us": us_n,
+        "uncached_over_cached": us_n / us_c, "cached_over_unsplit": us_c / us_u,
+        "tokens_per_s_cached": T / (us_c * 1e-6),
+        "shard_outputs_equal_unsplit": match,
+        "page_context": "the page reports shards without the cache taking 3.4x as long as "
+                        "with it (whole model, 349 requests, older hardware)",
+    }), flush=True)
+    cache.close()
+
+
+def cost_model_bench(a):
+    """Pass times of random pass shapes and the page's three-term cost model
+    fitted to them (section "Cost Model").  Shapes: 1-8 requests, views
+    log-uniform in [500, 18000] tokens, 1-64 branches of 24-128 tokens per
+    request (the page's ranges), H = 16, d = 64, bf16 -- seed 2024.  Each
+    pass is timed as `steps` graph-replayed passes after its warm-up.  The
+    fit uses the even-numbered shapes; the odd ones are predicted (hold-out)."""
+    import numpy as np
+    import torch
+    import chunked_linear_attention_packed_amd as la
+    from chunked_linear_attention_packed_amd import cost_model as cm
+    import synth
+    rng = np.random.default_rng(2024)
+    H, d = 16, 64
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream(dev)
+    rows = []
+    for i in range(a.cost_model):
+        r = int(rng.integers(1, 9))
+        vl = np.round(np.exp(rng.uniform(np.log(500), np.log(18000), size=r))).astype(np.int32)
+        bc = rng.integers(1, 65, size=r).astype(np.int32)
+        bl = rng.integers(24, 129, size=int(bc.sum())).astype(np.int32)
+        plan = la.pack(vl, bc, bl, heads=H, block_chunks=a.block_chunks)
+        T = plan.info.n_tokens
+        q, k, v = (x.to(dev) for x in synth.draw_qkv(rng, T, H, d, "bf16"))
+        out = torch.empty_like(v)
+        fin = torch.empty((plan.info.n_views, H, d, d), dtype=torch.float32, device=dev)
+        ws = torch.empty(max(la.workspace_size(plan, H, d, q.dtype), 1), dtype=torch.uint8,
+                         device=dev)
+        plan.device_plan(dev)
+        fn = lambda: la.scan_packed(q, k, v, plan, out=out, final_state=fin, workspace=ws,
+                                    stream=stream)
+        us = _graph_us(fn, a.steps, a.warmup, stream, a.eager)
+        rows.append((vl.tolist(), bc.tolist(), int(bl.sum()), T, us))
+        print(f"pass {i}: requests {r} tokens {T} branches {int(bc.sum())} "
+              f"block_chunks {plan.info.block_chunks} {us:.1f} us", file=sys.stderr, flush=True)
+        del q, k, v, out, fin, ws
+    X = np.array([cm.features(vl, bc) for vl, bc, _, _, _ in rows])
+    Xt = np.array([[1.0, float(np.sum(vl)), float(bt)] for vl, _, bt, _, _ in rows])
+    t = np.array([us for *_, us in rows])
+    tr, te = np.arange(0, len(t), 2), np.arange(1, len(t), 2)
+
+    def holdout(Xm):
+        f = cm.fit(Xm[tr], t[tr])
+        rel = (Xm[te] @ np.array(f["c"]) - t[te]) / t[te]
+        f["holdout_rel_rms"] = float(np.sqrt(np.mean(rel ** 2))) if len(te) else None
+        f["holdout_rel_max"] = float(np.max(np.abs(rel))) if len(te) else None
+        return f
+
+    print(json.dumps({
+        "experiment": "three-term pass cost model",
+        "model": "t_us = c0 + c1 * sum(view tokens) + c2 * branch rows",
+        "heads": H, "d": d, "dtype": "bf16", "passes": len(t), "steps_per_pass": a.steps,
+        "launch": "eager" if a.eager else "hip_graph",
+        "fit_all": cm.fit(X, t), "fit_even_holdout_odd": holdout(X),
+        "variant_branch_tokens": {"model": "t_us = c0 + c1 * sum(view) + c2 * sum(branch tokens)",
+                                  "fit_all": cm.fit(Xt, t), "fit_even_holdout_odd": holdout(Xt)},
+        "samples": [{"view_len": vl, "branches": int(np.sum(bc)), "branch_tokens": bt,
+                     "tokens": T, "us": us} for vl, bc, bt, T, us in rows],
+    }), flush=True)
+
+
 def traffic_from_profiles(kernel_tag, workload, src_hash):
     """HBM bytes per launch of the dominant kernel from committed rocprofv3
     --pmc summaries, only if they were taken on the current kernel source."""
@@ -186,6 +384,12 @@ def main():
         return
     if a.launch_floor:
         launch_floor(a.steps)
+        return
+    if a.shards:
+        shard_bench(a)
+        return
+    if a.cost_model:
+        cost_model_bench(a)
         return
     la.load_library()
     dev = torch.device("cuda:0")

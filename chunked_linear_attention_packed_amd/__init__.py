@@ -11,6 +11,15 @@ sections "The Workload", "Kernels" and "Long Requests".
     plan = pack(view_len, branch_count, branch_len, heads=H)
     out, final_state = scan_packed(q, k, v, plan)
     export_view_state(final_state, view_row, dst)
+
+Branch shards (section "Long Requests"): a ViewStateCache keeps view states
+in a device pool; a shard request (view length 0) packed with
+ext_row=[cache row] runs from the cached state:
+
+    cache = ViewStateCache(capacity, H, d, device)
+    row = cache.store(view_id, final_state, view_row)         # after the view
+    plan = pack([0], [n], lens, heads=H, ext_row=[cache.lookup(view_id)])
+    out, _ = scan_packed(q, k, v, plan, ext_state=cache.pool)
 """
 import ctypes
 import os
@@ -20,7 +29,8 @@ import numpy as np
 
 __all__ = ["LinAttnError", "PassInfo", "PassPlan", "pack", "plan_segments",
            "choose_block_chunks", "workspace_size", "scan_packed",
-           "export_view_state", "library_path", "load_library", "CHUNK"]
+           "export_view_state", "ViewStateCache", "library_path", "load_library",
+           "CHUNK"]
 
 CHUNK = 64
 LA_OK, LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED, LA_ERR_WORKSPACE, LA_ERR_HIP = range(5)
@@ -81,10 +91,22 @@ def load_library():
     lib.la_scan_packed_stages.argtypes = [ctypes.c_int32] + lib.la_scan_packed.argtypes
     lib.la_export_view_state.argtypes = [_P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                          ctypes.c_int32, ctypes.c_int32, _P, _P]
+    lib.la_pack_pass_ext.argtypes = [ctypes.c_int32, _I32P, _I32P, _I32P, _I32P,
+                                     ctypes.c_int32, ctypes.c_int32, _I32P, _I32P, _I32P,
+                                     _I32P, ctypes.POINTER(PassInfo)]
+    lib.la_cache_create.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p)]
+    lib.la_cache_destroy.argtypes = [ctypes.c_void_p]
+    lib.la_cache_lookup.argtypes = [ctypes.c_void_p, ctypes.c_int64, _I32P]
+    lib.la_cache_reserve.argtypes = [ctypes.c_void_p, ctypes.c_int64, _I32P,
+                                     ctypes.POINTER(ctypes.c_int64)]
+    lib.la_cache_erase.argtypes = [ctypes.c_void_p, ctypes.c_int64]
+    lib.la_cache_count.argtypes = [ctypes.c_void_p, _I32P]
     lib.la_status_string.argtypes = [ctypes.c_int32]
     lib.la_status_string.restype = ctypes.c_char_p
-    for fn in ("la_pack_pass", "la_plan_segments", "la_scan_workspace_size",
-               "la_scan_packed", "la_scan_packed_stages", "la_export_view_state"):
+    for fn in ("la_pack_pass", "la_pack_pass_ext", "la_plan_segments",
+               "la_scan_workspace_size", "la_scan_packed", "la_scan_packed_stages",
+               "la_export_view_state", "la_cache_create", "la_cache_destroy",
+               "la_cache_lookup", "la_cache_reserve", "la_cache_erase", "la_cache_count"):
         getattr(lib, fn).restype = ctypes.c_int32
     _lib = lib
     return lib
@@ -144,25 +166,30 @@ def _auto_g(lengths, heads):
     return choose_block_chunks((lengths + CHUNK - 1) // CHUNK, heads)
 
 
-def pack(view_len, branch_count, branch_len, heads=16, block_chunks=None, chunk=CHUNK):
-    """Request shapes -> PassPlan via la_pack_pass (view then branches per
-    request; view length 0 marks a shard request seeded from ext_state)."""
+def pack(view_len, branch_count, branch_len, heads=16, block_chunks=None, chunk=CHUNK,
+         ext_row=None):
+    """Request shapes -> PassPlan via la_pack_pass_ext (view then branches per
+    request; view length 0 marks a shard request seeded from ext_state: row
+    ext_row[r] if given, else the next row in order)."""
     lib = load_library()
     vl, bc, bl = _i32(view_len), _i32(branch_count), _i32(branch_len)
+    er = None if ext_row is None else _i32(ext_row)
+    if er is not None and len(er) != len(vl):
+        raise ValueError("ext_row needs one entry per request")
     if block_chunks is None:
         block_chunks = _auto_g(np.concatenate([vl[vl > 0], bl]), heads)
     info = PassInfo()
-    _check("la_pack_pass", lib.la_pack_pass(len(vl), _ptr(vl), _ptr(bc), _ptr(bl), chunk,
-                                            block_chunks, None, None, None, None,
-                                            ctypes.byref(info)))
+    _check("la_pack_pass", lib.la_pack_pass_ext(len(vl), _ptr(vl), _ptr(bc), _ptr(bl),
+                                                _ptr(er), chunk, block_chunks, None, None,
+                                                None, None, ctypes.byref(info)))
     so = np.zeros(info.n_segments + 1, dtype=np.int32)
     bp = np.zeros(info.n_segments, dtype=np.int32)
     vo = np.zeros(info.n_segments, dtype=np.int32)
     plan = np.zeros(info.plan_words, dtype=np.int32)
-    _check("la_pack_pass", lib.la_pack_pass(len(vl), _ptr(vl), _ptr(bc), _ptr(bl), chunk,
-                                            block_chunks, so.ctypes.data_as(_I32P),
-                                            _ptr(bp), _ptr(vo), _ptr(plan),
-                                            ctypes.byref(info)))
+    _check("la_pack_pass", lib.la_pack_pass_ext(len(vl), _ptr(vl), _ptr(bc), _ptr(bl),
+                                                _ptr(er), chunk, block_chunks,
+                                                so.ctypes.data_as(_I32P), _ptr(bp), _ptr(vo),
+                                                _ptr(plan), ctypes.byref(info)))
     return PassPlan(info, so, bp, vo, plan)
 
 
@@ -280,3 +307,62 @@ def export_view_state(final_state, view_row, dst=None, stream=None):
                                     dk, dv, ctypes.c_void_p(dst.data_ptr()),
                                     _stream_ptr(stream, final_state.device)))
     return dst
+
+
+class ViewStateCache:
+    """Device pool of view states [capacity, H, d, d] fp32 with the library's
+    least-recently-used directory (la_cache_*), for branch shards that start
+    from a cached view (section "Long Requests").  `pool` is the ext_state of
+    shard passes; `lookup` gives the row to pass as ext_row.  Device copies go
+    on the caller's stream; not thread-safe."""
+
+    def __init__(self, capacity, heads, d, device="cuda"):
+        import torch
+        lib = load_library()
+        self._lib = lib
+        self._h = ctypes.c_void_p()
+        _check("la_cache_create", lib.la_cache_create(capacity, ctypes.byref(self._h)))
+        self.capacity, self.heads, self.d = capacity, heads, d
+        self.pool = torch.empty((capacity, heads, d, d), dtype=torch.float32, device=device)
+
+    def lookup(self, view_id):
+        """Pool row holding view_id's state (now most recent), or None."""
+        row = ctypes.c_int32()
+        _check("la_cache_lookup", self._lib.la_cache_lookup(self._h, view_id, ctypes.byref(row)))
+        return None if row.value < 0 else row.value
+
+    def reserve(self, view_id):
+        """(row, evicted view id or None): the row to write view_id's state to."""
+        row, ev = ctypes.c_int32(), ctypes.c_int64()
+        _check("la_cache_reserve", self._lib.la_cache_reserve(self._h, view_id,
+                                                              ctypes.byref(row),
+                                                              ctypes.byref(ev)))
+        return row.value, (None if ev.value < 0 else ev.value)
+
+    def store(self, view_id, final_state, view_row, stream=None):
+        """Copy final_state[view_row] into view_id's pool row (evicting the
+        least recently used view if the pool is full); returns the row."""
+        if final_state.shape[1:] != self.pool.shape[1:]:
+            raise ValueError("final_state rows must be [H, d, d] of this cache")
+        row, _ = self.reserve(view_id)
+        export_view_state(final_state, view_row, self.pool[row], stream=stream)
+        return row
+
+    def erase(self, view_id):
+        _check("la_cache_erase", self._lib.la_cache_erase(self._h, view_id))
+
+    def __len__(self):
+        n = ctypes.c_int32()
+        _check("la_cache_count", self._lib.la_cache_count(self._h, ctypes.byref(n)))
+        return n.value
+
+    def close(self):
+        if self._h:
+            self._lib.la_cache_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -2,9 +2,10 @@
 
     python -m chunked_linear_attention_packed_amd.build
 
-The host packer (pack.cpp) is compiled with g++; the kernels and the scan's
-host entry points (scan.hip) with hipcc; both are linked into one shared
-library next to this file.  Always recompiles.
+The host code (pack.cpp: packer and planner; cache.cpp: view-state cache
+directory) is compiled with g++; the kernels and the scan's host entry points
+(scan.hip) with hipcc; all are linked into one shared library next to this
+file.  Always recompiles.
 """
 import os
 import shutil
@@ -17,6 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "liblinattn.so")
+HOST_SOURCES = ["pack.cpp", "cache.cpp"]
 
 HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -52,14 +54,17 @@ def _run(cmd, verbose):
 def build(verbose=False):
     hipcc = _hipcc()
     with tempfile.TemporaryDirectory(prefix="linattn_build_") as tmp:
-        pack_o = os.path.join(tmp, "pack.o")
+        host_o = []
+        for name in HOST_SOURCES:
+            obj = os.path.join(tmp, name.replace(".cpp", ".o"))
+            _run(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", INCLUDE, "-c",
+                  os.path.join(CSRC, name), "-o", obj], verbose)
+            host_o.append(obj)
         scan_o = os.path.join(tmp, "scan.o")
-        _run(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", INCLUDE, "-c",
-              os.path.join(CSRC, "pack.cpp"), "-o", pack_o], verbose)
         _run([hipcc] + HIP_FLAGS + ["-I", INCLUDE, "-c", os.path.join(CSRC, "scan.hip"),
                                     "-o", scan_o], verbose)
         tmp_lib = LIB + ".tmp"
-        _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", pack_o, scan_o,
+        _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC"] + host_o + [scan_o,
               "-o", tmp_lib], verbose)
         os.replace(tmp_lib, LIB)
     return LIB

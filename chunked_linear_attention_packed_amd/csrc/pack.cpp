@@ -188,11 +188,12 @@ extern "C" la_status la_plan_segments(int32_t n_segments, const int32_t* seg_off
                      plan, info);
 }
 
-extern "C" la_status la_pack_pass(int32_t n_requests, const int32_t* view_len,
-                                  const int32_t* branch_count, const int32_t* branch_len,
-                                  int32_t chunk, int32_t block_chunks, int32_t* seg_offsets,
-                                  int32_t* branch_parent, int32_t* view_ordinal, int32_t* plan,
-                                  la_pass_info* info) {
+extern "C" la_status la_pack_pass_ext(int32_t n_requests, const int32_t* view_len,
+                                      const int32_t* branch_count, const int32_t* branch_len,
+                                      const int32_t* ext_row, int32_t chunk,
+                                      int32_t block_chunks, int32_t* seg_offsets,
+                                      int32_t* branch_parent, int32_t* view_ordinal,
+                                      int32_t* plan, la_pass_info* info) {
     if (!info || n_requests < 0) return LA_ERR_INVALID_ARG;
     if (n_requests > 0 && (!view_len || !branch_count)) return LA_ERR_INVALID_ARG;
     if (chunk != LA_CHUNK) return LA_ERR_UNSUPPORTED;
@@ -200,6 +201,8 @@ extern "C" la_status la_pack_pass(int32_t n_requests, const int32_t* view_len,
     for (int32_t r = 0; r < n_requests; ++r) {
         if (view_len[r] < 0 || branch_count[r] < 0) return LA_ERR_INVALID_ARG;
         if (view_len[r] == 0 && branch_count[r] == 0) return LA_ERR_INVALID_ARG;
+        if (view_len[r] == 0 && ext_row && (ext_row[r] < 0 || ext_row[r] > (1 << 30)))
+            return LA_ERR_INVALID_ARG;
         n_br += branch_count[r];
     }
     if (n_br > 0 && !branch_len) return LA_ERR_INVALID_ARG;
@@ -223,7 +226,9 @@ extern "C" la_status la_pack_pass(int32_t n_requests, const int32_t* view_len,
             if (tok > INT32_MAX) return LA_ERR_INVALID_ARG;
             off.push_back(int32_t(tok));
         } else {
-            seed = -2 - n_ext;
+            // a shard request: its branches start from ext_state row
+            // ext_row[r], or from the next row in order
+            seed = -2 - (ext_row ? ext_row[r] : n_ext);
             ++n_ext;
         }
         for (int32_t i = 0; i < branch_count[r]; ++i, ++b) {
@@ -244,6 +249,15 @@ extern "C" la_status la_pack_pass(int32_t n_requests, const int32_t* view_len,
     if (branch_parent && n_seg > 0) std::memcpy(branch_parent, par.data(), sizeof(int32_t) * par.size());
     *info = inf;
     return LA_OK;
+}
+
+extern "C" la_status la_pack_pass(int32_t n_requests, const int32_t* view_len,
+                                  const int32_t* branch_count, const int32_t* branch_len,
+                                  int32_t chunk, int32_t block_chunks, int32_t* seg_offsets,
+                                  int32_t* branch_parent, int32_t* view_ordinal, int32_t* plan,
+                                  la_pass_info* info) {
+    return la_pack_pass_ext(n_requests, view_len, branch_count, branch_len, nullptr, chunk,
+                            block_chunks, seg_offsets, branch_parent, view_ordinal, plan, info);
 }
 
 extern "C" const char* la_status_string(la_status status) {

@@ -168,6 +168,24 @@ la_status la_pack_pass(int32_t n_requests, const int32_t* view_len,
                        int32_t* plan, la_pass_info* info);
 
 /*
+ * la_pack_pass_ext -- la_pack_pass where each shard request names the
+ * ext_state row its branches start from (a row of a view-state cache pool,
+ * see la_cache_* below; section "Long Requests").
+ *
+ *   ext_row        host [n_requests] or NULL: for a request with view_len 0,
+ *                  the ext_state row (0 <= row <= 2^30) its branches start
+ *                  from; entries of other requests are ignored.  NULL gives
+ *                  la_pack_pass (shard requests take rows 0, 1, ... in order).
+ * info->n_ext is one past the largest row used.  Other arguments, outputs and
+ * errors as la_pack_pass.
+ */
+la_status la_pack_pass_ext(int32_t n_requests, const int32_t* view_len,
+                           const int32_t* branch_count, const int32_t* branch_len,
+                           const int32_t* ext_row, int32_t chunk, int32_t block_chunks,
+                           int32_t* seg_offsets, int32_t* branch_parent,
+                           int32_t* view_ordinal, int32_t* plan, la_pass_info* info);
+
+/*
  * la_scan_workspace_size -- bytes of device workspace la_scan_packed needs:
  * one fp32 d_k x d_v state per (delta block, head).
  * Errors: LA_ERR_INVALID_ARG (NULL), LA_ERR_UNSUPPORTED (shape/dtype).
@@ -245,6 +263,42 @@ la_status la_scan_packed_stages(int32_t stages, const void* q, const void* k, co
 la_status la_export_view_state(const float* final_state, int32_t view_row,
                                int32_t n_views, int32_t H, int32_t d_k, int32_t d_v,
                                float* dst, void* stream);
+
+/*
+ * View-state cache directory (section "Long Requests": nodes cache the
+ * linear-attention state of recent views so that a branch shard does not
+ * recompute its view).  The states live in a caller-owned device pool
+ * [capacity][H][d_k][d_v] fp32, which a shard pass uses directly as its
+ * ext_state; the directory, a host object, maps view ids (>= 0) to pool rows
+ * with least-recently-used eviction.  Typical use:
+ *   miss:  la_cache_reserve(view) -> row; run a pass with the view;
+ *          la_export_view_state(final_state, view_row, ..., pool + row*H*d*d)
+ *   hit:   la_cache_lookup(view) -> row; la_pack_pass_ext with ext_row = row
+ *          for the shard request; la_scan_packed(..., ext_state = pool, ...)
+ * Device work that reads or writes a row is ordered by the caller's stream: an
+ * export into a reused row must be enqueued after every pass that read the
+ * evicted view's state, which holds automatically on one stream.  The
+ * directory is not thread-safe.
+ *
+ * la_cache_create   capacity rows (1 .. 2^30); *cache receives the directory
+ * la_cache_destroy  frees the directory (not the pool)
+ * la_cache_lookup   *row = the view's row (it becomes most recent), or -1
+ * la_cache_reserve  *row = a row for view_id: its own if cached, else a free
+ *                   row, else the least recently used row, whose view is
+ *                   evicted (*evicted_id = its id, or -1; evicted_id may be
+ *                   NULL).  The view becomes most recent.
+ * la_cache_erase    forget a view (no-op if absent); its row becomes free
+ * la_cache_count    *n = views held
+ * Errors: LA_ERR_INVALID_ARG for NULL pointers, negative ids, bad capacity.
+ */
+typedef struct la_state_cache la_state_cache;
+la_status la_cache_create(int32_t capacity, la_state_cache** cache);
+la_status la_cache_destroy(la_state_cache* cache);
+la_status la_cache_lookup(la_state_cache* cache, int64_t view_id, int32_t* row);
+la_status la_cache_reserve(la_state_cache* cache, int64_t view_id, int32_t* row,
+                           int64_t* evicted_id);
+la_status la_cache_erase(la_state_cache* cache, int64_t view_id);
+la_status la_cache_count(const la_state_cache* cache, int32_t* n);
 
 /* Static text for a status code. */
 const char* la_status_string(la_status status);
