@@ -21,11 +21,16 @@ Contents:
   scan.scan_chunked      -- chunked fp64 evaluator; pins chunk-size invariance
   scan.sample_rows       -- closed form for selected tokens (large passes)
   scan.view_states       -- final states of selected views (large passes)
+  attention.attention_dense -- tree-masked softmax attention of a pass (the
+                           other layer type, section "The Workload")
+  attention.attention_rows  -- the same for selected tokens
   metrics.row_rel_err    -- row-normalised max relative error
 """
 from .pack import pack_segments, view_ordinals
 from .scan import scan_recurrence, scan_bruteforce, scan_chunked, sample_rows, view_states
+from .attention import attention_dense, attention_rows, attention_flops
 from .metrics import row_rel_err, state_rel_err
 
 __all__ = ["pack_segments", "view_ordinals", "scan_recurrence", "scan_bruteforce",
-           "scan_chunked", "sample_rows", "view_states", "row_rel_err", "state_rel_err"]
+           "scan_chunked", "sample_rows", "view_states", "attention_dense", "attention_rows",
+           "attention_flops", "row_rel_err", "state_rel_err"]
