@@ -54,6 +54,9 @@ def parse():
                     help="instead of the headline: split the workload's one request "
                          "into this many branch shards and time them with and without "
                          "the view-state cache against the unsplit pass")
+    ap.add_argument("--attention", action="store_true",
+                    help="instead of the headline: time the tree-masked softmax attention "
+                         "(la_attn_packed) of the workload against the bf16 MFMA peak")
     ap.add_argument("--cost-model", type=int, default=0,
                     help="instead of the headline: time this many random pass shapes and "
                          "fit the three-term cost model t = c0 + c1*sum(view) + c2*branches")
@@ -288,6 +291,62 @@ def shard_bench(a):
     cache.close()
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def attention_bench(a):
+    """The softmax-attention layer of the same packed pass (la_attn_packed):
+    scores q.k and weighted values for every (token, attended key, head),
+    4*d FLOPs each, against the dense bf16 MFMA peak.  Inputs rotate like the
+    headline's; graph-replayed timing."""
+    import numpy as np
+    import torch
+    import chunked_linear_attention_packed_amd as la
+    import synth
+    w = synth.workload(a.workload)
+    if w.dtype != "bf16":
+        raise SystemExit("--attention runs bf16 workloads")
+    plan = la.pack(w.view_len, w.branch_count, w.branch_len, heads=w.H, block_chunks=1)
+    so, bp = plan.seg_offsets, plan.branch_parent
+    ap = la.attn_plan(so, bp)
+    T, H, d = w.n_tokens, w.H, w.d
+    pairs = 0
+    for s_ in range(len(bp)):
+        n = int(so[s_ + 1] - so[s_])
+        p = int(bp[s_])
+        lp = int(so[p + 1] - so[p]) if p >= 0 else 0
+        pairs += n * lp + n * (n + 1) // 2
+    flops = 4 * d * H * pairs
+    dev = torch.device("cuda:0")
+    set_bytes = 4 * T * H * d * 2
+    n_sets = min(64, max(2, int(np.ceil(a.rotate_gib * 2**30 / set_bytes))))
+    q0, k0, v0 = (x.to(dev) for x in (w.q, w.k, w.v))
+    sets = [dict(q=q0.clone(), k=k0.clone(), v=v0.clone(), out=torch.empty_like(v0))
+            for _ in range(n_sets)]
+    del q0, k0, v0
+    ap.device_items(dev)
+    stream = torch.cuda.Stream(dev)
+    ctr = [0]
+
+    def fn():
+        s_ = sets[ctr[0] % n_sets]
+        ctr[0] += 1
+        la.attn_packed(s_["q"], s_["k"], s_["v"], ap, 1.0, out=s_["out"], stream=stream)
+
+    us = _graph_us(fn, a.steps, a.warmup, stream, a.eager)
+    tf = flops / (us * 1e-6) / 1e12
+    print(json.dumps({
+        "experiment": "tree-masked softmax attention over the packed pass",
+        "workload": a.workload, "tokens": T, "heads": H, "d": d, "dtype": "bf16",
+        "work_items": int(len(ap.items)), "launch": "eager" if a.eager else "hip_graph",
+        "steps": a.steps, "us_per_pass": us, "tokens_per_s": T / (us * 1e-6),
+        "algorithmic_flops": flops,
+        "roofline": {"bound": "mfma", "achieved": tf, "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": tf / MFMA_BF16_PEAK_TFLOPS,
+                     "kernel": "attn_kernel_bf16"},
+    }), flush=True)
+
+
 def cost_model_bench(a):
     """Pass times of random pass shapes and the page's three-term cost model
     fitted to them (section "Cost Model").  Shapes: 1-8 requests, views
@@ -390,6 +449,9 @@ def main():
         return
     if a.cost_model:
         cost_model_bench(a)
+        return
+    if a.attention:
+        attention_bench(a)
         return
     la.load_library()
     dev = torch.device("cuda:0")

@@ -29,12 +29,13 @@ import numpy as np
 
 __all__ = ["LinAttnError", "PassInfo", "PassPlan", "pack", "plan_segments",
            "choose_block_chunks", "workspace_size", "scan_packed",
-           "export_view_state", "ViewStateCache", "library_path", "load_library",
-           "CHUNK"]
+           "export_view_state", "ViewStateCache", "AttnPlan", "attn_plan", "attn_packed",
+           "library_path", "load_library", "CHUNK"]
 
 CHUNK = 64
 LA_OK, LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED, LA_ERR_WORKSPACE, LA_ERR_HIP = range(5)
 LA_F32, LA_BF16 = 0, 1
+LA_ATTN_NO_VIEW, LA_ATTN_PACKED_VIEW, LA_ATTN_EXT_VIEW = 0, 1, 2
 STAGE_STATES, STAGE_PREFIX, STAGE_OUTPUT, STAGE_ALL = 1, 2, 4, 7
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -101,12 +102,18 @@ def load_library():
                                      ctypes.POINTER(ctypes.c_int64)]
     lib.la_cache_erase.argtypes = [ctypes.c_void_p, ctypes.c_int64]
     lib.la_cache_count.argtypes = [ctypes.c_void_p, _I32P]
+    lib.la_attn_plan.argtypes = [ctypes.c_int32, _I32P, _I32P, ctypes.c_int32, _I32P, _I32P,
+                                 _I32P]
+    lib.la_attn_packed.argtypes = [_P, _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                   ctypes.c_int32, ctypes.c_float, _P, ctypes.c_int32,
+                                   ctypes.c_int32, _P, _P, ctypes.c_int32, _P, _P]
     lib.la_status_string.argtypes = [ctypes.c_int32]
     lib.la_status_string.restype = ctypes.c_char_p
     for fn in ("la_pack_pass", "la_pack_pass_ext", "la_plan_segments",
                "la_scan_workspace_size", "la_scan_packed", "la_scan_packed_stages",
                "la_export_view_state", "la_cache_create", "la_cache_destroy",
-               "la_cache_lookup", "la_cache_reserve", "la_cache_erase", "la_cache_count"):
+               "la_cache_lookup", "la_cache_reserve", "la_cache_erase", "la_cache_count",
+               "la_attn_plan", "la_attn_packed"):
         getattr(lib, fn).restype = ctypes.c_int32
     _lib = lib
     return lib
@@ -366,3 +373,77 @@ class ViewStateCache:
             self.close()
         except Exception:
             pass
+
+
+@dataclass
+class AttnPlan:
+    """Work items of the tree-masked softmax attention of one segment table
+    (la_attn_plan): one per (segment, 64-token query block)."""
+    n_tokens: int
+    n_ext_tokens: int
+    items: np.ndarray            # [n_items, 8] int32
+    _dev: dict = field(default_factory=dict, repr=False)
+
+    def device_items(self, device):
+        import torch
+        key = str(torch.device(device))
+        if key not in self._dev:
+            self._dev[key] = torch.from_numpy(self.items.reshape(-1)).to(device)
+        return self._dev[key]
+
+
+def attn_plan(seg_offsets, branch_parent, ext_len=None):
+    """Segment table (parents >= 0 are views, -2 - e external view e of
+    ext_len[e] tokens) -> AttnPlan."""
+    lib = load_library()
+    so, bp = _i32(seg_offsets), _i32(branch_parent)
+    el = _i32([] if ext_len is None else ext_len)
+    n = ctypes.c_int32()
+    _check("la_attn_plan", lib.la_attn_plan(len(bp), _ptr(so), _ptr(bp), len(el), _ptr(el),
+                                            None, ctypes.byref(n)))
+    items = np.zeros((n.value, 8), dtype=np.int32)
+    _check("la_attn_plan", lib.la_attn_plan(len(bp), _ptr(so), _ptr(bp), len(el), _ptr(el),
+                                            _ptr(items), ctypes.byref(n)))
+    return AttnPlan(int(so[-1]) if len(so) else 0, int(el.sum()), items)
+
+
+def attn_packed(q, k, v, plan, scale, ext_k=None, ext_v=None, out=None, stream=None):
+    """Tree-masked softmax attention of a packed pass (bf16 q, k, v
+    [T, H, d]); ext_k / ext_v [n_ext_tokens, H, d] hold the external views
+    that shard branches attend to.  Returns out [T, H, d] bf16."""
+    import torch
+    lib = load_library()
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k, v must be device tensors")
+    if q.dim() != 3 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v: [T, H, d]")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share a dtype")
+    T, H, d = q.shape
+    if T != plan.n_tokens:
+        raise ValueError(f"q has {T} tokens, the plan {plan.n_tokens}")
+    n_ext = 0
+    ek = ev = None
+    if plan.n_ext_tokens:
+        if ext_k is None or ext_v is None:
+            raise ValueError("the plan reads external views: pass ext_k and ext_v")
+        if ext_k.shape != (plan.n_ext_tokens, H, d) or ext_v.shape != ext_k.shape:
+            raise ValueError(f"ext_k / ext_v must be [{plan.n_ext_tokens}, {H}, {d}]")
+        if ext_k.dtype != q.dtype or ext_v.dtype != q.dtype:
+            raise TypeError("ext_k / ext_v must have the dtype of q")
+        if not (ext_k.is_contiguous() and ext_v.is_contiguous()):
+            raise ValueError("ext_k / ext_v must be contiguous")
+        n_ext = plan.n_ext_tokens
+        ek, ev = ctypes.c_void_p(ext_k.data_ptr()), ctypes.c_void_p(ext_v.data_ptr())
+    if out is None:
+        out = torch.empty_like(v)
+    items = plan.device_items(q.device)
+    _check("la_attn_packed",
+           lib.la_attn_packed(ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
+                              ctypes.c_void_p(v.data_ptr()), _dtype_code(q), H, d, d,
+                              float(scale), ctypes.c_void_p(items.data_ptr()),
+                              len(plan.items), T, ek, ev, n_ext,
+                              ctypes.c_void_p(out.data_ptr()), _stream_ptr(stream, q.device)))
+    return out

@@ -2,9 +2,10 @@
 
     python -m chunked_linear_attention_packed_amd.build
 
-The host code (pack.cpp: packer and planner; cache.cpp: view-state cache
-directory) is compiled with g++; the kernels and the scan's host entry points
-(scan.hip) with hipcc; all are linked into one shared library next to this
+The host code (pack.cpp: packer and planners; cache.cpp: view-state cache
+directory) is compiled with g++; the kernels and their host entry points
+(scan.hip: the linear-attention scan; attn.hip: the tree-masked softmax
+attention) with hipcc; all are linked into one shared library next to this
 file.  Always recompiles.
 """
 import os
@@ -19,6 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "liblinattn.so")
 HOST_SOURCES = ["pack.cpp", "cache.cpp"]
+HIP_SOURCES = ["scan.hip", "attn.hip"]
 
 HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -60,12 +62,15 @@ def build(verbose=False):
             _run(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", INCLUDE, "-c",
                   os.path.join(CSRC, name), "-o", obj], verbose)
             host_o.append(obj)
-        scan_o = os.path.join(tmp, "scan.o")
-        _run([hipcc] + HIP_FLAGS + ["-I", INCLUDE, "-c", os.path.join(CSRC, "scan.hip"),
-                                    "-o", scan_o], verbose)
+        dev_o = []
+        for name in HIP_SOURCES:
+            obj = os.path.join(tmp, name.replace(".hip", ".o"))
+            _run([hipcc] + HIP_FLAGS + ["-I", INCLUDE, "-c", os.path.join(CSRC, name),
+                                        "-o", obj], verbose)
+            dev_o.append(obj)
         tmp_lib = LIB + ".tmp"
-        _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC"] + host_o + [scan_o,
-              "-o", tmp_lib], verbose)
+        _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC"] + host_o + dev_o +
+             ["-o", tmp_lib], verbose)
         os.replace(tmp_lib, LIB)
     return LIB
 

@@ -1,0 +1,234 @@
+// Tree-masked softmax attention over a packed pass, for gfx950 (MI355X).
+//
+// Source: "Serving 0.88M TPS from Two RTXs and Mac Minis", section "The
+// Workload": Span-1 is a hybrid of linear-attention layers and a few
+// softmax-attention layers, and a branch attends to its own view but never
+// to another branch; section "Long Requests": the view cache also holds the
+// K/V of the softmax layers, so a branch shard attends to cached view keys and
+// values.  Per head and token t, over the attend set A(t) (t's own segment up
+// to and including t, plus the whole parent view for a branch):
+//     o_t = sum_{u in A(t)} exp(s_tu - m_t) v_u / sum_{u in A(t)} exp(s_tu - m_t),
+//     s_tu = scale * q_t . k_u,   m_t = max_u s_tu.
+//
+// One workgroup of 4 waves per (query block of <= 64 tokens, head).  It walks
+// the block's keys in 64-key blocks -- first the parent view's (from the pass
+// or from the external K/V arrays), then its own segment's up to and
+// including the query block -- keeping for every query a running maximum, a
+// running sum and the unnormalised output (the usual online softmax).  Wave w
+// owns queries w*16 .. w*16+15.  MFMA orientation, as in the scan's output
+// kernel: scores are computed transposed, S^T = K Q^T (A = K rows from LDS,
+// B = Q^T fragments held in registers), so each lane owns one query (its
+// column) and 16 keys of the block; exponentiated scores, packed to bf16,
+// are the B operand of O^T += V^T P^T directly from the accumulator layout.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <initializer_list>
+
+#include "linattn.h"
+#include "tiles.h"
+
+namespace {
+
+struct AttnItem {
+    int q0, nq, seg0, view0, view_len, view_src, pad0, pad1;
+};
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void attn_kernel_bf16(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const uint16_t* __restrict__ ext_k,
+    const uint16_t* __restrict__ ext_v, const AttnItem* __restrict__ items,
+    uint16_t* __restrict__ out, int H, float scale_log2) {
+    constexpr int R = 4, NKS = D / 32, NVB = D / 16;
+    using ST = Stage<D, R>;
+    constexpr int NPER = KVStage<D, D, R, kThreads>::NPER;
+    constexpr int LDR = ST::LDR, LDT = ST::LDT;
+    __shared__ __attribute__((aligned(16))) uint16_t sK[kChunk * LDR];   // K block, row-major
+    __shared__ __attribute__((aligned(16))) uint16_t sVt[D * LDT];       // V block, transposed
+
+    const int h = blockIdx.x % H;
+    const AttnItem it = items[blockIdx.x / H];
+    const int w = wave_id(), lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
+    const int trow = w * 16 + c16;            // this lane's query within the block
+    const int64_t row_elems = int64_t(H) * D;
+
+    // key blocks: the parent view's, then the segment's own up to the query
+    // block (q0 - seg0 is a multiple of 64, so the last own block is the
+    // query block itself: the diagonal)
+    const int n_view_blk = (it.view_len + kChunk - 1) / kChunk;
+    const int n_own_blk = (it.q0 - it.seg0) / kChunk + 1;
+    const int nkb = n_view_blk + n_own_blk;
+    const bool ext_view = it.view_src == LA_ATTN_EXT_VIEW;
+
+    // Q^T fragments (B operand): lane holds q[trow][ks*32 + 8g .. +7]
+    u32x4 qf[NKS];
+    {
+        const auto rq = chunk_rsrc(q, int64_t(it.q0) * row_elems, 2, it.nq, H, D);
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+            qf[ks] = buf_load16(rq, uint32_t(((trow * H + h) * D + ks * 32 + 8 * g) * 2));
+    }
+
+    // source of key block b (wave-uniform): token offset and valid rows
+    auto block_src = [&](int b, int64_t& tok, int& rows, bool& from_ext) {
+        if (b < n_view_blk) {
+            tok = int64_t(it.view0) + int64_t(b) * kChunk;
+            rows = min(kChunk, it.view_len - b * kChunk);
+            from_ext = ext_view;
+        } else {
+            const int j = b - n_view_blk;
+            tok = int64_t(it.seg0) + int64_t(j) * kChunk;
+            rows = j == n_own_blk - 1 ? it.nq : kChunk;
+            from_ext = false;
+        }
+        if (b >= nkb) rows = 0;                       // past the end: empty window
+        if (from_ext && ext_k == nullptr) rows = 0;   // no external arrays given
+    };
+    BlkR<R> kv[NPER];
+    auto load = [&](int b) {
+        int64_t tok;
+        int rows;
+        bool fe;
+        block_src(b, tok, rows, fe);
+        const uint16_t* kb = fe ? ext_k : k;
+        const uint16_t* vb = fe ? ext_v : v;
+        load_kv<D, D, R, kThreads, NPER>(kv, chunk_rsrc(kb, tok * row_elems, 2, rows, H, D),
+                                         chunk_rsrc(vb, tok * row_elems, 2, rows, H, D), 0, H, h);
+    };
+
+    float m = -INFINITY;   // running max of this lane's query (log2 domain)
+    float l = 0.f;         // this lane's part of the running sum
+    f32x4 acc[NVB];        // O^T tiles: lane holds O[trow][x*16 + 4g + j]
+#pragma unroll
+    for (int x = 0; x < NVB; ++x) acc[x] = zero4();
+
+    load(0);
+    for (int b = 0; b < nkb; ++b) {
+        stage_kv<D, D, R, kThreads, NPER, true, false>(kv, sK, nullptr, sVt);
+        __syncthreads();
+        load(b + 1);
+        int64_t tok;
+        int rows;
+        bool fe;
+        block_src(b, tok, rows, fe);
+        const bool diag = b == nkb - 1;
+
+        // S^T tiles (ub = key tile): lane holds s[u = ub*16 + 4g + j][trow]
+        f32x4 s[4];
+#pragma unroll
+        for (int ub = 0; ub < 4; ++ub) s[ub] = zero4();
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            u32x4 kf[4];
+#pragma unroll
+            for (int ub = 0; ub < 4; ++ub)
+                kf[ub] = lds_u32x4(sK + (ub * 16 + c16) * LDR + ks * 32 + 8 * g);
+#pragma unroll
+            for (int ub = 0; ub < 4; ++ub) s[ub] = mfma_bf16(kf[ub], qf[ks], s[ub]);
+        }
+        // mask (ragged block, causal diagonal) and the block maximum
+        float bm = -INFINITY;
+#pragma unroll
+        for (int ub = 0; ub < 4; ++ub)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int u = ub * 16 + 4 * g + j;
+                const bool ok = u < rows && (!diag || u <= trow);
+                s[ub][j] = ok ? s[ub][j] * scale_log2 : -INFINITY;
+                bm = fmaxf(bm, s[ub][j]);
+            }
+        bm = fmaxf(bm, __shfl_xor(bm, 16));
+        bm = fmaxf(bm, __shfl_xor(bm, 32));
+        const float mn = fmaxf(m, bm);
+        // every query sees at least one key in each block it visits, so mn is
+        // finite; guard anyway so that a fully masked row cannot make NaNs
+        const float mref = mn == -INFINITY ? 0.f : mn;
+        const float alpha = __builtin_amdgcn_exp2f(m - mref);
+        m = mn;
+        u32x2 pb[4];
+        float ls = 0.f;
+#pragma unroll
+        for (int ub = 0; ub < 4; ++ub) {
+            float p[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                p[j] = __builtin_amdgcn_exp2f(s[ub][j] - mref);   // exp2(-inf) = 0
+                ls += p[j];
+            }
+            pb[ub] = u32x2{cvt_bf2(p[0], p[1]), cvt_bf2(p[2], p[3])};
+        }
+        l = l * alpha + ls;
+#pragma unroll
+        for (int x = 0; x < NVB; ++x) acc[x] *= alpha;
+        // O^T += V^T P^T; k-slots (g, i) -> key u = (2pp + i/4)*16 + 4g + i%4
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+            const u32x4 bp = cat2(pb[2 * pp], pb[2 * pp + 1]);
+            u32x4 av[NVB];
+#pragma unroll
+            for (int x = 0; x < NVB; ++x)
+                av[x] = lds_u32x4(sVt + (x * 16 + c16) * LDT + tpos(x * 16, pp * 32 + 4 * g));
+#pragma unroll
+            for (int x = 0; x < NVB; ++x) acc[x] = mfma_bf16(av[x], bp, acc[x]);
+        }
+        __syncthreads();
+    }
+    // the query's sum is split over the 4 lanes that share its column
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    const float inv = 1.f / l;
+    const auto ro = chunk_rsrc(out, int64_t(it.q0) * row_elems, 2, it.nq, H, D);
+    const uint32_t ooff = uint32_t(((trow * H + h) * D + 4 * g) * 2);
+#pragma unroll
+    for (int x = 0; x < NVB; ++x)
+        buf_store8(ro, ooff + x * 32,
+                   u32x2{cvt_bf2(acc[x][0] * inv, acc[x][1] * inv),
+                         cvt_bf2(acc[x][2] * inv, acc[x][3] * inv)});
+}
+
+}  // namespace
+
+extern "C" la_status la_attn_packed(const void* q, const void* k, const void* v, la_dtype dtype,
+                                    int32_t H, int32_t d_k, int32_t d_v, float scale,
+                                    const int32_t* items, int32_t n_items, int32_t n_tokens,
+                                    const void* ext_k, const void* ext_v, int32_t n_ext_tokens,
+                                    void* out, void* stream) {
+    if (dtype != LA_BF16 && dtype != LA_F32) return LA_ERR_INVALID_ARG;
+    if (dtype != LA_BF16) return LA_ERR_UNSUPPORTED;
+    if (d_k != d_v || (d_k != 64 && d_k != 128)) return LA_ERR_UNSUPPORTED;
+    if (H < 1 || n_items < 0 || n_tokens < 0 || n_ext_tokens < 0 || !std::isfinite(scale))
+        return LA_ERR_INVALID_ARG;
+    if (n_items == 0) return LA_OK;
+    if (!q || !k || !v || !out || !items) return LA_ERR_INVALID_ARG;
+    if (n_ext_tokens > 0 && (!ext_k || !ext_v)) return LA_ERR_INVALID_ARG;
+    for (const void* p : {q, k, v, static_cast<const void*>(out)})
+        if (reinterpret_cast<uintptr_t>(p) & 15u) return LA_ERR_INVALID_ARG;
+    if ((ext_k && (reinterpret_cast<uintptr_t>(ext_k) & 15u)) ||
+        (ext_v && (reinterpret_cast<uintptr_t>(ext_v) & 15u)))
+        return LA_ERR_INVALID_ARG;
+    if (int64_t(n_tokens) * H * d_k >= (int64_t(1) << 40) ||
+        int64_t(n_ext_tokens) * H * d_k >= (int64_t(1) << 40) ||
+        int64_t(kChunk) * H * d_k * 2 >= (int64_t(1) << 31) ||
+        int64_t(n_items) * H * kThreads >= (int64_t(1) << 32))
+        return LA_ERR_INVALID_ARG;
+    const float scale_log2 = scale * 1.4426950408889634f;   // exp(x) = exp2(x log2 e)
+    const auto* its = reinterpret_cast<const AttnItem*>(items);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const dim3 grid(unsigned(int64_t(n_items) * H)), blk(kThreads);
+    const auto* qq = static_cast<const uint16_t*>(q);
+    const auto* kk = static_cast<const uint16_t*>(k);
+    const auto* vv = static_cast<const uint16_t*>(v);
+    const auto* ek = static_cast<const uint16_t*>(ext_k);
+    const auto* ev = static_cast<const uint16_t*>(ext_v);
+    auto* oo = static_cast<uint16_t*>(out);
+    if (d_k == 64)
+        hipLaunchKernelGGL(attn_kernel_bf16<64>, grid, blk, 0, st, qq, kk, vv, ek, ev, its, oo, H,
+                           scale_log2);
+    else
+        hipLaunchKernelGGL(attn_kernel_bf16<128>, grid, blk, 0, st, qq, kk, vv, ek, ev, its, oo,
+                           H, scale_log2);
+    if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
+    return LA_OK;
+}

@@ -9,6 +9,7 @@
 // Everything here is integer bookkeeping on the host.  The output plan is the
 // only metadata the device kernels read: one descriptor per work block, per
 // delta block and per scanned segment.
+#include <algorithm>
 #include <cstdint>
 #include <cstring>
 #include <vector>
@@ -258,6 +259,60 @@ extern "C" la_status la_pack_pass(int32_t n_requests, const int32_t* view_len,
                                   la_pass_info* info) {
     return la_pack_pass_ext(n_requests, view_len, branch_count, branch_len, nullptr, chunk,
                             block_chunks, seg_offsets, branch_parent, view_ordinal, plan, info);
+}
+
+extern "C" la_status la_attn_plan(int32_t n_segments, const int32_t* seg_offsets,
+                                  const int32_t* branch_parent, int32_t n_ext,
+                                  const int32_t* ext_len, int32_t* items, int32_t* n_items) {
+    if (!n_items || n_segments < 0 || n_ext < 0) return LA_ERR_INVALID_ARG;
+    if (n_segments > 0 && (!seg_offsets || !branch_parent)) return LA_ERR_INVALID_ARG;
+    if (n_ext > 0 && !ext_len) return LA_ERR_INVALID_ARG;
+    if (n_segments > 0 && seg_offsets[0] != 0) return LA_ERR_INVALID_ARG;
+    for (int32_t s = 0; s < n_segments; ++s)
+        if (seg_offsets[s + 1] <= seg_offsets[s]) return LA_ERR_INVALID_ARG;
+    // external views, concatenated: view e is tokens [ext_off[e], ext_off[e] + ext_len[e])
+    std::vector<int64_t> ext_off(size_t(n_ext) + 1, 0);
+    for (int32_t e = 0; e < n_ext; ++e) {
+        if (ext_len[e] < 1) return LA_ERR_INVALID_ARG;
+        ext_off[e + 1] = ext_off[e] + ext_len[e];
+        if (ext_off[e + 1] > INT32_MAX) return LA_ERR_INVALID_ARG;
+    }
+    struct Item {
+        int32_t w[8];
+        int64_t keys;
+    };
+    std::vector<Item> out;
+    for (int32_t s = 0; s < n_segments; ++s) {
+        const int32_t p = branch_parent[s];
+        int32_t view0 = 0, view_len = 0, src = LA_ATTN_NO_VIEW;
+        if (p >= 0) {
+            if (p >= n_segments || branch_parent[p] != -1) return LA_ERR_INVALID_ARG;
+            view0 = seg_offsets[p];
+            view_len = seg_offsets[p + 1] - seg_offsets[p];
+            src = LA_ATTN_PACKED_VIEW;
+        } else if (p <= -2) {
+            const int64_t e = -int64_t(p) - 2;
+            if (e >= n_ext) return LA_ERR_INVALID_ARG;
+            view0 = int32_t(ext_off[size_t(e)]);
+            view_len = ext_len[e];
+            src = LA_ATTN_EXT_VIEW;
+        }
+        const int32_t a = seg_offsets[s], b = seg_offsets[s + 1];
+        for (int32_t q0 = a; q0 < b; q0 += LA_CHUNK) {
+            const int32_t nq = std::min(LA_CHUNK, b - q0);
+            Item it{{q0, nq, a, view0, view_len, src, 0, 0}, int64_t(view_len) + (q0 + nq - a)};
+            out.push_back(it);
+        }
+    }
+    // longest key range first, so the long items start before the short ones
+    std::stable_sort(out.begin(), out.end(),
+                     [](const Item& x, const Item& y) { return x.keys > y.keys; });
+    if (out.size() > size_t(INT32_MAX / LA_ATTN_ITEM_WORDS)) return LA_ERR_INVALID_ARG;
+    if (items)
+        for (size_t i = 0; i < out.size(); ++i)
+            std::memcpy(items + i * LA_ATTN_ITEM_WORDS, out[i].w, sizeof(out[i].w));
+    *n_items = int32_t(out.size());
+    return LA_OK;
 }
 
 extern "C" const char* la_status_string(la_status status) {

@@ -42,234 +42,9 @@
 #include <cstdint>
 
 #include "linattn.h"
+#include "tiles.h"
 
 namespace {
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
-typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
-
-constexpr int kThreads = 256;   // 4 waves of 64
-constexpr int kChunk = LA_CHUNK;
-
-__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-}
-
-__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
-// Two fp32 -> packed bf16 (low half = a), round to nearest even
-// (v_cvt_pk_bf16_f32).
-__device__ __forceinline__ uint32_t cvt_bf2(float a, float b) {
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2_t));
-}
-__device__ __forceinline__ float bf_lo(uint32_t p) { return __uint_as_float(p << 16); }
-__device__ __forceinline__ float bf_hi(uint32_t p) { return __uint_as_float(p & 0xffff0000u); }
-
-__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
-
-// Wave index as a wave-uniform (scalar) value, so that branches and buffer
-// resources chosen by it stay scalar.
-__device__ __forceinline__ int wave_id() {
-    return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x)) >> 6;
-}
-
-// Workspace slot layout: element e of a d x d state is stored at
-//   e = ((vb * NKB + kb) * 4 + j) * 64 + lane,   lane = 16 g + c
-// holding S[kb*16 + 4g + j][vb*16 + c]: one coalesced 256-byte row per
-// (tile, j) for the lane order of the accumulator layout.
-template <int D>
-__device__ __forceinline__ void slot_to_rc(int e, int& row, int& col) {
-    constexpr int NKB = D / 16;
-    const int lane = e & 63;
-    const int j = (e >> 6) & 3;
-    const int kb = (e >> 8) % NKB;
-    const int vb = (e >> 8) / NKB;
-    row = kb * 16 + 4 * (lane >> 4) + j;
-    col = vb * 16 + (lane & 15);
-}
-
-// ---------------------------------------------------------------------------
-// Range-checked chunk windows.  A chunk of `rows` tokens of a [T][H][D]
-// tensor is addressed through a raw buffer resource whose size is
-// rows*H*D*elem bytes from the chunk's first token: a token row r >= rows
-// lies entirely past the end (its offset is at least rows*H*D*elem), so the
-// hardware returns zeros for such loads and drops such stores.  Ragged last
-// chunks need no branches.
-// ---------------------------------------------------------------------------
-// A window with rows <= 0 is empty: every load through it returns zeros
-// without touching memory, so a prefetch past the last chunk can be issued
-// unconditionally (no branch, hence no register merge that would force the
-// compiler to wait for the loads).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rsrc(const void* base, int64_t first_elem,
-                                                             int elem_bytes, int rows, int H,
-                                                             int D) {
-    const char* p = static_cast<const char*>(base) + (rows > 0 ? first_elem * elem_bytes : 0);
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p), (short)0,
-                                             rows > 0 ? rows * H * D * elem_bytes : 0,
-                                             0x00020000);
-}
-__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-__device__ __forceinline__ void buf_store8(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x2 x) {
-    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, x), r, off, 0, 0);
-}
-
-// ---------------------------------------------------------------------------
-// bf16 tile staging.  A 64 x D tile is cut into R x 8 blocks (R tokens x 8
-// features, R = 4 or 2); one lane loads a block as R row pieces of 16 bytes
-// (8 lanes cover one D*2-byte row, so each load instruction reads whole cache
-// lines) and writes it to LDS row-major and/or transposed.  The transpose is
-// done in registers with v_perm_b32: column c of the block becomes R
-// consecutive tokens, one R*2-byte LDS store.
-// ---------------------------------------------------------------------------
-template <int D, int R>
-struct Stage {
-    static constexpr int NCG = D / 8;           // 8-feature groups per row
-    static constexpr int NB = (kChunk / R) * NCG;   // R x 8 blocks per 64-token tile
-    static constexpr int LDR = D + 8;           // row-major stride (elements)
-    static constexpr int LDT = kChunk + 8;      // transposed stride (elements)
-};
-
-template <int R>
-struct BlkR {
-    u32x4 r[R];  // r[i] = token i of the block, 8 bf16 features
-};
-
-template <int R>
-__device__ __forceinline__ void load_blk(BlkR<R>& b, __amdgpu_buffer_rsrc_t rs, int rg, int cg,
-                                         int H, int h, int D) {
-#pragma unroll
-    for (int i = 0; i < R; ++i)
-        b.r[i] = buf_load16(rs, uint32_t((((rg * R + i) * H + h) * D + cg * 8) * 2));
-}
-
-template <int R>
-__device__ __forceinline__ void store_rows(uint16_t* dst, const BlkR<R>& b, int rg, int cg,
-                                           int ld) {
-#pragma unroll
-    for (int i = 0; i < R; ++i)
-        *reinterpret_cast<u32x4*>(dst + (rg * R + i) * ld + cg * 8) = b.r[i];
-}
-
-// Transposed tiles [feature][token] hold the 64 tokens of a row in the order
-//   position(u) = 32 a + 8 c + 4 b + d   for   u = 32 a + 16 b + 4 c + d,
-// so that the 8 tokens {32a + 16b + 4c + d : b, d} (two 4-token groups 16
-// apart: the k-slots of lane group c in a K = 32 step whose two halves come
-// from 16-row tiles 2a and 2a + 1) are 16 contiguous bytes.  Every consumer
-// reads such 8-token groups: the carry K^T V (both operands in this order,
-// so the contraction is unchanged) and the intra-chunk V^T P^T (whose P^T
-// operand comes from accumulator tiles in exactly this slot order).  On top,
-// rows whose feature index has bit 4 set swap their two 32-token halves, so
-// the 8-byte column stores of one instruction spread over all LDS banks
-// (16-byte aligned rows 8 apart otherwise start on the same or the opposite
-// bank).
-__device__ __forceinline__ int tpos(int feature, int token) {
-    const int pos = (token & 32) | ((token & 12) << 1) | ((token & 16) >> 2) | (token & 3);
-    return pos ^ ((feature & 16) << 1);
-}
-
-// dst[(cg*8 + c) * ld + tpos(cg*8 + c, rg*R) .. + R-1] = column c of the block
-// (R = 2 or 4 consecutive tokens stay contiguous under tpos).
-template <int R>
-__device__ __forceinline__ void store_cols(uint16_t* dst, const BlkR<R>& b, int rg, int cg,
-                                           int ld) {
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {   // features 2m (low halves) and 2m+1 (high halves)
-        const int f0 = cg * 8 + 2 * m;   // f0 and f0 + 1 share bit 4
-        const int t0 = tpos(f0, rg * R);
-        if constexpr (R == 4) {
-            const u32x2 ev{__builtin_amdgcn_perm(b.r[1][m], b.r[0][m], 0x05040100u),
-                           __builtin_amdgcn_perm(b.r[3][m], b.r[2][m], 0x05040100u)};
-            const u32x2 od{__builtin_amdgcn_perm(b.r[1][m], b.r[0][m], 0x07060302u),
-                           __builtin_amdgcn_perm(b.r[3][m], b.r[2][m], 0x07060302u)};
-            *reinterpret_cast<u32x2*>(dst + f0 * ld + t0) = ev;
-            *reinterpret_cast<u32x2*>(dst + (f0 + 1) * ld + t0) = od;
-        } else {
-            static_assert(R == 2, "blocks of 2 or 4 tokens");
-            *reinterpret_cast<uint32_t*>(dst + f0 * ld + t0) =
-                __builtin_amdgcn_perm(b.r[1][m], b.r[0][m], 0x05040100u);
-            *reinterpret_cast<uint32_t*>(dst + (f0 + 1) * ld + t0) =
-                __builtin_amdgcn_perm(b.r[1][m], b.r[0][m], 0x07060302u);
-        }
-    }
-}
-
-__device__ __forceinline__ u32x2 lds_u32x2(const uint16_t* p) {
-    return *reinterpret_cast<const u32x2*>(p);
-}
-__device__ __forceinline__ u32x4 lds_u32x4(const uint16_t* p) {
-    return *reinterpret_cast<const u32x4*>(p);
-}
-__device__ __forceinline__ u32x4 cat2(u32x2 a, u32x2 b) { return u32x4{a[0], a[1], b[0], b[1]}; }
-
-// K and V blocks of one chunk: all D features of K, and the DVW features of V
-// starting at feature vcg0 * 8 (a workgroup that computes only part of the
-// output features needs only that part of V).  Block index b = tid + i*NT
-// over [K | V]; each half is a whole number of waves, so the tile choice and
-// whether a wave loads at all are wave-uniform.
-template <int D, int DVW, int R, int NT>
-struct KVStage {
-    static constexpr int NCGK = D / 8, NCGV = DVW / 8;   // 8-feature groups per row
-    static constexpr int NBK = (kChunk / R) * NCGK;     // K blocks
-    static constexpr int NBV = (kChunk / R) * NCGV;     // V blocks
-    static constexpr int NPER = (NBK + NBV + NT - 1) / NT;
-    static_assert(NBK % 64 == 0 && NBV % 64 == 0, "K and V parts are whole waves");
-};
-
-template <int D, int DVW, int R, int NT, int NPER>
-__device__ __forceinline__ void load_kv(BlkR<R> (&pre)[NPER], __amdgpu_buffer_rsrc_t rk,
-                                        __amdgpu_buffer_rsrc_t rv, int vcg0, int H, int h) {
-    using KS = KVStage<D, DVW, R, NT>;
-    const int wbase = wave_id() * 64;
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int i = 0; i < NPER; ++i) {
-        const int b0 = wbase + i * NT;                      // wave-uniform
-        if constexpr (NPER * NT > KS::NBK + KS::NBV)
-            if (b0 >= KS::NBK + KS::NBV) break;
-        const bool is_v = b0 >= KS::NBK;
-        const int wk = b0 + lane, wv = b0 - KS::NBK + lane;
-        // selects, not branches: the loads stay unconditional
-        const int rg = is_v ? wv / KS::NCGV : wk / KS::NCGK;
-        const int cg = is_v ? vcg0 + wv % KS::NCGV : wk % KS::NCGK;
-        load_blk<R>(pre[i], is_v ? rv : rk, rg, cg, H, h, D);
-    }
-}
-
-// Registers -> LDS: K transposed (and row-major if sK is given), V transposed
-// (rows are the workgroup's own V features, 0 .. DVW-1).
-template <int D, int DVW, int R, int NT, int NPER>
-__device__ __forceinline__ void stage_kv(const BlkR<R> (&pre)[NPER], uint16_t* sK,
-                                         uint16_t* sKt, uint16_t* sVt) {
-    using KS = KVStage<D, DVW, R, NT>;
-    using ST = Stage<D, R>;
-    const int wbase = wave_id() * 64;
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int i = 0; i < NPER; ++i) {
-        const int b0 = wbase + i * NT;                      // wave-uniform
-        if constexpr (NPER * NT > KS::NBK + KS::NBV)
-            if (b0 >= KS::NBK + KS::NBV) break;
-        if (b0 >= KS::NBK) {
-            const int wv = b0 - KS::NBK + lane;
-            store_cols<R>(sVt, pre[i], wv / KS::NCGV, wv % KS::NCGV, ST::LDT);
-        } else {
-            const int wk = b0 + lane;
-            if (sK) store_rows<R>(sK, pre[i], wk / KS::NCGK, wk % KS::NCGK, ST::LDR);
-            store_cols<R>(sKt, pre[i], wk / KS::NCGK, wk % KS::NCGK, ST::LDT);
-        }
-    }
-}
 
 // Work items (one per block or delta block and head) split over NP
 // workgroups by output feature.  Workgroups go to the 8 XCDs round-robin by
@@ -360,7 +135,7 @@ __global__ __launch_bounds__(kThreads) void delta_kernel_bf16(
                                            chunk_rsrc(v, first, 2, rows, H, D), vcg0, H, h);
     };
     auto step = [&](BlkR<R> (&cur)[NPER], int c) {
-        stage_kv<D, DVW, R, kThreads, NPER>(cur, nullptr, sKt, sVt);
+        stage_kv<D, DVW, R, kThreads, NPER, false, true>(cur, nullptr, sKt, sVt);
         __syncthreads();
         load(cur, c + 2);   // empty window past the last chunk
 #pragma unroll
@@ -805,7 +580,7 @@ __global__ __launch_bounds__(O3::NT) void output_kernel_bf16(
             *reinterpret_cast<u32x2*>(sSh + off) = u32x2{h01, h23};
             *reinterpret_cast<u32x2*>(sSl + off) = u32x2{l01, l23};
         }
-        stage_kv<D, DV, R, NT, NPER>(kv, sK, sKt, sVt);
+        stage_kv<D, DV, R, NT, NPER, true, true>(kv, sK, sKt, sVt);
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) qf[ks] = qn[ks];
         __syncthreads();

@@ -265,6 +265,61 @@ la_status la_export_view_state(const float* final_state, int32_t view_row,
                                float* dst, void* stream);
 
 /*
+ * Tree-masked softmax attention over a packed pass -- the other layer type of
+ * the pass (section "The Workload": Span-1 is mostly linear attention with a
+ * few softmax-attention layers; branches attend to their view, never to each
+ * other; section "Long Requests": a branch shard attends to its view's
+ * cached K/V).  Per head, for every token t:
+ *
+ *     o_t = sum_{u in A(t)} softmax_u(scale * q_t . k_u) v_u
+ *
+ * where A(t) is t's own segment up to and including t, plus every token of
+ * the parent view for a branch.  A shard branch (parent -2 - e) takes its
+ * view's keys and values from external arrays instead (the cached view K/V).
+ *
+ * la_attn_plan -- host: one work item per (segment, 64-token query block).
+ *   n_segments, seg_offsets, branch_parent   the segment table, as for
+ *                    la_plan_segments (parents >= 0 must be views; -2 - e
+ *                    names external view e)
+ *   n_ext            external views (>= 0)
+ *   ext_len          host [n_ext]: tokens of each external view (>= 1); the
+ *                    views are concatenated in ext_k / ext_v in this order
+ *   items            host [*n_items][LA_ATTN_ITEM_WORDS] or NULL (size query)
+ *   n_items          host, required: number of items
+ * Item layout: {q0, nq, seg0, view0, view_len, view_src, 0, 0}: queries
+ * q0 .. q0+nq-1 (nq <= LA_CHUNK) of the segment starting at seg0, whose
+ * extra keys are tokens view0 .. view0+view_len-1 of the pass (view_src
+ * LA_ATTN_PACKED_VIEW), of ext_k / ext_v (LA_ATTN_EXT_VIEW), or none
+ * (LA_ATTN_NO_VIEW).  Items are ordered longest key range first.
+ * Errors: LA_ERR_INVALID_ARG (bad table, parent or length).
+ *
+ * la_attn_packed -- device: the attention of the pass on `stream`, one
+ * workgroup per (item, head): online softmax over 64-key blocks (bf16 MFMA
+ * for q.k and p.v, fp32 scores, running max and sums), out rounded to bf16.
+ *   q, k, v        device [n_tokens][H][d] bf16 (dtype must be LA_BF16)
+ *   d_k, d_v       equal, 64 or 128
+ *   scale          score scale (e.g. 1/sqrt(d) if k is not pre-scaled)
+ *   items          device [n_items][LA_ATTN_ITEM_WORDS] int32, a copy of the
+ *                  la_attn_plan output for this segment table
+ *   ext_k, ext_v   device [n_ext_tokens][H][d] bf16, or NULL if no item
+ *                  reads an external view
+ *   out            device [n_tokens][H][d_v] bf16: fully overwritten
+ * Errors: LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED (dtype, dims), LA_ERR_HIP.
+ * The items are trusted (build them with la_attn_plan).
+ */
+#define LA_ATTN_ITEM_WORDS 8
+#define LA_ATTN_NO_VIEW 0
+#define LA_ATTN_PACKED_VIEW 1
+#define LA_ATTN_EXT_VIEW 2
+la_status la_attn_plan(int32_t n_segments, const int32_t* seg_offsets,
+                       const int32_t* branch_parent, int32_t n_ext, const int32_t* ext_len,
+                       int32_t* items, int32_t* n_items);
+la_status la_attn_packed(const void* q, const void* k, const void* v, la_dtype dtype, int32_t H,
+                         int32_t d_k, int32_t d_v, float scale, const int32_t* items,
+                         int32_t n_items, int32_t n_tokens, const void* ext_k,
+                         const void* ext_v, int32_t n_ext_tokens, void* out, void* stream);
+
+/*
  * View-state cache directory (section "Long Requests": nodes cache the
  * linear-attention state of recent views so that a branch shard does not
  * recompute its view).  The states live in a caller-owned device pool

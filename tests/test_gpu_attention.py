@@ -1,0 +1,150 @@
+"""GPU parity of the tree-masked softmax attention (la_attn_packed) against
+the fp64 oracle (oracle/attention.py), through the C ABI.
+
+Tolerance: row-normalised max relative error 2e-2 (bf16 inputs), the same
+rule as the scan.  Shard branches reading their view from external K/V arrays
+are compared bit for bit with the same branches in the full pass."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import chunked_linear_attention_packed_amd as la
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+TOL = 2e-2
+
+
+def _run(q, k, v, so, bp, scale, ext_len=None, ext_k=None, ext_v=None):
+    plan = la.attn_plan(so, bp, ext_len)
+    ek = None if ext_k is None else ext_k.to(DEV).contiguous()
+    ev = None if ext_v is None else ext_v.to(DEV).contiguous()
+    out = la.attn_packed(q.to(DEV), k.to(DEV), v.to(DEV), plan, scale, ext_k=ek, ext_v=ev)
+    torch.cuda.synchronize()
+    return out.cpu()
+
+
+STRUCTS = {
+    "view1": ([1], [0], []),
+    "view63": ([63], [0], []),
+    "view64": ([64], [0], []),
+    "view65": ([65], [0], []),
+    "view200_br3": ([200], [3], [1, 64, 130]),
+    "two_requests": ([129, 70], [2, 1], [65, 5, 64]),
+    "branch_len1_view_len1": ([1, 3], [2, 1], [1, 1, 2]),
+}
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("name", list(STRUCTS))
+def test_attention_matches_oracle(name, d):
+    vl, bc, bl = STRUCTS[name]
+    so, bp, _ = oracle.pack_segments(vl, bc, bl)
+    H = 3
+    q, k, v = synth.draw_qkv(np.random.default_rng(sum(name.encode()) + d), int(so[-1]),
+                             H, d, "bf16")
+    out = _run(q, k, v, so, bp, 1.0)
+    ref = oracle.attention_dense(q, k, v, so, bp, 1.0)
+    err = oracle.row_rel_err(out, ref)
+    print(f"{name} d={d}: err {err:.2e}", flush=True)
+    assert err <= TOL
+
+
+@pytest.mark.parametrize("scale", [0.05, 8.0])
+def test_attention_extreme_scales(scale):
+    """Near-uniform weights and near-argmax weights (large logits: the
+    running maximum must keep exp() finite)."""
+    so, bp, _ = oracle.pack_segments([300], [2], [40, 90])
+    q, k, v = synth.draw_qkv(np.random.default_rng(3), int(so[-1]), 2, 64, "bf16")
+    out = _run(q, k, v, so, bp, scale)
+    assert torch.isfinite(out.float()).all()
+    err = oracle.row_rel_err(out, oracle.attention_dense(q, k, v, so, bp, scale))
+    print(f"scale {scale}: err {err:.2e}", flush=True)
+    assert err <= TOL
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_shard_branches_from_external_view_kv(d):
+    H = 2
+    vl, bc, bl = [150], [4], [20, 64, 65, 3]
+    so, bp, _ = oracle.pack_segments(vl, bc, bl)
+    q, k, v = synth.draw_qkv(np.random.default_rng(21), int(so[-1]), H, d, "bf16")
+    full = _run(q, k, v, so, bp, 1.0)
+    # the branches alone, their view's K/V given as external view 0
+    a = int(so[1])
+    so_s = np.asarray(so[1:]) - a
+    bp_s = np.full(len(bl), -2)
+    shard = _run(q[a:], k[a:], v[a:], so_s, bp_s, 1.0, ext_len=[vl[0]], ext_k=k[:a],
+                 ext_v=v[:a])
+    assert torch.equal(shard, full[a:])
+    ref = oracle.attention_dense(q[a:], k[a:], v[a:], so_s, bp_s, 1.0,
+                                 ext_kv=[(k[:a], v[:a])])
+    assert oracle.row_rel_err(shard, ref) <= TOL
+
+
+def test_several_external_views_and_a_packed_view_in_one_pass():
+    H, d = 2, 64
+    rng = np.random.default_rng(22)
+    ext_len = [70, 5, 200]
+    ek, ev, _ = synth.draw_qkv(rng, sum(ext_len), H, d, "bf16")
+    # segments: shard branch of ext view 2, a view, its branch, shard branch of ext view 0
+    so = np.array([0, 30, 130, 200, 201])
+    bp = np.array([-4, -1, 1, -2])
+    q, k, v = synth.draw_qkv(rng, int(so[-1]), H, d, "bf16")
+    out = _run(q, k, v, so, bp, 1.0, ext_len=ext_len, ext_k=ek, ext_v=ev)
+    offs = np.concatenate([[0], np.cumsum(ext_len)])
+    ext_kv = [(ek[offs[e]:offs[e + 1]], ev[offs[e]:offs[e + 1]]) for e in range(3)]
+    ref = oracle.attention_dense(q, k, v, so, bp, 1.0, ext_kv=ext_kv)
+    err = oracle.row_rel_err(out, ref)
+    print(f"mixed external views: err {err:.2e}", flush=True)
+    assert err <= TOL
+
+
+@pytest.mark.parametrize("name", ["view7400_br8x48_h16_d64_bf16",
+                                  "view18000_br256x32-128_h16_d64_bf16"])
+def test_attention_workload_sampled_rows(name):
+    w = synth.workload(name)
+    so, bp, _ = oracle.pack_segments(w.view_len, w.branch_count, w.branch_len)
+    plan = la.attn_plan(so, bp)
+    out = la.attn_packed(w.q.to(DEV), w.k.to(DEV), w.v.to(DEV), plan, 1.0)
+    torch.cuda.synchronize()
+    T = int(so[-1])
+    rng = np.random.default_rng(5)
+    rows = sorted(set(rng.integers(0, T, size=48).tolist()) |
+                  {0, 63, 64, int(so[1]) - 1, int(so[1]), T - 1})
+    ref = oracle.attention_rows(w.q, w.k, w.v, so, bp, 1.0, rows)
+    err = oracle.row_rel_err(out[rows].cpu(), ref)
+    print(f"{name}: {len(rows)} sampled rows, err {err:.2e}", flush=True)
+    assert err <= TOL
+
+
+def test_attention_is_deterministic_and_overwrites_out():
+    so, bp, _ = oracle.pack_segments([257], [2], [33, 70])
+    q, k, v = (x.to(DEV) for x in synth.draw_qkv(np.random.default_rng(9), int(so[-1]), 4, 64,
+                                                   "bf16"))
+    plan = la.attn_plan(so, bp)
+    a = la.attn_packed(q, k, v, plan, 1.0)
+    b = torch.full_like(a, float("nan"))
+    la.attn_packed(q, k, v, plan, 1.0, out=b)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_attention_rejects_bad_arguments():
+    so, bp, _ = oracle.pack_segments([10], [1], [5])
+    plan = la.attn_plan(so, bp)
+    q = torch.zeros((15, 2, 64), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(la.LinAttnError):
+        la.attn_packed(q.float(), q.float(), q.float(), plan, 1.0)      # fp32: unsupported
+    q96 = torch.zeros((15, 2, 96), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(la.LinAttnError):
+        la.attn_packed(q96, q96, q96, plan, 1.0)                         # d = 96
+    with pytest.raises(ValueError):
+        la.attn_packed(q[:10], q[:10], q[:10], plan, 1.0)                # token count
+    ext_plan = la.attn_plan([0, 4], [-2], ext_len=[7])
+    q4 = torch.zeros((4, 2, 64), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(ValueError):
+        la.attn_packed(q4, q4, q4, ext_plan, 1.0)                        # ext arrays missing
