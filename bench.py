@@ -54,6 +54,9 @@ def parse():
                     help="instead of the headline: split the workload's one request "
                          "into this many branch shards and time them with and without "
                          "the view-state cache against the unsplit pass")
+    ap.add_argument("--split-fp32", action="store_true",
+                    help="fp32 workloads: evaluate products as three bf16 MFMAs over hi/lo "
+                         "operand splits (LA_F32_SPLIT) instead of fp32 MFMAs")
     ap.add_argument("--attention", action="store_true",
                     help="instead of the headline: time the tree-masked softmax attention "
                          "(la_attn_packed) of the workload against the bf16 MFMA peak")
@@ -474,11 +477,13 @@ def main():
                      device=dev)
     plan.device_plan(dev)
     stream = torch.cuda.Stream(dev)
+    if a.split_fp32 and w.dtype != "f32":
+        raise SystemExit("--split-fp32 applies to fp32 workloads")
 
     def step(i, stages=la.STAGE_ALL):
         s = sets[i % n_sets]
         la.scan_packed(s["q"], s["k"], s["v"], plan, out=s["out"], final_state=fin,
-                       workspace=ws, stream=stream, stages=stages)
+                       workspace=ws, stream=stream, stages=stages, split_fp32=a.split_fp32)
 
     # first pass eagerly (also validates arguments)
     with torch.cuda.stream(stream):
@@ -535,7 +540,8 @@ def main():
     src = os.path.join(ROOT, "chunked_linear_attention_packed_amd", "csrc", "scan.hip")
     with open(src, "rb") as f:
         src_hash = hashlib.sha256(f.read()).hexdigest()
-    traffic = traffic_from_profiles("output_kernel", a.workload, src_hash)
+    traffic = traffic_from_profiles("output_kernel_split" if a.split_fp32 else "output_kernel",
+                                    a.workload, src_hash)
     pass_us = gpu_ms * 1e3 / a.steps
 
     cpu = None
@@ -562,6 +568,9 @@ def main():
             "chunk": info.chunk, "block_chunks": info.block_chunks,
             "work_blocks": info.n_blocks, "delta_blocks": info.n_delta,
             "launch": "eager" if a.eager else "hip_graph",
+            "precision": ("fp32 data, products as 3 bf16 MFMAs (hi.hi + hi.lo + lo.hi)"
+                          if a.split_fp32 else
+                          ("fp32 MFMA" if w.dtype == "f32" else "bf16 MFMA, fp32 accumulate")),
             "rotating_input_sets": n_sets,
             "gpu_us_per_pass": pass_us,
             "pass_algorithmic_bytes": pass_bytes,

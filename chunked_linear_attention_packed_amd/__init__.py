@@ -34,7 +34,7 @@ __all__ = ["LinAttnError", "PassInfo", "PassPlan", "pack", "plan_segments",
 
 CHUNK = 64
 LA_OK, LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED, LA_ERR_WORKSPACE, LA_ERR_HIP = range(5)
-LA_F32, LA_BF16 = 0, 1
+LA_F32, LA_BF16, LA_F32_SPLIT = 0, 1, 2
 LA_ATTN_NO_VIEW, LA_ATTN_PACKED_VIEW, LA_ATTN_EXT_VIEW = 0, 1, 2
 STAGE_STATES, STAGE_PREFIX, STAGE_OUTPUT, STAGE_ALL = 1, 2, 4, 7
 
@@ -249,14 +249,16 @@ def _stream_ptr(stream, device):
 
 
 def scan_packed(q, k, v, plan, ext_state=None, out=None, final_state=None, workspace=None,
-                stream=None, stages=STAGE_ALL):
+                stream=None, stages=STAGE_ALL, split_fp32=False):
     """Run the three-launch scan on `stream` (default: torch's current stream).
 
     q, k: [T, H, d] and v: [T, H, d] contiguous CUDA tensors, bf16 or fp32.
     Returns (out [T, H, d] in the input dtype, final_state [n_views, H, d, d]
     fp32).  Pre-allocated out / final_state / workspace tensors are used as
     given (no allocation then).  `stages` selects launches (STAGE_* bits, see
-    la_scan_packed_stages) for profiling; the default runs all three."""
+    la_scan_packed_stages) for profiling; the default runs all three.  For
+    fp32 inputs, split_fp32=True evaluates every product as three bf16 MFMAs
+    over hi/lo operand splits (LA_F32_SPLIT) instead of fp32 MFMAs."""
     import torch
     lib = load_library()
     if not (q.is_cuda and k.is_cuda and v.is_cuda):
@@ -273,6 +275,10 @@ def scan_packed(q, k, v, plan, ext_state=None, out=None, final_state=None, works
     if T != info.n_tokens:
         raise ValueError(f"q has {T} tokens, the plan {info.n_tokens}")
     code = _dtype_code(q)
+    if split_fp32:
+        if code != LA_F32:
+            raise TypeError("split_fp32 applies to float32 inputs")
+        code = LA_F32_SPLIT
     dev = q.device
     if out is None:
         out = torch.empty((T, H, dv), dtype=q.dtype, device=dev)

@@ -712,6 +712,360 @@ __global__ __launch_bounds__(kThreads) void output_kernel_f32(
 }
 
 // ===========================================================================
+// Split-precision fp32 path (section "Kernels", paragraph "Tensor cores for
+// linear attention": the page runs its fp32 data on tf32 tensor cores with
+// each product split into three for accuracy).  Here each fp32 operand x is
+// split into two bf16 terms, x_hi = bf16(x) and x_lo = bf16(x - x_hi), and a
+// product a.b is evaluated as three bf16 MFMAs, a_hi.b_hi + a_hi.b_lo +
+// a_lo.b_hi, accumulated in fp32: what is dropped (a_lo.b_lo and the rounding
+// of the low terms) is about 2^-16 of |a.b|.  Same structure as the bf16
+// kernels; every staged tile and every register operand exists as a hi and a
+// lo copy, and outputs are stored as fp32.
+// ===========================================================================
+template <int R>
+struct BlkF {            // R rows x 8 fp32 features (raw bits)
+    u32x4 a[R], b[R];    // features 0..3 and 4..7 of row i
+};
+
+template <int R>
+__device__ __forceinline__ void load_blk_f32(BlkF<R>& bl, __amdgpu_buffer_rsrc_t rs, int rg,
+                                             int cg, int H, int h, int D) {
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+        const uint32_t off = uint32_t((((rg * R + i) * H + h) * D + cg * 8) * 4);
+        bl.a[i] = buf_load16(rs, off);
+        bl.b[i] = buf_load16(rs, off + 16);
+    }
+}
+
+// 8 fp32 values (two 16-byte pieces) -> their bf16 hi and lo terms
+__device__ __forceinline__ void split8(u32x4 a, u32x4 b, u32x4& hi, u32x4& lo) {
+    const float f[8] = {__uint_as_float(a[0]), __uint_as_float(a[1]), __uint_as_float(a[2]),
+                        __uint_as_float(a[3]), __uint_as_float(b[0]), __uint_as_float(b[1]),
+                        __uint_as_float(b[2]), __uint_as_float(b[3])};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const uint32_t hh = cvt_bf2(f[2 * m], f[2 * m + 1]);
+        hi[m] = hh;
+        lo[m] = cvt_bf2(f[2 * m] - bf_lo(hh), f[2 * m + 1] - bf_hi(hh));
+    }
+}
+
+template <int D, int DVW, int R, int NT, int NPER>
+__device__ __forceinline__ void load_kv_f32(BlkF<R> (&pre)[NPER], __amdgpu_buffer_rsrc_t rk,
+                                            __amdgpu_buffer_rsrc_t rv, int vcg0, int H, int h) {
+    using KS = KVStage<D, DVW, R, NT>;
+    const int wbase = wave_id() * 64;
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < NPER; ++i) {
+        const int b0 = wbase + i * NT;                      // wave-uniform
+        if constexpr (NPER * NT > KS::NBK + KS::NBV)
+            if (b0 >= KS::NBK + KS::NBV) break;
+        const bool is_v = b0 >= KS::NBK;
+        const int wk = b0 + lane, wv = b0 - KS::NBK + lane;
+        const int rg = is_v ? wv / KS::NCGV : wk / KS::NCGK;
+        const int cg = is_v ? vcg0 + wv % KS::NCGV : wk % KS::NCGK;
+        load_blk_f32<R>(pre[i], is_v ? rv : rk, rg, cg, H, h, D);
+    }
+}
+
+// Registers -> LDS, each block as its hi and lo terms: K row-major
+// (K_ROWS), K transposed, V transposed.
+template <int D, int DVW, int R, int NT, int NPER, bool K_ROWS>
+__device__ __forceinline__ void stage_kv_split(const BlkF<R> (&pre)[NPER], uint16_t* sKh,
+                                               uint16_t* sKl, uint16_t* sKth, uint16_t* sKtl,
+                                               uint16_t* sVth, uint16_t* sVtl) {
+    using KS = KVStage<D, DVW, R, NT>;
+    using ST = Stage<D, R>;
+    const int wbase = wave_id() * 64;
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < NPER; ++i) {
+        const int b0 = wbase + i * NT;                      // wave-uniform
+        if constexpr (NPER * NT > KS::NBK + KS::NBV)
+            if (b0 >= KS::NBK + KS::NBV) break;
+        BlkR<R> hi, lo;
+#pragma unroll
+        for (int r = 0; r < R; ++r) split8(pre[i].a[r], pre[i].b[r], hi.r[r], lo.r[r]);
+        if (b0 >= KS::NBK) {
+            const int wv = b0 - KS::NBK + lane;
+            store_cols<R>(sVth, hi, wv / KS::NCGV, wv % KS::NCGV, ST::LDT);
+            store_cols<R>(sVtl, lo, wv / KS::NCGV, wv % KS::NCGV, ST::LDT);
+        } else {
+            const int wk = b0 + lane;
+            if constexpr (K_ROWS) {
+                store_rows<R>(sKh, hi, wk / KS::NCGK, wk % KS::NCGK, ST::LDR);
+                store_rows<R>(sKl, lo, wk / KS::NCGK, wk % KS::NCGK, ST::LDR);
+            }
+            store_cols<R>(sKth, hi, wk / KS::NCGK, wk % KS::NCGK, ST::LDT);
+            store_cols<R>(sKtl, lo, wk / KS::NCGK, wk % KS::NCGK, ST::LDT);
+        }
+    }
+}
+
+// a.b ~ a_hi.b_hi + a_hi.b_lo + a_lo.b_hi
+__device__ __forceinline__ f32x4 mfma3(u32x4 ah, u32x4 al, u32x4 bh, u32x4 bl, f32x4 c) {
+    c = mfma_bf16(ah, bh, c);
+    c = mfma_bf16(ah, bl, c);
+    return mfma_bf16(al, bh, c);
+}
+
+// Launch 1, split precision: as delta_kernel_bf16 with NP = 1.
+template <int D>
+__global__ __launch_bounds__(kThreads) void delta_kernel_split(
+    const float* __restrict__ k, const float* __restrict__ v,
+    const DeltaDesc* __restrict__ deltas, float* __restrict__ ws, int H) {
+    using D1 = Delta1<D, 1>;
+    constexpr int R = D1::R, NKB = D1::NKB, VBW = D1::VBW, KBW = D1::KBW, DD = D * D;
+    using ST = Stage<D, R>;
+    constexpr int NPER = KVStage<D, D, R, kThreads>::NPER;
+    __shared__ __attribute__((aligned(16))) uint16_t sKth[D * ST::LDT];
+    __shared__ __attribute__((aligned(16))) uint16_t sKtl[D * ST::LDT];
+    __shared__ __attribute__((aligned(16))) uint16_t sVth[D * ST::LDT];
+    __shared__ __attribute__((aligned(16))) uint16_t sVtl[D * ST::LDT];
+
+    const int h = blockIdx.x % H;
+    const DeltaDesc dd = deltas[blockIdx.x / H];
+    const int w = wave_id(), lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
+    const int vbw = D1::vb0(w), kbw = D1::kb0(w);
+
+    f32x4 S[VBW][KBW];
+#pragma unroll
+    for (int x = 0; x < VBW; ++x)
+#pragma unroll
+        for (int i = 0; i < KBW; ++i) S[x][i] = zero4();
+
+    const int nch = (dd.ntok + kChunk - 1) / kChunk;
+    const int64_t row_elems = int64_t(H) * D;
+    BlkF<R> pre[NPER];
+    auto load = [&](int c) {
+        const int64_t first = (int64_t(dd.tok0) + c * kChunk) * row_elems;
+        const int rows = min(kChunk, dd.ntok - c * kChunk);   // <= 0: empty window
+        load_kv_f32<D, D, R, kThreads, NPER>(pre, chunk_rsrc(k, first, 4, rows, H, D),
+                                             chunk_rsrc(v, first, 4, rows, H, D), 0, H, h);
+    };
+    load(0);
+    for (int c = 0; c < nch; ++c) {
+        stage_kv_split<D, D, R, kThreads, NPER, false>(pre, nullptr, nullptr, sKth, sKtl, sVth,
+                                                       sVtl);
+        __syncthreads();
+        load(c + 1);   // empty window past the last chunk
+#pragma unroll
+        for (int ks = 0; ks < kChunk / 32; ++ks) {
+#pragma unroll
+            for (int x = 0; x < VBW; ++x) {
+                const int vb = vbw + x;
+                const int vo = (vb * 16 + c16) * ST::LDT + tpos(vb * 16, ks * 32 + 4 * g);
+                const u32x4 bvh = lds_u32x4(sVth + vo), bvl = lds_u32x4(sVtl + vo);
+#pragma unroll
+                for (int i = 0; i < KBW; ++i) {
+                    const int kb = kbw + i;
+                    const int ko = (kb * 16 + c16) * ST::LDT + tpos(kb * 16, ks * 32 + 4 * g);
+                    S[x][i] = mfma3(lds_u32x4(sKth + ko), lds_u32x4(sKtl + ko), bvh, bvl, S[x][i]);
+                }
+            }
+        }
+        __syncthreads();
+    }
+    float* dst = ws + ((int64_t)dd.slot * H + h) * DD;
+#pragma unroll
+    for (int x = 0; x < VBW; ++x)
+#pragma unroll
+        for (int i = 0; i < KBW; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                dst[(((vbw + x) * NKB + kbw + i) * 4 + j) * 64 + lane] = S[x][i][j];
+}
+
+// The outputs of one wave for one chunk, split precision (see out_tiles).
+template <int D, int TB, int VBH>
+__device__ __forceinline__ void out_tiles_split(const uint16_t* sKh, const uint16_t* sKl,
+                                                const uint16_t* sVth, const uint16_t* sVtl,
+                                                const uint16_t* sSh, const uint16_t* sSl,
+                                                const u32x4 (&qh)[D / 32],
+                                                const u32x4 (&ql)[D / 32], int vb0, int g,
+                                                int c16, f32x4 (&acc)[VBH]) {
+    constexpr int NKS = D / 32;
+    constexpr int LDR = Stage<D, 4>::LDR, LDT = Stage<D, 4>::LDT;
+    f32x4 p[TB + 1];
+#pragma unroll
+    for (int ub = 0; ub <= TB; ++ub) p[ub] = zero4();
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+        for (int ub = 0; ub <= TB; ++ub) {
+            const int o = (ub * 16 + c16) * LDR + ks * 32 + 8 * g;
+            p[ub] = mfma3(lds_u32x4(sKh + o), lds_u32x4(sKl + o), qh[ks], ql[ks], p[ub]);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)   // causal mask inside the diagonal tile: u <= t
+        if (4 * g + j > c16) p[TB][j] = 0.f;
+    u32x2 ph[4], pl[4];
+#pragma unroll
+    for (int ub = 0; ub < 4; ++ub) {
+        if (ub <= TB) {
+            const uint32_t h01 = cvt_bf2(p[ub][0], p[ub][1]), h23 = cvt_bf2(p[ub][2], p[ub][3]);
+            ph[ub] = u32x2{h01, h23};
+            pl[ub] = u32x2{cvt_bf2(p[ub][0] - bf_lo(h01), p[ub][1] - bf_hi(h01)),
+                           cvt_bf2(p[ub][2] - bf_lo(h23), p[ub][3] - bf_hi(h23))};
+        } else {
+            ph[ub] = pl[ub] = u32x2{0u, 0u};
+        }
+    }
+#pragma unroll
+    for (int x = 0; x < VBH; ++x) acc[x] = zero4();
+    // inter-chunk: O^T += S^T Q^T
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int x = 0; x < VBH; ++x) {
+            const int o = ((vb0 + x) * 16 + c16) * LDR + ks * 32 + 8 * g;
+            acc[x] = mfma3(lds_u32x4(sSh + o), lds_u32x4(sSl + o), qh[ks], ql[ks], acc[x]);
+        }
+    // intra-chunk: O^T += V^T P^T
+#pragma unroll
+    for (int pp = 0; pp <= TB / 2; ++pp) {
+        const u32x4 bh = cat2(ph[2 * pp], ph[2 * pp + 1]), bl = cat2(pl[2 * pp], pl[2 * pp + 1]);
+#pragma unroll
+        for (int x = 0; x < VBH; ++x) {
+            const int vb = vb0 + x;
+            const int o = (vb * 16 + c16) * LDT + tpos(vb * 16, pp * 32 + 4 * g);
+            acc[x] = mfma3(lds_u32x4(sVth + o), lds_u32x4(sVtl + o), bh, bl, acc[x]);
+        }
+    }
+}
+
+// Launch 3, split precision: as output_kernel_bf16 (same launch shape O3).
+template <int D, class O3>
+__global__ __launch_bounds__(O3::NT) void output_kernel_split(
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+    const BlockDesc* __restrict__ blocks, const float* __restrict__ ws,
+    const float* __restrict__ final_state, const float* __restrict__ ext_state,
+    float* __restrict__ out, int H, int n_items) {
+    constexpr int R = O3::R, NT = O3::NT, NP = O3::NP_, DV = O3::DV;
+    using ST = Stage<D, R>;
+    constexpr int NKB = O3::NKB, NVB = O3::NVB, NKS = O3::NKS, VBH = O3::VBH, TPW = O3::TPW;
+    constexpr int DD = D * D;
+    constexpr int NPER = KVStage<D, DV, R, NT>::NPER;
+    constexpr int LDR = ST::LDR, LDT = ST::LDT;
+    __shared__ __attribute__((aligned(16))) uint16_t sKh[kChunk * LDR];
+    __shared__ __attribute__((aligned(16))) uint16_t sKl[kChunk * LDR];
+    __shared__ __attribute__((aligned(16))) uint16_t sKth[D * LDT];
+    __shared__ __attribute__((aligned(16))) uint16_t sKtl[D * LDT];
+    __shared__ __attribute__((aligned(16))) uint16_t sVth[DV * LDT];
+    __shared__ __attribute__((aligned(16))) uint16_t sVtl[DV * LDT];
+    __shared__ __attribute__((aligned(16))) uint16_t sSh[DV * LDR];
+    __shared__ __attribute__((aligned(16))) uint16_t sSl[DV * LDR];
+
+    int item, part;
+    split_id<NP>(blockIdx.x, item, part);
+    if (item >= n_items) return;   // whole workgroup: padding of the split grid
+    const int h = item % H;
+    const BlockDesc bd = blocks[item / H];
+    const int w = wave_id(), lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
+    const int tb = w & 3, hv = w >> 2;
+    const int vbo = O3::vb_own(w), kbo = O3::kb0(w);
+    const int vbg = part * NVB + vbo;
+
+    f32x4 S[TPW];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) S[i] = zero4();
+    {
+        const float* seed = nullptr;
+        if (bd.seed >= 0)
+            seed = final_state + ((int64_t)bd.seed * H + h) * DD;
+        else if (bd.seed <= -2)
+            seed = ext_state + ((int64_t)(-bd.seed - 2) * H + h) * DD;
+        if (seed) {
+#pragma unroll
+            for (int i = 0; i < TPW; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    S[i][j] = seed[((kbo + i) * 16 + 4 * g + j) * D + vbg * 16 + c16];
+        }
+        if (bd.sin_slot >= 0) {
+            const float* src = ws + ((int64_t)bd.sin_slot * H + h) * DD;
+#pragma unroll
+            for (int i = 0; i < TPW; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    S[i][j] += src[((vbg * NKB + kbo + i) * 4 + j) * 64 + lane];
+        }
+    }
+
+    const int nch = (bd.ntok + kChunk - 1) / kChunk;
+    const int64_t row_elems = int64_t(H) * D;
+    const int trow = tb * 16 + c16;
+    const uint32_t qoff = uint32_t(((trow * H + h) * D + 8 * g) * 4);
+    const uint32_t ooff =
+        uint32_t(((trow * H + h) * D + part * DV + hv * VBH * 16 + 4 * g) * 4);
+    const int vcg0 = part * (DV / 8);
+
+    BlkF<R> kv[NPER];
+    u32x4 qa[NKS], qb[NKS], qh[NKS], ql[NKS];
+    auto load = [&](int c) {
+        const int64_t first = (int64_t(bd.tok0) + c * kChunk) * row_elems;
+        const int rows = min(kChunk, bd.ntok - c * kChunk);   // <= 0: empty window
+        load_kv_f32<D, DV, R, NT, NPER>(kv, chunk_rsrc(k, first, 4, rows, H, D),
+                                        chunk_rsrc(v, first, 4, rows, H, D), vcg0, H, h);
+        const auto rq = chunk_rsrc(q, first, 4, rows, H, D);
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            qa[ks] = buf_load16(rq, qoff + ks * 128);
+            qb[ks] = buf_load16(rq, qoff + ks * 128 + 16);
+        }
+    };
+    load(0);
+    for (int c = 0; c < nch; ++c) {
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) {
+            const f32x4 s = S[i];
+            const uint32_t h01 = cvt_bf2(s[0], s[1]), h23 = cvt_bf2(s[2], s[3]);
+            const uint32_t l01 = cvt_bf2(s[0] - bf_lo(h01), s[1] - bf_hi(h01));
+            const uint32_t l23 = cvt_bf2(s[2] - bf_lo(h23), s[3] - bf_hi(h23));
+            const int off = (vbo * 16 + c16) * LDR + (kbo + i) * 16 + 4 * g;
+            *reinterpret_cast<u32x2*>(sSh + off) = u32x2{h01, h23};
+            *reinterpret_cast<u32x2*>(sSl + off) = u32x2{l01, l23};
+        }
+        stage_kv_split<D, DV, R, NT, NPER, true>(kv, sKh, sKl, sKth, sKtl, sVth, sVtl);
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) split8(qa[ks], qb[ks], qh[ks], ql[ks]);
+        __syncthreads();
+        load(c + 1);
+
+        const int rows = min(kChunk, bd.ntok - c * kChunk);
+        const int64_t first = (int64_t(bd.tok0) + c * kChunk) * row_elems;
+        f32x4 acc[VBH];
+        switch (tb) {
+            case 0: out_tiles_split<D, 0, VBH>(sKh, sKl, sVth, sVtl, sSh, sSl, qh, ql, hv * VBH, g, c16, acc); break;
+            case 1: out_tiles_split<D, 1, VBH>(sKh, sKl, sVth, sVtl, sSh, sSl, qh, ql, hv * VBH, g, c16, acc); break;
+            case 2: out_tiles_split<D, 2, VBH>(sKh, sKl, sVth, sVtl, sSh, sSl, qh, ql, hv * VBH, g, c16, acc); break;
+            default: out_tiles_split<D, 3, VBH>(sKh, sKl, sVth, sVtl, sSh, sSl, qh, ql, hv * VBH, g, c16, acc); break;
+        }
+        {
+            const auto ro = chunk_rsrc(out, first, 4, rows, H, D);
+#pragma unroll
+            for (int x = 0; x < VBH; ++x) buf_store16(ro, ooff + x * 64, acc[x]);
+        }
+        if (c + 1 < nch) {
+#pragma unroll
+            for (int ks = 0; ks < kChunk / 32; ++ks) {
+                const int vo = (vbo * 16 + c16) * LDT + tpos(vbo * 16, ks * 32 + 4 * g);
+                const u32x4 bvh = lds_u32x4(sVth + vo), bvl = lds_u32x4(sVtl + vo);
+#pragma unroll
+                for (int i = 0; i < TPW; ++i) {
+                    const int ko = ((kbo + i) * 16 + c16) * LDT + tpos((kbo + i) * 16, ks * 32 + 4 * g);
+                    S[i] = mfma3(lds_u32x4(sKth + ko), lds_u32x4(sKtl + ko), bvh, bvl, S[i]);
+                }
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// ===========================================================================
 // View-state export: plain vectorised copy of H*d_k*d_v floats.
 // ===========================================================================
 __global__ __launch_bounds__(kThreads) void copy_kernel(const f32x4* __restrict__ src,
@@ -759,6 +1113,10 @@ la_status launch_all(int32_t stages, const void* q, const void* k, const void* v
             hipLaunchKernelGGL((delta_kernel_bf16<D, NP>), dim3(unsigned(split_grid<NP>(items))),
                                blk, 0, st, static_cast<const uint16_t*>(k),
                                static_cast<const uint16_t*>(v), deltas, ws, H, items);
+        else if (dtype == LA_F32_SPLIT)
+            hipLaunchKernelGGL(delta_kernel_split<D>, dim3(unsigned(items)), blk, 0, st,
+                               static_cast<const float*>(k), static_cast<const float*>(v),
+                               deltas, ws, H);
         else
             hipLaunchKernelGGL(delta_kernel_f32<D>, dim3(unsigned(items)), blk, 0, st,
                                static_cast<const float*>(k), static_cast<const float*>(v), deltas,
@@ -779,6 +1137,12 @@ la_status launch_all(int32_t stages, const void* q, const void* k, const void* v
                                static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                static_cast<const uint16_t*>(v), blocks, ws, final_state,
                                ext_state, static_cast<uint16_t*>(out), H, items);
+        else if (dtype == LA_F32_SPLIT)
+            hipLaunchKernelGGL((output_kernel_split<D, O3>),
+                               dim3(unsigned(split_grid<O3::NP_>(items))), dim3(O3::NT), 0, st,
+                               static_cast<const float*>(q), static_cast<const float*>(k),
+                               static_cast<const float*>(v), blocks, ws, final_state, ext_state,
+                               static_cast<float*>(out), H, items);
         else
             hipLaunchKernelGGL(output_kernel_f32<D>, dim3(unsigned(items)), blk, 0, st,
                                static_cast<const float*>(q), static_cast<const float*>(k),
@@ -794,7 +1158,7 @@ la_status launch_all(int32_t stages, const void* q, const void* k, const void* v
 extern "C" la_status la_scan_workspace_size(const la_pass_info* info, int32_t H, int32_t d_k,
                                             int32_t d_v, la_dtype dtype, size_t* bytes) {
     if (!info || !bytes || H < 1 || info->n_delta < 0) return LA_ERR_INVALID_ARG;
-    if (!supported_dims(d_k, d_v) || (dtype != LA_F32 && dtype != LA_BF16))
+    if (!supported_dims(d_k, d_v) || (dtype != LA_F32 && dtype != LA_BF16 && dtype != LA_F32_SPLIT))
         return LA_ERR_UNSUPPORTED;
     *bytes = size_t(info->n_delta) * size_t(H) * size_t(d_k) * size_t(d_v) * sizeof(float);
     return LA_OK;
@@ -808,7 +1172,7 @@ extern "C" la_status la_scan_packed_stages(int32_t stages, const void* q, const 
                                            void* workspace, size_t workspace_bytes,
                                            void* stream) {
     if (!info || stages < 1 || stages > LA_STAGE_ALL) return LA_ERR_INVALID_ARG;
-    if (dtype != LA_F32 && dtype != LA_BF16) return LA_ERR_UNSUPPORTED;
+    if (dtype != LA_F32 && dtype != LA_BF16 && dtype != LA_F32_SPLIT) return LA_ERR_UNSUPPORTED;
     if (!supported_dims(d_k, d_v) || info->chunk != LA_CHUNK) return LA_ERR_UNSUPPORTED;
     if (H < 1 || info->n_tokens < 0 || info->n_blocks < 0 || info->n_delta < 0 ||
         info->n_scan < 0 || info->n_views < 0 || info->n_ext < 0 || n_ext < 0)

@@ -57,8 +57,14 @@ enum {
 
 typedef int32_t la_dtype;
 enum {
-    LA_F32 = 0,               /* fp32 q/k/v/out                            */
-    LA_BF16 = 1               /* bf16 q/k/v/out, fp32 state and accumulate */
+    LA_F32 = 0,               /* fp32 q/k/v/out, fp32 MFMA products        */
+    LA_BF16 = 1,              /* bf16 q/k/v/out, fp32 state and accumulate */
+    LA_F32_SPLIT = 2          /* fp32 q/k/v/out; every product as three bf16
+                                 MFMAs over hi/lo splits of its operands
+                                 (hi.hi + hi.lo + lo.hi), the analogue of the
+                                 page's split 3xtf32 (section "Kernels",
+                                 paragraph "Tensor cores for linear
+                                 attention"); fp32 state and accumulate   */
 };
 
 /* Chunk size of the scan (tokens per chunk tile).  Section "Kernels" of the
@@ -205,7 +211,7 @@ la_status la_scan_workspace_size(const la_pass_info* info, int32_t H, int32_t d_
  *
  *   q, k           device [T][H][d_k], dtype
  *   v              device [T][H][d_v], dtype
- *   dtype          LA_F32 or LA_BF16
+ *   dtype          LA_F32, LA_F32_SPLIT (both fp32 tensors) or LA_BF16
  *   H              heads >= 1
  *   d_k, d_v       head dims; d_k == d_v, 64 or 128
  *   info           host, from the planner that built `plan`

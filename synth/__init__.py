@@ -92,6 +92,8 @@ WORKLOADS = {
     "view18000_br256x32-128_h16_d64_bf16": (1004, 16, 64, "bf16", _shape_view18000),
     # 32 requests: views logU[500,18000], U[1,64] branches of U[24,128], H=32, d=128
     "req32_view500-18000_br1-64x24-128_h32_d128_bf16": (1005, 32, 128, "bf16", _shape_req32),
+    # the fp32 case scaled up to the 7,400-token pass (fp32 MFMA vs split bf16)
+    "view7400_br8x48_h16_d64_f32": (1006, 16, 64, "f32", _shape_view7400),
 }
 
 
