@@ -25,6 +25,7 @@
 #include <cmath>
 #include <cstdint>
 #include <initializer_list>
+#include <type_traits>
 
 #include "linattn.h"
 #include "tiles.h"
@@ -34,6 +35,18 @@ namespace {
 struct AttnItem {
     int q0, nq, seg0, view0, view_len, view_src, pad0, pad1;
 };
+
+// Maximum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the lanes that hold
+// one query's scores), with the gfx950 lane-swap instructions: each swap
+// leaves a lane's own value in one result and its partner's in the other.
+__device__ __forceinline__ float max_over_groups(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const uint32_t uy = __float_as_uint(y);
+    const auto b = __builtin_amdgcn_permlane16_swap(uy, uy, false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void attn_kernel_bf16(
@@ -98,23 +111,16 @@ __global__ __launch_bounds__(kThreads) void attn_kernel_bf16(
                                          chunk_rsrc(vb, tok * row_elems, 2, rows, H, D), 0, H, h);
     };
 
-    float m = -INFINITY;   // running max of this lane's query (log2 domain)
+    float m = -INFINITY;   // running max of this lane's query (raw scores)
     float l = 0.f;         // this lane's part of the running sum
     f32x4 acc[NVB];        // O^T tiles: lane holds O[trow][x*16 + 4g + j]
 #pragma unroll
     for (int x = 0; x < NVB; ++x) acc[x] = zero4();
 
-    load(0);
-    for (int b = 0; b < nkb; ++b) {
-        stage_kv<D, D, R, kThreads, NPER, true, false>(kv, sK, nullptr, sVt);
-        __syncthreads();
-        load(b + 1);
-        int64_t tok;
-        int rows;
-        bool fe;
-        block_src(b, tok, rows, fe);
-        const bool diag = b == nkb - 1;
-
+    // one key block: scores, online softmax update, O^T += V^T P^T.  Only the
+    // diagonal block and a ragged last view block need the mask (MASKED).
+    auto block = [&](int rows, bool diag, auto masked) {
+        constexpr bool MASKED = decltype(masked)::value;
         // S^T tiles (ub = key tile): lane holds s[u = ub*16 + 4g + j][trow]
         f32x4 s[4];
 #pragma unroll
@@ -128,24 +134,24 @@ __global__ __launch_bounds__(kThreads) void attn_kernel_bf16(
 #pragma unroll
             for (int ub = 0; ub < 4; ++ub) s[ub] = mfma_bf16(kf[ub], qf[ks], s[ub]);
         }
-        // mask (ragged block, causal diagonal) and the block maximum
         float bm = -INFINITY;
 #pragma unroll
         for (int ub = 0; ub < 4; ++ub)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int u = ub * 16 + 4 * g + j;
-                const bool ok = u < rows && (!diag || u <= trow);
-                s[ub][j] = ok ? s[ub][j] * scale_log2 : -INFINITY;
+                if constexpr (MASKED) {
+                    const int u = ub * 16 + 4 * g + j;
+                    if (!(u < rows && (!diag || u <= trow))) s[ub][j] = -INFINITY;
+                }
                 bm = fmaxf(bm, s[ub][j]);
             }
-        bm = fmaxf(bm, __shfl_xor(bm, 16));
-        bm = fmaxf(bm, __shfl_xor(bm, 32));
-        const float mn = fmaxf(m, bm);
-        // every query sees at least one key in each block it visits, so mn is
-        // finite; guard anyway so that a fully masked row cannot make NaNs
+        const float mn = fmaxf(m, max_over_groups(bm));
+        // each query sees a key in every block it visits, so mn is finite;
+        // the guard keeps a fully masked row from producing NaNs.  scale > 0,
+        // so the maximum of the raw scores is that of the scaled ones.
         const float mref = mn == -INFINITY ? 0.f : mn;
-        const float alpha = __builtin_amdgcn_exp2f(m - mref);
+        const float alpha = __builtin_amdgcn_exp2f((m - mref) * scale_log2);
+        const float nb = -mref * scale_log2;
         m = mn;
         u32x2 pb[4];
         float ls = 0.f;
@@ -154,7 +160,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel_bf16(
             float p[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                p[j] = __builtin_amdgcn_exp2f(s[ub][j] - mref);   // exp2(-inf) = 0
+                p[j] = __builtin_amdgcn_exp2f(fmaf(s[ub][j], scale_log2, nb));   // exp2(-inf) = 0
                 ls += p[j];
             }
             pb[ub] = u32x2{cvt_bf2(p[0], p[1]), cvt_bf2(p[2], p[3])};
@@ -173,6 +179,24 @@ __global__ __launch_bounds__(kThreads) void attn_kernel_bf16(
 #pragma unroll
             for (int x = 0; x < NVB; ++x) acc[x] = mfma_bf16(av[x], bp, acc[x]);
         }
+    };
+
+    load(0);
+    for (int b = 0; b < nkb; ++b) {
+        stage_kv<D, D, R, kThreads, NPER, true, false>(kv, sK, nullptr, sVt);
+        __syncthreads();
+        load(b + 1);
+        int64_t tok;
+        int rows;
+        bool fe;
+        block_src(b, tok, rows, fe);
+        const bool diag = b == nkb - 1;
+        // a mask-free copy of the block body pays at d = 64; at d = 128 the
+        // second copy costs more in registers (occupancy) than it saves
+        if (D == 128 || diag || rows < kChunk)
+            block(rows, diag, std::true_type{});
+        else if constexpr (D == 64)
+            block(rows, diag, std::false_type{});
         __syncthreads();
     }
     // the query's sum is split over the 4 lanes that share its column
@@ -198,7 +222,8 @@ extern "C" la_status la_attn_packed(const void* q, const void* k, const void* v,
     if (dtype != LA_BF16 && dtype != LA_F32) return LA_ERR_INVALID_ARG;
     if (dtype != LA_BF16) return LA_ERR_UNSUPPORTED;
     if (d_k != d_v || (d_k != 64 && d_k != 128)) return LA_ERR_UNSUPPORTED;
-    if (H < 1 || n_items < 0 || n_tokens < 0 || n_ext_tokens < 0 || !std::isfinite(scale))
+    if (H < 1 || n_items < 0 || n_tokens < 0 || n_ext_tokens < 0 || !std::isfinite(scale) ||
+        !(scale > 0.f))
         return LA_ERR_INVALID_ARG;
     if (n_items == 0) return LA_OK;
     if (!q || !k || !v || !out || !items) return LA_ERR_INVALID_ARG;

@@ -304,7 +304,8 @@ la_status la_export_view_state(const float* final_state, int32_t view_row,
  * for q.k and p.v, fp32 scores, running max and sums), out rounded to bf16.
  *   q, k, v        device [n_tokens][H][d] bf16 (dtype must be LA_BF16)
  *   d_k, d_v       equal, 64 or 128
- *   scale          score scale (e.g. 1/sqrt(d) if k is not pre-scaled)
+ *   scale          score scale, finite and > 0 (e.g. 1/sqrt(d) if k is not
+ *                  pre-scaled)
  *   items          device [n_items][LA_ATTN_ITEM_WORDS] int32, a copy of the
  *                  la_attn_plan output for this segment table
  *   ext_k, ext_v   device [n_ext_tokens][H][d] bf16, or NULL if no item

@@ -144,6 +144,9 @@ def test_attention_rejects_bad_arguments():
         la.attn_packed(q96, q96, q96, plan, 1.0)                         # d = 96
     with pytest.raises(ValueError):
         la.attn_packed(q[:10], q[:10], q[:10], plan, 1.0)                # token count
+    for bad_scale in (0.0, -1.0, float("inf")):
+        with pytest.raises(la.LinAttnError):
+            la.attn_packed(q, q, q, plan, bad_scale)                     # scale must be > 0
     ext_plan = la.attn_plan([0, 4], [-2], ext_len=[7])
     q4 = torch.zeros((4, 2, 64), dtype=torch.bfloat16, device=DEV)
     with pytest.raises(ValueError):
