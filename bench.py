@@ -93,10 +93,10 @@ def calibrate_copy(mib, steps):
                       "us_per_launch": us, "GBps": 2 * n * 4 / (us * 1e-6) / 1e9}), flush=True)
 
 
-def launch_floor(steps):
+def launch_floor(steps, quiet=False):
     """Three dependent launches of the library's smallest kernel (a 64 KiB
     state export) per step, replayed as a HIP graph: the fixed cost of a
-    three-launch pass with no work in it."""
+    three-launch pass with no work in it.  Returns microseconds per step."""
     import torch
     import chunked_linear_attention_packed_amd as la
     src = torch.zeros((1, 1, 64, 64), dtype=torch.float32, device="cuda:0")
@@ -118,8 +118,11 @@ def launch_floor(steps):
         g.replay()
         e1.record(st)
     torch.cuda.synchronize()
-    print(json.dumps({"calibration": "launch floor", "launches_per_step": 3,
-                      "us_per_step": e0.elapsed_time(e1) * 1e3 / steps}), flush=True)
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    if not quiet:
+        print(json.dumps({"calibration": "launch floor", "launches_per_step": 3,
+                          "us_per_step": us}), flush=True)
+    return us
 
 
 def _oracle_task(args):
@@ -544,6 +547,20 @@ def main():
                                     a.workload, src_hash)
     pass_us = gpu_ms * 1e3 / a.steps
 
+    # spread of single passes: each of `steps` eager passes bracketed by its own
+    # events on the stream (eager launches add host submission gaps, so these
+    # sit above the graph figure; they show the distribution, not the rate)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(a.steps)]
+    with torch.cuda.stream(stream):
+        for i, (e_a, e_b) in enumerate(evs):
+            e_a.record(stream)
+            step(i)
+            e_b.record(stream)
+    torch.cuda.synchronize()
+    singles = np.array([e_a.elapsed_time(e_b) * 1e3 for e_a, e_b in evs])
+    floor_us = launch_floor(max(a.steps, 20), quiet=True)
+
     cpu = None
     if not a.no_cpu_baseline:
         cpu = cpu_baseline(w, plan.seg_offsets, plan.branch_parent, a.cpu_seconds)
@@ -576,6 +593,10 @@ def main():
             "pass_algorithmic_bytes": pass_bytes,
             "pass_roofline_frac": pass_bytes / (pass_us * 1e-6) / (HBM_PEAK_GBS * 1e9),
             "output_kernel_us": l3_us,
+            "single_pass_us_eager": {"p10": float(np.percentile(singles, 10)),
+                                     "median": float(np.median(singles)),
+                                     "p90": float(np.percentile(singles, 90))},
+            "launch_floor_us": floor_us,
         },
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
