@@ -4,6 +4,10 @@ the fp64 oracle (oracle/attention.py), through the C ABI.
 Tolerance: row-normalised max relative error 2e-2 (bf16 inputs), the same
 rule as the scan.  Shard branches reading their view from external K/V arrays
 are compared bit for bit with the same branches in the full pass."""
+import json
+import math
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -151,3 +155,22 @@ def test_attention_rejects_bad_arguments():
     q4 = torch.zeros((4, 2, 64), dtype=torch.bfloat16, device=DEV)
     with pytest.raises(ValueError):
         la.attn_packed(q4, q4, q4, ext_plan, 1.0)                        # ext arrays missing
+
+
+def test_hand_worked_example_on_the_gpu():
+    """tests/golden/attention_hand_example.json, zero-padded to d = 64 (the
+    padding changes no dot product): every weight is a power of two and every
+    v an integer, so only the final bf16 rounding (and the fp32 reciprocal of
+    the sum) separates the kernel from the exact values."""
+    with open(os.path.join(os.path.dirname(__file__), "golden",
+                           "attention_hand_example.json")) as f:
+        g = json.load(f)
+    T = len(g["out"])
+    pad = lambda key: torch.nn.functional.pad(torch.tensor(g[key], dtype=torch.float32),
+                                              (0, 64 - len(g[key][0])))
+    q, k, v = (pad(x).reshape(T, 1, 64).to(torch.bfloat16) for x in ("q", "k", "v"))
+    out = _run(q, k, v, g["seg_offsets"], g["branch_parent"], math.log(2.0))
+    exp = torch.tensor(g["out"], dtype=torch.float64)[:, 0]
+    got = out[:, 0, 0].double()
+    assert torch.all((got - exp).abs() <= exp.abs() * 2.0 ** -8 + 1e-6), (got, exp)
+    assert torch.all(out[:, 0, 1:] == 0)

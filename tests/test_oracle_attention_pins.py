@@ -1,6 +1,9 @@
 """Pins of the tree-masked softmax attention oracle (oracle/attention.py)
 against results fixed independently of it:
 
+* a worked example derived by hand (tests/golden/attention_hand_example.json:
+  with scale = ln 2 every weight is a power of two, so each output is an exact
+  rational; the derivation is in the file);
 * a single view with no branches is textbook causal softmax attention: torch's
   scaled_dot_product_attention (float64, CPU) with is_causal=True;
 * a branch sees its whole view and itself causally, and nothing else: its rows
@@ -11,6 +14,10 @@ against results fixed independently of it:
 Planted mistakes (exclusive diagonal, sibling leak, missing scale) in copies
 of the oracle must each fail one of these pins.
 """
+import json
+import math
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -18,6 +25,26 @@ import torch.nn.functional as F
 
 import oracle
 from oracle import attention as A
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden", "attention_hand_example.json")
+
+
+def _hand():
+    with open(GOLD) as f:
+        g = json.load(f)
+    arr = lambda key: np.asarray(g[key], dtype=np.float64)[:, None, :]   # [T, 1, d]
+    return g, arr("q"), arr("k"), arr("v")
+
+
+def test_hand_worked_example():
+    g, q, k, v = _hand()
+    so, bp, _ = oracle.pack_segments(g["view_len"], g["branch_count"], g["branch_len"])
+    assert list(so) == g["seg_offsets"] and list(bp) == g["branch_parent"]
+    got = oracle.attention_dense(q, k, v, so, bp, math.log(2.0))
+    assert np.allclose(got[:, 0, :], np.asarray(g["out"]), rtol=1e-13, atol=1e-13)
+    rows = list(range(len(g["out"])))
+    got_r = oracle.attention_rows(q, k, v, so, bp, math.log(2.0), rows)
+    assert np.allclose(got_r[:, 0, :], np.asarray(g["out"]), rtol=1e-13, atol=1e-13)
 
 
 def _rand(rng, T, H, d, dv=None):
@@ -130,6 +157,14 @@ def _planted(kind):
                 out[t] = np.einsum("hu,uhd->hd", w, v[idx])
         return out
     return f
+
+
+@pytest.mark.parametrize("kind", ["exclusive", "sibling_leak", "no_scale"])
+def test_planted_mistakes_fail_the_hand_example(kind):
+    g, q, k, v = _hand()
+    so, bp, _ = oracle.pack_segments(g["view_len"], g["branch_count"], g["branch_len"])
+    bad = _planted(kind)(q, k, v, so, bp, math.log(2.0))
+    assert not np.allclose(bad[:, 0, :], np.asarray(g["out"]), rtol=1e-9, atol=1e-9)
 
 
 @pytest.mark.parametrize("kind", ["exclusive", "sibling_leak", "no_scale"])
