@@ -120,7 +120,9 @@ typedef struct {
  *   plan             host [info->plan_words] or NULL: the plan to upload to
  *                    the device as int32 (layout below)
  *   info             host, required: filled on success
- * Call with view_ordinal = plan = NULL to learn info->plan_words first.
+ * Call with view_ordinal = plan = NULL to learn info->plan_words first, then
+ * again with the same table and block_chunks and buffers of that size (the
+ * library cannot see their capacity).
  * Errors: LA_ERR_INVALID_ARG (bad table), LA_ERR_UNSUPPORTED (chunk).
  *
  * Plan layout (int32 words):
@@ -163,7 +165,8 @@ la_status la_plan_segments(int32_t n_segments, const int32_t* seg_offsets,
  *   plan           host [plan_words] or NULL
  *   info           host, required
  * Segment order: request by request, the view then its branches.  Call with
- * all outputs NULL to learn the sizes (info->n_segments, info->plan_words).
+ * all outputs NULL to learn the sizes (info->n_segments, info->plan_words),
+ * then again with the same arguments and buffers of those sizes.
  * Errors: LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED.  Outputs are written only
  * on success.
  */
@@ -290,7 +293,8 @@ la_status la_export_view_state(const float* final_state, int32_t view_row,
  *   n_ext            external views (>= 0)
  *   ext_len          host [n_ext]: tokens of each external view (>= 1); the
  *                    views are concatenated in ext_k / ext_v in this order
- *   items            host [*n_items][LA_ATTN_ITEM_WORDS] or NULL (size query)
+ *   items            host [*n_items][LA_ATTN_ITEM_WORDS] or NULL (size query;
+ *                    fill with a second call on the same arguments)
  *   n_items          host, required: number of items
  * Item layout: {q0, nq, seg0, view0, view_len, view_src, 0, 0}: queries
  * q0 .. q0+nq-1 (nq <= LA_CHUNK) of the segment starting at seg0, whose

@@ -91,3 +91,45 @@ def test_random_attention(i):
     err = oracle.row_rel_err(out.cpu(), ref)
     print(f"  err {err:.2e}", flush=True)
     assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_request_order_does_not_change_results(dtype):
+    """Section "Kernels" ("one scan covers every view in a pass"): a request's
+    outputs and final state are the same, bit for bit, whatever its position
+    in the pass (same block size, so every sum runs in the same order)."""
+    rng = np.random.default_rng(77)
+    reqs = [(300, [40, 1, 129]), (65, [64]), (0, [70, 3]), (1000, []), (128, [1, 1])]
+    H, d, G = 2, 64, 2
+    data = []
+    for v_len, bls in reqs:
+        T = v_len + sum(bls)
+        data.append(synth.draw_qkv(rng, T, H, d, dtype))
+    ext = torch.from_numpy(rng.standard_normal((1, H, d, d)).astype(np.float32)).to(DEV)
+
+    def run(order):
+        vl = [reqs[r][0] for r in order]
+        bc = [len(reqs[r][1]) for r in order]
+        bl = [x for r in order for x in reqs[r][1]]
+        plan = la.pack(vl, bc, bl, heads=H, block_chunks=G)
+        q, k, v = (torch.cat([data[r][i] for r in order]).to(DEV) for i in range(3))
+        out, fin = la.scan_packed(q, k, v, plan, ext_state=ext)
+        torch.cuda.synchronize()
+        # per request: its token range and its view row
+        res, t, row = {}, 0, 0
+        for r in order:
+            n = reqs[r][0] + sum(reqs[r][1])
+            f = None
+            if reqs[r][0] > 0:
+                f = fin[row].cpu()
+                row += 1
+            res[r] = (out[t:t + n].cpu(), f)
+            t += n
+        return res
+
+    a = run([0, 1, 2, 3, 4])
+    b = run([3, 2, 4, 0, 1])
+    for r in range(len(reqs)):
+        assert torch.equal(a[r][0], b[r][0]), f"request {r} outputs differ"
+        if a[r][1] is not None:
+            assert torch.equal(a[r][1], b[r][1]), f"request {r} final state differs"
