@@ -540,6 +540,19 @@ def main():
     l3_bytes = T * H * per_token_head
     pass_bytes = l3_bytes + info.n_views * H * d * d * 4
     achieved = l3_bytes / (l3_us * 1e-6) / 1e9
+    # algorithmic matrix work per chunk of c tokens and head: q.S (2 c d^2),
+    # the causal scores and weighted values (c (c + 1) 2d), and the chunk's
+    # own state K^T V (2 c d^2) where a later chunk needs it (every chunk but
+    # the last of a segment)
+    so = plan.seg_offsets
+    flops = 0
+    for s_ in range(len(plan.branch_parent)):
+        n = int(so[s_ + 1] - so[s_])
+        full, rem = divmod(n, 64)
+        sizes = [64] * full + ([rem] if rem else [])
+        flops += sum(2 * c * d * d + c * (c + 1) * 2 * d for c in sizes)
+        flops += sum(2 * c * d * d for c in sizes[:-1])
+    flops *= H
     src = os.path.join(ROOT, "chunked_linear_attention_packed_amd", "csrc", "scan.hip")
     with open(src, "rb") as f:
         src_hash = hashlib.sha256(f.read()).hexdigest()
@@ -592,6 +605,9 @@ def main():
             "gpu_us_per_pass": pass_us,
             "pass_algorithmic_bytes": pass_bytes,
             "pass_roofline_frac": pass_bytes / (pass_us * 1e-6) / (HBM_PEAK_GBS * 1e9),
+            "pass_algorithmic_flops": flops,
+            "pass_mfma_frac": flops / (pass_us * 1e-6) / (
+                2.5e15 if (w.dtype == "bf16" or a.split_fp32) else 157.3e12),
             "output_kernel_us": l3_us,
             "single_pass_us_eager": {"p10": float(np.percentile(singles, 10)),
                                      "median": float(np.median(singles)),
