@@ -341,6 +341,37 @@ def attention_bench(a):
 
     us = _graph_us(fn, a.steps, a.warmup, stream, a.eager)
     tf = flops / (us * 1e-6) / 1e12
+    cpu = None
+    if not a.no_cpu_baseline:
+        # the fp64 attention oracle, unmodified, on a bounded sample: evenly
+        # spaced query rows (all heads) until ~cpu_seconds of work; a row's
+        # cost grows with its key count, so the sample spans the whole pass
+        import numpy as np
+        import oracle
+        rows = np.linspace(0, T - 1, 4096).astype(int)
+        done, t0 = 0, time.perf_counter()
+        pairs_done = 0
+        sizes = []
+        for s_ in range(len(bp)):
+            n = int(so[s_ + 1] - so[s_])
+            p = int(bp[s_])
+            lp = int(so[p + 1] - so[p]) if p >= 0 else 0
+            sizes += [lp + i + 1 for i in range(n)]
+        for start in range(0, len(rows), 64):
+            chunk = rows[start:start + 64].tolist()
+            oracle.attention_rows(w.q, w.k, w.v, so, bp, 1.0, chunk)
+            done += len(chunk)
+            pairs_done += sum(sizes[r] for r in chunk)
+            if time.perf_counter() - t0 > a.cpu_seconds:
+                break
+        wall = time.perf_counter() - t0
+        # scale by attended-key pairs: the sample's pairs/s over the pass's pairs
+        rate = pairs_done / wall
+        cpu = {"value": T * rate / pairs / 1.0, "unit": "tokens/s", "cores": 1,
+               "kind": "oracle",
+               "sample": f"{done} evenly spaced query rows x {H} heads ({pairs_done} attended "
+                         f"key pairs of {pairs}), {wall:.1f} s, one process; scaled to the "
+                         f"whole pass by attended pairs"}
     print(json.dumps({
         "experiment": "tree-masked softmax attention over the packed pass",
         "workload": a.workload, "tokens": T, "heads": H, "d": d, "dtype": "bf16",
@@ -350,6 +381,7 @@ def attention_bench(a):
         "roofline": {"bound": "mfma", "achieved": tf, "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": tf / MFMA_BF16_PEAK_TFLOPS,
                      "kernel": "attn_kernel_bf16"},
+        "cpu_baseline": cpu,
     }), flush=True)
 
 
