@@ -1082,6 +1082,7 @@ bool supported_dims(int32_t d_k, int32_t d_v) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 // Every launch's grid, in work-items, must fit the 32-bit dispatch size.
 template <int D>
@@ -1188,6 +1189,11 @@ extern "C" la_status la_scan_packed_stages(int32_t stages, const void* q, const 
         return LA_ERR_INVALID_ARG;
     if (info->n_views > 0 && !final_state) return LA_ERR_INVALID_ARG;
     if (info->n_ext > 0 && (!ext_state || n_ext < info->n_ext)) return LA_ERR_INVALID_ARG;
+    // the states and the workspace are read and written as fp32 (16-byte rows
+    // for the workspace), the plan as int32
+    if ((final_state && !aligned4(final_state)) || (ext_state && !aligned4(ext_state)) ||
+        (workspace && !aligned16(workspace)) || !aligned4(plan))
+        return LA_ERR_INVALID_ARG;
     size_t need = 0;
     la_status stw = la_scan_workspace_size(info, H, d_k, d_v, dtype, &need);
     if (stw != LA_OK) return stw;

@@ -196,6 +196,10 @@ def test_scan_rejects_bad_arguments_before_launch():
     assert call(ws=None) == la.LA_ERR_WORKSPACE
     assert call(wsb=need.value - 1) == la.LA_ERR_WORKSPACE
     assert call(q=ctypes.c_void_p(4098)) == la.LA_ERR_INVALID_ARG   # misaligned
+    assert call(fin=ctypes.c_void_p(4098)) == la.LA_ERR_INVALID_ARG
+    assert call(ws=ctypes.c_void_p(4100)) == la.LA_ERR_INVALID_ARG
+    assert call(plan=ctypes.c_void_p(4097)) == la.LA_ERR_INVALID_ARG
+    assert call(dtype=la.LA_F32_SPLIT, dk=96, dv=96) == la.LA_ERR_UNSUPPORTED
     shard = la.pack([0], [2], [10, 20], block_chunks=1)
     st = lib.la_scan_packed(fake, fake, fake, la.LA_BF16, 2, 64, 64, ctypes.byref(shard.info),
                             fake, None, 0, fake, None, fake, 1 << 20, None)
