@@ -517,7 +517,36 @@ __global__ __launch_bounds__(O3::NT) void output_kernel_bf16(
     const int vbo = O3::vb_own(w), kbo = O3::kb0(w);   // vbo local to the part
     const int vbg = part * NVB + vbo;                   // global column block
 
-    // carry state: tiles (vbg, kbo + i); lane holds S[kb*16 + 4g + j][vbg*16 + c16]
+    const int nch = (bd.ntok + kChunk - 1) / kChunk;
+    const int64_t row_elems = int64_t(H) * D;
+    // this lane's token within the chunk and the byte offsets of its q / out
+    // row pieces inside a chunk window
+    const int trow = tb * 16 + c16;
+    const uint32_t qoff = uint32_t(((trow * H + h) * D + 8 * g) * 2);
+    const uint32_t ooff =
+        uint32_t(((trow * H + h) * D + part * DV + hv * VBH * 16 + 4 * g) * 2);
+    const int vcg0 = part * (DV / 8);
+
+    // one chunk in flight: kv / qn hold chunk c + 1 while chunk c is computed
+    BlkR<R> kv[NPER];
+    u32x4 qf[NKS], qn[NKS];
+    auto load = [&](int c, u32x4 (&qdst)[NKS]) {
+        const int64_t first = (int64_t(bd.tok0) + c * kChunk) * row_elems;
+        const int rows = min(kChunk, bd.ntok - c * kChunk);   // <= 0: empty window
+        load_kv<D, DV, R, NT, NPER>(kv, chunk_rsrc(k, first, 2, rows, H, D),
+                                    chunk_rsrc(v, first, 2, rows, H, D), vcg0, H, h);
+        const auto rq = chunk_rsrc(q, first, 2, rows, H, D);
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) qdst[ks] = buf_load16(rq, qoff + ks * 64);
+    };
+    // the first chunk's loads go out before the initial state is read; q goes
+    // straight to the registers the products read (later chunks' q lands in
+    // qn while the current chunk is computed)
+    load(0, qf);
+
+    // carry state: tiles (vbg, kbo + i); lane holds S[kb*16 + 4g + j][vbg*16 + c16]:
+    // the seed (a view's final state, an external state, or zero) plus the
+    // segment-local prefix of the earlier blocks
     f32x4 S[TPW];
 #pragma unroll
     for (int i = 0; i < TPW; ++i) S[i] = zero4();
@@ -544,32 +573,10 @@ __global__ __launch_bounds__(O3::NT) void output_kernel_bf16(
         }
     }
 
-    const int nch = (bd.ntok + kChunk - 1) / kChunk;
-    const int64_t row_elems = int64_t(H) * D;
-    // this lane's token within the chunk and the byte offsets of its q / out
-    // row pieces inside a chunk window
-    const int trow = tb * 16 + c16;
-    const uint32_t qoff = uint32_t(((trow * H + h) * D + 8 * g) * 2);
-    const uint32_t ooff =
-        uint32_t(((trow * H + h) * D + part * DV + hv * VBH * 16 + 4 * g) * 2);
-    const int vcg0 = part * (DV / 8);
-
-    // one chunk in flight: kv / qn hold chunk c + 1 while chunk c is computed
-    BlkR<R> kv[NPER];
-    u32x4 qf[NKS], qn[NKS];
-    auto load = [&](int c) {
-        const int64_t first = (int64_t(bd.tok0) + c * kChunk) * row_elems;
-        const int rows = min(kChunk, bd.ntok - c * kChunk);   // <= 0: empty window
-        load_kv<D, DV, R, NT, NPER>(kv, chunk_rsrc(k, first, 2, rows, H, D),
-                                    chunk_rsrc(v, first, 2, rows, H, D), vcg0, H, h);
-        const auto rq = chunk_rsrc(q, first, 2, rows, H, D);
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) qn[ks] = buf_load16(rq, qoff + ks * 64);
-    };
-    load(0);
-    for (int c = 0; c < nch; ++c) {
-        // publish S^T = S_hi + S_lo (bf16 terms) for the inter-chunk product;
-        // lane holds 4 consecutive d_k of row vbo*16 + c16 of the part's S^T
+    // LDS inputs of one chunk: S^T = S_hi + S_lo (bf16 terms) for the
+    // inter-chunk product (lane holds 4 consecutive d_k of row vbo*16 + c16
+    // of the part's S^T), K row-major and transposed, V transposed.
+    auto publish_and_stage = [&]() {
 #pragma unroll
         for (int i = 0; i < TPW; ++i) {
             const f32x4 s = S[i];
@@ -581,11 +588,20 @@ __global__ __launch_bounds__(O3::NT) void output_kernel_bf16(
             *reinterpret_cast<u32x2*>(sSl + off) = u32x2{l01, l23};
         }
         stage_kv<D, DV, R, NT, NPER, true, true>(kv, sK, sKt, sVt);
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) qf[ks] = qn[ks];
+    };
+    // The loop is rotated: chunk c + 1 is staged (and its q moved to qf) at
+    // the end of iteration c, right after chunk c's output stores.  Its loads
+    // were issued before those stores, so the waits for them leave the
+    // stores in flight; the loop entry has no loads outstanding, so nothing
+    // merges into a wait for the stores either.
+    publish_and_stage();
+    // every load of the entry is complete here (chunk 0's q is needed first
+    // thing anyway); stating it lets the wait counts inside the loop be exact
+    __builtin_amdgcn_s_waitcnt(kWaitVmem0);
+    for (int c = 0; c < nch; ++c) {
         __syncthreads();
         // fetch the next chunk (an empty window past the last one)
-        load(c + 1);
+        load(c + 1, qn);
 
         const int rows = min(kChunk, bd.ntok - c * kChunk);
         const int64_t first = (int64_t(bd.tok0) + c * kChunk) * row_elems;
@@ -606,21 +622,22 @@ __global__ __launch_bounds__(O3::NT) void output_kernel_bf16(
                 buf_store8(ro, ooff + x * 32,
                            u32x2{cvt_bf2(acc[x][0], acc[x][1]), cvt_bf2(acc[x][2], acc[x][3])});
         }
-        // carry: S += K^T V for this wave's tiles (not needed after the
-        // block's last chunk)
-        if (c + 1 < nch) {
+        if (c + 1 >= nch) break;   // no carry and no staging after the last chunk
+        // carry: S += K^T V for this wave's tiles
 #pragma unroll
-            for (int ks = 0; ks < kChunk / 32; ++ks) {
-                const u32x4 bv = lds_u32x4(sVt + (vbo * 16 + c16) * LDT +
-                                           tpos(vbo * 16, ks * 32 + 4 * g));
+        for (int ks = 0; ks < kChunk / 32; ++ks) {
+            const u32x4 bv = lds_u32x4(sVt + (vbo * 16 + c16) * LDT +
+                                       tpos(vbo * 16, ks * 32 + 4 * g));
 #pragma unroll
-                for (int i = 0; i < TPW; ++i)
-                    S[i] = mfma_bf16(lds_u32x4(sKt + ((kbo + i) * 16 + c16) * LDT +
-                                               tpos((kbo + i) * 16, ks * 32 + 4 * g)),
-                                     bv, S[i]);
-            }
+            for (int i = 0; i < TPW; ++i)
+                S[i] = mfma_bf16(lds_u32x4(sKt + ((kbo + i) * 16 + c16) * LDT +
+                                           tpos((kbo + i) * 16, ks * 32 + 4 * g)),
+                                 bv, S[i]);
         }
         __syncthreads();
+        publish_and_stage();
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) qf[ks] = qn[ks];
     }
 }
 
@@ -969,6 +986,31 @@ __global__ __launch_bounds__(O3::NT) void output_kernel_split(
     const int vbo = O3::vb_own(w), kbo = O3::kb0(w);
     const int vbg = part * NVB + vbo;
 
+    const int nch = (bd.ntok + kChunk - 1) / kChunk;
+    const int64_t row_elems = int64_t(H) * D;
+    const int trow = tb * 16 + c16;
+    const uint32_t qoff = uint32_t(((trow * H + h) * D + 8 * g) * 4);
+    const uint32_t ooff =
+        uint32_t(((trow * H + h) * D + part * DV + hv * VBH * 16 + 4 * g) * 4);
+    const int vcg0 = part * (DV / 8);
+
+    BlkF<R> kv[NPER];
+    u32x4 qa[NKS], qb[NKS], qh[NKS], ql[NKS];
+    auto load = [&](int c) {
+        const int64_t first = (int64_t(bd.tok0) + c * kChunk) * row_elems;
+        const int rows = min(kChunk, bd.ntok - c * kChunk);   // <= 0: empty window
+        load_kv_f32<D, DV, R, NT, NPER>(kv, chunk_rsrc(k, first, 4, rows, H, D),
+                                        chunk_rsrc(v, first, 4, rows, H, D), vcg0, H, h);
+        const auto rq = chunk_rsrc(q, first, 4, rows, H, D);
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            qa[ks] = buf_load16(rq, qoff + ks * 128);
+            qb[ks] = buf_load16(rq, qoff + ks * 128 + 16);
+        }
+    };
+    // first chunk's loads before the initial state's (see output_kernel_bf16)
+    load(0);
+
     f32x4 S[TPW];
 #pragma unroll
     for (int i = 0; i < TPW; ++i) S[i] = zero4();
@@ -995,30 +1037,7 @@ __global__ __launch_bounds__(O3::NT) void output_kernel_split(
         }
     }
 
-    const int nch = (bd.ntok + kChunk - 1) / kChunk;
-    const int64_t row_elems = int64_t(H) * D;
-    const int trow = tb * 16 + c16;
-    const uint32_t qoff = uint32_t(((trow * H + h) * D + 8 * g) * 4);
-    const uint32_t ooff =
-        uint32_t(((trow * H + h) * D + part * DV + hv * VBH * 16 + 4 * g) * 4);
-    const int vcg0 = part * (DV / 8);
-
-    BlkF<R> kv[NPER];
-    u32x4 qa[NKS], qb[NKS], qh[NKS], ql[NKS];
-    auto load = [&](int c) {
-        const int64_t first = (int64_t(bd.tok0) + c * kChunk) * row_elems;
-        const int rows = min(kChunk, bd.ntok - c * kChunk);   // <= 0: empty window
-        load_kv_f32<D, DV, R, NT, NPER>(kv, chunk_rsrc(k, first, 4, rows, H, D),
-                                        chunk_rsrc(v, first, 4, rows, H, D), vcg0, H, h);
-        const auto rq = chunk_rsrc(q, first, 4, rows, H, D);
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            qa[ks] = buf_load16(rq, qoff + ks * 128);
-            qb[ks] = buf_load16(rq, qoff + ks * 128 + 16);
-        }
-    };
-    load(0);
-    for (int c = 0; c < nch; ++c) {
+    auto publish_and_stage = [&]() {
 #pragma unroll
         for (int i = 0; i < TPW; ++i) {
             const f32x4 s = S[i];
@@ -1032,6 +1051,12 @@ __global__ __launch_bounds__(O3::NT) void output_kernel_split(
         stage_kv_split<D, DV, R, NT, NPER, true>(kv, sKh, sKl, sKth, sKtl, sVth, sVtl);
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) split8(qa[ks], qb[ks], qh[ks], ql[ks]);
+    };
+    // rotated loop, as in output_kernel_bf16: chunk c + 1 is staged after
+    // chunk c's output stores, and the entry leaves no loads outstanding
+    publish_and_stage();
+    __builtin_amdgcn_s_waitcnt(kWaitVmem0);
+    for (int c = 0; c < nch; ++c) {
         __syncthreads();
         load(c + 1);
 
@@ -1049,19 +1074,19 @@ __global__ __launch_bounds__(O3::NT) void output_kernel_split(
 #pragma unroll
             for (int x = 0; x < VBH; ++x) buf_store16(ro, ooff + x * 64, acc[x]);
         }
-        if (c + 1 < nch) {
+        if (c + 1 >= nch) break;
 #pragma unroll
-            for (int ks = 0; ks < kChunk / 32; ++ks) {
-                const int vo = (vbo * 16 + c16) * LDT + tpos(vbo * 16, ks * 32 + 4 * g);
-                const u32x4 bvh = lds_u32x4(sVth + vo), bvl = lds_u32x4(sVtl + vo);
+        for (int ks = 0; ks < kChunk / 32; ++ks) {
+            const int vo = (vbo * 16 + c16) * LDT + tpos(vbo * 16, ks * 32 + 4 * g);
+            const u32x4 bvh = lds_u32x4(sVth + vo), bvl = lds_u32x4(sVtl + vo);
 #pragma unroll
-                for (int i = 0; i < TPW; ++i) {
-                    const int ko = ((kbo + i) * 16 + c16) * LDT + tpos((kbo + i) * 16, ks * 32 + 4 * g);
-                    S[i] = mfma3(lds_u32x4(sKth + ko), lds_u32x4(sKtl + ko), bvh, bvl, S[i]);
-                }
+            for (int i = 0; i < TPW; ++i) {
+                const int ko = ((kbo + i) * 16 + c16) * LDT + tpos((kbo + i) * 16, ks * 32 + 4 * g);
+                S[i] = mfma3(lds_u32x4(sKth + ko), lds_u32x4(sKtl + ko), bvh, bvl, S[i]);
             }
         }
         __syncthreads();
+        publish_and_stage();
     }
 }
 

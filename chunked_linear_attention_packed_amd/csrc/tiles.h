@@ -24,6 +24,9 @@ typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;   // 4 waves of 64
+// s_waitcnt operand (gfx9 encoding): vector memory count 0, the export and
+// LDS/scalar counts left at their maxima
+constexpr int kWaitVmem0 = 0x0F70;
 constexpr int kChunk = LA_CHUNK;
 
 __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
