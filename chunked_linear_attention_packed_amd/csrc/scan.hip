@@ -126,7 +126,7 @@ __global__ __launch_bounds__(kThreads) void delta_kernel_bf16(
     const int nch = (dd.ntok + kChunk - 1) / kChunk;
     const int64_t row_elems = int64_t(H) * D;
     const int vcg0 = part * (DVW / 8);
-    // two chunks in flight: registers A hold chunk c, B chunk c + 1
+    // two chunks in flight: registers A hold the even chunks, B the odd ones
     BlkR<R> pa[NPER], pb[NPER];
     auto load = [&](BlkR<R> (&dst)[NPER], int c) {
         const int64_t first = (int64_t(dd.tok0) + c * kChunk) * row_elems;
@@ -134,10 +134,11 @@ __global__ __launch_bounds__(kThreads) void delta_kernel_bf16(
         load_kv<D, DVW, R, kThreads, NPER>(dst, chunk_rsrc(k, first, 2, rows, H, D),
                                            chunk_rsrc(v, first, 2, rows, H, D), vcg0, H, h);
     };
-    auto step = [&](BlkR<R> (&cur)[NPER], int c) {
+    auto stage = [&](const BlkR<R> (&cur)[NPER]) {
         stage_kv<D, DVW, R, kThreads, NPER, false, true>(cur, nullptr, sKt, sVt);
-        __syncthreads();
-        load(cur, c + 2);   // empty window past the last chunk
+    };
+    // S += K^T V of the chunk staged in LDS
+    auto accumulate = [&]() {
 #pragma unroll
         for (int ks = 0; ks < kChunk / 32; ++ks) {
 #pragma unroll
@@ -154,14 +155,29 @@ __global__ __launch_bounds__(kThreads) void delta_kernel_bf16(
                 }
             }
         }
-        __syncthreads();
     };
+    // The loop is rotated like launch 3's: a chunk is staged at the end of
+    // the previous step, when exactly one later chunk's loads were issued
+    // after its own, and the loop entry has the same outstanding loads as the
+    // back edge (chunk 1 in B).  The wait before each staging then leaves the
+    // next chunk in flight.  Loads past the last chunk read an empty window.
     load(pa, 0);
+    __builtin_amdgcn_sched_barrier(0);   // keep chunk 0's loads ahead of chunk 1's
     load(pb, 1);
+    stage(pa);
     for (int c = 0; c < nch; c += 2) {
-        step(pa, c);
+        __syncthreads();
+        load(pa, c + 2);
+        accumulate();
+        __syncthreads();
         if (c + 1 >= nch) break;
-        step(pb, c + 1);
+        stage(pb);
+        __syncthreads();
+        load(pb, c + 3);
+        accumulate();
+        __syncthreads();
+        if (c + 2 >= nch) break;
+        stage(pa);
     }
     float* dst = ws + ((int64_t)dd.slot * H + h) * DD;
 #pragma unroll
