@@ -48,15 +48,18 @@ __device__ __forceinline__ float max_over_groups(float x) {
     return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads) void attn_kernel_bf16(
+// QT query tiles of 16 per wave (4 / QT waves per 64-query item): every K
+// and V fragment a wave reads from LDS feeds QT MFMAs.
+template <int D, int QT>
+__global__ __launch_bounds__(64 * (4 / QT)) void attn_kernel_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ ext_k,
     const uint16_t* __restrict__ ext_v, const AttnItem* __restrict__ items,
     uint16_t* __restrict__ out, int H, float scale_log2) {
+    constexpr int NT = 64 * (4 / QT);
     constexpr int R = 4, NKS = D / 32, NVB = D / 16;
     using ST = Stage<D, R>;
-    constexpr int NPER = KVStage<D, D, R, kThreads>::NPER;
+    constexpr int NPER = KVStage<D, D, R, NT>::NPER;
     constexpr int LDR = ST::LDR, LDT = ST::LDT;
     __shared__ __attribute__((aligned(16))) uint16_t sK[kChunk * LDR];   // K block, row-major
     __shared__ __attribute__((aligned(16))) uint16_t sVt[D * LDT];       // V block, transposed
@@ -64,7 +67,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel_bf16(
     const int h = blockIdx.x % H;
     const AttnItem it = items[blockIdx.x / H];
     const int w = wave_id(), lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
-    const int trow = w * 16 + c16;            // this lane's query within the block
+    // this lane's queries within the block: tile t holds trow0 + 16 t
+    const int trow0 = w * 16 * QT + c16;
     const int64_t row_elems = int64_t(H) * D;
 
     // key blocks: the parent view's, then the segment's own up to the query
@@ -76,12 +80,15 @@ __global__ __launch_bounds__(kThreads) void attn_kernel_bf16(
     const bool ext_view = it.view_src == LA_ATTN_EXT_VIEW;
 
     // Q^T fragments (B operand): lane holds q[trow][ks*32 + 8g .. +7]
-    u32x4 qf[NKS];
+    u32x4 qf[QT][NKS];
     {
         const auto rq = chunk_rsrc(q, int64_t(it.q0) * row_elems, 2, it.nq, H, D);
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
-            qf[ks] = buf_load16(rq, uint32_t(((trow * H + h) * D + ks * 32 + 8 * g) * 2));
+        for (int t = 0; t < QT; ++t)
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+                qf[t][ks] = buf_load16(
+                    rq, uint32_t((((trow0 + 16 * t) * H + h) * D + ks * 32 + 8 * g) * 2));
     }
 
     // source of key block b (wave-uniform): token offset and valid rows
@@ -107,24 +114,42 @@ __global__ __launch_bounds__(kThreads) void attn_kernel_bf16(
         block_src(b, tok, rows, fe);
         const uint16_t* kb = fe ? ext_k : k;
         const uint16_t* vb = fe ? ext_v : v;
-        load_kv<D, D, R, kThreads, NPER>(kv, chunk_rsrc(kb, tok * row_elems, 2, rows, H, D),
-                                         chunk_rsrc(vb, tok * row_elems, 2, rows, H, D), 0, H, h);
+        load_kv<D, D, R, NT, NPER>(kv, chunk_rsrc(kb, tok * row_elems, 2, rows, H, D),
+                                   chunk_rsrc(vb, tok * row_elems, 2, rows, H, D), 0, H, h);
     };
 
-    float m = -INFINITY;   // running max of this lane's query (raw scores)
-    float l = 0.f;         // this lane's part of the running sum
-    f32x4 acc[NVB];        // O^T tiles: lane holds O[trow][x*16 + 4g + j]
+    // Online softmax with a lazily moved reference maximum: a lane's weights
+    // are exp2((s - m) * scale_log2) against a reference m that is raised
+    // only when a block's maximum exceeds it by more than 2^kLazy in weight
+    // (then the running sums are rescaled); otherwise weights up to 2^kLazy
+    // are accumulated as they are.  The final division by the running sum
+    // cancels the reference, so the result is the softmax for any m.
+    constexpr float kLazy = 8.f;
+    float m[QT];           // reference maximum of each of this lane's queries (raw scores)
+    f32x4 acc[QT][NVB];    // O^T tiles: lane holds O[trow][x*16 + 4g + j]
+    // running sums of the weights, as one more O^T tile whose A operand is
+    // all ones: every row of it holds the sum for the lane's query (column),
+    // in the bf16-rounded weights that also multiply V
+    f32x4 accl[QT];
 #pragma unroll
-    for (int x = 0; x < NVB; ++x) acc[x] = zero4();
+    for (int t = 0; t < QT; ++t) {
+        m[t] = -INFINITY;
+        accl[t] = zero4();
+#pragma unroll
+        for (int x = 0; x < NVB; ++x) acc[t][x] = zero4();
+    }
+    const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
 
     // one key block: scores, online softmax update, O^T += V^T P^T.  Only the
     // diagonal block and a ragged last view block need the mask (MASKED).
     auto block = [&](int rows, bool diag, auto masked) {
         constexpr bool MASKED = decltype(masked)::value;
         // S^T tiles (ub = key tile): lane holds s[u = ub*16 + 4g + j][trow]
-        f32x4 s[4];
+        f32x4 s[QT][4];
 #pragma unroll
-        for (int ub = 0; ub < 4; ++ub) s[ub] = zero4();
+        for (int t = 0; t < QT; ++t)
+#pragma unroll
+            for (int ub = 0; ub < 4; ++ub) s[t][ub] = zero4();
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
             u32x4 kf[4];
@@ -132,85 +157,133 @@ __global__ __launch_bounds__(kThreads) void attn_kernel_bf16(
             for (int ub = 0; ub < 4; ++ub)
                 kf[ub] = lds_u32x4(sK + (ub * 16 + c16) * LDR + ks * 32 + 8 * g);
 #pragma unroll
-            for (int ub = 0; ub < 4; ++ub) s[ub] = mfma_bf16(kf[ub], qf[ks], s[ub]);
+            for (int t = 0; t < QT; ++t)
+#pragma unroll
+                for (int ub = 0; ub < 4; ++ub) s[t][ub] = mfma_bf16(kf[ub], qf[t][ks], s[t][ub]);
         }
-        float bm = -INFINITY;
+        bool any_raise = false;
+        float bm[QT];
 #pragma unroll
-        for (int ub = 0; ub < 4; ++ub)
+        for (int t = 0; t < QT; ++t) {
+            float mx = -INFINITY;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if constexpr (MASKED) {
-                    const int u = ub * 16 + 4 * g + j;
-                    if (!(u < rows && (!diag || u <= trow))) s[ub][j] = -INFINITY;
+            for (int ub = 0; ub < 4; ++ub)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if constexpr (MASKED) {
+                        const int u = ub * 16 + 4 * g + j;
+                        if (!(u < rows && (!diag || u <= trow0 + 16 * t))) s[t][ub][j] = -INFINITY;
+                    }
+                    mx = fmaxf(mx, s[t][ub][j]);
                 }
-                bm = fmaxf(bm, s[ub][j]);
-            }
-        const float mn = fmaxf(m, max_over_groups(bm));
-        // each query sees a key in every block it visits, so mn is finite;
-        // the guard keeps a fully masked row from producing NaNs.  scale > 0,
-        // so the maximum of the raw scores is that of the scaled ones.
-        const float mref = mn == -INFINITY ? 0.f : mn;
-        const float alpha = __builtin_amdgcn_exp2f((m - mref) * scale_log2);
-        const float nb = -mref * scale_log2;
-        m = mn;
-        u32x2 pb[4];
-        float ls = 0.f;
-#pragma unroll
-        for (int ub = 0; ub < 4; ++ub) {
-            float p[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                p[j] = __builtin_amdgcn_exp2f(fmaf(s[ub][j], scale_log2, nb));   // exp2(-inf) = 0
-                ls += p[j];
-            }
-            pb[ub] = u32x2{cvt_bf2(p[0], p[1]), cvt_bf2(p[2], p[3])};
+            bm[t] = max_over_groups(mx);
+            // raise the reference where the block's maximum is more than
+            // 2^kLazy above it in weight (always from -inf); scale > 0, so
+            // comparing raw scores is comparing scaled ones
+            any_raise |= m[t] == -INFINITY ? bm[t] != -INFINITY
+                                           : (bm[t] - m[t]) * scale_log2 > kLazy;
         }
-        l = l * alpha + ls;
+        if (__builtin_amdgcn_ballot_w64(any_raise) != 0) {   // wave-uniform
 #pragma unroll
-        for (int x = 0; x < NVB; ++x) acc[x] *= alpha;
+            for (int t = 0; t < QT; ++t) {
+                const bool raise = m[t] == -INFINITY ? bm[t] != -INFINITY
+                                                     : (bm[t] - m[t]) * scale_log2 > kLazy;
+                const float mn = raise ? bm[t] : m[t];
+                const float alpha =
+                    m[t] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m[t] - mn) * scale_log2);
+#pragma unroll
+                for (int x = 0; x < NVB; ++x) acc[t][x] *= alpha;
+                accl[t][0] *= alpha;
+                m[t] = mn;
+            }
+        }
+        // a query sees a key in every block it visits, so m is finite here
+        // (the guard keeps a row that is masked so far from producing NaNs)
+        u32x2 pb[QT][4];
+#pragma unroll
+        for (int t = 0; t < QT; ++t) {
+            const float nb = m[t] == -INFINITY ? 0.f : -m[t] * scale_log2;
+#pragma unroll
+            for (int ub = 0; ub < 4; ++ub) {
+                float p[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j)   // exp2(-inf) = 0
+                    p[j] = __builtin_amdgcn_exp2f(fmaf(s[t][ub][j], scale_log2, nb));
+                pb[t][ub] = u32x2{cvt_bf2(p[0], p[1]), cvt_bf2(p[2], p[3])};
+            }
+        }
         // O^T += V^T P^T; k-slots (g, i) -> key u = (2pp + i/4)*16 + 4g + i%4
 #pragma unroll
         for (int pp = 0; pp < 2; ++pp) {
-            const u32x4 bp = cat2(pb[2 * pp], pb[2 * pp + 1]);
             u32x4 av[NVB];
 #pragma unroll
             for (int x = 0; x < NVB; ++x)
                 av[x] = lds_u32x4(sVt + (x * 16 + c16) * LDT + tpos(x * 16, pp * 32 + 4 * g));
 #pragma unroll
-            for (int x = 0; x < NVB; ++x) acc[x] = mfma_bf16(av[x], bp, acc[x]);
+            for (int t = 0; t < QT; ++t) {
+                const u32x4 bp = cat2(pb[t][2 * pp], pb[t][2 * pp + 1]);
+#pragma unroll
+                for (int x = 0; x < NVB; ++x) acc[t][x] = mfma_bf16(av[x], bp, acc[t][x]);
+                accl[t] = mfma_bf16(ones, bp, accl[t]);
+            }
         }
     };
 
-    load(0);
-    for (int b = 0; b < nkb; ++b) {
-        stage_kv<D, D, R, kThreads, NPER, true, false>(kv, sK, nullptr, sVt);
+    // Processing order: the full key blocks first (view blocks, then the
+    // segment's own blocks before the diagonal), then the blocks that need
+    // the mask: a ragged last view block and the diagonal.  Each group runs
+    // one copy of the block body.
+    const int n_full_view = it.view_len / kChunk;
+    const bool view_ragged = n_full_view < n_view_blk;
+    const int n_full = n_full_view + n_own_blk - 1;
+    auto order = [&](int i) -> int {   // processing index -> key block (as in block_src)
+        if (i < n_full_view) return i;
+        if (i < n_full) return n_view_blk + (i - n_full_view);
+        if (view_ragged && i == n_full) return n_view_blk - 1;
+        return i < nkb ? nkb - 1 : nkb;   // nkb: past the end, an empty window
+    };
+    load(order(0));
+    int i = 0;
+    for (; i < n_full; ++i) {
+        stage_kv<D, D, R, NT, NPER, true, false>(kv, sK, nullptr, sVt);
         __syncthreads();
-        load(b + 1);
+        load(order(i + 1));
+        block(kChunk, false, std::false_type{});
+        __syncthreads();
+    }
+    for (; i < nkb; ++i) {
+        stage_kv<D, D, R, NT, NPER, true, false>(kv, sK, nullptr, sVt);
+        __syncthreads();
+        load(order(i + 1));
+        const int b = order(i);
         int64_t tok;
         int rows;
         bool fe;
         block_src(b, tok, rows, fe);
-        const bool diag = b == nkb - 1;
-        // a mask-free copy of the block body pays at d = 64; at d = 128 the
-        // second copy costs more in registers (occupancy) than it saves
-        if (D == 128 || diag || rows < kChunk)
-            block(rows, diag, std::true_type{});
-        else if constexpr (D == 64)
-            block(rows, diag, std::false_type{});
+        block(rows, b == nkb - 1, std::true_type{});
         __syncthreads();
     }
-    // the query's sum is split over the 4 lanes that share its column
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-    const float inv = 1.f / l;
     const auto ro = chunk_rsrc(out, int64_t(it.q0) * row_elems, 2, it.nq, H, D);
-    const uint32_t ooff = uint32_t(((trow * H + h) * D + 4 * g) * 2);
 #pragma unroll
-    for (int x = 0; x < NVB; ++x)
-        buf_store8(ro, ooff + x * 32,
-                   u32x2{cvt_bf2(acc[x][0] * inv, acc[x][1] * inv),
-                         cvt_bf2(acc[x][2] * inv, acc[x][3] * inv)});
+    for (int t = 0; t < QT; ++t) {
+        // every row of accl holds the lane's query's sum
+        const float inv = 1.f / accl[t][0];
+        const uint32_t ooff = uint32_t((((trow0 + 16 * t) * H + h) * D + 4 * g) * 2);
+#pragma unroll
+        for (int x = 0; x < NVB; ++x)
+            buf_store8(ro, ooff + x * 32,
+                       u32x2{cvt_bf2(acc[t][x][0] * inv, acc[t][x][1] * inv),
+                             cvt_bf2(acc[t][x][2] * inv, acc[t][x][3] * inv)});
+    }
 }
+
+// Query tiles per wave, chosen by measurement on MI355X.
+#ifndef LA_ATTN_QT_64
+#define LA_ATTN_QT_64 1
+#endif
+#ifndef LA_ATTN_QT_128
+#define LA_ATTN_QT_128 2
+#endif
 
 }  // namespace
 
@@ -241,7 +314,7 @@ extern "C" la_status la_attn_packed(const void* q, const void* k, const void* v,
     const float scale_log2 = scale * 1.4426950408889634f;   // exp(x) = exp2(x log2 e)
     const auto* its = reinterpret_cast<const AttnItem*>(items);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const dim3 grid(unsigned(int64_t(n_items) * H)), blk(kThreads);
+    const dim3 grid(unsigned(int64_t(n_items) * H));
     const auto* qq = static_cast<const uint16_t*>(q);
     const auto* kk = static_cast<const uint16_t*>(k);
     const auto* vv = static_cast<const uint16_t*>(v);
@@ -249,11 +322,12 @@ extern "C" la_status la_attn_packed(const void* q, const void* k, const void* v,
     const auto* ev = static_cast<const uint16_t*>(ext_v);
     auto* oo = static_cast<uint16_t*>(out);
     if (d_k == 64)
-        hipLaunchKernelGGL(attn_kernel_bf16<64>, grid, blk, 0, st, qq, kk, vv, ek, ev, its, oo, H,
-                           scale_log2);
+        hipLaunchKernelGGL((attn_kernel_bf16<64, LA_ATTN_QT_64>), grid, dim3(64 * (4 / LA_ATTN_QT_64)),
+                           0, st, qq, kk, vv, ek, ev, its, oo, H, scale_log2);
     else
-        hipLaunchKernelGGL(attn_kernel_bf16<128>, grid, blk, 0, st, qq, kk, vv, ek, ev, its, oo,
-                           H, scale_log2);
+        hipLaunchKernelGGL((attn_kernel_bf16<128, LA_ATTN_QT_128>), grid,
+                           dim3(64 * (4 / LA_ATTN_QT_128)), 0, st, qq, kk, vv, ek, ev, its, oo, H,
+                           scale_log2);
     if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
     return LA_OK;
 }
