@@ -174,3 +174,25 @@ def test_hand_worked_example_on_the_gpu():
     got = out[:, 0, 0].double()
     assert torch.all((got - exp).abs() <= exp.abs() * 2.0 ** -8 + 1e-6), (got, exp)
     assert torch.all(out[:, 0, 1:] == 0)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_attention_rising_scores_rescale_every_block(d):
+    """Scores that grow along the keys, so that nearly every key block raises
+    a query's running maximum by far more than the lazy-rescale slack: the
+    rescale path runs block after block and must still give the softmax."""
+    H = 2
+    so, bp, _ = oracle.pack_segments([520], [2], [70, 130])
+    T = int(so[-1])
+    rng = np.random.default_rng(31)
+    qn = rng.standard_normal((T, H, d)).astype(np.float32) * 0.1 + 1.0
+    ramp = np.linspace(0.0, 1.0, T, dtype=np.float32)[:, None, None]
+    kn = rng.standard_normal((T, H, d)).astype(np.float32) * 0.05 + ramp * (20.0 / d)
+    vn = rng.standard_normal((T, H, d)).astype(np.float32)
+    q, k, v = (torch.from_numpy(x).to(torch.bfloat16) for x in (qn, kn, vn))
+    out = _run(q, k, v, so, bp, 1.0)
+    ref = oracle.attention_dense(q, k, v, so, bp, 1.0)
+    err = oracle.row_rel_err(out, ref)
+    print(f"rising scores d={d}: err {err:.2e}", flush=True)
+    assert torch.isfinite(out.float()).all()
+    assert err <= TOL
