@@ -260,3 +260,26 @@ def test_outputs_fully_overwritten():
     o2, f2 = la.scan_packed(qd, kd, vd, plan)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(f1, f2)
+
+
+@pytest.mark.parametrize("dtype,d,split", [("bf16", 64, False), ("bf16", 128, False),
+                                           ("f32", 64, False), ("f32", 64, True)])
+def test_long_prefix_chains(dtype, d, split):
+    """More than 32 workspace slots in one segment (launch 2 sums them in
+    batches of 32): a view of 70 full chunks and a branch of 40 chunks plus a
+    ragged tail, one chunk per work block, so the view's chain has 70 slots
+    and the branch's 40."""
+    H = 2
+    vl, bc, bl = [70 * 64], [2], [40 * 64 + 17, 5]
+    plan = la.pack(vl, bc, bl, heads=H, block_chunks=1)
+    T = plan.info.n_tokens
+    q, k, v = synth.draw_qkv(np.random.default_rng(77 + d), T, H, d, dtype)
+    print(f"long chains {dtype} d={d} split={split}: T={T} delta slots={plan.info.n_delta}",
+          flush=True)
+    out, fin = la.scan_packed(q.to(DEV), k.to(DEV), v.to(DEV), plan, split_fp32=split)
+    torch.cuda.synchronize()
+    ref_o, ref_f = oracle.scan_recurrence(q, k, v, plan.seg_offsets, plan.branch_parent)
+    eo = oracle.row_rel_err(out.cpu(), ref_o)
+    ef = oracle.state_rel_err(fin.cpu(), ref_f)
+    print(f"  out err {eo:.3e}  final err {ef:.3e}", flush=True)
+    assert eo <= TOL[dtype] and ef <= TOL[dtype]
