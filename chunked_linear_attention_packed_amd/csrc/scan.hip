@@ -482,8 +482,9 @@ __device__ __forceinline__ void out_tiles(const uint16_t* sK, const uint16_t* sV
 #pragma unroll
         for (int x = 0; x < VBH; ++x) {
             const int f = (vb0 + x) * 16 + c16;
-            ah[x] = lds_u32x4(sSh + f * LDR + ks * 32 + 8 * g);
-            al[x] = lds_u32x4(sSl + f * LDR + ks * 32 + 8 * g);
+            const int o = f * LDR + scol<D>(f, ks * 32 + 8 * g);
+            ah[x] = lds_u32x4(sSh + o);
+            al[x] = lds_u32x4(sSl + o);
         }
 #pragma unroll
         for (int x = 0; x < VBH; ++x) acc[x] = mfma_bf16(ah[x], qf[ks], acc[x]);
@@ -599,7 +600,7 @@ __global__ __launch_bounds__(O3::NT) void output_kernel_bf16(
             const uint32_t h01 = cvt_bf2(s[0], s[1]), h23 = cvt_bf2(s[2], s[3]);
             const uint32_t l01 = cvt_bf2(s[0] - bf_lo(h01), s[1] - bf_hi(h01));
             const uint32_t l23 = cvt_bf2(s[2] - bf_lo(h23), s[3] - bf_hi(h23));
-            const int off = (vbo * 16 + c16) * LDR + (kbo + i) * 16 + 4 * g;
+            const int off = (vbo * 16 + c16) * LDR + scol<D>(vbo * 16 + c16, (kbo + i) * 16 + 4 * g);
             *reinterpret_cast<u32x2*>(sSh + off) = u32x2{h01, h23};
             *reinterpret_cast<u32x2*>(sSl + off) = u32x2{l01, l23};
         }
@@ -954,7 +955,8 @@ __device__ __forceinline__ void out_tiles_split(const uint16_t* sKh, const uint1
     for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
         for (int x = 0; x < VBH; ++x) {
-            const int o = ((vb0 + x) * 16 + c16) * LDR + ks * 32 + 8 * g;
+            const int f = (vb0 + x) * 16 + c16;
+            const int o = f * LDR + scol<D>(f, ks * 32 + 8 * g);
             acc[x] = mfma3(lds_u32x4(sSh + o), lds_u32x4(sSl + o), qh[ks], ql[ks], acc[x]);
         }
     // intra-chunk: O^T += V^T P^T
@@ -1060,7 +1062,7 @@ __global__ __launch_bounds__(O3::NT) void output_kernel_split(
             const uint32_t h01 = cvt_bf2(s[0], s[1]), h23 = cvt_bf2(s[2], s[3]);
             const uint32_t l01 = cvt_bf2(s[0] - bf_lo(h01), s[1] - bf_hi(h01));
             const uint32_t l23 = cvt_bf2(s[2] - bf_lo(h23), s[3] - bf_hi(h23));
-            const int off = (vbo * 16 + c16) * LDR + (kbo + i) * 16 + 4 * g;
+            const int off = (vbo * 16 + c16) * LDR + scol<D>(vbo * 16 + c16, (kbo + i) * 16 + 4 * g);
             *reinterpret_cast<u32x2*>(sSh + off) = u32x2{h01, h23};
             *reinterpret_cast<u32x2*>(sSl + off) = u32x2{l01, l23};
         }

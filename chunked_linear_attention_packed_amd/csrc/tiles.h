@@ -107,13 +107,32 @@ __device__ __forceinline__ void buf_store8(__amdgpu_buffer_rsrc_t r, uint32_t of
 // done in registers with v_perm_b32: column c of the block becomes R
 // consecutive tokens, one R*2-byte LDS store.
 // ---------------------------------------------------------------------------
+// Row strides are padded so that the 16-byte fragment reads of the MFMA
+// operands (lane 16g + c reads row c at column offset 16 g bytes) hit no LDS
+// bank twice: measured on gfx950 with the bank-conflict counter, rows of 160
+// bytes are conflict-free where rows of 144 bytes are not.  At d = 128 the
+// workgroups of the output launch would no longer fit two per CU with the
+// wider padding, so rows there keep 8 elements of padding.
 template <int D, int R>
 struct Stage {
     static constexpr int NCG = D / 8;           // 8-feature groups per row
     static constexpr int NB = (kChunk / R) * NCG;   // R x 8 blocks per 64-token tile
-    static constexpr int LDR = D + 8;           // row-major stride (elements)
-    static constexpr int LDT = kChunk + 8;      // transposed stride (elements)
+    static constexpr int PAD = D == 64 ? 16 : 8;
+    static constexpr int LDR = D + PAD;         // row-major stride (elements)
+    static constexpr int LDT = kChunk + PAD;    // transposed stride (elements)
 };
+
+// Column at which element k of row f of a row-major D-column state tile is
+// kept: with 160-byte rows (d = 64), rows with bit 2 set swap 8-element
+// halves of each 16-element group, which keeps the 8-byte stores of the
+// state publication at the conflict level of the unswizzled 144-byte rows
+// while the 16-byte reads stay conflict-free.  8-element groups stay
+// contiguous, so a 16-byte read at an 8-aligned k reads k .. k + 7.
+template <int D>
+__device__ __forceinline__ int scol(int f, int k) {
+    if constexpr (D == 64) return k ^ ((f & 4) << 1);
+    return k;
+}
 
 template <int R>
 struct BlkR {
@@ -144,13 +163,14 @@ __device__ __forceinline__ void store_rows(uint16_t* dst, const BlkR<R>& b, int 
 // reads such 8-token groups: the carry K^T V (both operands in this order,
 // so the contraction is unchanged) and the intra-chunk V^T P^T (whose P^T
 // operand comes from accumulator tiles in exactly this slot order).  On top,
-// rows whose feature index has bit 4 set swap their two 32-token halves, so
-// the 8-byte column stores of one instruction spread over all LDS banks
-// (16-byte aligned rows 8 apart otherwise start on the same or the opposite
-// bank).
+// the 16-position groups of a row are permuted by the feature's bits 4 and 5
+// (the same for all 16 rows of a tile, so every reader addresses a tile with
+// its first feature), which spreads the 8-byte column stores of one staging
+// instruction over the LDS banks: measured, 3.8 instead of 11.3 conflict
+// cycles per store against swapping 32-token halves by bit 4 alone.
 __device__ __forceinline__ int tpos(int feature, int token) {
     const int pos = (token & 32) | ((token & 12) << 1) | ((token & 16) >> 2) | (token & 3);
-    return pos ^ ((feature & 16) << 1);
+    return pos ^ (feature & 48);
 }
 
 // dst[(cg*8 + c) * ld + tpos(cg*8 + c, rg*R) .. + R-1] = column c of the block
