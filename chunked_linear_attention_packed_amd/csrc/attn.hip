@@ -60,9 +60,10 @@ __global__ __launch_bounds__(64 * (4 / QT)) void attn_kernel_bf16(
     constexpr int R = 4, NKS = D / 32, NVB = D / 16;
     using ST = Stage<D, R>;
     constexpr int NPER = KVStage<D, D, R, NT>::NPER;
-    constexpr int LDR = ST::LDR, LDT = ST::LDT;
+    constexpr int LDR = ST::LDR;
     __shared__ __attribute__((aligned(16))) uint16_t sK[kChunk * LDR];   // K block, row-major
-    __shared__ __attribute__((aligned(16))) uint16_t sVt[D * LDT];       // V block, transposed
+    constexpr int LDV = ST::template LDV<D>;
+    __shared__ __attribute__((aligned(16))) uint16_t sV[kChunk * LDV];   // V block, row-major
 
     const int h = blockIdx.x % H;
     const AttnItem it = items[blockIdx.x / H];
@@ -218,7 +219,7 @@ __global__ __launch_bounds__(64 * (4 / QT)) void attn_kernel_bf16(
             u32x4 av[NVB];
 #pragma unroll
             for (int x = 0; x < NVB; ++x)
-                av[x] = lds_u32x4(sVt + (x * 16 + c16) * LDT + tpos(x * 16, pp * 32 + 4 * g));
+                av[x] = tr_frag(sV, LDV, x * 16, pp, g, c16);
 #pragma unroll
             for (int t = 0; t < QT; ++t) {
                 const u32x4 bp = cat2(pb[t][2 * pp], pb[t][2 * pp + 1]);
@@ -245,14 +246,14 @@ __global__ __launch_bounds__(64 * (4 / QT)) void attn_kernel_bf16(
     load(order(0));
     int i = 0;
     for (; i < n_full; ++i) {
-        stage_kv<D, D, R, NT, NPER, true, false>(kv, sK, nullptr, sVt);
+        stage_kv_rows<D, D, R, NT, NPER>(kv, sK, sV);
         __syncthreads();
         load(order(i + 1));
         block(kChunk, false, std::false_type{});
         __syncthreads();
     }
     for (; i < nkb; ++i) {
-        stage_kv<D, D, R, NT, NPER, true, false>(kv, sK, nullptr, sVt);
+        stage_kv_rows<D, D, R, NT, NPER>(kv, sK, sV);
         __syncthreads();
         load(order(i + 1));
         const int b = order(i);

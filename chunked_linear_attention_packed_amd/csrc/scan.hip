@@ -106,8 +106,9 @@ __global__ __launch_bounds__(kThreads) void delta_kernel_bf16(
     constexpr int VBW = D1::VBW, KBW = D1::KBW, DD = D * D;
     using ST = Stage<D, R>;
     constexpr int NPER = KVStage<D, DVW, R, kThreads>::NPER;
-    __shared__ __attribute__((aligned(16))) uint16_t sKt[D * ST::LDT];
-    __shared__ __attribute__((aligned(16))) uint16_t sVt[DVW * ST::LDT];
+    constexpr int LDV = ST::template LDV<DVW>;
+    __shared__ __attribute__((aligned(16))) uint16_t sK[kChunk * ST::LDR];   // K, row-major
+    __shared__ __attribute__((aligned(16))) uint16_t sV[kChunk * LDV];       // V part, row-major
 
     int item, part;
     split_id<NP>(blockIdx.x, item, part);
@@ -135,7 +136,7 @@ __global__ __launch_bounds__(kThreads) void delta_kernel_bf16(
                                            chunk_rsrc(v, first, 2, rows, H, D), vcg0, H, h);
     };
     auto stage = [&](const BlkR<R> (&cur)[NPER]) {
-        stage_kv<D, DVW, R, kThreads, NPER, false, true>(cur, nullptr, sKt, sVt);
+        stage_kv_rows<D, DVW, R, kThreads, NPER>(cur, sK, sV);
     };
     // S += K^T V of the chunk staged in LDS
     auto accumulate = [&]() {
@@ -144,13 +145,11 @@ __global__ __launch_bounds__(kThreads) void delta_kernel_bf16(
 #pragma unroll
             for (int x = 0; x < VBW; ++x) {
                 const int vb = vbw + x;
-                const u32x4 bv = lds_u32x4(sVt + (vb * 16 + c16) * ST::LDT +
-                                           tpos(vb * 16, ks * 32 + 4 * g));
+                const u32x4 bv = tr_frag(sV, LDV, vb * 16, ks, g, c16);
 #pragma unroll
                 for (int i = 0; i < KBW; ++i) {
                     const int kb = kbw + i;
-                    const u32x4 ak = lds_u32x4(sKt + (kb * 16 + c16) * ST::LDT +
-                                               tpos(kb * 16, ks * 32 + 4 * g));
+                    const u32x4 ak = tr_frag(sK, ST::LDR, kb * 16, ks, g, c16);
                     S[x][i] = mfma_bf16(ak, bv, S[x][i]);
                 }
             }
@@ -444,13 +443,13 @@ struct LaunchCfg<128> {
 // structure (TB + 1 score tiles, TB / 2 + 1 intra-chunk steps) is known at
 // compile time and every loop runs over independent accumulators with its
 // LDS fragments loaded in batches.
-template <int D, int TB, int VBH>
-__device__ __forceinline__ void out_tiles(const uint16_t* sK, const uint16_t* sVt,
+template <int D, int TB, int VBH, int LDV>
+__device__ __forceinline__ void out_tiles(const uint16_t* sK, const uint16_t* sV,
                                           const uint16_t* sSh, const uint16_t* sSl,
                                           const u32x4 (&qf)[D / 32], int vb0, int g, int c16,
                                           f32x4 (&acc)[VBH]) {
     constexpr int NKS = D / 32;
-    constexpr int LDR = Stage<D, 4>::LDR, LDT = Stage<D, 4>::LDT;
+    constexpr int LDR = Stage<D, 4>::LDR;
     // P^T tiles (ub, TB), ub <= TB: P^T[u][t] = sum_d K[u][d] Q[t][d]
     f32x4 p[TB + 1];
 #pragma unroll
@@ -499,7 +498,7 @@ __device__ __forceinline__ void out_tiles(const uint16_t* sK, const uint16_t* sV
 #pragma unroll
         for (int x = 0; x < VBH; ++x) {
             const int vb = vb0 + x;
-            av[x] = lds_u32x4(sVt + (vb * 16 + c16) * LDT + tpos(vb * 16, pp * 32 + 4 * g));
+            av[x] = tr_frag(sV, LDV, vb * 16, pp, g, c16);
         }
 #pragma unroll
         for (int x = 0; x < VBH; ++x) acc[x] = mfma_bf16(av[x], bp, acc[x]);
@@ -517,10 +516,10 @@ __global__ __launch_bounds__(O3::NT) void output_kernel_bf16(
     constexpr int NKB = O3::NKB, NVB = O3::NVB, NKS = O3::NKS, VBH = O3::VBH, TPW = O3::TPW;
     constexpr int DD = D * D;
     constexpr int NPER = KVStage<D, DV, R, NT>::NPER;
-    constexpr int LDR = ST::LDR, LDT = ST::LDT;
-    __shared__ __attribute__((aligned(16))) uint16_t sK[kChunk * LDR];
-    __shared__ __attribute__((aligned(16))) uint16_t sKt[D * LDT];
-    __shared__ __attribute__((aligned(16))) uint16_t sVt[DV * LDT];
+    constexpr int LDR = ST::LDR;
+    constexpr int LDV = ST::template LDV<DV>;
+    __shared__ __attribute__((aligned(16))) uint16_t sK[kChunk * LDR];   // K, row-major
+    __shared__ __attribute__((aligned(16))) uint16_t sV[kChunk * LDV];   // V part, row-major
     __shared__ __attribute__((aligned(16))) uint16_t sSh[DV * LDR];   // S^T, bf16 high term
     __shared__ __attribute__((aligned(16))) uint16_t sSl[DV * LDR];   // S^T, bf16 low term
 
@@ -604,7 +603,7 @@ __global__ __launch_bounds__(O3::NT) void output_kernel_bf16(
             *reinterpret_cast<u32x2*>(sSh + off) = u32x2{h01, h23};
             *reinterpret_cast<u32x2*>(sSl + off) = u32x2{l01, l23};
         }
-        stage_kv<D, DV, R, NT, NPER, true, true>(kv, sK, sKt, sVt);
+        stage_kv_rows<D, DV, R, NT, NPER>(kv, sK, sV);
     };
     // The loop is rotated: chunk c + 1 is staged (and its q moved to qf) at
     // the end of iteration c, right after chunk c's output stores.  Its loads
@@ -626,10 +625,10 @@ __global__ __launch_bounds__(O3::NT) void output_kernel_bf16(
         // O^T tiles: this wave's 16 tokens, local feature tiles hv*VBH .. +VBH-1
         f32x4 acc[VBH];
         switch (tb) {
-            case 0: out_tiles<D, 0, VBH>(sK, sVt, sSh, sSl, qf, hv * VBH, g, c16, acc); break;
-            case 1: out_tiles<D, 1, VBH>(sK, sVt, sSh, sSl, qf, hv * VBH, g, c16, acc); break;
-            case 2: out_tiles<D, 2, VBH>(sK, sVt, sSh, sSl, qf, hv * VBH, g, c16, acc); break;
-            default: out_tiles<D, 3, VBH>(sK, sVt, sSh, sSl, qf, hv * VBH, g, c16, acc); break;
+            case 0: out_tiles<D, 0, VBH, LDV>(sK, sV, sSh, sSl, qf, hv * VBH, g, c16, acc); break;
+            case 1: out_tiles<D, 1, VBH, LDV>(sK, sV, sSh, sSl, qf, hv * VBH, g, c16, acc); break;
+            case 2: out_tiles<D, 2, VBH, LDV>(sK, sV, sSh, sSl, qf, hv * VBH, g, c16, acc); break;
+            default: out_tiles<D, 3, VBH, LDV>(sK, sV, sSh, sSl, qf, hv * VBH, g, c16, acc); break;
         }
         // lane holds O[t = tb*16 + c16][part*DV + (hv*VBH + x)*16 + 4g + j], j = 0..3
         {
@@ -643,13 +642,10 @@ __global__ __launch_bounds__(O3::NT) void output_kernel_bf16(
         // carry: S += K^T V for this wave's tiles
 #pragma unroll
         for (int ks = 0; ks < kChunk / 32; ++ks) {
-            const u32x4 bv = lds_u32x4(sVt + (vbo * 16 + c16) * LDT +
-                                       tpos(vbo * 16, ks * 32 + 4 * g));
+            const u32x4 bv = tr_frag(sV, LDV, vbo * 16, ks, g, c16);
 #pragma unroll
             for (int i = 0; i < TPW; ++i)
-                S[i] = mfma_bf16(lds_u32x4(sKt + ((kbo + i) * 16 + c16) * LDT +
-                                           tpos((kbo + i) * 16, ks * 32 + 4 * g)),
-                                 bv, S[i]);
+                S[i] = mfma_bf16(tr_frag(sK, LDR, (kbo + i) * 16, ks, g, c16), bv, S[i]);
         }
         __syncthreads();
         publish_and_stage();

@@ -120,6 +120,8 @@ struct Stage {
     static constexpr int PAD = D == 64 ? 16 : 8;
     static constexpr int LDR = D + PAD;         // row-major stride (elements)
     static constexpr int LDT = kChunk + PAD;    // transposed stride (elements)
+    template <int W>
+    static constexpr int LDV = W + PAD;         // row-major stride of a W-feature tile
 };
 
 // Column at which element k of row f of a row-major D-column state tile is
@@ -155,7 +157,10 @@ __device__ __forceinline__ void store_rows(uint16_t* dst, const BlkR<R>& b, int 
         *reinterpret_cast<u32x4*>(dst + (rg * R + i) * ld + cg * 8) = b.r[i];
 }
 
-// Transposed tiles [feature][token] hold the 64 tokens of a row in the order
+// Transposed tiles [feature][token] (used by the split-precision kernels,
+// whose fp32 data is split into bf16 terms while staging; the bf16 kernels
+// read the same fragments from row-major tiles with tr_frag) hold the 64
+// tokens of a row in the order
 //   position(u) = 32 a + 8 c + 4 b + d   for   u = 32 a + 16 b + 4 c + d,
 // so that the 8 tokens {32a + 16b + 4c + d : b, d} (two 4-token groups 16
 // apart: the k-slots of lane group c in a K = 32 step whose two halves come
@@ -199,13 +204,39 @@ __device__ __forceinline__ void store_cols(uint16_t* dst, const BlkR<R>& b, int 
     }
 }
 
+__device__ __forceinline__ u32x4 cat2(u32x2 a, u32x2 b) { return u32x4{a[0], a[1], b[0], b[1]}; }
+
+// ---------------------------------------------------------------------------
+// Transposed fragments read from row-major [token][feature] tiles with the
+// gfx950 transposing LDS read (ds_read_b64_tr_b16).  Within each 16-lane
+// group, lane 4a + e receives element e of the 8-byte pieces addressed by
+// lanes a, a + 4, a + 8, a + 12 (probed on the GPU).  So if lane lam of the
+// group addresses token t0 + lam / 4, features f0 + 4 (lam % 4) .. + 3, lane
+// lam receives feature f0 + lam of tokens t0 .. t0 + 3.
+// ---------------------------------------------------------------------------
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 lds_tr4(const uint16_t* p) {
+    const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(p));
+    return __builtin_bit_cast(u32x2, r);
+}
+// Operand fragment of a transposed 16-row tile (rows = features f0 .. f0+15,
+// k = tokens) for K step ks of a 64-token chunk: lane 16 g + c gets row
+// f0 + c, k-slots 4 h + j = token (2 ks + h) * 16 + 4 g + j (h = 0, 1,
+// j = 0 .. 3) -- the slot order of the accumulator-layout P^T operand and the
+// one the former transposed tiles stored.
+__device__ __forceinline__ u32x4 tr_frag(const uint16_t* tile, int ld, int f0, int ks, int g,
+                                         int c16) {
+    const uint16_t* p = tile + (4 * g + (c16 >> 2)) * ld + f0 + 4 * (c16 & 3);
+    return cat2(lds_tr4(p + (2 * ks) * 16 * ld), lds_tr4(p + (2 * ks + 1) * 16 * ld));
+}
+
 __device__ __forceinline__ u32x2 lds_u32x2(const uint16_t* p) {
     return *reinterpret_cast<const u32x2*>(p);
 }
 __device__ __forceinline__ u32x4 lds_u32x4(const uint16_t* p) {
     return *reinterpret_cast<const u32x4*>(p);
 }
-__device__ __forceinline__ u32x4 cat2(u32x2 a, u32x2 b) { return u32x4{a[0], a[1], b[0], b[1]}; }
 
 // K and V blocks of one chunk: all D features of K, and the DVW features of V
 // starting at feature vcg0 * 8 (a workgroup that computes only part of the
@@ -241,13 +272,13 @@ __device__ __forceinline__ void load_kv(BlkR<R> (&pre)[NPER], __amdgpu_buffer_rs
     }
 }
 
-// Registers -> LDS: K row-major (K_ROWS) and/or transposed (K_TRANS), V
-// transposed (rows are the workgroup's own V features, 0 .. DVW-1).
-template <int D, int DVW, int R, int NT, int NPER, bool K_ROWS, bool K_TRANS>
-__device__ __forceinline__ void stage_kv(const BlkR<R> (&pre)[NPER], uint16_t* sK,
-                                         uint16_t* sKt, uint16_t* sVt) {
+// Registers -> LDS, both tiles row-major: K rows into sK (stride LDR), the
+// workgroup's DVW features of V into sV (stride LDR of a DVW-wide tile);
+// transposed operands are then read with tr_frag.
+template <int D, int DVW, int R, int NT, int NPER>
+__device__ __forceinline__ void stage_kv_rows(const BlkR<R> (&pre)[NPER], uint16_t* sK,
+                                              uint16_t* sV) {
     using KS = KVStage<D, DVW, R, NT>;
-    using ST = Stage<D, R>;
     const int wbase = wave_id() * 64;
     const int lane = threadIdx.x & 63;
 #pragma unroll
@@ -257,11 +288,10 @@ __device__ __forceinline__ void stage_kv(const BlkR<R> (&pre)[NPER], uint16_t* s
             if (b0 >= KS::NBK + KS::NBV) break;
         if (b0 >= KS::NBK) {
             const int wv = b0 - KS::NBK + lane;
-            store_cols<R>(sVt, pre[i], wv / KS::NCGV, wv % KS::NCGV, ST::LDT);
+            store_rows<R>(sV, pre[i], wv / KS::NCGV, wv % KS::NCGV, Stage<D, R>::template LDV<DVW>);
         } else {
             const int wk = b0 + lane;
-            if constexpr (K_ROWS) store_rows<R>(sK, pre[i], wk / KS::NCGK, wk % KS::NCGK, ST::LDR);
-            if constexpr (K_TRANS) store_cols<R>(sKt, pre[i], wk / KS::NCGK, wk % KS::NCGK, ST::LDT);
+            store_rows<R>(sK, pre[i], wk / KS::NCGK, wk % KS::NCGK, Stage<D, R>::LDR);
         }
     }
 }
