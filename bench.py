@@ -38,6 +38,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--block-chunks", type=int, default=None)
+    ap.add_argument("--form", choices=["auto", "two", "three"], default="auto",
+                    help="scan form: two launches (no prefix launch), three, or the "
+                         "library's choice for the pass shape")
     ap.add_argument("--rotate-gib", type=float, default=1.0,
                     help="total size of the rotated input copies")
     ap.add_argument("--eager", action="store_true",
@@ -93,10 +96,11 @@ def calibrate_copy(mib, steps):
                       "us_per_launch": us, "GBps": 2 * n * 4 / (us * 1e-6) / 1e9}), flush=True)
 
 
-def launch_floor(steps, quiet=False):
-    """Three dependent launches of the library's smallest kernel (a 64 KiB
-    state export) per step, replayed as a HIP graph: the fixed cost of a
-    three-launch pass with no work in it.  Returns microseconds per step."""
+def launch_floor(steps, quiet=False, n_launches=3):
+    """n_launches dependent launches of the library's smallest kernel (a
+    64 KiB state export) per step, replayed as a HIP graph: the fixed cost of
+    a pass of that many launches with no work in it.  Returns microseconds
+    per step."""
     import torch
     import chunked_linear_attention_packed_amd as la
     src = torch.zeros((1, 1, 64, 64), dtype=torch.float32, device="cuda:0")
@@ -108,7 +112,7 @@ def launch_floor(steps, quiet=False):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=st):
         for _ in range(steps):
-            for _ in range(3):
+            for _ in range(n_launches):
                 la.export_view_state(src, 0, dst, stream=st)
     g.replay()
     torch.cuda.synchronize()
@@ -120,7 +124,7 @@ def launch_floor(steps, quiet=False):
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / steps
     if not quiet:
-        print(json.dumps({"calibration": "launch floor", "launches_per_step": 3,
+        print(json.dumps({"calibration": "launch floor", "launches_per_step": n_launches,
                           "us_per_step": us}), flush=True)
     return us
 
@@ -514,11 +518,14 @@ def main():
     stream = torch.cuda.Stream(dev)
     if a.split_fp32 and w.dtype != "f32":
         raise SystemExit("--split-fp32 applies to fp32 workloads")
+    form = None if a.form == "auto" else a.form
+    n_launches = {"two": 2, "three": 3}.get(a.form) or la.scan_launches(plan, H, d)
 
     def step(i, stages=la.STAGE_ALL):
         s = sets[i % n_sets]
         la.scan_packed(s["q"], s["k"], s["v"], plan, out=s["out"], final_state=fin,
-                       workspace=ws, stream=stream, stages=stages, split_fp32=a.split_fp32)
+                       workspace=ws, stream=stream, stages=stages, split_fp32=a.split_fp32,
+                       form=form)
 
     # first pass eagerly (also validates arguments)
     with torch.cuda.stream(stream):
@@ -568,7 +575,7 @@ def main():
             st_ = stream if i % 2 == 0 else s1
             la.scan_packed(s_["q"], s_["k"], s_["v"], plan, out=s_["out"],
                            final_state=fin2[i % 2], workspace=ws2[i % 2], stream=st_,
-                           split_fp32=a.split_fp32)
+                           split_fp32=a.split_fp32, form=form)
 
         def make_graph2(n):
             g = torch.cuda.CUDAGraph()
@@ -665,7 +672,7 @@ def main():
             e_b.record(stream)
     torch.cuda.synchronize()
     singles = np.array([e_a.elapsed_time(e_b) * 1e3 for e_a, e_b in evs])
-    floor_us = launch_floor(max(a.steps, 20), quiet=True)
+    floor_us = launch_floor(max(a.steps, 20), quiet=True, n_launches=n_launches)
 
     cpu = None
     if not a.no_cpu_baseline:
@@ -690,6 +697,7 @@ def main():
             "views": info.n_views, "branches": info.n_branches,
             "chunk": info.chunk, "block_chunks": info.block_chunks,
             "work_blocks": info.n_blocks, "delta_blocks": info.n_delta,
+            "launches": n_launches,
             "launch": "eager" if a.eager else "hip_graph",
             "precision": ("fp32 data, products as 3 bf16 MFMAs (hi.hi + hi.lo + lo.hi)"
                           if a.split_fp32 else

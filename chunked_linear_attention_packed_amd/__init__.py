@@ -28,7 +28,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 __all__ = ["LinAttnError", "PassInfo", "PassPlan", "pack", "plan_segments",
-           "choose_block_chunks", "workspace_size", "scan_packed",
+           "choose_block_chunks", "workspace_size", "scan_launches", "scan_packed",
            "export_view_state", "ViewStateCache", "AttnPlan", "attn_plan", "attn_packed",
            "library_path", "load_library", "CHUNK"]
 
@@ -37,6 +37,8 @@ LA_OK, LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED, LA_ERR_WORKSPACE, LA_ERR_HIP = ra
 LA_F32, LA_BF16, LA_F32_SPLIT = 0, 1, 2
 LA_ATTN_NO_VIEW, LA_ATTN_PACKED_VIEW, LA_ATTN_EXT_VIEW = 0, 1, 2
 STAGE_STATES, STAGE_PREFIX, STAGE_OUTPUT, STAGE_ALL = 1, 2, 4, 7
+FORM_TWO_LAUNCH, FORM_THREE_LAUNCH = 8, 16
+_FORMS = {None: 0, "auto": 0, "two": FORM_TWO_LAUNCH, "three": FORM_THREE_LAUNCH}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -55,7 +57,7 @@ class PassInfo(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "n_requests", "n_segments", "n_views", "n_branches", "n_ext", "n_tokens", "chunk",
         "block_chunks", "n_chunks", "n_view_chunks", "n_blocks", "n_delta", "n_scan",
-        "plan_words", "max_seg_tokens")] + [("reserved", ctypes.c_int32 * 9)]
+        "plan_words", "max_seg_tokens", "fused_slot_reads")] + [("reserved", ctypes.c_int32 * 8)]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_ if n != "reserved"}
@@ -90,6 +92,8 @@ def load_library():
                                    ctypes.c_int32, ctypes.POINTER(PassInfo), _P, _P,
                                    ctypes.c_int32, _P, _P, _P, ctypes.c_size_t, _P]
     lib.la_scan_packed_stages.argtypes = [ctypes.c_int32] + lib.la_scan_packed.argtypes
+    lib.la_scan_launches.argtypes = [ctypes.POINTER(PassInfo), ctypes.c_int32, ctypes.c_int32,
+                                     ctypes.c_int32, _I32P]
     lib.la_export_view_state.argtypes = [_P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                          ctypes.c_int32, ctypes.c_int32, _P, _P]
     lib.la_pack_pass_ext.argtypes = [ctypes.c_int32, _I32P, _I32P, _I32P, _I32P,
@@ -111,7 +115,7 @@ def load_library():
     lib.la_status_string.restype = ctypes.c_char_p
     for fn in ("la_pack_pass", "la_pack_pass_ext", "la_plan_segments",
                "la_scan_workspace_size", "la_scan_packed", "la_scan_packed_stages",
-               "la_export_view_state", "la_cache_create", "la_cache_destroy",
+               "la_scan_launches", "la_export_view_state", "la_cache_create", "la_cache_destroy",
                "la_cache_lookup", "la_cache_reserve", "la_cache_erase", "la_cache_count",
                "la_attn_plan", "la_attn_packed"):
         getattr(lib, fn).restype = ctypes.c_int32
@@ -237,6 +241,15 @@ def workspace_size(plan, heads, d, dtype):
     return n.value
 
 
+def scan_launches(plan, heads, d):
+    """Launches scan_packed uses for this pass by default: 2 or 3."""
+    lib = load_library()
+    n = ctypes.c_int32()
+    _check("la_scan_launches",
+           lib.la_scan_launches(ctypes.byref(plan.info), heads, d, d, ctypes.byref(n)))
+    return n.value
+
+
 def _dtype_code_from_torch(dt):
     import torch
     return {torch.bfloat16: LA_BF16, torch.float32: LA_F32}[dt]
@@ -249,8 +262,8 @@ def _stream_ptr(stream, device):
 
 
 def scan_packed(q, k, v, plan, ext_state=None, out=None, final_state=None, workspace=None,
-                stream=None, stages=STAGE_ALL, split_fp32=False):
-    """Run the three-launch scan on `stream` (default: torch's current stream).
+                stream=None, stages=STAGE_ALL, split_fp32=False, form=None):
+    """Run the scan on `stream` (default: torch's current stream).
 
     q, k: [T, H, d] and v: [T, H, d] contiguous CUDA tensors, bf16 or fp32.
     Returns (out [T, H, d] in the input dtype, final_state [n_views, H, d, d]
@@ -258,7 +271,9 @@ def scan_packed(q, k, v, plan, ext_state=None, out=None, final_state=None, works
     given (no allocation then).  `stages` selects launches (STAGE_* bits, see
     la_scan_packed_stages) for profiling; the default runs all three.  For
     fp32 inputs, split_fp32=True evaluates every product as three bf16 MFMAs
-    over hi/lo operand splits (LA_F32_SPLIT) instead of fp32 MFMAs."""
+    over hi/lo operand splits (LA_F32_SPLIT) instead of fp32 MFMAs.  `form`
+    forces the two-launch ("two": no prefix launch) or the three-launch
+    ("three") form; None lets the library choose from the pass shape."""
     import torch
     lib = load_library()
     if not (q.is_cuda and k.is_cuda and v.is_cuda):
@@ -295,8 +310,10 @@ def scan_packed(q, k, v, plan, ext_state=None, out=None, final_state=None, works
             raise TypeError("ext_state must be contiguous float32 [n_ext, H, d, d]")
         n_ext = ext_state.shape[0]
         ext_ptr = ctypes.c_void_p(ext_state.data_ptr())
+    if form not in _FORMS:
+        raise ValueError(f"form must be one of {sorted(k for k in _FORMS if k)} or None")
     dplan = plan.device_plan(dev)
-    st = lib.la_scan_packed_stages(stages, ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
+    st = lib.la_scan_packed_stages(stages | _FORMS[form], ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
                             ctypes.c_void_p(v.data_ptr()), code, H, dk, dv,
                             ctypes.byref(info), ctypes.c_void_p(dplan.data_ptr()), ext_ptr,
                             n_ext, ctypes.c_void_p(out.data_ptr()),

@@ -18,7 +18,7 @@
 
 namespace {
 
-constexpr int32_t kPlanVersion = 1;
+constexpr int32_t kPlanVersion = 2;
 
 struct Seg {
     int32_t off, len, parent;
@@ -70,10 +70,15 @@ la_status plan_impl(int32_t n_seg, const int32_t* seg_offsets, const int32_t* br
     }
 
     // Work blocks: views first (their blocks are the longest), then branches.
-    int64_t n_blocks = 0, n_delta = 0, n_scan = 0;
+    // fused_reads counts the workspace slots the output launch reads per head
+    // when it sums the block states itself (no prefix launch): block j of a
+    // segment reads the j earlier slots of its segment, a branch of a view
+    // also all slots of that view, and a view's last block its own slot.
+    int64_t n_blocks = 0, n_delta = 0, n_scan = 0, fused_reads = 0;
     for (int pass = 0; pass < 2; ++pass) {
         for (int32_t s = 0; s < n_seg; ++s) {
-            const bool is_view = branch_parent[s] == -1;
+            const int32_t p = branch_parent[s];
+            const bool is_view = p == -1;
             if (is_view != (pass == 0)) continue;
             const int64_t len = int64_t(seg_offsets[s + 1]) - seg_offsets[s];
             const int64_t nb = ceil_div(len, blk_tok);
@@ -83,6 +88,9 @@ la_status plan_impl(int32_t n_seg, const int32_t* seg_offsets, const int32_t* br
             const int64_t nslots = is_view ? nb : nb - 1;
             n_delta += nslots;
             if (is_view || nslots >= 2) ++n_scan;
+            fused_reads += nb * (nb - 1) / 2 + (is_view ? 1 : 0);
+            if (p >= 0)
+                fused_reads += nb * ceil_div(int64_t(seg_offsets[p + 1]) - seg_offsets[p], blk_tok);
         }
     }
     const int64_t words = int64_t(LA_PLAN_HEADER_WORDS) + n_blocks * LA_PLAN_BLOCK_WORDS +
@@ -106,6 +114,7 @@ la_status plan_impl(int32_t n_seg, const int32_t* seg_offsets, const int32_t* br
     inf.n_scan = int32_t(n_scan);
     inf.plan_words = int32_t(words);
     inf.max_seg_tokens = max_len;
+    inf.fused_slot_reads = int32_t(std::min<int64_t>(fused_reads, INT32_MAX));
 
     if (view_ordinal)
         for (int32_t s = 0; s < n_seg; ++s) view_ordinal[s] = ord[size_t(s)];
@@ -129,6 +138,7 @@ la_status plan_impl(int32_t n_seg, const int32_t* seg_offsets, const int32_t* br
         h[10] = off_scan;
         h[11] = n_ext;
         h[12] = n_views;
+        h[13] = inf.fused_slot_reads;
         int32_t* blk = plan + off_blocks;
         int32_t* del = plan + off_delta;
         int32_t* scn = plan + off_scan;
@@ -143,6 +153,7 @@ la_status plan_impl(int32_t n_seg, const int32_t* seg_offsets, const int32_t* br
                 const int32_t nb = int32_t(ceil_div(len, blk_tok));
                 const int32_t nslots = is_view ? nb : nb - 1;
                 const int32_t seed = is_view ? -1 : (p >= 0 ? ord[size_t(p)] : p);
+                const int32_t slot0 = nslots > 0 ? slot : -1;
                 for (int32_t j = 0; j < nb; ++j) {
                     const int32_t tok0 = off + int32_t(j * blk_tok);
                     const int32_t ntok = int32_t(len - j * blk_tok < blk_tok ? len - j * blk_tok
@@ -153,8 +164,8 @@ la_status plan_impl(int32_t n_seg, const int32_t* seg_offsets, const int32_t* br
                     blk[3] = j < nslots ? slot + j : -1;
                     blk[4] = seed;
                     blk[5] = s;
-                    blk[6] = 0;
-                    blk[7] = 0;
+                    blk[6] = slot0;
+                    blk[7] = is_view && j == nb - 1 ? ord[size_t(s)] : -1;
                     blk += LA_PLAN_BLOCK_WORDS;
                     if (j < nslots) {
                         del[0] = tok0;

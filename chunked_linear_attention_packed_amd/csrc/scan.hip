@@ -69,7 +69,7 @@ inline int64_t split_grid(int64_t items) {
 // Plan descriptors (see linattn.h).
 // ---------------------------------------------------------------------------
 struct BlockDesc {
-    int tok0, ntok, sin_slot, delta_slot, seed, seg, pad0, pad1;
+    int tok0, ntok, sin_slot, delta_slot, seed, seg, slot0, final_row;
 };
 struct DeltaDesc {
     int tok0, ntok, slot, seg;
@@ -178,14 +178,12 @@ __global__ __launch_bounds__(kThreads) void delta_kernel_bf16(
         if (c + 2 >= nch) break;
         stage(pa);
     }
-    float* dst = ws + ((int64_t)dd.slot * H + h) * DD;
+    f32x4* dst = reinterpret_cast<f32x4*>(ws + ((int64_t)dd.slot * H + h) * DD);
 #pragma unroll
     for (int x = 0; x < VBW; ++x)
 #pragma unroll
         for (int i = 0; i < KBW; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                dst[(((part * NVB + vbw + x) * NKB + kbw + i) * 4 + j) * 64 + lane] = S[x][i][j];
+            dst[((part * NVB + vbw + x) * NKB + kbw + i) * 64 + lane] = S[x][i];
 }
 
 // fp32 tiles: row-major [64][D+4] floats in LDS, loaded as 16-byte pieces.
@@ -279,14 +277,11 @@ __global__ __launch_bounds__(kThreads) void delta_kernel_f32(
         f32_state_update<D>(S, sK, sV, w, g, c16);
         __syncthreads();
     }
-    float* dst = ws + ((int64_t)dd.slot * H + h) * DD;
+    f32x4* dst = reinterpret_cast<f32x4*>(ws + ((int64_t)dd.slot * H + h) * DD);
 #pragma unroll
     for (int x = 0; x < VBW; ++x)
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                dst[(((w * VBW + x) * NKB + kb) * 4 + j) * 64 + lane] = S[x][kb][j];
+        for (int kb = 0; kb < NKB; ++kb) dst[((w * VBW + x) * NKB + kb) * 64 + lane] = S[x][kb];
 }
 
 // ===========================================================================
@@ -339,46 +334,101 @@ __global__ __launch_bounds__(kThreads) void prefix_kernel(const ScanDesc* __rest
 // Launch 3: outputs.  Per work block and head, chunk by chunk.
 // ===========================================================================
 
-// Initial state of a block: seed (zero, a view's final state, or an external
-// state) plus the segment-local prefix of the earlier blocks.
-template <int D>
-__device__ __forceinline__ void init_state(f32x4 (&S)[D / 64][D / 16], const BlockDesc& bd,
-                                           const float* __restrict__ ws,
-                                           const float* __restrict__ final_state,
-                                           const float* __restrict__ ext_state, int H, int h,
-                                           int w, int lane) {
-    constexpr int NKB = D / 16, VBW = D / 64, DD = D * D;
-    const int g = lane >> 4, c16 = lane & 15;
+// Initial state of a block, for the state tiles a lane carries: tile i is
+// tile index tix[i] = vb * NKB + kb of the slot layout, and the lane holds
+// S[kb*16 + 4g + j][vb*16 + c] (lane = 16 g + c), j = 0..3.
+//   S_in = seed + own
+// seed: zero (a view), the view's final state (a branch) or an external state
+// (a shard branch); own: the segment-local sum of the earlier blocks' states.
+// Three-launch form: the prefix launch has left own in slot sin_slot and the
+// view totals in final_state.  Two-launch form (`fused`): the slots hold the
+// blocks' own states and the block sums them here, in slot order: own =
+// slots slot0 .. sin_slot, a branch's seed = all slots of its view (scan
+// entry `seed`); a view's last block also writes the view's total, own plus
+// its own slot, to final_state.  Both forms add in the same order as the
+// prefix launch (from zero, one slot after the other), so they give the same
+// bits, and a branch's seed equals the final_state written for its view.
+template <int D, int NT>
+__device__ __forceinline__ void sum_slots(f32x4 (&acc)[NT], const int (&tix)[NT],
+                                          const float* __restrict__ ws, int first, int n, int H,
+                                          int h, int lane) {
+    constexpr int64_t SLOT4 = D * D / 4;   // 16-byte pieces per slot
+    const int64_t stride = int64_t(H) * SLOT4;
+    const f32x4* p = reinterpret_cast<const f32x4*>(ws) + (int64_t(first) * H + h) * SLOT4 + lane;
 #pragma unroll
-    for (int x = 0; x < VBW; ++x)
+    for (int i = 0; i < NT; ++i) acc[i] = zero4();
+    // B slots of loads in flight: 16 pieces per lane at most, so the batch
+    // does not raise the register count of the kernels around it
+    constexpr int B = NT >= 16 ? 1 : 16 / NT;
+    int s = 0;
+    for (; s + B <= n; s += B) {
+        f32x4 x[B][NT];
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) S[x][kb] = zero4();
-    const float* seed = nullptr;
-    if (bd.seed >= 0)
-        seed = final_state + ((int64_t)bd.seed * H + h) * DD;
-    else if (bd.seed <= -2)
-        seed = ext_state + ((int64_t)(-bd.seed - 2) * H + h) * DD;
-    if (seed) {
+        for (int b = 0; b < B; ++b)
 #pragma unroll
-        for (int x = 0; x < VBW; ++x)
+            for (int i = 0; i < NT; ++i) x[b][i] = p[(s + b) * stride + tix[i] * 64];
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
+        for (int b = 0; b < B; ++b)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    S[x][kb][j] = seed[(kb * 16 + 4 * g + j) * D + (w * VBW + x) * 16 + c16];
+            for (int i = 0; i < NT; ++i) acc[i] += x[b][i];
     }
-    if (bd.sin_slot >= 0) {
-        const float* src = ws + ((int64_t)bd.sin_slot * H + h) * DD;
+    for (; s < n; ++s)
 #pragma unroll
-        for (int x = 0; x < VBW; ++x)
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    S[x][kb][j] += src[(((w * VBW + x) * NKB + kb) * 4 + j) * 64 + lane];
-    }
+        for (int i = 0; i < NT; ++i) acc[i] += p[s * stride + tix[i] * 64];
 }
 
+template <int D, int NT>
+__device__ __forceinline__ void block_init_state(
+    f32x4 (&S)[NT], const int (&tix)[NT], const BlockDesc& bd, const ScanDesc* __restrict__ scans,
+    const float* __restrict__ ws, float* __restrict__ final_state,
+    const float* __restrict__ ext_state, int H, int h, int lane, bool fused) {
+    constexpr int NKB = D / 16, DD = D * D;
+    const int g = lane >> 4, c16 = lane & 15;
+    // row-major [D][D] seed (final_state or ext_state row) into the tiles
+    auto read_rows = [&](const float* __restrict__ src) {
+#pragma unroll
+        for (int i = 0; i < NT; ++i) {
+            const int kb = tix[i] % NKB, vb = tix[i] / NKB;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) S[i][j] = src[(kb * 16 + 4 * g + j) * D + vb * 16 + c16];
+        }
+    };
+#pragma unroll
+    for (int i = 0; i < NT; ++i) S[i] = zero4();
+    if (bd.seed <= -2) {
+        read_rows(ext_state + ((int64_t)(-bd.seed - 2) * H + h) * DD);
+    } else if (bd.seed >= 0) {
+        if (fused) {
+            const ScanDesc sc = scans[bd.seed];
+            sum_slots<D, NT>(S, tix, ws, sc.first_slot, sc.n_slots, H, h, lane);
+        } else {
+            read_rows(final_state + ((int64_t)bd.seed * H + h) * DD);
+        }
+    }
+    if (bd.sin_slot >= 0) {
+        f32x4 own[NT];
+        if (fused) {
+            sum_slots<D, NT>(own, tix, ws, bd.slot0, bd.sin_slot - bd.slot0 + 1, H, h, lane);
+        } else {
+            const f32x4* p = reinterpret_cast<const f32x4*>(ws + ((int64_t)bd.sin_slot * H + h) * DD);
+#pragma unroll
+            for (int i = 0; i < NT; ++i) own[i] = p[tix[i] * 64 + lane];
+        }
+#pragma unroll
+        for (int i = 0; i < NT; ++i) S[i] += own[i];
+    }
+    if (fused && bd.final_row >= 0) {
+        const f32x4* p = reinterpret_cast<const f32x4*>(ws + ((int64_t)bd.delta_slot * H + h) * DD);
+        float* dst = final_state + ((int64_t)bd.final_row * H + h) * DD;
+#pragma unroll
+        for (int i = 0; i < NT; ++i) {
+            const f32x4 t = S[i] + p[tix[i] * 64 + lane];
+            const int kb = tix[i] % NKB, vb = tix[i] / NKB;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) dst[(kb * 16 + 4 * g + j) * D + vb * 16 + c16] = t[j];
+        }
+    }
+}
 
 // Launch 3 (bf16): NP workgroups share a (work block, head) item, each
 // computing the DV = D / NP output features starting at part * DV and
@@ -509,8 +559,9 @@ template <int D, class O3>
 __global__ __launch_bounds__(O3::NT) void output_kernel_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const BlockDesc* __restrict__ blocks,
-    const float* __restrict__ ws, const float* __restrict__ final_state,
-    const float* __restrict__ ext_state, uint16_t* __restrict__ out, int H, int n_items) {
+    const ScanDesc* __restrict__ scans, const float* __restrict__ ws,
+    float* __restrict__ final_state, const float* __restrict__ ext_state,
+    uint16_t* __restrict__ out, int H, int n_items, int fused) {
     constexpr int R = O3::R, NT = O3::NT, NP = O3::NP_, DV = O3::DV;
     using ST = Stage<D, R>;
     constexpr int NKB = O3::NKB, NVB = O3::NVB, NKS = O3::NKS, VBH = O3::VBH, TPW = O3::TPW;
@@ -560,33 +611,14 @@ __global__ __launch_bounds__(O3::NT) void output_kernel_bf16(
     // qn while the current chunk is computed)
     load(0, qf);
 
-    // carry state: tiles (vbg, kbo + i); lane holds S[kb*16 + 4g + j][vbg*16 + c16]:
-    // the seed (a view's final state, an external state, or zero) plus the
-    // segment-local prefix of the earlier blocks
+    // carry state: tiles (vbg, kbo + i); lane holds S[kb*16 + 4g + j][vbg*16 + c16]
     f32x4 S[TPW];
-#pragma unroll
-    for (int i = 0; i < TPW; ++i) S[i] = zero4();
     {
-        const float* seed = nullptr;
-        if (bd.seed >= 0)
-            seed = final_state + ((int64_t)bd.seed * H + h) * DD;
-        else if (bd.seed <= -2)
-            seed = ext_state + ((int64_t)(-bd.seed - 2) * H + h) * DD;
-        if (seed) {
+        int tix[TPW];
 #pragma unroll
-            for (int i = 0; i < TPW; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    S[i][j] = seed[((kbo + i) * 16 + 4 * g + j) * D + vbg * 16 + c16];
-        }
-        if (bd.sin_slot >= 0) {
-            const float* src = ws + ((int64_t)bd.sin_slot * H + h) * DD;
-#pragma unroll
-            for (int i = 0; i < TPW; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    S[i][j] += src[((vbg * NKB + kbo + i) * 4 + j) * 64 + lane];
-        }
+        for (int i = 0; i < TPW; ++i) tix[i] = vbg * NKB + kbo + i;
+        block_init_state<D, TPW>(S, tix, bd, scans, ws, final_state, ext_state, H, h, lane,
+                                 fused != 0);
     }
 
     // LDS inputs of one chunk: S^T = S_hi + S_lo (bf16 terms) for the
@@ -657,9 +689,9 @@ __global__ __launch_bounds__(O3::NT) void output_kernel_bf16(
 template <int D>
 __global__ __launch_bounds__(kThreads) void output_kernel_f32(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
-    const BlockDesc* __restrict__ blocks, const float* __restrict__ ws,
-    const float* __restrict__ final_state, const float* __restrict__ ext_state,
-    float* __restrict__ out, int H) {
+    const BlockDesc* __restrict__ blocks, const ScanDesc* __restrict__ scans,
+    const float* __restrict__ ws, float* __restrict__ final_state,
+    const float* __restrict__ ext_state, float* __restrict__ out, int H, int fused) {
     using TL = F32Tiles<D>;
     constexpr int NKB = D / 16, VBW = D / 64;
     __shared__ __attribute__((aligned(16))) float sQ[kChunk * TL::LD];
@@ -671,7 +703,21 @@ __global__ __launch_bounds__(kThreads) void output_kernel_f32(
     const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, g = lane >> 4, c16 = lane & 15;
 
     f32x4 S[VBW][NKB];
-    init_state<D>(S, bd, ws, final_state, ext_state, H, h, w, lane);
+    {
+        // the wave's tiles (w * VBW + x, kb), flattened as x * NKB + kb
+        int tix[VBW * NKB];
+#pragma unroll
+        for (int x = 0; x < VBW; ++x)
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) tix[x * NKB + kb] = (w * VBW + x) * NKB + kb;
+        f32x4 Sf[VBW * NKB];
+        block_init_state<D, VBW * NKB>(Sf, tix, bd, scans, ws, final_state, ext_state, H, h,
+                                       lane, fused != 0);
+#pragma unroll
+        for (int x = 0; x < VBW; ++x)
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) S[x][kb] = Sf[x * NKB + kb];
+    }
 
     const int nch = (bd.ntok + kChunk - 1) / kChunk;
     f32x4 pq[TL::PER], pk[TL::PER], pv[TL::PER];
@@ -898,14 +944,11 @@ __global__ __launch_bounds__(kThreads) void delta_kernel_split(
         }
         __syncthreads();
     }
-    float* dst = ws + ((int64_t)dd.slot * H + h) * DD;
+    f32x4* dst = reinterpret_cast<f32x4*>(ws + ((int64_t)dd.slot * H + h) * DD);
 #pragma unroll
     for (int x = 0; x < VBW; ++x)
 #pragma unroll
-        for (int i = 0; i < KBW; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                dst[(((vbw + x) * NKB + kbw + i) * 4 + j) * 64 + lane] = S[x][i][j];
+        for (int i = 0; i < KBW; ++i) dst[((vbw + x) * NKB + kbw + i) * 64 + lane] = S[x][i];
 }
 
 // The outputs of one wave for one chunk, split precision (see out_tiles).
@@ -972,9 +1015,10 @@ __device__ __forceinline__ void out_tiles_split(const uint16_t* sKh, const uint1
 template <int D, class O3>
 __global__ __launch_bounds__(O3::NT) void output_kernel_split(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
-    const BlockDesc* __restrict__ blocks, const float* __restrict__ ws,
-    const float* __restrict__ final_state, const float* __restrict__ ext_state,
-    float* __restrict__ out, int H, int n_items) {
+    const BlockDesc* __restrict__ blocks, const ScanDesc* __restrict__ scans,
+    const float* __restrict__ ws, float* __restrict__ final_state,
+    const float* __restrict__ ext_state, float* __restrict__ out, int H, int n_items,
+    int fused) {
     constexpr int R = O3::R, NT = O3::NT, NP = O3::NP_, DV = O3::DV;
     using ST = Stage<D, R>;
     constexpr int NKB = O3::NKB, NVB = O3::NVB, NKS = O3::NKS, VBH = O3::VBH, TPW = O3::TPW;
@@ -1026,29 +1070,12 @@ __global__ __launch_bounds__(O3::NT) void output_kernel_split(
     load(0);
 
     f32x4 S[TPW];
-#pragma unroll
-    for (int i = 0; i < TPW; ++i) S[i] = zero4();
     {
-        const float* seed = nullptr;
-        if (bd.seed >= 0)
-            seed = final_state + ((int64_t)bd.seed * H + h) * DD;
-        else if (bd.seed <= -2)
-            seed = ext_state + ((int64_t)(-bd.seed - 2) * H + h) * DD;
-        if (seed) {
+        int tix[TPW];
 #pragma unroll
-            for (int i = 0; i < TPW; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    S[i][j] = seed[((kbo + i) * 16 + 4 * g + j) * D + vbg * 16 + c16];
-        }
-        if (bd.sin_slot >= 0) {
-            const float* src = ws + ((int64_t)bd.sin_slot * H + h) * DD;
-#pragma unroll
-            for (int i = 0; i < TPW; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    S[i][j] += src[((vbg * NKB + kbo + i) * 4 + j) * 64 + lane];
-        }
+        for (int i = 0; i < TPW; ++i) tix[i] = vbg * NKB + kbo + i;
+        block_init_state<D, TPW>(S, tix, bd, scans, ws, final_state, ext_state, H, h, lane,
+                                 fused != 0);
     }
 
     auto publish_and_stage = [&]() {
@@ -1120,6 +1147,20 @@ bool supported_dims(int32_t d_k, int32_t d_v) {
     return d_k == d_v && (d_k == 64 || d_k == 128);
 }
 
+// The two-launch form trades the prefix launch (about 3 us of launch and
+// memory latency, whatever the pass) for workspace reads at the start of
+// output workgroups.  Those reads are bound by one CU's load rate (a block
+// late in a long view sums a dozen 16 KB slots before its first chunk), so
+// the form only pays for small passes.  Measured on MI355X (pass us, three
+// / two launches): 7,400 tokens 30.5 / 30.5 (58 MB of slot reads); four
+// requests of 27,187 tokens 85.4 / 83.4 (113 MB); one view of 18,000 with
+// 256 branches 100.9 / 131.1 (1.25 GB).  The threshold keeps the
+// three-launch form wherever the two were level or the reads are larger.
+constexpr double kTwoLaunchReadBytes = 16.0 * 1024 * 1024;
+bool two_launch_pays(const la_pass_info& info, int32_t H, int32_t d) {
+    return double(info.fused_slot_reads) * H * d * d * 4 <= kTwoLaunchReadBytes;
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
@@ -1136,9 +1177,11 @@ bool grids_fit(const la_pass_info& info, int32_t H) {
 }
 
 template <int D>
-la_status launch_all(int32_t stages, const void* q, const void* k, const void* v, la_dtype dtype, int32_t H,
-                     const la_pass_info& info, const int32_t* plan, const float* ext_state,
-                     void* out, float* final_state, float* ws, hipStream_t st) {
+la_status launch_all(int32_t stages, bool fused, const void* q, const void* k, const void* v,
+                     la_dtype dtype, int32_t H, const la_pass_info& info, const int32_t* plan,
+                     const float* ext_state, void* out, float* final_state, float* ws,
+                     hipStream_t st) {
+    const int fz = fused ? 1 : 0;
     const int32_t off_blocks = LA_PLAN_HEADER_WORDS;
     const int32_t off_delta = off_blocks + info.n_blocks * LA_PLAN_BLOCK_WORDS;
     const int32_t off_scan = off_delta + info.n_delta * LA_PLAN_DELTA_WORDS;
@@ -1163,7 +1206,7 @@ la_status launch_all(int32_t stages, const void* q, const void* k, const void* v
                                ws, H);
         if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
     }
-    if ((stages & LA_STAGE_PREFIX) && info.n_scan > 0) {
+    if ((stages & LA_STAGE_PREFIX) && !fused && info.n_scan > 0) {
         const dim3 grid(unsigned(int64_t(info.n_scan) * H * (D * D / kThreads)));
         hipLaunchKernelGGL(prefix_kernel<D>, grid, blk, 0, st, scans, ws, final_state, H);
         if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
@@ -1175,19 +1218,20 @@ la_status launch_all(int32_t stages, const void* q, const void* k, const void* v
             hipLaunchKernelGGL((output_kernel_bf16<D, O3>),
                                dim3(unsigned(split_grid<O3::NP_>(items))), dim3(O3::NT), 0, st,
                                static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                               static_cast<const uint16_t*>(v), blocks, ws, final_state,
-                               ext_state, static_cast<uint16_t*>(out), H, items);
+                               static_cast<const uint16_t*>(v), blocks, scans, ws,
+                               final_state, ext_state, static_cast<uint16_t*>(out), H, items,
+                               fz);
         else if (dtype == LA_F32_SPLIT)
             hipLaunchKernelGGL((output_kernel_split<D, O3>),
                                dim3(unsigned(split_grid<O3::NP_>(items))), dim3(O3::NT), 0, st,
                                static_cast<const float*>(q), static_cast<const float*>(k),
-                               static_cast<const float*>(v), blocks, ws, final_state, ext_state,
-                               static_cast<float*>(out), H, items);
+                               static_cast<const float*>(v), blocks, scans, ws, final_state,
+                               ext_state, static_cast<float*>(out), H, items, fz);
         else
             hipLaunchKernelGGL(output_kernel_f32<D>, dim3(unsigned(items)), blk, 0, st,
                                static_cast<const float*>(q), static_cast<const float*>(k),
-                               static_cast<const float*>(v), blocks, ws, final_state, ext_state,
-                               static_cast<float*>(out), H);
+                               static_cast<const float*>(v), blocks, scans, ws, final_state,
+                               ext_state, static_cast<float*>(out), H, fz);
         if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
     }
     return LA_OK;
@@ -1211,7 +1255,10 @@ extern "C" la_status la_scan_packed_stages(int32_t stages, const void* q, const 
                                            int32_t n_ext, void* out, float* final_state,
                                            void* workspace, size_t workspace_bytes,
                                            void* stream) {
-    if (!info || stages < 1 || stages > LA_STAGE_ALL) return LA_ERR_INVALID_ARG;
+    if (!info || (stages & ~(LA_STAGE_ALL | LA_FORM_TWO_LAUNCH | LA_FORM_THREE_LAUNCH)) ||
+        !(stages & LA_STAGE_ALL) ||
+        ((stages & LA_FORM_TWO_LAUNCH) && (stages & LA_FORM_THREE_LAUNCH)))
+        return LA_ERR_INVALID_ARG;
     if (dtype != LA_F32 && dtype != LA_BF16 && dtype != LA_F32_SPLIT) return LA_ERR_UNSUPPORTED;
     if (!supported_dims(d_k, d_v) || info->chunk != LA_CHUNK) return LA_ERR_UNSUPPORTED;
     if (H < 1 || info->n_tokens < 0 || info->n_blocks < 0 || info->n_delta < 0 ||
@@ -1239,9 +1286,21 @@ extern "C" la_status la_scan_packed_stages(int32_t stages, const void* q, const 
     if (need > 0 && (!workspace || workspace_bytes < need)) return LA_ERR_WORKSPACE;
     hipStream_t st = static_cast<hipStream_t>(stream);
     float* ws = static_cast<float*>(workspace);
+    const bool fused = (stages & LA_FORM_TWO_LAUNCH) ||
+                       (!(stages & LA_FORM_THREE_LAUNCH) && two_launch_pays(*info, H, d_k));
     if (d_k == 64)
-        return launch_all<64>(stages, q, k, v, dtype, H, *info, plan, ext_state, out, final_state, ws, st);
-    return launch_all<128>(stages, q, k, v, dtype, H, *info, plan, ext_state, out, final_state, ws, st);
+        return launch_all<64>(stages, fused, q, k, v, dtype, H, *info, plan, ext_state, out,
+                              final_state, ws, st);
+    return launch_all<128>(stages, fused, q, k, v, dtype, H, *info, plan, ext_state, out,
+                           final_state, ws, st);
+}
+
+extern "C" la_status la_scan_launches(const la_pass_info* info, int32_t H, int32_t d_k,
+                                      int32_t d_v, int32_t* n_launches) {
+    if (!info || !n_launches || H < 1) return LA_ERR_INVALID_ARG;
+    if (!supported_dims(d_k, d_v)) return LA_ERR_UNSUPPORTED;
+    *n_launches = two_launch_pays(*info, H, d_k) ? 2 : 3;
+    return LA_OK;
 }
 
 extern "C" la_status la_scan_packed(const void* q, const void* k, const void* v, la_dtype dtype,

@@ -55,14 +55,15 @@ __device__ __forceinline__ int wave_id() {
 }
 
 // Workspace slot layout: element e of a d x d state is stored at
-//   e = ((vb * NKB + kb) * 4 + j) * 64 + lane,   lane = 16 g + c
-// holding S[kb*16 + 4g + j][vb*16 + c]: one coalesced 256-byte row per
-// (tile, j) for the lane order of the accumulator layout.
+//   e = ((vb * NKB + kb) * 64 + lane) * 4 + j,   lane = 16 g + c
+// holding S[kb*16 + 4g + j][vb*16 + c]: each lane keeps the 4 values of an
+// accumulator tile in one 16-byte piece, and a tile is one coalesced
+// 1 KB row of the slot.
 template <int D>
 __device__ __forceinline__ void slot_to_rc(int e, int& row, int& col) {
     constexpr int NKB = D / 16;
-    const int lane = e & 63;
-    const int j = (e >> 6) & 3;
+    const int j = e & 3;
+    const int lane = (e >> 2) & 63;
     const int kb = (e >> 8) % NKB;
     const int vb = (e >> 8) / NKB;
     row = kb * 16 + 4 * (lane >> 4) + j;

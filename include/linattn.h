@@ -96,7 +96,11 @@ typedef struct {
     int32_t n_scan;           /* segments launch 2 scans                       */
     int32_t plan_words;       /* int32 words of the plan                       */
     int32_t max_seg_tokens;   /* longest segment                               */
-    int32_t reserved[9];
+    int32_t fused_slot_reads; /* workspace slots read per head by the output
+                                 launch when it sums the block states itself
+                                 (two-launch form, see la_scan_packed),
+                                 saturated at INT32_MAX                        */
+    int32_t reserved[8];
 } la_pass_info;
 
 /*
@@ -126,18 +130,27 @@ typedef struct {
  * Errors: LA_ERR_INVALID_ARG (bad table), LA_ERR_UNSUPPORTED (chunk).
  *
  * Plan layout (int32 words):
- *   [0..15]   header: magic, version 1, n_blocks, n_delta, n_scan, chunk,
+ *   [0..15]   header: magic, version 2, n_blocks, n_delta, n_scan, chunk,
  *             block_chunks, n_tokens, off_blocks, off_delta, off_scan, n_ext,
- *             n_views, 0, 0, 0
- *   blocks    n_blocks x 8: {tok0, ntok, sin_slot, delta_slot, seed, seg, 0, 0}
+ *             n_views, fused_slot_reads, 0, 0
+ *   blocks    n_blocks x 8:
+ *             {tok0, ntok, sin_slot, delta_slot, seed, seg, slot0, final_row}
  *             sin_slot   workspace slot holding the segment-local state before
- *                        the block, -1 for a segment's first block
+ *                        the block (after the prefix launch), -1 for a
+ *                        segment's first block
  *             delta_slot slot that launch 1 fills with the block's own
  *                        sum of k_t^T v_t, -1 if no later block needs it
  *             seed       -1: start from zero (view); v >= 0: start from
  *                        final_state row v; <= -2: ext_state row -seed-2
+ *             slot0      first slot of the block's segment (-1: none); in the
+ *                        two-launch form the block sums slots slot0 ..
+ *                        sin_slot itself
+ *             final_row  final_state row that a view's last block writes in
+ *                        the two-launch form; -1 for every other block
  *   delta     n_delta x 4: {tok0, ntok, slot, seg}
- *   scan      n_scan x 4:  {first_slot, n_slots, final_row (-1: branch), seg}
+ *   scan      n_scan x 4:  {first_slot, n_slots, final_row (-1: branch), seg};
+ *             the first n_views entries are the views, in ordinal order (the
+ *             two-launch form finds a branch's view slots at scan[seed])
  * View blocks come first (longest work first), then branch blocks.
  */
 la_status la_plan_segments(int32_t n_segments, const int32_t* seg_offsets,
@@ -211,6 +224,11 @@ la_status la_scan_workspace_size(const la_pass_info* info, int32_t H, int32_t d_
  *   3. per work block and head, chunk by chunk: o = q S_in + (causal
  *      (q k^T)) v, carrying S in registers; branch blocks start from
  *      final_state of their view or from ext_state.
+ * For passes whose block states are few (la_pass_info.fused_slot_reads x H
+ * x d_k x d_v x 4 bytes up to 16 MiB) launch 2 is left out: each launch-3
+ * workgroup sums the block states before it (and a branch those of its view)
+ * itself, and each view's last block writes final_state.  Both forms add the
+ * states in the same order and give the same bits.
  *
  *   q, k           device [T][H][d_k], dtype
  *   v              device [T][H][d_v], dtype
@@ -237,21 +255,38 @@ la_status la_scan_packed(const void* q, const void* k, const void* v, la_dtype d
                          void* out, float* final_state, void* workspace,
                          size_t workspace_bytes, void* stream);
 
+/*
+ * la_scan_launches -- the form la_scan_packed picks for a pass: 2 (no prefix
+ * launch) or 3, written to *n_launches.  Host only; no device work.
+ * Errors: LA_ERR_INVALID_ARG (NULL, H < 1), LA_ERR_UNSUPPORTED (head dims).
+ */
+la_status la_scan_launches(const la_pass_info* info, int32_t H, int32_t d_k, int32_t d_v,
+                           int32_t* n_launches);
+
 /* Launch selection bits for la_scan_packed_stages. */
 #define LA_STAGE_STATES 1     /* launch 1: per-block states          */
 #define LA_STAGE_PREFIX 2     /* launch 2: segmented prefix          */
 #define LA_STAGE_OUTPUT 4     /* launch 3: chunk outputs             */
 #define LA_STAGE_ALL 7
+/* Form of the scan, for la_scan_packed_stages (at most one of the two; with
+ * neither the library picks the form from the pass shape). */
+#define LA_FORM_TWO_LAUNCH 8    /* no prefix launch: each output workgroup sums
+                                   the block states it needs itself        */
+#define LA_FORM_THREE_LAUNCH 16 /* the prefix launch runs between 1 and 3   */
 
 /*
  * la_scan_packed_stages -- la_scan_packed restricted to the launches whose
  * bits are set in `stages` (LA_STAGE_*), with the same arguments and checks.
  * For profiling one launch in isolation.  Launch 2 rewrites the workspace in
  * place, so it must follow a launch 1 on the same buffers; launch 3 only
- * reads the workspace and final_state, so after one complete pass it may be
- * repeated alone and produces the same out.  la_scan_packed(...) is
+ * reads the workspace (and, in the three-launch form, final_state), so after
+ * one complete pass it may be repeated alone and produces the same out.  One
+ * of LA_FORM_TWO_LAUNCH / LA_FORM_THREE_LAUNCH may be or-ed in to force the
+ * form (in the two-launch form the LA_STAGE_PREFIX bit does nothing); every
+ * call on one workspace must use the same form.  la_scan_packed(...) is
  * la_scan_packed_stages(LA_STAGE_ALL, ...).
- * Errors: as la_scan_packed, plus LA_ERR_INVALID_ARG for stages outside 1..7.
+ * Errors: as la_scan_packed, plus LA_ERR_INVALID_ARG when no LA_STAGE_* bit
+ * is set, an unknown bit is set, or both LA_FORM_* bits are set.
  */
 la_status la_scan_packed_stages(int32_t stages, const void* q, const void* k, const void* v,
                                 la_dtype dtype, int32_t H, int32_t d_k, int32_t d_v,

@@ -52,7 +52,7 @@ def _check_plan(plan, so, bp, vo):
     list covers views plus branches with >= 2 slots."""
     info, P = plan.info, plan.plan
     G, C = info.block_chunks, info.chunk
-    assert P[0] == 0x4C41504E and P[1] == 1
+    assert P[0] == 0x4C41504E and P[1] == 2
     assert (P[2], P[3], P[4]) == (info.n_blocks, info.n_delta, info.n_scan)
     ob, od, osc = P[8], P[9], P[10]
     blocks = P[ob:ob + 8 * info.n_blocks].reshape(-1, 8)
@@ -61,20 +61,36 @@ def _check_plan(plan, so, bp, vo):
     assert osc + 4 * info.n_scan == info.plan_words
     cover = np.zeros(info.n_tokens, dtype=np.int64)
     seg_blocks = {}
-    for tok0, ntok, sin, dsl, seed, seg, _, _ in blocks:
+    fused_reads = 0
+    for tok0, ntok, sin, dsl, seed, seg, slot0, frow in blocks:
         assert 1 <= ntok <= G * C
         assert so[seg] <= tok0 and tok0 + ntok <= so[seg + 1]
         cover[tok0:tok0 + ntok] += 1
-        seg_blocks.setdefault(seg, []).append((tok0, sin, dsl, seed))
+        seg_blocks.setdefault(seg, []).append((tok0, sin, dsl, seed, slot0, frow))
         p = bp[seg]
         assert seed == (-1 if p == -1 else (vo[p] if p >= 0 else p))
+        # two-launch form: own prefix = slots slot0 .. sin; a branch's seed =
+        # the slots of its view's scan entry, which sits at index vo[p]
+        j = (tok0 - so[seg]) // (G * C)
+        if sin >= 0:
+            assert slot0 >= 0 and sin - slot0 + 1 == j
+        fused_reads += j
+        if p >= 0:
+            first, n, frow_v, seg_v = scans[vo[p]]
+            assert seg_v == p and frow_v == vo[p]
+            fused_reads += n
+        last = tok0 + ntok == so[seg + 1]
+        assert frow == (vo[seg] if (p == -1 and last) else -1)
+        if frow >= 0:
+            fused_reads += 1
     assert np.all(cover == 1)
+    assert info.fused_slot_reads == fused_reads == P[13]
     dl = {int(r[2]): r for r in deltas}
     seen_views = 0
     for seg, bl in seg_blocks.items():
         bl.sort()
         first = None
-        for j, (tok0, sin, dsl, seed) in enumerate(bl):
+        for j, (tok0, sin, dsl, seed, slot0, _) in enumerate(bl):
             assert tok0 == so[seg] + j * G * C
             if j == 0:
                 assert sin == -1
@@ -83,6 +99,7 @@ def _check_plan(plan, so, bp, vo):
             if dsl >= 0:
                 first = dsl - j if first is None else first
                 assert dsl == first + j and dl[dsl][0] == tok0
+                assert slot0 == first
         if bp[seg] == -1:
             seen_views += 1
             assert all(b[2] >= 0 for b in bl)
@@ -206,3 +223,28 @@ def test_scan_rejects_bad_arguments_before_launch():
     assert st == la.LA_ERR_INVALID_ARG
     assert lib.la_export_view_state(fake, 3, 2, 2, 64, 64, fake, None) == la.LA_ERR_INVALID_ARG
     assert lib.la_export_view_state(fake, 0, 2, 2, 96, 96, fake, None) == la.LA_ERR_UNSUPPORTED
+
+
+def test_scan_launches_by_pass_shape():
+    """The two-launch form is taken while the workspace reads it adds stay
+    small (fused_slot_reads x H x d^2 x 4 bytes up to 16 MiB): the 628-token
+    pass qualifies; the 7,400-token pass (one view of 15 blocks, 8 one-block
+    branches: 58 MB) and the view of 18,000 tokens with 256 branches (each
+    branch reading all view slots) do not."""
+    w7 = synth.shapes("view7400_br8x48_h16_d64_bf16")
+    p7 = la.pack(*w7, heads=16)
+    nb = -(-7400 // (64 * p7.info.block_chunks))
+    assert p7.info.fused_slot_reads == nb * (nb - 1) // 2 + 1 + 8 * nb
+    assert la.scan_launches(p7, 16, 64) == 3
+    w1 = synth.shapes("view500_br4x32_h2_d64_f32")
+    assert la.scan_launches(la.pack(*w1, heads=2), 2, 64) == 2
+    w4 = synth.shapes("view18000_br256x32-128_h16_d64_bf16")
+    assert la.scan_launches(la.pack(*w4, heads=16), 16, 64) == 3
+    # a view of two one-chunk blocks: the second block reads the first slot,
+    # and its own to write final_state
+    p1 = la.pack([100], [0], [], block_chunks=1)
+    assert p1.info.fused_slot_reads == 1 + 1 and la.scan_launches(p1, 1, 64) == 2
+    with pytest.raises(la.LinAttnError):
+        la.scan_launches(p1, 0, 64)
+    with pytest.raises(la.LinAttnError):
+        la.scan_launches(p1, 1, 96)
