@@ -488,16 +488,30 @@ struct LaunchCfg<128> {
     using O3 = Out3<128, LA_OUT_NP_128, LA_OUT_NW_128>;
 };
 
-// The outputs of one wave for one chunk: its 16 tokens (token block TB) and
-// VBH feature tiles starting at vb0.  Specialised per TB so that the causal
-// structure (TB + 1 score tiles, TB / 2 + 1 intra-chunk steps) is known at
-// compile time and every loop runs over independent accumulators with its
-// LDS fragments loaded in batches.
+// Output feature order of the bf16 output launch (64 output features per
+// workgroup, 4 output tiles per wave): row 4 g + j of output tile x holds
+// feature 32 (x >> 1) + 8 g + 4 (x & 1) + j, so lane group g ends with
+// features 8 g .. 8 g + 7 (tiles 0, 1) and 32 + 8 g .. 32 + 8 g + 7 (tiles
+// 2, 3) of its token: two 16-byte stores, and the four lane groups of a token
+// cover 64 contiguous bytes of its row per store.  The A operands follow:
+// V^T rows are read in that order, and S^T is published at LDS row
+// out_row(f), which puts the feature that A-operand lane c of tile x needs at
+// row 16 x + c.
+__device__ __forceinline__ int out_row(int f) {
+    return 32 * (f >> 5) + 16 * ((f >> 2) & 1) + 4 * ((f >> 3) & 3) + (f & 3);
+}
+
+// The outputs of one wave for one chunk: its 16 tokens (token block TB), all
+// 64 output features of the workgroup in the order above.  Specialised per
+// TB so that the causal structure (TB + 1 score tiles, TB / 2 + 1
+// intra-chunk steps) is known at compile time and every loop runs over
+// independent accumulators with its LDS fragments loaded in batches.
 template <int D, int TB, int VBH, int LDV>
 __device__ __forceinline__ void out_tiles(const uint16_t* sK, const uint16_t* sV,
                                           const uint16_t* sSh, const uint16_t* sSl,
-                                          const u32x4 (&qf)[D / 32], int vb0, int g, int c16,
+                                          const u32x4 (&qf)[D / 32], int g, int c16,
                                           f32x4 (&acc)[VBH]) {
+    static_assert(VBH == 4, "one wave covers the 64 output features of its workgroup");
     constexpr int NKS = D / 32;
     constexpr int LDR = Stage<D, 4>::LDR;
     // P^T tiles (ub, TB), ub <= TB: P^T[u][t] = sum_d K[u][d] Q[t][d]
@@ -530,8 +544,8 @@ __device__ __forceinline__ void out_tiles(const uint16_t* sK, const uint16_t* sV
         u32x4 ah[VBH], al[VBH];
 #pragma unroll
         for (int x = 0; x < VBH; ++x) {
-            const int f = (vb0 + x) * 16 + c16;
-            const int o = f * LDR + scol<D>(f, ks * 32 + 8 * g);
+            const int row = x * 16 + c16;
+            const int o = row * LDR + scol<D>(row, ks * 32 + 8 * g);
             ah[x] = lds_u32x4(sSh + o);
             al[x] = lds_u32x4(sSl + o);
         }
@@ -547,8 +561,11 @@ __device__ __forceinline__ void out_tiles(const uint16_t* sK, const uint16_t* sV
         u32x4 av[VBH];
 #pragma unroll
         for (int x = 0; x < VBH; ++x) {
-            const int vb = vb0 + x;
-            av[x] = tr_frag(sV, LDV, vb * 16, pp, g, c16);
+            // as tr_frag, with lane c of the tile receiving feature
+            // 32 (x >> 1) + 8 (c >> 2) + 4 (x & 1) + (c & 3)
+            const uint16_t* pv = sV + (4 * g + (c16 >> 2)) * LDV + 32 * (x >> 1) +
+                                 8 * (c16 & 3) + 4 * (x & 1);
+            av[x] = cat2(lds_tr4(pv + (2 * pp) * 16 * LDV), lds_tr4(pv + (2 * pp + 1) * 16 * LDV));
         }
 #pragma unroll
         for (int x = 0; x < VBH; ++x) acc[x] = mfma_bf16(av[x], bp, acc[x]);
@@ -568,7 +585,11 @@ __global__ __launch_bounds__(O3::NT) void output_kernel_bf16(
     constexpr int DD = D * D;
     constexpr int NPER = KVStage<D, DV, R, NT>::NPER;
     constexpr int LDR = ST::LDR;
-    constexpr int LDV = ST::template LDV<DV>;
+    // V rows of 192 bytes: the permuted V^T fragment reads of out_tiles (8-byte
+    // pieces 16 bytes apart on four rows) and the carry's reads both hit every
+    // LDS bank at most once per 128 bytes
+    constexpr int LDV = DV + 32;
+    static_assert(DV == 64 && O3::NHV == 1, "one feature part of 64 per workgroup");
     __shared__ __attribute__((aligned(16))) uint16_t sK[kChunk * LDR];   // K, row-major
     __shared__ __attribute__((aligned(16))) uint16_t sV[kChunk * LDV];   // V part, row-major
     __shared__ __attribute__((aligned(16))) uint16_t sSh[DV * LDR];   // S^T, bf16 high term
@@ -580,7 +601,7 @@ __global__ __launch_bounds__(O3::NT) void output_kernel_bf16(
     const int h = item % H;
     const BlockDesc bd = blocks[item / H];
     const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, g = lane >> 4, c16 = lane & 15;
-    const int tb = w & 3, hv = w >> 2;
+    const int tb = w & 3;
     const int vbo = O3::vb_own(w), kbo = O3::kb0(w);   // vbo local to the part
     const int vbg = part * NVB + vbo;                   // global column block
 
@@ -590,8 +611,7 @@ __global__ __launch_bounds__(O3::NT) void output_kernel_bf16(
     // row pieces inside a chunk window
     const int trow = tb * 16 + c16;
     const uint32_t qoff = uint32_t(((trow * H + h) * D + 8 * g) * 2);
-    const uint32_t ooff =
-        uint32_t(((trow * H + h) * D + part * DV + hv * VBH * 16 + 4 * g) * 2);
+    const uint32_t ooff = uint32_t(((trow * H + h) * D + part * DV + 8 * g) * 2);
     const int vcg0 = part * (DV / 8);
 
     // one chunk in flight: kv / qn hold chunk c + 1 while chunk c is computed
@@ -631,11 +651,12 @@ __global__ __launch_bounds__(O3::NT) void output_kernel_bf16(
             const uint32_t h01 = cvt_bf2(s[0], s[1]), h23 = cvt_bf2(s[2], s[3]);
             const uint32_t l01 = cvt_bf2(s[0] - bf_lo(h01), s[1] - bf_hi(h01));
             const uint32_t l23 = cvt_bf2(s[2] - bf_lo(h23), s[3] - bf_hi(h23));
-            const int off = (vbo * 16 + c16) * LDR + scol<D>(vbo * 16 + c16, (kbo + i) * 16 + 4 * g);
+            const int row = out_row(vbo * 16 + c16);
+            const int off = row * LDR + scol<D>(row, (kbo + i) * 16 + 4 * g);
             *reinterpret_cast<u32x2*>(sSh + off) = u32x2{h01, h23};
             *reinterpret_cast<u32x2*>(sSl + off) = u32x2{l01, l23};
         }
-        stage_kv_rows<D, DV, R, NT, NPER>(kv, sK, sV);
+        stage_kv_rows<D, DV, R, NT, NPER, LDV>(kv, sK, sV);
     };
     // The loop is rotated: chunk c + 1 is staged (and its q moved to qf) at
     // the end of iteration c, right after chunk c's output stores.  Its loads
@@ -654,21 +675,24 @@ __global__ __launch_bounds__(O3::NT) void output_kernel_bf16(
         const int rows = min(kChunk, bd.ntok - c * kChunk);
         const int64_t first = (int64_t(bd.tok0) + c * kChunk) * row_elems;
 
-        // O^T tiles: this wave's 16 tokens, local feature tiles hv*VBH .. +VBH-1
+        // O^T tiles: this wave's 16 tokens, the workgroup's 64 output features
         f32x4 acc[VBH];
         switch (tb) {
-            case 0: out_tiles<D, 0, VBH, LDV>(sK, sV, sSh, sSl, qf, hv * VBH, g, c16, acc); break;
-            case 1: out_tiles<D, 1, VBH, LDV>(sK, sV, sSh, sSl, qf, hv * VBH, g, c16, acc); break;
-            case 2: out_tiles<D, 2, VBH, LDV>(sK, sV, sSh, sSl, qf, hv * VBH, g, c16, acc); break;
-            default: out_tiles<D, 3, VBH, LDV>(sK, sV, sSh, sSl, qf, hv * VBH, g, c16, acc); break;
+            case 0: out_tiles<D, 0, VBH, LDV>(sK, sV, sSh, sSl, qf, g, c16, acc); break;
+            case 1: out_tiles<D, 1, VBH, LDV>(sK, sV, sSh, sSl, qf, g, c16, acc); break;
+            case 2: out_tiles<D, 2, VBH, LDV>(sK, sV, sSh, sSl, qf, g, c16, acc); break;
+            default: out_tiles<D, 3, VBH, LDV>(sK, sV, sSh, sSl, qf, g, c16, acc); break;
         }
-        // lane holds O[t = tb*16 + c16][part*DV + (hv*VBH + x)*16 + 4g + j], j = 0..3
+        // lane holds O[t = tb*16 + c16][part*DV + 32 (x >> 1) + 8g + 4 (x & 1) + j]
         {
             const auto ro = chunk_rsrc(out, first, 2, rows, H, D);
 #pragma unroll
-            for (int x = 0; x < VBH; ++x)
-                buf_store8(ro, ooff + x * 32,
-                           u32x2{cvt_bf2(acc[x][0], acc[x][1]), cvt_bf2(acc[x][2], acc[x][3])});
+            for (int y = 0; y < 2; ++y)
+                buf_store16u(ro, ooff + y * 64,
+                             u32x4{cvt_bf2(acc[2 * y][0], acc[2 * y][1]),
+                                   cvt_bf2(acc[2 * y][2], acc[2 * y][3]),
+                                   cvt_bf2(acc[2 * y + 1][0], acc[2 * y + 1][1]),
+                                   cvt_bf2(acc[2 * y + 1][2], acc[2 * y + 1][3])});
         }
         if (c + 1 >= nch) break;   // no carry and no staging after the last chunk
         // carry: S += K^T V for this wave's tiles

@@ -96,6 +96,9 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t o
 __device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 x) {
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, x), r, off, 0, 0);
 }
+__device__ __forceinline__ void buf_store16u(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 x) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, x), r, off, 0, 0);
+}
 __device__ __forceinline__ void buf_store8(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x2 x) {
     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, x), r, off, 0, 0);
 }
@@ -276,7 +279,8 @@ __device__ __forceinline__ void load_kv(BlkR<R> (&pre)[NPER], __amdgpu_buffer_rs
 // Registers -> LDS, both tiles row-major: K rows into sK (stride LDR), the
 // workgroup's DVW features of V into sV (stride LDR of a DVW-wide tile);
 // transposed operands are then read with tr_frag.
-template <int D, int DVW, int R, int NT, int NPER>
+template <int D, int DVW, int R, int NT, int NPER,
+          int LDVS = Stage<D, R>::template LDV<DVW>>
 __device__ __forceinline__ void stage_kv_rows(const BlkR<R> (&pre)[NPER], uint16_t* sK,
                                               uint16_t* sV) {
     using KS = KVStage<D, DVW, R, NT>;
@@ -289,7 +293,7 @@ __device__ __forceinline__ void stage_kv_rows(const BlkR<R> (&pre)[NPER], uint16
             if (b0 >= KS::NBK + KS::NBV) break;
         if (b0 >= KS::NBK) {
             const int wv = b0 - KS::NBK + lane;
-            store_rows<R>(sV, pre[i], wv / KS::NCGV, wv % KS::NCGV, Stage<D, R>::template LDV<DVW>);
+            store_rows<R>(sV, pre[i], wv / KS::NCGV, wv % KS::NCGV, LDVS);
         } else {
             const int wk = b0 + lane;
             store_rows<R>(sK, pre[i], wk / KS::NCGK, wk % KS::NCGK, Stage<D, R>::LDR);
