@@ -348,7 +348,8 @@ __global__ __launch_bounds__(kThreads) void prefix_kernel(const ScanDesc* __rest
 // its own slot, to final_state.  Both forms add in the same order as the
 // prefix launch (from zero, one slot after the other), so they give the same
 // bits, and a branch's seed equals the final_state written for its view.
-template <int D, int NT>
+// B slots of loads in flight per batch (B * NT 16-byte pieces per lane).
+template <int D, int NT, int B>
 __device__ __forceinline__ void sum_slots(f32x4 (&acc)[NT], const int (&tix)[NT],
                                           const float* __restrict__ ws, int first, int n, int H,
                                           int h, int lane) {
@@ -357,9 +358,6 @@ __device__ __forceinline__ void sum_slots(f32x4 (&acc)[NT], const int (&tix)[NT]
     const f32x4* p = reinterpret_cast<const f32x4*>(ws) + (int64_t(first) * H + h) * SLOT4 + lane;
 #pragma unroll
     for (int i = 0; i < NT; ++i) acc[i] = zero4();
-    // B slots of loads in flight: 16 pieces per lane at most, so the batch
-    // does not raise the register count of the kernels around it
-    constexpr int B = NT >= 16 ? 1 : 16 / NT;
     int s = 0;
     for (; s + B <= n; s += B) {
         f32x4 x[B][NT];
@@ -377,11 +375,15 @@ __device__ __forceinline__ void sum_slots(f32x4 (&acc)[NT], const int (&tix)[NT]
         for (int i = 0; i < NT; ++i) acc[i] += p[s * stride + tix[i] * 64];
 }
 
-template <int D, int NT>
+// The slot sums of the two-launch form keep B slots of loads in flight: 16
+// pieces per lane (the register count of the kernels stays that of the
+// three-launch form) or, where the kernel has registers to spare, 32.
+template <int D, int NT, bool FUSED, int B = (NT >= 16 ? 1 : 16 / NT)>
 __device__ __forceinline__ void block_init_state(
     f32x4 (&S)[NT], const int (&tix)[NT], const BlockDesc& bd, const ScanDesc* __restrict__ scans,
     const float* __restrict__ ws, float* __restrict__ final_state,
-    const float* __restrict__ ext_state, int H, int h, int lane, bool fused) {
+    const float* __restrict__ ext_state, int H, int h, int lane) {
+    constexpr bool fused = FUSED;
     constexpr int NKB = D / 16, DD = D * D;
     const int g = lane >> 4, c16 = lane & 15;
     // row-major [D][D] seed (final_state or ext_state row) into the tiles
@@ -398,17 +400,17 @@ __device__ __forceinline__ void block_init_state(
     if (bd.seed <= -2) {
         read_rows(ext_state + ((int64_t)(-bd.seed - 2) * H + h) * DD);
     } else if (bd.seed >= 0) {
-        if (fused) {
+        if constexpr (fused) {
             const ScanDesc sc = scans[bd.seed];
-            sum_slots<D, NT>(S, tix, ws, sc.first_slot, sc.n_slots, H, h, lane);
+            sum_slots<D, NT, B>(S, tix, ws, sc.first_slot, sc.n_slots, H, h, lane);
         } else {
             read_rows(final_state + ((int64_t)bd.seed * H + h) * DD);
         }
     }
     if (bd.sin_slot >= 0) {
         f32x4 own[NT];
-        if (fused) {
-            sum_slots<D, NT>(own, tix, ws, bd.slot0, bd.sin_slot - bd.slot0 + 1, H, h, lane);
+        if constexpr (fused) {
+            sum_slots<D, NT, B>(own, tix, ws, bd.slot0, bd.sin_slot - bd.slot0 + 1, H, h, lane);
         } else {
             const f32x4* p = reinterpret_cast<const f32x4*>(ws + ((int64_t)bd.sin_slot * H + h) * DD);
 #pragma unroll
@@ -572,13 +574,13 @@ __device__ __forceinline__ void out_tiles(const uint16_t* sK, const uint16_t* sV
     }
 }
 
-template <int D, class O3>
+template <int D, class O3, bool FUSED>
 __global__ __launch_bounds__(O3::NT) void output_kernel_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const BlockDesc* __restrict__ blocks,
     const ScanDesc* __restrict__ scans, const float* __restrict__ ws,
     float* __restrict__ final_state, const float* __restrict__ ext_state,
-    uint16_t* __restrict__ out, int H, int n_items, int fused) {
+    uint16_t* __restrict__ out, int H, int n_items) {
     constexpr int R = O3::R, NT = O3::NT, NP = O3::NP_, DV = O3::DV;
     using ST = Stage<D, R>;
     constexpr int NKB = O3::NKB, NVB = O3::NVB, NKS = O3::NKS, VBH = O3::VBH, TPW = O3::TPW;
@@ -637,8 +639,9 @@ __global__ __launch_bounds__(O3::NT) void output_kernel_bf16(
         int tix[TPW];
 #pragma unroll
         for (int i = 0; i < TPW; ++i) tix[i] = vbg * NKB + kbo + i;
-        block_init_state<D, TPW>(S, tix, bd, scans, ws, final_state, ext_state, H, h, lane,
-                                 fused != 0);
+        // at d = 64 the two-launch kernel has registers for 8 slots in flight
+        block_init_state<D, TPW, FUSED, (FUSED && D == 64 ? 8 : 16 / TPW)>(
+            S, tix, bd, scans, ws, final_state, ext_state, H, h, lane);
     }
 
     // LDS inputs of one chunk: S^T = S_hi + S_lo (bf16 terms) for the
@@ -683,16 +686,30 @@ __global__ __launch_bounds__(O3::NT) void output_kernel_bf16(
             case 2: out_tiles<D, 2, VBH, LDV>(sK, sV, sSh, sSl, qf, g, c16, acc); break;
             default: out_tiles<D, 3, VBH, LDV>(sK, sV, sSh, sSl, qf, g, c16, acc); break;
         }
-        // lane holds O[t = tb*16 + c16][part*DV + 32 (x >> 1) + 8g + 4 (x & 1) + j]
+        // lane holds O[t = tb*16 + c16][part*DV + 32 (x >> 1) + 8g + 4 (x & 1) + j]:
+        // piece A (features 8g ..) and piece B (32 + 8g ..) of its token.  Lanes
+        // of neighbouring tokens (c16, c16 ^ 1) swap one piece, so that each of
+        // the two stores writes whole 128-byte feature rows (one token each from
+        // 8 lanes): the even token's row in the first, the odd token's in the
+        // second.
         {
             const auto ro = chunk_rsrc(out, first, 2, rows, H, D);
+            u32x4 pc[2];
 #pragma unroll
             for (int y = 0; y < 2; ++y)
-                buf_store16u(ro, ooff + y * 64,
-                             u32x4{cvt_bf2(acc[2 * y][0], acc[2 * y][1]),
-                                   cvt_bf2(acc[2 * y][2], acc[2 * y][3]),
-                                   cvt_bf2(acc[2 * y + 1][0], acc[2 * y + 1][1]),
-                                   cvt_bf2(acc[2 * y + 1][2], acc[2 * y + 1][3])});
+                pc[y] = u32x4{cvt_bf2(acc[2 * y][0], acc[2 * y][1]),
+                              cvt_bf2(acc[2 * y][2], acc[2 * y][3]),
+                              cvt_bf2(acc[2 * y + 1][0], acc[2 * y + 1][1]),
+                              cvt_bf2(acc[2 * y + 1][2], acc[2 * y + 1][3])};
+            const bool odd = (c16 & 1) != 0;
+            const u32x4 give = odd ? pc[0] : pc[1];
+            u32x4 got;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)   // quad_perm [1, 0, 3, 2]: lane c16 ^ 1
+                got[i] = __builtin_amdgcn_mov_dpp(int(give[i]), 0xB1, 0xF, 0xF, false);
+            const uint32_t row_bytes = uint32_t(H * D * 2);
+            buf_store16u(ro, odd ? ooff - row_bytes + 64 : ooff, odd ? got : pc[0]);
+            buf_store16u(ro, odd ? ooff + 64 : ooff + row_bytes, odd ? pc[1] : got);
         }
         if (c + 1 >= nch) break;   // no carry and no staging after the last chunk
         // carry: S += K^T V for this wave's tiles
@@ -710,12 +727,12 @@ __global__ __launch_bounds__(O3::NT) void output_kernel_bf16(
     }
 }
 
-template <int D>
+template <int D, bool FUSED>
 __global__ __launch_bounds__(kThreads) void output_kernel_f32(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const BlockDesc* __restrict__ blocks, const ScanDesc* __restrict__ scans,
     const float* __restrict__ ws, float* __restrict__ final_state,
-    const float* __restrict__ ext_state, float* __restrict__ out, int H, int fused) {
+    const float* __restrict__ ext_state, float* __restrict__ out, int H) {
     using TL = F32Tiles<D>;
     constexpr int NKB = D / 16, VBW = D / 64;
     __shared__ __attribute__((aligned(16))) float sQ[kChunk * TL::LD];
@@ -735,8 +752,8 @@ __global__ __launch_bounds__(kThreads) void output_kernel_f32(
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) tix[x * NKB + kb] = (w * VBW + x) * NKB + kb;
         f32x4 Sf[VBW * NKB];
-        block_init_state<D, VBW * NKB>(Sf, tix, bd, scans, ws, final_state, ext_state, H, h,
-                                       lane, fused != 0);
+        block_init_state<D, VBW * NKB, FUSED>(Sf, tix, bd, scans, ws, final_state, ext_state,
+                                              H, h, lane);
 #pragma unroll
         for (int x = 0; x < VBW; ++x)
 #pragma unroll
@@ -1036,13 +1053,12 @@ __device__ __forceinline__ void out_tiles_split(const uint16_t* sKh, const uint1
 }
 
 // Launch 3, split precision: as output_kernel_bf16 (same launch shape O3).
-template <int D, class O3>
+template <int D, class O3, bool FUSED>
 __global__ __launch_bounds__(O3::NT) void output_kernel_split(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const BlockDesc* __restrict__ blocks, const ScanDesc* __restrict__ scans,
     const float* __restrict__ ws, float* __restrict__ final_state,
-    const float* __restrict__ ext_state, float* __restrict__ out, int H, int n_items,
-    int fused) {
+    const float* __restrict__ ext_state, float* __restrict__ out, int H, int n_items) {
     constexpr int R = O3::R, NT = O3::NT, NP = O3::NP_, DV = O3::DV;
     using ST = Stage<D, R>;
     constexpr int NKB = O3::NKB, NVB = O3::NVB, NKS = O3::NKS, VBH = O3::VBH, TPW = O3::TPW;
@@ -1098,8 +1114,8 @@ __global__ __launch_bounds__(O3::NT) void output_kernel_split(
         int tix[TPW];
 #pragma unroll
         for (int i = 0; i < TPW; ++i) tix[i] = vbg * NKB + kbo + i;
-        block_init_state<D, TPW>(S, tix, bd, scans, ws, final_state, ext_state, H, h, lane,
-                                 fused != 0);
+        block_init_state<D, TPW, FUSED>(S, tix, bd, scans, ws, final_state, ext_state, H, h,
+                                        lane);
     }
 
     auto publish_and_stage = [&]() {
@@ -1173,14 +1189,13 @@ bool supported_dims(int32_t d_k, int32_t d_v) {
 
 // The two-launch form trades the prefix launch (about 3 us of launch and
 // memory latency, whatever the pass) for workspace reads at the start of
-// output workgroups.  Those reads are bound by one CU's load rate (a block
-// late in a long view sums a dozen 16 KB slots before its first chunk), so
-// the form only pays for small passes.  Measured on MI355X (pass us, three
-// / two launches): 7,400 tokens 30.5 / 30.5 (58 MB of slot reads); four
-// requests of 27,187 tokens 85.4 / 83.4 (113 MB); one view of 18,000 with
-// 256 branches 100.9 / 131.1 (1.25 GB).  The threshold keeps the
-// three-launch form wherever the two were level or the reads are larger.
-constexpr double kTwoLaunchReadBytes = 16.0 * 1024 * 1024;
+// output workgroups, bound by one CU's load rate (a block late in a long view
+// sums a dozen 16 KB slots before its first chunk).  Measured on MI355X,
+// pass us with three / two launches: 628 tokens (fp32) 16.9 / 15.7; 7,400
+// tokens 29.1-29.4 / 28.2 (58 MB of slot reads); four requests of 27,187
+// tokens 79.3 / 77.0 (113 MB); one view of 18,000 with 256 branches
+// 100.9 / 131.1 (1.25 GB).
+constexpr double kTwoLaunchReadBytes = 128.0 * 1024 * 1024;
 bool two_launch_pays(const la_pass_info& info, int32_t H, int32_t d) {
     return double(info.fused_slot_reads) * H * d * d * 4 <= kTwoLaunchReadBytes;
 }
@@ -1205,7 +1220,6 @@ la_status launch_all(int32_t stages, bool fused, const void* q, const void* k, c
                      la_dtype dtype, int32_t H, const la_pass_info& info, const int32_t* plan,
                      const float* ext_state, void* out, float* final_state, float* ws,
                      hipStream_t st) {
-    const int fz = fused ? 1 : 0;
     const int32_t off_blocks = LA_PLAN_HEADER_WORDS;
     const int32_t off_delta = off_blocks + info.n_blocks * LA_PLAN_BLOCK_WORDS;
     const int32_t off_scan = off_delta + info.n_delta * LA_PLAN_DELTA_WORDS;
@@ -1238,24 +1252,26 @@ la_status launch_all(int32_t stages, bool fused, const void* q, const void* k, c
     if ((stages & LA_STAGE_OUTPUT) && info.n_blocks > 0) {
         const int items = info.n_blocks * H;
         using O3 = typename LaunchCfg<D>::O3;
-        if (dtype == LA_BF16)
-            hipLaunchKernelGGL((output_kernel_bf16<D, O3>),
-                               dim3(unsigned(split_grid<O3::NP_>(items))), dim3(O3::NT), 0, st,
-                               static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                               static_cast<const uint16_t*>(v), blocks, scans, ws,
-                               final_state, ext_state, static_cast<uint16_t*>(out), H, items,
-                               fz);
-        else if (dtype == LA_F32_SPLIT)
-            hipLaunchKernelGGL((output_kernel_split<D, O3>),
-                               dim3(unsigned(split_grid<O3::NP_>(items))), dim3(O3::NT), 0, st,
+        const dim3 g3(unsigned(split_grid<O3::NP_>(items)));
+        if (dtype == LA_BF16) {
+            auto kern = fused ? output_kernel_bf16<D, O3, true> : output_kernel_bf16<D, O3, false>;
+            hipLaunchKernelGGL(kern, g3, dim3(O3::NT), 0, st, static_cast<const uint16_t*>(q),
+                               static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+                               blocks, scans, ws, final_state, ext_state,
+                               static_cast<uint16_t*>(out), H, items);
+        } else if (dtype == LA_F32_SPLIT) {
+            auto kern = fused ? output_kernel_split<D, O3, true> : output_kernel_split<D, O3, false>;
+            hipLaunchKernelGGL(kern, g3, dim3(O3::NT), 0, st, static_cast<const float*>(q),
+                               static_cast<const float*>(k), static_cast<const float*>(v), blocks,
+                               scans, ws, final_state, ext_state, static_cast<float*>(out), H,
+                               items);
+        } else {
+            auto kern = fused ? output_kernel_f32<D, true> : output_kernel_f32<D, false>;
+            hipLaunchKernelGGL(kern, dim3(unsigned(items)), blk, 0, st,
                                static_cast<const float*>(q), static_cast<const float*>(k),
                                static_cast<const float*>(v), blocks, scans, ws, final_state,
-                               ext_state, static_cast<float*>(out), H, items, fz);
-        else
-            hipLaunchKernelGGL(output_kernel_f32<D>, dim3(unsigned(items)), blk, 0, st,
-                               static_cast<const float*>(q), static_cast<const float*>(k),
-                               static_cast<const float*>(v), blocks, scans, ws, final_state,
-                               ext_state, static_cast<float*>(out), H, fz);
+                               ext_state, static_cast<float*>(out), H);
+        }
         if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
     }
     return LA_OK;

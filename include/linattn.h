@@ -225,7 +225,7 @@ la_status la_scan_workspace_size(const la_pass_info* info, int32_t H, int32_t d_
  *      (q k^T)) v, carrying S in registers; branch blocks start from
  *      final_state of their view or from ext_state.
  * For passes whose block states are few (la_pass_info.fused_slot_reads x H
- * x d_k x d_v x 4 bytes up to 16 MiB) launch 2 is left out: each launch-3
+ * x d_k x d_v x 4 bytes up to 128 MiB) launch 2 is left out: each launch-3
  * workgroup sums the block states before it (and a branch those of its view)
  * itself, and each view's last block writes final_state.  Both forms add the
  * states in the same order and give the same bits.
