@@ -248,3 +248,19 @@ def test_scan_launches_by_pass_shape():
         la.scan_launches(p1, 0, 64)
     with pytest.raises(la.LinAttnError):
         la.scan_launches(p1, 1, 96)
+
+
+def test_block_size_choice_on_the_workloads():
+    """The binding's block size: the largest power of two up to 16 chunks that
+    keeps >= 300 workgroups, doubled up to 64 while the views alone keep
+    >= 2048 workgroups (the choices measured fastest on MI355X)."""
+    expect = {"view7400_br8x48_h16_d64_bf16": (16, 8),
+              "req4_view500-18000_br8x24-96_h16_d64_bf16": (16, 16),
+              "view18000_br256x32-128_h16_d64_bf16": (16, 16),
+              "req32_view500-18000_br1-64x24-128_h32_d128_bf16": (32, 64)}
+    for name, (H, G) in expect.items():
+        assert la.pack(*synth.shapes(name), heads=H).info.block_chunks == G, name
+    # views too short for 2048 long workgroups stay at 16
+    assert la.choose_block_chunks([300] * 4, 16, view_chunks=[300] * 4) == 16
+    assert la.choose_block_chunks([300] * 64, 32, view_chunks=[300] * 64) == 64
+    assert la.choose_block_chunks([3], 2) == 1
