@@ -264,3 +264,23 @@ def test_block_size_choice_on_the_workloads():
     assert la.choose_block_chunks([300] * 4, 16, view_chunks=[300] * 4) == 16
     assert la.choose_block_chunks([300] * 64, 32, view_chunks=[300] * 64) == 64
     assert la.choose_block_chunks([3], 2) == 1
+
+
+def test_stage_and_form_bits_checked_before_any_device_work():
+    """la_scan_packed_stages rejects unknown bits, a mask without launches and
+    both form bits at once, on the host, before it looks at any pointer; an
+    empty pass with valid bits returns LA_OK without touching the device."""
+    lib = la.load_library()
+    info = la.PassInfo()
+    info.chunk = la.CHUNK
+
+    def call(stages):
+        return lib.la_scan_packed_stages(stages, None, None, None, la.LA_BF16, 1, 64, 64,
+                                         ctypes.byref(info), None, None, 0, None, None, None,
+                                         0, None)
+    assert call(la.STAGE_ALL) == la.LA_OK
+    assert call(la.STAGE_ALL | la.FORM_TWO_LAUNCH) == la.LA_OK
+    assert call(la.STAGE_OUTPUT | la.FORM_THREE_LAUNCH) == la.LA_OK
+    for bad in (0, la.FORM_TWO_LAUNCH, la.STAGE_ALL | la.FORM_TWO_LAUNCH | la.FORM_THREE_LAUNCH,
+                la.STAGE_ALL | 32, -1):
+        assert call(bad) == la.LA_ERR_INVALID_ARG, bad
