@@ -40,6 +40,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "linattn.h"
 #include "tiles.h"
@@ -286,47 +287,62 @@ __global__ __launch_bounds__(kThreads) void delta_kernel_f32(
 
 // ===========================================================================
 // Launch 2: segmented inclusive prefix over each scanned segment's slots.
-// One thread per state element of one (segment, head); consecutive threads
-// take consecutive elements, so every slot access is a coalesced row.  Up to
-// kPrefixBatch slot loads per thread are in flight at once (one memory round
-// trip for segments of up to that many slots).  Slot j >= 1 is rewritten
-// with the sum of slots 0..j; a view skips its last slot, whose sum is the
-// view's final state and goes to final_state instead.
+// One thread per EPT consecutive state elements of one (segment, head);
+// consecutive threads take consecutive elements, so every slot access is a
+// coalesced row.  Up to BATCH slot loads per thread are in flight at once
+// (one memory round trip for segments of up to that many slots).  Slot
+// j >= 1 is rewritten with the sum of slots 0..j; a view skips its last
+// slot, whose sum is the view's final state and goes to final_state instead.
+// Every element is summed from zero in slot order, whatever EPT.
+// EPT = 1 with BATCH = 32 suits passes with few segments (one round trip for
+// the long views, as many workgroups as elements allow); EPT = 4 with
+// BATCH = 8 suits passes with many segment-heads, where one element per
+// thread made tens of thousands of latency-bound workgroups (the 272k-token
+// pass at d = 128: 65,536 of them).
 // ===========================================================================
-constexpr int kPrefixBatch = 32;
+constexpr int64_t kPrefixWideGroups = 8192;   // workgroups at one element per thread
 
-template <int D>
+template <int D, int EPT, int BATCH>
 __global__ __launch_bounds__(kThreads) void prefix_kernel(const ScanDesc* __restrict__ scans,
                                                           float* __restrict__ ws,
                                                           float* __restrict__ final_state,
                                                           int H) {
-    constexpr int DD = D * D, WPS = DD / kThreads;
+    static_assert(EPT == 1 || EPT == 4, "one element or one 16-byte piece per thread");
+    using V = typename std::conditional<EPT == 4, f32x4, float>::type;
+    constexpr int DD = D * D, WPS = DD / (kThreads * EPT);
     const int per_seg = H * WPS;
     const ScanDesc sd = scans[blockIdx.x / per_seg];
     const int rem = blockIdx.x % per_seg;
     const int h = rem / WPS;
-    const int e = (rem % WPS) * kThreads + threadIdx.x;
-    const int64_t stride = (int64_t)H * DD;
-    float* p = ws + ((int64_t)sd.first_slot * H + h) * DD + e;
+    const int e = ((rem % WPS) * kThreads + threadIdx.x) * EPT;
+    const int64_t stride = (int64_t)H * DD / EPT;   // one slot, in units of V
+    V* p = reinterpret_cast<V*>(ws + ((int64_t)sd.first_slot * H + h) * DD + e);
     const int n = sd.n_slots;
     const int last_store = sd.final_row >= 0 ? n - 1 : n;   // exclusive bound
-    float acc = 0.f;
-    for (int j0 = 0; j0 < n; j0 += kPrefixBatch) {
-        float x[kPrefixBatch];
+    V acc = V(0.f);
+    for (int j0 = 0; j0 < n; j0 += BATCH) {
+        V x[BATCH];
 #pragma unroll
-        for (int i = 0; i < kPrefixBatch; ++i)
-            x[i] = (j0 + i < n) ? p[(j0 + i) * stride] : 0.f;
+        for (int i = 0; i < BATCH; ++i)
+            x[i] = (j0 + i < n) ? p[(j0 + i) * stride] : V(0.f);
 #pragma unroll
-        for (int i = 0; i < kPrefixBatch; ++i) {
+        for (int i = 0; i < BATCH; ++i) {
             const int j = j0 + i;
             acc += x[i];
             if (j >= 1 && j < last_store) p[j * stride] = acc;
         }
     }
     if (sd.final_row >= 0) {
-        int row, col;
-        slot_to_rc<D>(e, row, col);
-        final_state[(((int64_t)sd.final_row * H + h) * D + row) * D + col] = acc;
+        float* dst = final_state + ((int64_t)sd.final_row * H + h) * DD;
+#pragma unroll
+        for (int t = 0; t < EPT; ++t) {
+            int row, col;
+            slot_to_rc<D>(e + t, row, col);
+            if constexpr (EPT == 4)
+                dst[row * D + col] = acc[t];
+            else
+                dst[row * D + col] = acc;
+        }
     }
 }
 
@@ -1245,8 +1261,13 @@ la_status launch_all(int32_t stages, bool fused, const void* q, const void* k, c
         if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
     }
     if ((stages & LA_STAGE_PREFIX) && !fused && info.n_scan > 0) {
-        const dim3 grid(unsigned(int64_t(info.n_scan) * H * (D * D / kThreads)));
-        hipLaunchKernelGGL(prefix_kernel<D>, grid, blk, 0, st, scans, ws, final_state, H);
+        const int64_t wgs = int64_t(info.n_scan) * H * (D * D / kThreads);
+        if (wgs >= kPrefixWideGroups)
+            hipLaunchKernelGGL((prefix_kernel<D, 4, 8>), dim3(unsigned(wgs / 4)), blk, 0, st,
+                               scans, ws, final_state, H);
+        else
+            hipLaunchKernelGGL((prefix_kernel<D, 1, 32>), dim3(unsigned(wgs)), blk, 0, st,
+                               scans, ws, final_state, H);
         if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
     }
     if ((stages & LA_STAGE_OUTPUT) && info.n_blocks > 0) {

@@ -127,3 +127,29 @@ def test_output_launch_alone_repeats_in_two_launch_form():
                    stages=la.STAGE_OUTPUT, form="two")
     torch.cuda.synchronize()
     assert torch.equal(o1, o2)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_wide_prefix_launch_agrees(d):
+    """Enough segment-heads for the prefix launch to take 4 elements per
+    thread (>= 8192 workgroups at one element per thread): 24 views of 150-700
+    tokens and 40 branches, some of several blocks, H = 32, one chunk per
+    block.  The three-launch form must equal the two-launch form (no prefix
+    launch) bit for bit and match the oracle."""
+    rng = np.random.default_rng(900 + d)
+    vl = rng.integers(150, 700, size=24)
+    bc = rng.integers(0, 4, size=24)
+    bl = rng.integers(1, 200, size=int(bc.sum()))
+    H = 32
+    plan = la.pack(vl, bc, bl, heads=H, block_chunks=1)
+    assert plan.info.n_scan * H * (d * d // 256) >= 8192
+    T = plan.info.n_tokens
+    q, k, v = synth.draw_qkv(rng, T, H, d, "bf16")
+    o3, f3 = _run(q, k, v, plan, "three")
+    o2, f2 = _run(q, k, v, plan, "two")
+    assert torch.equal(o2, o3) and torch.equal(f2, f3)
+    ref_o, ref_f = oracle.scan_recurrence(q, k, v, plan.seg_offsets, plan.branch_parent)
+    eo, ef = oracle.row_rel_err(o3, ref_o), oracle.state_rel_err(f3, ref_f)
+    print(f"  wide prefix d={d}: T={T} scans={plan.info.n_scan} out err {eo:.3e} final err {ef:.3e}",
+          flush=True)
+    assert eo <= TOL["bf16"] and ef <= TOL["bf16"]
