@@ -1,6 +1,7 @@
 """Benchmark: linear-attention layer tokens/s per packed pass on one MI355X.
 
-One step = one packed pass through la_scan_packed (all three launches) over
+One step = one packed pass through la_scan_packed (all its launches: two or
+three, the form the library picks for the pass, or --form) over
 one batch of synthetic input already resident in HBM.  The default workload
 is one 7,400-token view with 8 branches of 48 tokens, H = 16, d = 64, bf16
 (the pass size of the page "Serving 0.88M TPS from Two RTXs and Mac Minis",

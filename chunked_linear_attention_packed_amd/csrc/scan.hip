@@ -14,12 +14,14 @@
 // The three launches:
 //   delta_kernel   one workgroup per (delta block, head): sum over the block's
 //                  chunks of K_c^T V_c, written to a workspace slot
-//   prefix_kernel  one thread per (scanned segment, head, state element):
-//                  inclusive prefix over the segment's slots, in place; the
-//                  total of a view goes to final_state
+//   prefix_kernel  one thread per (scanned segment, head, 1 or 4 state
+//                  elements): inclusive prefix over the segment's slots, in
+//                  place; the total of a view goes to final_state
 //   output_kernel  one workgroup per (work block, head): chunk by chunk,
 //                  O^T = S^T Q^T + V^T P^T with P = tril(Q K^T), carrying S in
 //                  registers across the block's chunks
+// For small passes the prefix launch is left out (the two-launch form): each
+// output workgroup sums the slots before its block itself, in the same order.
 //
 // MFMA use (v_mfma_f32_16x16x32_bf16 for bf16, v_mfma_f32_16x16x4_f32 for
 // fp32).  Accumulator layout of a 16x16 tile: lane l = 16 g + c holds rows
