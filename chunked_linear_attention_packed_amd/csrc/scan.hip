@@ -1343,6 +1343,15 @@ extern "C" la_status la_scan_packed_stages(int32_t stages, const void* q, const 
     if ((final_state && !aligned4(final_state)) || (ext_state && !aligned4(ext_state)) ||
         (workspace && !aligned16(workspace)) || !aligned4(plan))
         return LA_ERR_INVALID_ARG;
+    // final_state is written while ext_state is read (by the same launch in the
+    // two-launch form): the two must not overlap
+    if (final_state && ext_state && info->n_views > 0 && n_ext > 0) {
+        const uintptr_t st = uintptr_t(H) * d_k * d_v * sizeof(float);
+        const uintptr_t f0 = reinterpret_cast<uintptr_t>(final_state);
+        const uintptr_t e0 = reinterpret_cast<uintptr_t>(ext_state);
+        if (f0 < e0 + uintptr_t(n_ext) * st && e0 < f0 + uintptr_t(info->n_views) * st)
+            return LA_ERR_INVALID_ARG;
+    }
     size_t need = 0;
     la_status stw = la_scan_workspace_size(info, H, d_k, d_v, dtype, &need);
     if (stw != LA_OK) return stw;

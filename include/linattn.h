@@ -238,7 +238,8 @@ la_status la_scan_workspace_size(const la_pass_info* info, int32_t H, int32_t d_
  *   info           host, from the planner that built `plan`
  *   plan           device [info->plan_words] int32, a copy of the plan
  *   ext_state      device [n_ext][H][d_k][d_v] fp32 or NULL when the pass has
- *                  no shard branches (info->n_ext == 0)
+ *                  no shard branches (info->n_ext == 0); must not overlap
+ *                  final_state
  *   n_ext          rows of ext_state (>= info->n_ext)
  *   out            device [T][H][d_v], dtype: fully overwritten
  *   final_state    device [info->n_views][H][d_k][d_v] fp32, row-major
@@ -248,6 +249,13 @@ la_status la_scan_workspace_size(const la_pass_info* info, int32_t H, int32_t d_
  * Accumulation is fp32; bf16 outputs are rounded to nearest even.  A pass is
  * idempotent: it reads only its inputs and overwrites all outputs.  Calls
  * that share a workspace must be ordered on one stream.
+ * Errors (all detected on the host before anything is enqueued; outputs are
+ * then untouched): LA_ERR_INVALID_ARG for NULL or misaligned pointers (q, k,
+ * v, out 16-byte aligned; states and plan 4-byte; workspace 16-byte), H < 1,
+ * n_ext < info->n_ext, ext_state overlapping final_state, or sizes past the
+ * 32-bit dispatch and buffer limits; LA_ERR_UNSUPPORTED for other dtypes,
+ * head dims or chunk sizes; LA_ERR_WORKSPACE for a missing or short
+ * workspace; LA_ERR_HIP if a launch fails.
  */
 la_status la_scan_packed(const void* q, const void* k, const void* v, la_dtype dtype,
                          int32_t H, int32_t d_k, int32_t d_v, const la_pass_info* info,
@@ -285,7 +293,8 @@ la_status la_scan_launches(const la_pass_info* info, int32_t H, int32_t d_k, int
  * form (in the two-launch form the LA_STAGE_PREFIX bit does nothing); every
  * call on one workspace must use the same form.  la_scan_packed(...) is
  * la_scan_packed_stages(LA_STAGE_ALL, ...).
- * Errors: as la_scan_packed, plus LA_ERR_INVALID_ARG when no LA_STAGE_* bit
+ * Errors: as la_scan_packed (LA_ERR_INVALID_ARG also for ext_state overlapping
+ * final_state), plus LA_ERR_INVALID_ARG when no LA_STAGE_* bit
  * is set, an unknown bit is set, or both LA_FORM_* bits are set.
  */
 la_status la_scan_packed_stages(int32_t stages, const void* q, const void* k, const void* v,

@@ -284,3 +284,22 @@ def test_stage_and_form_bits_checked_before_any_device_work():
     for bad in (0, la.FORM_TWO_LAUNCH, la.STAGE_ALL | la.FORM_TWO_LAUNCH | la.FORM_THREE_LAUNCH,
                 la.STAGE_ALL | 32, -1):
         assert call(bad) == la.LA_ERR_INVALID_ARG, bad
+
+
+def test_ext_state_overlapping_final_state_rejected():
+    """final_state is written while ext_state is read (in the two-launch form
+    by the same launch), so overlapping buffers are refused on the host
+    before any device work (the pointers here are never dereferenced)."""
+    lib = la.load_library()
+    p = la.pack([100, 0], [1, 1], [30, 40], heads=2)
+    assert p.info.n_views == 1 and p.info.n_ext == 1
+    plan = p.plan
+    st = 2 * 64 * 64 * 4
+    base = 1 << 20                     # fake, aligned, never touched
+    fake = ctypes.c_void_p(base)
+    for ext in (base, base + st - 16, base - st + 16):
+        r = lib.la_scan_packed_stages(la.STAGE_ALL, fake, fake, fake, la.LA_BF16, 2, 64, 64,
+                                      ctypes.byref(p.info), fake, ctypes.c_void_p(ext), 1,
+                                      fake, ctypes.c_void_p(base), None, 0, None)
+        assert r == la.LA_ERR_INVALID_ARG, hex(ext)
+    del plan
