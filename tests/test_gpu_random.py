@@ -1,7 +1,9 @@
 """Randomised pass structures on the GPU, against the fp64 oracles: request
 counts, view and branch lengths (including 1 and chunk-boundary lengths),
 shard requests seeded from external states, block sizes G, dtypes and head
-dims drawn from a fixed seed, so every run checks the same 24 + 12 cases."""
+dims drawn from a fixed seed, so every run checks the same 24 + 12 cases.
+Each scan case also runs in both forms (two and three launches), which must
+agree bit for bit."""
 import numpy as np
 import pytest
 import torch
@@ -55,8 +57,14 @@ def test_random_scan(i):
            if n_ext else None)
     print(f"case {i}: views {vl} branches {bc} T={T} {dtype} d={d} H={H} G={G} "
           f"ext={n_ext} split={split}", flush=True)
-    out, fin = la.scan_packed(q.to(DEV), k.to(DEV), v.to(DEV), plan,
-                              ext_state=None if ext is None else ext.to(DEV), split_fp32=split)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    ed = None if ext is None else ext.to(DEV)
+    out, fin = la.scan_packed(qd, kd, vd, plan, ext_state=ed, split_fp32=split)
+    # both forms of the scan (two launches; three with the prefix launch) give
+    # the same bits as the one the library picked
+    for form in ("two", "three"):
+        o_f, f_f = la.scan_packed(qd, kd, vd, plan, ext_state=ed, split_fp32=split, form=form)
+        assert torch.equal(o_f, out) and torch.equal(f_f, fin), form
     torch.cuda.synchronize()
     ref_o, ref_f = oracle.scan_recurrence(q, k, v, plan.seg_offsets, plan.branch_parent,
                                           ext_state=ext)
