@@ -476,7 +476,11 @@ struct Out3 {
 
 // Launch configurations, chosen by measurement on MI355X: launch 1 splits
 // each item over DELTA_NP workgroups, launch 3 over OUT_NP workgroups of
-// OUT_NW waves.
+// OUT_NW waves (the split-precision launch 3 over SPLIT_NP of SPLIT_NW).  At
+// d = 128 one workgroup of 8 waves per item (both 64-feature halves, q and k
+// read once) ran launch 3 of the 272k-token pass in 2505 us against 2345 us
+// for two workgroups of 4 waves (one per half): the larger workgroup needs
+// 105 KB of LDS, one per CU.
 #ifndef LA_DELTA_NP_64
 #define LA_DELTA_NP_64 1
 #endif
@@ -495,17 +499,25 @@ struct Out3 {
 #ifndef LA_OUT_NW_128
 #define LA_OUT_NW_128 4
 #endif
+#ifndef LA_SPLIT_NP_128
+#define LA_SPLIT_NP_128 2
+#endif
+#ifndef LA_SPLIT_NW_128
+#define LA_SPLIT_NW_128 4
+#endif
 template <int D>
 struct LaunchCfg;
 template <>
 struct LaunchCfg<64> {
     static constexpr int DELTA_NP = LA_DELTA_NP_64;
     using O3 = Out3<64, LA_OUT_NP_64, LA_OUT_NW_64>;
+    using O3S = O3;   // split-precision launch 3
 };
 template <>
 struct LaunchCfg<128> {
     static constexpr int DELTA_NP = LA_DELTA_NP_128;
     using O3 = Out3<128, LA_OUT_NP_128, LA_OUT_NW_128>;
+    using O3S = Out3<128, LA_SPLIT_NP_128, LA_SPLIT_NW_128>;
 };
 
 // Output feature order of the bf16 output launch (64 output features per
@@ -521,15 +533,15 @@ __device__ __forceinline__ int out_row(int f) {
     return 32 * (f >> 5) + 16 * ((f >> 2) & 1) + 4 * ((f >> 3) & 3) + (f & 3);
 }
 
-// The outputs of one wave for one chunk: its 16 tokens (token block TB), all
-// 64 output features of the workgroup in the order above.  Specialised per
+// The outputs of one wave for one chunk: its 16 tokens (token block TB), the
+// 64 output features of feature half hv of the workgroup in the order above.  Specialised per
 // TB so that the causal structure (TB + 1 score tiles, TB / 2 + 1
 // intra-chunk steps) is known at compile time and every loop runs over
 // independent accumulators with its LDS fragments loaded in batches.
 template <int D, int TB, int VBH, int LDV>
 __device__ __forceinline__ void out_tiles(const uint16_t* sK, const uint16_t* sV,
                                           const uint16_t* sSh, const uint16_t* sSl,
-                                          const u32x4 (&qf)[D / 32], int g, int c16,
+                                          const u32x4 (&qf)[D / 32], int hv, int g, int c16,
                                           f32x4 (&acc)[VBH]) {
     static_assert(VBH == 4, "one wave covers the 64 output features of its workgroup");
     constexpr int NKS = D / 32;
@@ -564,7 +576,7 @@ __device__ __forceinline__ void out_tiles(const uint16_t* sK, const uint16_t* sV
         u32x4 ah[VBH], al[VBH];
 #pragma unroll
         for (int x = 0; x < VBH; ++x) {
-            const int row = x * 16 + c16;
+            const int row = hv * 64 + x * 16 + c16;
             const int o = row * LDR + scol<D>(row, ks * 32 + 8 * g);
             ah[x] = lds_u32x4(sSh + o);
             al[x] = lds_u32x4(sSl + o);
@@ -583,7 +595,7 @@ __device__ __forceinline__ void out_tiles(const uint16_t* sK, const uint16_t* sV
         for (int x = 0; x < VBH; ++x) {
             // as tr_frag, with lane c of the tile receiving feature
             // 32 (x >> 1) + 8 (c >> 2) + 4 (x & 1) + (c & 3)
-            const uint16_t* pv = sV + (4 * g + (c16 >> 2)) * LDV + 32 * (x >> 1) +
+            const uint16_t* pv = sV + (4 * g + (c16 >> 2)) * LDV + hv * 64 + 32 * (x >> 1) +
                                  8 * (c16 & 3) + 4 * (x & 1);
             av[x] = cat2(lds_tr4(pv + (2 * pp) * 16 * LDV), lds_tr4(pv + (2 * pp + 1) * 16 * LDV));
         }
@@ -609,7 +621,7 @@ __global__ __launch_bounds__(O3::NT) void output_kernel_bf16(
     // pieces 16 bytes apart on four rows) and the carry's reads both hit every
     // LDS bank at most once per 128 bytes
     constexpr int LDV = DV + 32;
-    static_assert(DV == 64 && O3::NHV == 1, "one feature part of 64 per workgroup");
+    static_assert(DV == 64 * O3::NHV && VBH == 4, "waves cover 64-feature halves");
     __shared__ __attribute__((aligned(16))) uint16_t sK[kChunk * LDR];   // K, row-major
     __shared__ __attribute__((aligned(16))) uint16_t sV[kChunk * LDV];   // V part, row-major
     __shared__ __attribute__((aligned(16))) uint16_t sSh[DV * LDR];   // S^T, bf16 high term
@@ -621,7 +633,7 @@ __global__ __launch_bounds__(O3::NT) void output_kernel_bf16(
     const int h = item % H;
     const BlockDesc bd = blocks[item / H];
     const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, g = lane >> 4, c16 = lane & 15;
-    const int tb = w & 3;
+    const int tb = w & 3, hv = O3::NHV == 1 ? 0 : w >> 2;
     const int vbo = O3::vb_own(w), kbo = O3::kb0(w);   // vbo local to the part
     const int vbg = part * NVB + vbo;                   // global column block
 
@@ -631,7 +643,7 @@ __global__ __launch_bounds__(O3::NT) void output_kernel_bf16(
     // row pieces inside a chunk window
     const int trow = tb * 16 + c16;
     const uint32_t qoff = uint32_t(((trow * H + h) * D + 8 * g) * 2);
-    const uint32_t ooff = uint32_t(((trow * H + h) * D + part * DV + 8 * g) * 2);
+    const uint32_t ooff = uint32_t(((trow * H + h) * D + part * DV + hv * 64 + 8 * g) * 2);
     const int vcg0 = part * (DV / 8);
 
     // one chunk in flight: kv / qn hold chunk c + 1 while chunk c is computed
@@ -672,7 +684,8 @@ __global__ __launch_bounds__(O3::NT) void output_kernel_bf16(
             const uint32_t h01 = cvt_bf2(s[0], s[1]), h23 = cvt_bf2(s[2], s[3]);
             const uint32_t l01 = cvt_bf2(s[0] - bf_lo(h01), s[1] - bf_hi(h01));
             const uint32_t l23 = cvt_bf2(s[2] - bf_lo(h23), s[3] - bf_hi(h23));
-            const int row = out_row(vbo * 16 + c16);
+            const int f = vbo * 16 + c16;   // feature within the part
+            const int row = (f & ~63) + out_row(f & 63);
             const int off = row * LDR + scol<D>(row, (kbo + i) * 16 + 4 * g);
             *reinterpret_cast<u32x2*>(sSh + off) = u32x2{h01, h23};
             *reinterpret_cast<u32x2*>(sSl + off) = u32x2{l01, l23};
@@ -696,15 +709,15 @@ __global__ __launch_bounds__(O3::NT) void output_kernel_bf16(
         const int rows = min(kChunk, bd.ntok - c * kChunk);
         const int64_t first = (int64_t(bd.tok0) + c * kChunk) * row_elems;
 
-        // O^T tiles: this wave's 16 tokens, the workgroup's 64 output features
+        // O^T tiles: this wave's 16 tokens, the 64 output features of half hv
         f32x4 acc[VBH];
         switch (tb) {
-            case 0: out_tiles<D, 0, VBH, LDV>(sK, sV, sSh, sSl, qf, g, c16, acc); break;
-            case 1: out_tiles<D, 1, VBH, LDV>(sK, sV, sSh, sSl, qf, g, c16, acc); break;
-            case 2: out_tiles<D, 2, VBH, LDV>(sK, sV, sSh, sSl, qf, g, c16, acc); break;
-            default: out_tiles<D, 3, VBH, LDV>(sK, sV, sSh, sSl, qf, g, c16, acc); break;
+            case 0: out_tiles<D, 0, VBH, LDV>(sK, sV, sSh, sSl, qf, hv, g, c16, acc); break;
+            case 1: out_tiles<D, 1, VBH, LDV>(sK, sV, sSh, sSl, qf, hv, g, c16, acc); break;
+            case 2: out_tiles<D, 2, VBH, LDV>(sK, sV, sSh, sSl, qf, hv, g, c16, acc); break;
+            default: out_tiles<D, 3, VBH, LDV>(sK, sV, sSh, sSl, qf, hv, g, c16, acc); break;
         }
-        // lane holds O[t = tb*16 + c16][part*DV + 32 (x >> 1) + 8g + 4 (x & 1) + j]:
+        // lane holds O[t = tb*16 + c16][part*DV + hv*64 + 32 (x >> 1) + 8g + 4 (x & 1) + j]:
         // piece A (features 8g ..) and piece B (32 + 8g ..) of its token.  Lanes
         // of neighbouring tokens (c16, c16 ^ 1) swap one piece, so that each of
         // the two stores writes whole 128-byte feature rows (one token each from
@@ -1226,11 +1239,14 @@ template <int D>
 bool grids_fit(const la_pass_info& info, int32_t H) {
     constexpr int64_t kMax = (int64_t(1) << 32) - 1;
     using O3 = typename LaunchCfg<D>::O3;
+    using O3S = typename LaunchCfg<D>::O3S;
     const int64_t l1 = split_grid<LaunchCfg<D>::DELTA_NP>(int64_t(info.n_delta) * H) * kThreads;
     const int64_t l2 = int64_t(info.n_scan) * H * (D * D);
     const int64_t l3 = split_grid<O3::NP_>(int64_t(info.n_blocks) * H) *
                        (O3::NT > kThreads ? O3::NT : kThreads);
-    return l1 <= kMax && l2 <= kMax && l3 <= kMax;
+    const int64_t l3s = split_grid<O3S::NP_>(int64_t(info.n_blocks) * H) *
+                        (O3S::NT > kThreads ? O3S::NT : kThreads);
+    return l1 <= kMax && l2 <= kMax && l3 <= kMax && l3s <= kMax;
 }
 
 template <int D>
@@ -1283,8 +1299,10 @@ la_status launch_all(int32_t stages, bool fused, const void* q, const void* k, c
                                blocks, scans, ws, final_state, ext_state,
                                static_cast<uint16_t*>(out), H, items);
         } else if (dtype == LA_F32_SPLIT) {
-            auto kern = fused ? output_kernel_split<D, O3, true> : output_kernel_split<D, O3, false>;
-            hipLaunchKernelGGL(kern, g3, dim3(O3::NT), 0, st, static_cast<const float*>(q),
+            using O3S = typename LaunchCfg<D>::O3S;
+            auto kern = fused ? output_kernel_split<D, O3S, true> : output_kernel_split<D, O3S, false>;
+            const dim3 g3s(unsigned(split_grid<O3S::NP_>(items)));
+            hipLaunchKernelGGL(kern, g3s, dim3(O3S::NT), 0, st, static_cast<const float*>(q),
                                static_cast<const float*>(k), static_cast<const float*>(v), blocks,
                                scans, ws, final_state, ext_state, static_cast<float*>(out), H,
                                items);
