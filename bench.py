@@ -721,7 +721,9 @@ def main():
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-            "kernel": "output_kernel (launch 3)",
+            "kernel": ("output_kernel (launch 3; in the two-launch form it also sums the "
+                       "block states before its block)" if n_launches == 2
+                       else "output_kernel (launch 3)"),
             "bytes_per_launch": l3_bytes,
         },
         "cpu_baseline": cpu,
