@@ -153,3 +153,25 @@ def test_wide_prefix_launch_agrees(d):
     print(f"  wide prefix d={d}: T={T} scans={plan.info.n_scan} out err {eo:.3e} final err {ef:.3e}",
           flush=True)
     assert eo <= TOL["bf16"] and ef <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("form", ["two", "three"])
+def test_launches_one_at_a_time_equal_the_full_pass(form):
+    """la_scan_packed_stages run launch by launch on one workspace (block
+    states, prefix, outputs; the prefix bit does nothing in the two-launch
+    form) gives the bits of the full pass, in either form."""
+    vl, bc, bl = [900, 300], [3, 2], [70, 129, 1, 64, 200]
+    H, d = 2, 64
+    plan = la.pack(vl, bc, bl, heads=H, block_chunks=2)
+    T = plan.info.n_tokens
+    q, k, v = synth.draw_qkv(np.random.default_rng(77), T, H, d, "bf16")
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    o_full, f_full = la.scan_packed(qd, kd, vd, plan, form=form)
+    ws = torch.empty(la.workspace_size(plan, H, d, la.LA_BF16), dtype=torch.uint8, device=DEV)
+    out = torch.full_like(o_full, float("nan"))
+    fin = torch.full_like(f_full, float("nan"))
+    for stage in (la.STAGE_STATES, la.STAGE_PREFIX, la.STAGE_OUTPUT):
+        la.scan_packed(qd, kd, vd, plan, out=out, final_state=fin, workspace=ws, stages=stage,
+                       form=form)
+    torch.cuda.synchronize()
+    assert torch.equal(out, o_full) and torch.equal(fin, f_full)
