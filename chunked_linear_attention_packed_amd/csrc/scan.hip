@@ -293,8 +293,10 @@ __global__ __launch_bounds__(kThreads) void delta_kernel_f32(
 // consecutive threads take consecutive elements, so every slot access is a
 // coalesced row.  Up to BATCH slot loads per thread are in flight at once
 // (one memory round trip for segments of up to that many slots).  Slot
-// j >= 1 is rewritten with the sum of slots 0..j; a view skips its last
-// slot, whose sum is the view's final state and goes to final_state instead.
+// j >= 1 is rewritten with the sum of slots 0..j; for a view that sum at
+// the last slot is its final state, which also goes to final_state
+// (row-major); branch blocks read their seed from the slot, whose lane
+// layout gives 16-byte loads.
 // Every element is summed from zero in slot order, whatever EPT.
 // EPT = 1 with BATCH = 32 suits passes with few segments (one round trip for
 // the long views, as many workgroups as elements allow); EPT = 4 with
@@ -320,7 +322,7 @@ __global__ __launch_bounds__(kThreads) void prefix_kernel(const ScanDesc* __rest
     const int64_t stride = (int64_t)H * DD / EPT;   // one slot, in units of V
     V* p = reinterpret_cast<V*>(ws + ((int64_t)sd.first_slot * H + h) * DD + e);
     const int n = sd.n_slots;
-    const int last_store = sd.final_row >= 0 ? n - 1 : n;   // exclusive bound
+    const int last_store = n;   // exclusive bound: a view's last slot gets its total too
     V acc = V(0.f);
     for (int j0 = 0; j0 < n; j0 += BATCH) {
         V x[BATCH];
@@ -358,8 +360,8 @@ __global__ __launch_bounds__(kThreads) void prefix_kernel(const ScanDesc* __rest
 //   S_in = seed + own
 // seed: zero (a view), the view's final state (a branch) or an external state
 // (a shard branch); own: the segment-local sum of the earlier blocks' states.
-// Three-launch form: the prefix launch has left own in slot sin_slot and the
-// view totals in final_state.  Two-launch form (`fused`): the slots hold the
+// Three-launch form: the prefix launch has left own in slot sin_slot and each
+// view's total in the view's last slot.  Two-launch form (`fused`): the slots hold the
 // blocks' own states and the block sums them here, in slot order: own =
 // slots slot0 .. sin_slot, a branch's seed = all slots of its view (scan
 // entry `seed`); a view's last block also writes the view's total, own plus
@@ -422,7 +424,13 @@ __device__ __forceinline__ void block_init_state(
             const ScanDesc sc = scans[bd.seed];
             sum_slots<D, NT, B>(S, tix, ws, sc.first_slot, sc.n_slots, H, h, lane);
         } else {
-            read_rows(final_state + ((int64_t)bd.seed * H + h) * DD);
+            // the prefix launch left the view's total in its last slot too
+            // (the same bits as its final_state row), in the lane layout
+            const ScanDesc sc = scans[bd.seed];
+            const f32x4* p = reinterpret_cast<const f32x4*>(
+                ws + ((int64_t)(sc.first_slot + sc.n_slots - 1) * H + h) * DD);
+#pragma unroll
+            for (int i = 0; i < NT; ++i) S[i] = p[tix[i] * 64 + lane];
         }
     }
     if (bd.sin_slot >= 0) {

@@ -222,8 +222,8 @@ la_status la_scan_workspace_size(const la_pass_info* info, int32_t H, int32_t d_
  *   2. per segment, head and state element, the prefix of those block
  *      states; writes final_state for every view;
  *   3. per work block and head, chunk by chunk: o = q S_in + (causal
- *      (q k^T)) v, carrying S in registers; branch blocks start from
- *      final_state of their view or from ext_state.
+ *      (q k^T)) v, carrying S in registers; branch blocks start from their
+ *      view's total (the same bits as its final_state row) or from ext_state.
  * For passes whose block states are few (la_pass_info.fused_slot_reads x H
  * x d_k x d_v x 4 bytes up to 128 MiB) launch 2 is left out: each launch-3
  * workgroup sums the block states before it (and a branch those of its view)
@@ -287,8 +287,8 @@ la_status la_scan_launches(const la_pass_info* info, int32_t H, int32_t d_k, int
  * bits are set in `stages` (LA_STAGE_*), with the same arguments and checks.
  * For profiling one launch in isolation.  Launch 2 rewrites the workspace in
  * place, so it must follow a launch 1 on the same buffers; launch 3 only
- * reads the workspace (and, in the three-launch form, final_state), so after
- * one complete pass it may be repeated alone and produces the same out.  One
+ * reads the workspace (and ext_state), so after one complete pass it may be
+ * repeated alone and produces the same out.  One
  * of LA_FORM_TWO_LAUNCH / LA_FORM_THREE_LAUNCH may be or-ed in to force the
  * form (in the two-launch form the LA_STAGE_PREFIX bit does nothing); every
  * call on one workspace must use the same form.  la_scan_packed(...) is
