@@ -94,6 +94,7 @@ def load_library():
     lib.la_scan_packed_stages.argtypes = [ctypes.c_int32] + lib.la_scan_packed.argtypes
     lib.la_scan_launches.argtypes = [ctypes.POINTER(PassInfo), ctypes.c_int32, ctypes.c_int32,
                                      ctypes.c_int32, _I32P]
+    lib.la_choose_block_chunks.argtypes = [ctypes.c_int32, _I32P, _I32P, ctypes.c_int32, _I32P]
     lib.la_export_view_state.argtypes = [_P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                          ctypes.c_int32, ctypes.c_int32, _P, _P]
     lib.la_pack_pass_ext.argtypes = [ctypes.c_int32, _I32P, _I32P, _I32P, _I32P,
@@ -115,7 +116,7 @@ def load_library():
     lib.la_status_string.restype = ctypes.c_char_p
     for fn in ("la_pack_pass", "la_pack_pass_ext", "la_plan_segments",
                "la_scan_workspace_size", "la_scan_packed", "la_scan_packed_stages",
-               "la_scan_launches", "la_export_view_state", "la_cache_create", "la_cache_destroy",
+               "la_scan_launches", "la_choose_block_chunks", "la_export_view_state", "la_cache_create", "la_cache_destroy",
                "la_cache_lookup", "la_cache_reserve", "la_cache_erase", "la_cache_count",
                "la_attn_plan", "la_attn_packed"):
         getattr(lib, fn).restype = ctypes.c_int32
@@ -156,38 +157,15 @@ class PassPlan:
         return self._dev[key]
 
 
-def choose_block_chunks(chunks_per_segment, heads, target_groups=300, max_g=16,
-                        view_chunks=None, long_groups=2048, long_max_g=64):
-    """Chunks per work block: the largest power of two (<= max_g) whose block
-    count times `heads` still reaches `target_groups` workgroups (about one
-    per compute unit); 1 if none.  Larger blocks carry the state in registers
-    longer (less state traffic, fewer workgroup prologues and block states to
-    scan); smaller ones give more workgroups to fill 256 compute units and
-    shorter serial chains.  Past max_g the block doubles (up to long_max_g)
-    while the views alone still give `long_groups` workgroups (8 per compute
-    unit), i.e. while the pass is far from being bound by its longest chain:
-    measured on MI355X, the 272k-token pass of 32 requests at H = 32, d = 128
-    runs 3408 / 3276 / 3225 us at G = 16 / 32 / 64, while a single view of
-    18,000 tokens (144 view workgroups at G = 32) is fastest at G = 16."""
-    cps = np.asarray(chunks_per_segment, dtype=np.int64)
-    g = max_g
-    while g > 1:
-        nb = int(np.sum((cps + g - 1) // g))
-        if nb * heads >= target_groups:
-            break
-        g //= 2
-    if g == max_g and view_chunks is not None:
-        vc = np.asarray(view_chunks, dtype=np.int64)
-        while 2 * g <= long_max_g and int(np.sum((vc + 2 * g - 1) // (2 * g))) * heads >= long_groups:
-            g *= 2
-    return g
-
-
-def _auto_g(lengths, heads, view_lengths):
-    lengths = np.asarray(lengths, dtype=np.int64)
-    views = np.asarray(view_lengths, dtype=np.int64)
-    return choose_block_chunks((lengths + CHUNK - 1) // CHUNK, heads,
-                               view_chunks=(views + CHUNK - 1) // CHUNK)
+def choose_block_chunks(seg_offsets, branch_parent, heads):
+    """Work-block size for a segment table and H heads, from the library's
+    rule (la_choose_block_chunks)."""
+    lib = load_library()
+    so, bp = _i32(seg_offsets), _i32(branch_parent)
+    g = ctypes.c_int32()
+    _check("la_choose_block_chunks",
+           lib.la_choose_block_chunks(len(bp), _ptr(so), _ptr(bp), heads, ctypes.byref(g)))
+    return g.value
 
 
 def pack(view_len, branch_count, branch_len, heads=16, block_chunks=None, chunk=CHUNK,
@@ -200,9 +178,18 @@ def pack(view_len, branch_count, branch_len, heads=16, block_chunks=None, chunk=
     er = None if ext_row is None else _i32(ext_row)
     if er is not None and len(er) != len(vl):
         raise ValueError("ext_row needs one entry per request")
-    if block_chunks is None:
-        block_chunks = _auto_g(np.concatenate([vl[vl > 0], bl]), heads, vl[vl > 0])
     info = PassInfo()
+    if block_chunks is None:   # the segment table first, then the library's block size
+        _check("la_pack_pass", lib.la_pack_pass_ext(len(vl), _ptr(vl), _ptr(bc), _ptr(bl),
+                                                    _ptr(er), chunk, 1, None, None, None, None,
+                                                    ctypes.byref(info)))
+        so = np.zeros(info.n_segments + 1, dtype=np.int32)
+        bp = np.zeros(info.n_segments, dtype=np.int32)
+        _check("la_pack_pass", lib.la_pack_pass_ext(len(vl), _ptr(vl), _ptr(bc), _ptr(bl),
+                                                    _ptr(er), chunk, 1,
+                                                    so.ctypes.data_as(_I32P), _ptr(bp), None,
+                                                    None, ctypes.byref(info)))
+        block_chunks = choose_block_chunks(so, bp, heads)
     _check("la_pack_pass", lib.la_pack_pass_ext(len(vl), _ptr(vl), _ptr(bc), _ptr(bl),
                                                 _ptr(er), chunk, block_chunks, None, None,
                                                 None, None, ctypes.byref(info)))
@@ -222,8 +209,7 @@ def plan_segments(seg_offsets, branch_parent, heads=16, block_chunks=None, chunk
     lib = load_library()
     so, bp = _i32(seg_offsets), _i32(branch_parent)
     if block_chunks is None:
-        block_chunks = (_auto_g(np.diff(so), heads, np.diff(so)[np.asarray(bp) == -1])
-                        if len(bp) else 1)
+        block_chunks = choose_block_chunks(so, bp, heads)
     info = PassInfo()
     _check("la_plan_segments", lib.la_plan_segments(len(bp), _ptr(so), _ptr(bp), chunk,
                                                     block_chunks, None, None,

@@ -192,6 +192,45 @@ la_status plan_impl(int32_t n_seg, const int32_t* seg_offsets, const int32_t* br
 
 }  // namespace
 
+// Work-block size (chunks per block) for a pass of H heads: the largest
+// power of two up to kGroupMaxG whose blocks times H reach kGroupTarget
+// workgroups (about one per compute unit of an MI355X), 1 if none; then,
+// while the views alone still give kLongTarget workgroups at twice the size
+// (8 per compute unit, so the pass is far from bound by its longest chain),
+// doubled up to kLongMaxG.  Larger blocks carry the state in registers
+// longer (fewer block states to write, scan and read, fewer prologues);
+// smaller ones give more workgroups and shorter serial chains.  Measured on
+// MI355X: the 7,400-token pass is fastest at 8, a view of 18,000 tokens with
+// 256 branches at 16 (144 view workgroups at 32: 93.7 -> 102.6 us), the
+// 272k-token pass of 32 requests (H 32, d 128) at 64 (3408 / 3276 / 3225 us
+// at 16 / 32 / 64).
+extern "C" la_status la_choose_block_chunks(int32_t n_segments, const int32_t* seg_offsets,
+                                            const int32_t* branch_parent, int32_t heads,
+                                            int32_t* block_chunks) {
+    constexpr int64_t kGroupTarget = 300, kLongTarget = 2048;
+    constexpr int32_t kGroupMaxG = 16, kLongMaxG = 64;
+    if (!block_chunks || heads < 1 || n_segments < 0) return LA_ERR_INVALID_ARG;
+    if (n_segments > 0 && (!seg_offsets || !branch_parent)) return LA_ERR_INVALID_ARG;
+    std::vector<int64_t> chunks(static_cast<size_t>(n_segments));
+    for (int32_t s = 0; s < n_segments; ++s) {
+        const int64_t len = int64_t(seg_offsets[s + 1]) - seg_offsets[s];
+        if (len < 1) return LA_ERR_INVALID_ARG;
+        chunks[size_t(s)] = ceil_div(len, LA_CHUNK);
+    }
+    auto blocks = [&](int32_t g, bool views_only) {
+        int64_t nb = 0;
+        for (int32_t s = 0; s < n_segments; ++s)
+            if (!views_only || branch_parent[s] == -1) nb += ceil_div(chunks[size_t(s)], g);
+        return nb;
+    };
+    int32_t g = kGroupMaxG;
+    while (g > 1 && blocks(g, false) * heads < kGroupTarget) g /= 2;
+    if (g == kGroupMaxG)
+        while (2 * g <= kLongMaxG && blocks(2 * g, true) * heads >= kLongTarget) g *= 2;
+    *block_chunks = g;
+    return LA_OK;
+}
+
 extern "C" la_status la_plan_segments(int32_t n_segments, const int32_t* seg_offsets,
                                       const int32_t* branch_parent, int32_t chunk,
                                       int32_t block_chunks, int32_t* view_ordinal,

@@ -159,6 +159,22 @@ la_status la_plan_segments(int32_t n_segments, const int32_t* seg_offsets,
                            int32_t* plan, la_pass_info* info);
 
 /*
+ * la_choose_block_chunks -- a work-block size (chunks per block, the
+ * block_chunks argument of the planners) for a pass of `heads` heads: the
+ * largest power of two up to 16 whose blocks times heads reach 300
+ * workgroups (1 if none), doubled up to 64 while the view blocks alone
+ * still give 2048 workgroups.  Host only.
+ *   n_segments, seg_offsets, branch_parent   the segment table, as for
+ *                                            la_plan_segments
+ *   heads                                    H >= 1
+ *   block_chunks                             host, out
+ * Errors: LA_ERR_INVALID_ARG (NULL, heads < 1, an empty segment).
+ */
+la_status la_choose_block_chunks(int32_t n_segments, const int32_t* seg_offsets,
+                                 const int32_t* branch_parent, int32_t heads,
+                                 int32_t* block_chunks);
+
+/*
  * la_pack_pass -- pack request shapes into segments and build the plan
  * (section "The Workload": one view, then that request's branches;
  * paragraph "Shared branch passes": all requests of a pass in one forward).

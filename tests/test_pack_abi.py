@@ -260,10 +260,23 @@ def test_block_size_choice_on_the_workloads():
               "req32_view500-18000_br1-64x24-128_h32_d128_bf16": (32, 64)}
     for name, (H, G) in expect.items():
         assert la.pack(*synth.shapes(name), heads=H).info.block_chunks == G, name
-    # views too short for 2048 long workgroups stay at 16
-    assert la.choose_block_chunks([300] * 4, 16, view_chunks=[300] * 4) == 16
-    assert la.choose_block_chunks([300] * 64, 32, view_chunks=[300] * 64) == 64
-    assert la.choose_block_chunks([3], 2) == 1
+    def table(lens, parents):
+        return np.r_[0, np.cumsum(lens)].astype(np.int32), np.asarray(parents, dtype=np.int32)
+    # views too short for 2048 long workgroups stay at 16 (4 views of 300 chunks)
+    so, bp = table([300 * 64] * 4, [-1] * 4)
+    assert la.choose_block_chunks(so, bp, 16) == 16
+    so, bp = table([300 * 64] * 64, [-1] * 64)
+    assert la.choose_block_chunks(so, bp, 32) == 64
+    # branches count towards the 300 workgroups but not towards 2048
+    so, bp = table([3 * 64] + [64] * 400, [-1] + [0] * 400)
+    assert la.choose_block_chunks(so, bp, 1) == 16
+    so, bp = table([3 * 64], [-1])
+    assert la.choose_block_chunks(so, bp, 2) == 1
+    with pytest.raises(la.LinAttnError):
+        la.choose_block_chunks(so, bp, 0)
+    so, bp = table([5, 0], [-1, 0])
+    with pytest.raises(la.LinAttnError):
+        la.choose_block_chunks(so, bp, 2)
 
 
 def test_stage_and_form_bits_checked_before_any_device_work():
