@@ -51,7 +51,7 @@ def _run(q, k, v, plan, form, ext=None, split=False):
 
 @pytest.mark.parametrize("dtype,d,split", [("bf16", 64, False), ("bf16", 128, False),
                                            ("f32", 64, False), ("f32", 128, False),
-                                           ("f32", 64, True)])
+                                           ("f32", 64, True), ("f32", 128, True)])
 @pytest.mark.parametrize("G", [1, 3])
 @pytest.mark.parametrize("case", range(len(STRUCTS)))
 def test_two_and_three_launch_forms_agree(dtype, d, split, G, case):
