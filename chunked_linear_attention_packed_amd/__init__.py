@@ -261,6 +261,62 @@ def _stream_ptr(stream, device):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _alloc(shape, dtype, device, stream):
+    """torch.empty on `stream`'s side of the caching allocator: a buffer made
+    for work enqueued on a caller-given stream is returned to that stream's
+    pool when it is dropped, so no later allocation on another stream can
+    reuse it while the work still runs."""
+    import torch
+    if stream is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    with torch.cuda.stream(stream):
+        return torch.empty(shape, dtype=dtype, device=device)
+
+
+def _check_tensor(name, t, shape, dtype, device, min_rows=None):
+    """Shape, dtype, device and layout of a caller-supplied buffer; the C ABI
+    sees only its address, so a wrong one would be read or written past its
+    end."""
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if min_rows is None:
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    elif t.dim() != len(shape) or tuple(t.shape[1:]) != tuple(shape[1:]) or t.shape[0] < min_rows:
+        raise ValueError(f"{name} must have shape [>= {min_rows}, {', '.join(map(str, shape[1:]))}],"
+                         f" got {tuple(t.shape)}")
+
+
+def check_scan_buffers(q, v, info, out=None, final_state=None, ext_state=None, workspace=None,
+                       need=0):
+    """Validates the caller-supplied buffers of scan_packed against the inputs
+    and the pass (any device: also usable on CPU tensors)."""
+    import torch
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    dev = q.device
+    if out is not None:
+        _check_tensor("out", out, (T, H, dv), q.dtype, dev)
+    if final_state is not None:
+        _check_tensor("final_state", final_state, (info.n_views, H, dk, dv), torch.float32, dev)
+    if ext_state is not None:
+        _check_tensor("ext_state", ext_state, (info.n_ext, H, dk, dv), torch.float32, dev,
+                      min_rows=info.n_ext)
+    elif info.n_ext > 0:
+        raise ValueError(f"the pass has shard branches: ext_state needs >= {info.n_ext} rows")
+    if workspace is not None:
+        if workspace.device != dev:
+            raise ValueError(f"workspace must be on {dev}, got {workspace.device}")
+        if not workspace.is_contiguous():
+            raise ValueError("workspace must be contiguous")
+        if workspace.numel() * workspace.element_size() < need:
+            raise ValueError(f"workspace needs {need} bytes")
+
+
 def scan_packed(q, k, v, plan, ext_state=None, out=None, final_state=None, workspace=None,
                 stream=None, stages=STAGE_ALL, split_fp32=False, form=None):
     """Run the scan on `stream` (default: torch's current stream).
@@ -268,8 +324,10 @@ def scan_packed(q, k, v, plan, ext_state=None, out=None, final_state=None, works
     q, k: [T, H, d] and v: [T, H, d] contiguous CUDA tensors, bf16 or fp32.
     Returns (out [T, H, d] in the input dtype, final_state [n_views, H, d, d]
     fp32).  Pre-allocated out / final_state / workspace tensors are used as
-    given (no allocation then).  `stages` selects launches (STAGE_* bits, see
-    la_scan_packed_stages) for profiling; the default runs all three.  For
+    given (no allocation then); they are checked for shape, dtype, device and
+    layout.  Buffers allocated here for work on a caller-given stream come
+    from that stream's pool.  `stages` selects launches (STAGE_* bits, see
+    la_scan_packed_stages) for profiling; the default runs all of them.  For
     fp32 inputs, split_fp32=True evaluates every product as three bf16 MFMAs
     over hi/lo operand splits (LA_F32_SPLIT) instead of fp32 MFMAs.  `form`
     forces the two-launch ("two": no prefix launch) or the three-launch
@@ -284,6 +342,8 @@ def scan_packed(q, k, v, plan, ext_state=None, out=None, final_state=None, works
         raise ValueError("q, k, v must be contiguous")
     if not (q.dtype == k.dtype == v.dtype):
         raise TypeError("q, k, v must share a dtype")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on one device")
     T, H, dk = q.shape
     dv = v.shape[2]
     info = plan.info
@@ -294,24 +354,23 @@ def scan_packed(q, k, v, plan, ext_state=None, out=None, final_state=None, works
         if code != LA_F32:
             raise TypeError("split_fp32 applies to float32 inputs")
         code = LA_F32_SPLIT
+    if form not in _FORMS:
+        raise ValueError(f"form must be one of {sorted(k for k in _FORMS if k)} or None")
     dev = q.device
-    if out is None:
-        out = torch.empty((T, H, dv), dtype=q.dtype, device=dev)
-    if final_state is None:
-        final_state = torch.empty((info.n_views, H, dk, dv), dtype=torch.float32, device=dev)
     need = workspace_size(plan, H, dk, code)
+    check_scan_buffers(q, v, info, out, final_state, ext_state, workspace, need)
+    if out is None:
+        out = _alloc((T, H, dv), q.dtype, dev, stream)
+    if final_state is None:
+        final_state = _alloc((info.n_views, H, dk, dv), torch.float32, dev, stream)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        workspace = _alloc((max(need, 1),), torch.uint8, dev, stream)
     ws_bytes = workspace.numel() * workspace.element_size()
     n_ext = 0
     ext_ptr = None
     if ext_state is not None:
-        if ext_state.dtype != torch.float32 or not ext_state.is_contiguous():
-            raise TypeError("ext_state must be contiguous float32 [n_ext, H, d, d]")
         n_ext = ext_state.shape[0]
         ext_ptr = ctypes.c_void_p(ext_state.data_ptr())
-    if form not in _FORMS:
-        raise ValueError(f"form must be one of {sorted(k for k in _FORMS if k)} or None")
     dplan = plan.device_plan(dev)
     st = lib.la_scan_packed_stages(stages | _FORMS[form], ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
                             ctypes.c_void_p(v.data_ptr()), code, H, dk, dv,
@@ -330,8 +389,12 @@ def export_view_state(final_state, view_row, dst=None, stream=None):
     import torch
     lib = load_library()
     nv, H, dk, dv = final_state.shape
+    if final_state.dtype != torch.float32 or not final_state.is_contiguous():
+        raise TypeError("final_state must be contiguous float32 [n_views, H, d, d]")
     if dst is None:
-        dst = torch.empty((H, dk, dv), dtype=torch.float32, device=final_state.device)
+        dst = _alloc((H, dk, dv), torch.float32, final_state.device, stream)
+    else:
+        _check_tensor("dst", dst, (H, dk, dv), torch.float32, final_state.device)
     _check("la_export_view_state",
            lib.la_export_view_state(ctypes.c_void_p(final_state.data_ptr()), view_row, nv, H,
                                     dk, dv, ctypes.c_void_p(dst.data_ptr()),
