@@ -14,6 +14,7 @@ import torch
 
 import oracle
 import synth
+from tests import oracle_pool
 import chunked_linear_attention_packed_amd as la
 
 pytestmark = pytest.mark.gpu
@@ -107,21 +108,30 @@ def test_several_external_views_and_a_packed_view_in_one_pass():
     assert err <= TOL
 
 
+def _attn_heads_worker(h):
+    """fp64 attention oracle (attention_dense) for one head of the shared pass."""
+    sh = oracle_pool.SHARED
+    sl = slice(h, h + 1)
+    return oracle.attention_dense(sh["q"][:, sl], sh["k"][:, sl], sh["v"][:, sl], sh["so"],
+                                  sh["bp"], 1.0)
+
+
 @pytest.mark.parametrize("name", ["view7400_br8x48_h16_d64_bf16",
                                   "view18000_br256x32-128_h16_d64_bf16"])
-def test_attention_workload_sampled_rows(name):
+def test_attention_workload_full_parity(name):
+    """The workload's whole pass compared element by element with the fp64
+    attention oracle (every row of every head; heads on a process pool)."""
     w = synth.workload(name)
     so, bp, _ = oracle.pack_segments(w.view_len, w.branch_count, w.branch_len)
     plan = la.attn_plan(so, bp)
     out = la.attn_packed(w.q.to(DEV), w.k.to(DEV), w.v.to(DEV), plan, 1.0)
     torch.cuda.synchronize()
-    T = int(so[-1])
-    rng = np.random.default_rng(5)
-    rows = sorted(set(rng.integers(0, T, size=48).tolist()) |
-                  {0, 63, 64, int(so[1]) - 1, int(so[1]), T - 1})
-    ref = oracle.attention_rows(w.q, w.k, w.v, so, bp, 1.0, rows)
-    err = oracle.row_rel_err(out[rows].cpu(), ref)
-    print(f"{name}: {len(rows)} sampled rows, err {err:.2e}", flush=True)
+    shared = dict(q=oracle_pool.to_f32(w.q), k=oracle_pool.to_f32(w.k),
+                  v=oracle_pool.to_f32(w.v), so=so, bp=bp)
+    parts = oracle_pool.run(_attn_heads_worker, list(range(w.H)), shared)
+    ref = np.concatenate(parts, axis=1)
+    err = oracle.row_rel_err(out.cpu(), ref)
+    print(f"{name}: all {w.n_tokens} rows x {w.H} heads, err {err:.2e}", flush=True)
     assert err <= TOL
 
 

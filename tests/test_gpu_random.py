@@ -74,6 +74,38 @@ def test_random_scan(i):
     assert eo <= TOL[dtype] and ef <= TOL[dtype]
 
 
+@pytest.mark.parametrize("i", range(4))
+def test_random_scan_d128_large_blocks(i):
+    """d = 128 at the large block sizes the library picks for long passes
+    (G = 16 and 64), random structures with shard requests, all three forms
+    equal bit for bit and within tolerance of the oracle."""
+    rng = np.random.default_rng(7500 + i)
+    vl, bc, bl = _structure(rng)
+    vl = [x * 6 if x else 0 for x in vl]          # views long enough for several blocks
+    G = (16, 64)[i % 2]
+    H = 2
+    plan = la.pack(vl, bc, bl, heads=H, block_chunks=G)
+    T = plan.info.n_tokens
+    q, k, v = synth.draw_qkv(rng, T, H, 128, "bf16")
+    n_ext = plan.info.n_ext
+    ext = (torch.from_numpy(rng.standard_normal((n_ext, H, 128, 128)).astype(np.float32))
+           if n_ext else None)
+    print(f"case {i}: views {vl} branches {bc} T={T} G={G} ext={n_ext}", flush=True)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    ed = None if ext is None else ext.to(DEV)
+    out, fin = la.scan_packed(qd, kd, vd, plan, ext_state=ed)
+    for form in ("two", "three"):
+        o_f, f_f = la.scan_packed(qd, kd, vd, plan, ext_state=ed, form=form)
+        assert torch.equal(o_f, out) and torch.equal(f_f, fin), form
+    torch.cuda.synchronize()
+    ref_o, ref_f = oracle.scan_recurrence(q, k, v, plan.seg_offsets, plan.branch_parent,
+                                          ext_state=ext)
+    eo = oracle.row_rel_err(out.cpu(), ref_o)
+    ef = oracle.state_rel_err(fin.cpu(), ref_f) if plan.info.n_views else 0.0
+    print(f"  out err {eo:.2e} final err {ef:.2e}", flush=True)
+    assert eo <= TOL["bf16"] and ef <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("i", range(12))
 def test_random_attention(i):
     rng = np.random.default_rng(8000 + i)
