@@ -33,7 +33,9 @@ __all__ = ["LinAttnError", "PassInfo", "PassPlan", "pack", "plan_segments",
            "library_path", "load_library", "CHUNK"]
 
 CHUNK = 64
-LA_OK, LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED, LA_ERR_WORKSPACE, LA_ERR_HIP = range(5)
+(LA_OK, LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED, LA_ERR_WORKSPACE, LA_ERR_HIP,
+ LA_ERR_TOO_LARGE) = range(6)
+NOALLOC_SCRATCH_BYTES = 64 << 20
 LA_F32, LA_BF16, LA_F32_SPLIT = 0, 1, 2
 LA_ATTN_NO_VIEW, LA_ATTN_PACKED_VIEW, LA_ATTN_EXT_VIEW = 0, 1, 2
 STAGE_STATES, STAGE_PREFIX, STAGE_OUTPUT, STAGE_ALL = 1, 2, 4, 7
@@ -92,6 +94,7 @@ def load_library():
                                    ctypes.c_int32, ctypes.POINTER(PassInfo), _P, _P,
                                    ctypes.c_int32, _P, _P, _P, ctypes.c_size_t, _P]
     lib.la_scan_packed_stages.argtypes = [ctypes.c_int32] + lib.la_scan_packed.argtypes
+    lib.la_scan_packed_noalloc.argtypes = lib.la_scan_packed.argtypes[:13] + [_P]
     lib.la_scan_launches.argtypes = [ctypes.POINTER(PassInfo), ctypes.c_int32, ctypes.c_int32,
                                      ctypes.c_int32, _I32P]
     lib.la_choose_block_chunks.argtypes = [ctypes.c_int32, _I32P, _I32P, ctypes.c_int32, _I32P]
@@ -116,6 +119,7 @@ def load_library():
     lib.la_status_string.restype = ctypes.c_char_p
     for fn in ("la_pack_pass", "la_pack_pass_ext", "la_plan_segments",
                "la_scan_workspace_size", "la_scan_packed", "la_scan_packed_stages",
+               "la_scan_packed_noalloc",
                "la_scan_launches", "la_choose_block_chunks", "la_export_view_state", "la_cache_create", "la_cache_destroy",
                "la_cache_lookup", "la_cache_reserve", "la_cache_erase", "la_cache_count",
                "la_attn_plan", "la_attn_packed"):

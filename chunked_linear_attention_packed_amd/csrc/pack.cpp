@@ -372,6 +372,8 @@ extern "C" const char* la_status_string(la_status status) {
         case LA_ERR_UNSUPPORTED: return "unsupported dtype, head dim or chunk size";
         case LA_ERR_WORKSPACE: return "workspace missing or too small";
         case LA_ERR_HIP: return "HIP runtime error";
+        case LA_ERR_TOO_LARGE:
+            return "the pass needs more workspace than the library's built-in scratch array holds";
         default: return "unknown status";
     }
 }

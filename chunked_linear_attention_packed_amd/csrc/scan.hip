@@ -42,6 +42,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <mutex>
 #include <type_traits>
 
 #include "linattn.h"
@@ -1326,6 +1327,52 @@ la_status launch_all(int32_t stages, bool fused, const void* q, const void* k, c
     return LA_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Built-in scratch memory for la_scan_packed_noalloc (callers that cannot
+// allocate).  One copy per GPU; host code never uses the array's name as an
+// address: each device's copy is found once with hipGetSymbolAddress and that
+// pointer is what the kernels receive, exactly like a caller's workspace.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[LA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxScratchDevices = 64;
+// the first bytes of the array are cleared once per GPU at set-up
+constexpr size_t kScratchClearBytes = size_t(1) << 20;
+
+struct ScratchDevice {
+    std::once_flag once;
+    void* ptr = nullptr;
+    la_status status = LA_ERR_HIP;
+};
+ScratchDevice g_scratch[kMaxScratchDevices];
+
+__global__ __launch_bounds__(kThreads) void fill_zero_kernel(f32x4* __restrict__ p, int64_t n4) {
+    const int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+    if (i < n4) p[i] = zero4();
+}
+
+// The current device's copy of `scratch`; set-up (address, clearing) on the
+// first call for that device, with the device current.
+la_status scratch_for_current_device(hipStream_t st, void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices)
+        return LA_ERR_HIP;
+    ScratchDevice& sd = g_scratch[dev];
+    std::call_once(sd.once, [&]() {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return;
+        const int64_t n4 = int64_t(kScratchClearBytes / 16);
+        hipLaunchKernelGGL(fill_zero_kernel, dim3(unsigned((n4 + kThreads - 1) / kThreads)),
+                           dim3(kThreads), 0, st, static_cast<f32x4*>(p), n4);
+        if (hipGetLastError() != hipSuccess) return;
+        sd.ptr = p;
+        sd.status = LA_OK;
+    });
+    if (sd.status != LA_OK) return sd.status;
+    *out = sd.ptr;
+    return LA_OK;
+}
+
 }  // namespace
 
 extern "C" la_status la_scan_workspace_size(const la_pass_info* info, int32_t H, int32_t d_k,
@@ -1428,4 +1475,23 @@ extern "C" la_status la_export_view_state(const float* final_state, int32_t view
                        reinterpret_cast<f32x4*>(dst), n4);
     if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
     return LA_OK;
+}
+
+extern "C" la_status la_scan_packed_noalloc(const void* q, const void* k, const void* v,
+                                            la_dtype dtype, int32_t H, int32_t d_k,
+                                            int32_t d_v, const la_pass_info* info,
+                                            const int32_t* plan, const float* ext_state,
+                                            int32_t n_ext, void* out, float* final_state,
+                                            void* stream) {
+    if (!info) return LA_ERR_INVALID_ARG;
+    size_t need = 0;
+    const la_status sz = la_scan_workspace_size(info, H, d_k, d_v, dtype, &need);
+    if (sz != LA_OK) return sz;
+    if (need > size_t(LA_NOALLOC_SCRATCH_BYTES)) return LA_ERR_TOO_LARGE;
+    void* ws = nullptr;
+    const la_status ss = scratch_for_current_device(static_cast<hipStream_t>(stream), &ws);
+    if (ss != LA_OK) return ss;
+    return la_scan_packed_stages(LA_STAGE_ALL, q, k, v, dtype, H, d_k, d_v, info, plan,
+                                 ext_state, n_ext, out, final_state, ws,
+                                 size_t(LA_NOALLOC_SCRATCH_BYTES), stream);
 }

@@ -25,7 +25,9 @@
  *     segment; q, k, v and out are dense, token-major [T][H][d] arrays.
  *   - "host" pointers are ordinary CPU memory; "device" pointers are HIP device
  *     memory of the current device.  The caller owns every buffer; the library
- *     allocates nothing and keeps no state between calls.
+ *     allocates nothing and keeps no state between calls, except the built-in
+ *     scratch array behind la_scan_packed_noalloc (for callers that cannot
+ *     allocate).
  *   - stream is a hipStream_t passed as void* (NULL = the null stream).
  *     Device calls only enqueue work and return; results are ready when the
  *     stream is synchronised.  Calls on different streams may overlap.
@@ -52,7 +54,10 @@ enum {
     LA_ERR_INVALID_ARG = 1,   /* NULL pointer, bad length, bad parent, ... */
     LA_ERR_UNSUPPORTED = 2,   /* dtype, head dim or chunk size not built   */
     LA_ERR_WORKSPACE = 3,     /* workspace missing or too small            */
-    LA_ERR_HIP = 4            /* a HIP runtime call or launch failed       */
+    LA_ERR_HIP = 4,           /* a HIP runtime call or launch failed       */
+    LA_ERR_TOO_LARGE = 5      /* the pass needs more scratch memory than the
+                                 library's built-in array holds
+                                 (la_scan_packed_noalloc)                  */
 };
 
 typedef int32_t la_dtype;
@@ -425,6 +430,33 @@ la_status la_cache_reserve(la_state_cache* cache, int64_t view_id, int32_t* row,
                            int64_t* evicted_id);
 la_status la_cache_erase(la_state_cache* cache, int64_t view_id);
 la_status la_cache_count(const la_state_cache* cache, int32_t* n);
+
+/*
+ * la_scan_packed_noalloc -- la_scan_packed for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the workspace is taken from an array the library
+ * holds in device memory, LA_NOALLOC_SCRATCH_BYTES bytes per GPU, resident
+ * from the first call on that GPU until the process ends.  Nothing is
+ * allocated and no allocating routine is called; the caller still passes the
+ * inputs and outputs.
+ *   Arguments, layouts and results as la_scan_packed, without workspace and
+ *   workspace_bytes.  The results are those of la_scan_packed (the same
+ *   kernels run on the same arguments).
+ * Every call on one GPU shares that GPU's array, and the array keeps the last
+ * call's contents: calls that may overlap on one GPU (different streams, or
+ * graph replays running concurrently) race and must be ordered by the
+ * caller.  The first call on a GPU also clears the start of the array (one
+ * small kernel on `stream`).
+ * Errors: as la_scan_packed, plus LA_ERR_TOO_LARGE when the pass needs more
+ * than LA_NOALLOC_SCRATCH_BYTES of workspace (la_scan_workspace_size), and
+ * LA_ERR_HIP when the array's device address cannot be obtained.
+ */
+#define LA_NOALLOC_SCRATCH_BYTES (64u << 20)
+la_status la_scan_packed_noalloc(const void* q, const void* k, const void* v, la_dtype dtype,
+                                 int32_t H, int32_t d_k, int32_t d_v,
+                                 const la_pass_info* info, const int32_t* plan,
+                                 const float* ext_state, int32_t n_ext, void* out,
+                                 float* final_state, void* stream);
 
 /* Static text for a status code. */
 const char* la_status_string(la_status status);

@@ -316,3 +316,20 @@ def test_ext_state_overlapping_final_state_rejected():
                                       fake, ctypes.c_void_p(base), None, 0, None)
         assert r == la.LA_ERR_INVALID_ARG, hex(ext)
     del plan
+
+
+def test_noalloc_rejects_passes_beyond_its_scratch():
+    """la_scan_packed_noalloc checks the pass's workspace against its built-in
+    array on the host and returns LA_ERR_TOO_LARGE before any device work (so
+    this runs without a GPU)."""
+    lib = la.load_library()
+    # one view of 2^17 tokens in blocks of one chunk: 2048 block states of
+    # 16 KiB per head, 32 MiB per head, 128 MiB at 4 heads
+    plan = la.pack([1 << 17], [0], [], heads=4, block_chunks=1)
+    need = la.workspace_size(plan, 4, 64, la.LA_BF16)
+    assert need > la.NOALLOC_SCRATCH_BYTES
+    fake = ctypes.c_void_p(16)
+    st = lib.la_scan_packed_noalloc(fake, fake, fake, la.LA_BF16, 4, 64, 64,
+                                    ctypes.byref(plan.info), fake, None, 0, fake, fake, None)
+    assert st == la.LA_ERR_TOO_LARGE
+    assert b"scratch" in lib.la_status_string(st)
