@@ -39,9 +39,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--block-chunks", type=int, default=None)
-    ap.add_argument("--form", choices=["auto", "two", "three"], default="auto",
-                    help="scan form: two launches (no prefix launch), three, or the "
-                         "library's choice for the pass shape")
+    ap.add_argument("--form", choices=["auto", "one", "two", "three"], default="auto",
+                    help="scan form: one launch (d 64 bf16), two launches (no prefix "
+                         "launch), three, or the library's choice for the pass shape")
     ap.add_argument("--rotate-gib", type=float, default=1.0,
                     help="total size of the rotated input copies")
     ap.add_argument("--eager", action="store_true",
@@ -236,8 +236,7 @@ def shard_bench(a):
         qq, kk, vv = qq.contiguous(), kk.contiguous(), vv.contiguous()
         out = torch.empty_like(vv)
         fin = torch.empty((plan.info.n_views, H, d, d), dtype=torch.float32, device=dev)
-        ws = torch.empty(max(la.workspace_size(plan, H, d, qq.dtype), 1), dtype=torch.uint8,
-                         device=dev)
+        ws = la.new_workspace(plan, H, d, qq.dtype, dev)
         plan.device_plan(dev)
         return dict(plan=plan, q=qq, k=kk, v=vv, out=out, fin=fin, ws=ws, ext=ext)
 
@@ -417,8 +416,7 @@ def cost_model_bench(a):
         q, k, v = (x.to(dev) for x in synth.draw_qkv(rng, T, H, d, "bf16"))
         out = torch.empty_like(v)
         fin = torch.empty((plan.info.n_views, H, d, d), dtype=torch.float32, device=dev)
-        ws = torch.empty(max(la.workspace_size(plan, H, d, q.dtype), 1), dtype=torch.uint8,
-                         device=dev)
+        ws = la.new_workspace(plan, H, d, q.dtype, dev)
         plan.device_plan(dev)
         fn = lambda: la.scan_packed(q, k, v, plan, out=out, final_state=fin, workspace=ws,
                                     stream=stream)
@@ -513,14 +511,15 @@ def main():
         sets.append(dict(q=q0.clone(), k=k0.clone(), v=v0.clone(), out=torch.empty_like(v0)))
     del q0, k0, v0
     fin = torch.empty((info.n_views, H, d, d), dtype=torch.float32, device=dev)
-    ws = torch.empty(max(la.workspace_size(plan, H, d, w.q.dtype), 1), dtype=torch.uint8,
-                     device=dev)
+    ws = la.new_workspace(plan, H, d, w.q.dtype, dev)
     plan.device_plan(dev)
     stream = torch.cuda.Stream(dev)
     if a.split_fp32 and w.dtype != "f32":
         raise SystemExit("--split-fp32 applies to fp32 workloads")
     form = None if a.form == "auto" else a.form
-    n_launches = {"two": 2, "three": 3}.get(a.form) or la.scan_launches(plan, H, d)
+    code = la.LA_F32_SPLIT if a.split_fp32 else (la.LA_BF16 if w.dtype == "bf16" else la.LA_F32)
+    n_launches = {"one": 1, "two": 2, "three": 3}.get(a.form) or la.scan_launches(plan, H, d,
+                                                                                  code)
 
     def step(i, stages=la.STAGE_ALL):
         s = sets[i % n_sets]
@@ -568,7 +567,7 @@ def main():
     two_stream = None
     if not a.eager:
         s1 = torch.cuda.Stream(dev)
-        ws2 = [ws, torch.empty_like(ws)]
+        ws2 = [ws, torch.zeros_like(ws)]
         fin2 = [fin, torch.empty_like(fin)]
 
         def step2(i):

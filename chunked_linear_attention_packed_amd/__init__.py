@@ -28,19 +28,22 @@ from dataclasses import dataclass, field
 import numpy as np
 
 __all__ = ["LinAttnError", "PassInfo", "PassPlan", "pack", "plan_segments",
-           "choose_block_chunks", "workspace_size", "scan_launches", "scan_packed",
+           "choose_block_chunks", "workspace_size", "new_workspace", "scan_launches",
+           "scan_status", "scan_packed",
            "export_view_state", "ViewStateCache", "AttnPlan", "attn_plan", "attn_packed",
            "library_path", "load_library", "CHUNK"]
 
 CHUNK = 64
 (LA_OK, LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED, LA_ERR_WORKSPACE, LA_ERR_HIP,
- LA_ERR_TOO_LARGE) = range(6)
+ LA_ERR_TOO_LARGE, LA_ERR_PLAN, LA_ERR_TIMEOUT) = range(8)
 NOALLOC_SCRATCH_BYTES = 64 << 20
 LA_F32, LA_BF16, LA_F32_SPLIT = 0, 1, 2
 LA_ATTN_NO_VIEW, LA_ATTN_PACKED_VIEW, LA_ATTN_EXT_VIEW = 0, 1, 2
 STAGE_STATES, STAGE_PREFIX, STAGE_OUTPUT, STAGE_ALL = 1, 2, 4, 7
-FORM_TWO_LAUNCH, FORM_THREE_LAUNCH = 8, 16
-_FORMS = {None: 0, "auto": 0, "two": FORM_TWO_LAUNCH, "three": FORM_THREE_LAUNCH}
+FORM_TWO_LAUNCH, FORM_THREE_LAUNCH, FORM_ONE_LAUNCH = 8, 16, 32
+DEBUG_FORCE_TIMEOUT = 64
+_FORMS = {None: 0, "auto": 0, "one": FORM_ONE_LAUNCH, "two": FORM_TWO_LAUNCH,
+          "three": FORM_THREE_LAUNCH}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -59,7 +62,9 @@ class PassInfo(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "n_requests", "n_segments", "n_views", "n_branches", "n_ext", "n_tokens", "chunk",
         "block_chunks", "n_chunks", "n_view_chunks", "n_blocks", "n_delta", "n_scan",
-        "plan_words", "max_seg_tokens", "fused_slot_reads")] + [("reserved", ctypes.c_int32 * 8)]
+        "plan_words", "max_seg_tokens", "fused_slot_reads", "piece_blocks", "piece_items",
+        "piece_block_items", "piece_slots", "piece_scans", "plan_hash", "info_check")] + [
+        ("reserved", ctypes.c_int32 * 1)]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_ if n != "reserved"}
@@ -96,7 +101,10 @@ def load_library():
     lib.la_scan_packed_stages.argtypes = [ctypes.c_int32] + lib.la_scan_packed.argtypes
     lib.la_scan_packed_noalloc.argtypes = lib.la_scan_packed.argtypes[:13] + [_P]
     lib.la_scan_launches.argtypes = [ctypes.POINTER(PassInfo), ctypes.c_int32, ctypes.c_int32,
-                                     ctypes.c_int32, _I32P]
+                                     ctypes.c_int32, ctypes.c_int32, _I32P]
+    lib.la_scan_status.argtypes = [_P, ctypes.c_size_t, _I32P, ctypes.c_int32, _P]
+    lib.la_info_checksum.argtypes = [ctypes.POINTER(PassInfo)]
+    lib.la_info_checksum.restype = ctypes.c_uint32
     lib.la_choose_block_chunks.argtypes = [ctypes.c_int32, _I32P, _I32P, ctypes.c_int32, _I32P]
     lib.la_export_view_state.argtypes = [_P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                          ctypes.c_int32, ctypes.c_int32, _P, _P]
@@ -119,7 +127,7 @@ def load_library():
     lib.la_status_string.restype = ctypes.c_char_p
     for fn in ("la_pack_pass", "la_pack_pass_ext", "la_plan_segments",
                "la_scan_workspace_size", "la_scan_packed", "la_scan_packed_stages",
-               "la_scan_packed_noalloc",
+               "la_scan_packed_noalloc", "la_scan_status",
                "la_scan_launches", "la_choose_block_chunks", "la_export_view_state", "la_cache_create", "la_cache_destroy",
                "la_cache_lookup", "la_cache_reserve", "la_cache_erase", "la_cache_count",
                "la_attn_plan", "la_attn_packed"):
@@ -245,13 +253,37 @@ def workspace_size(plan, heads, d, dtype):
     return n.value
 
 
-def scan_launches(plan, heads, d):
-    """Launches scan_packed uses for this pass by default: 2 or 3."""
+def scan_launches(plan, heads, d, dtype=LA_BF16):
+    """Launches scan_packed uses for this pass by default: 1, 2 or 3."""
     lib = load_library()
     n = ctypes.c_int32()
+    code = dtype if isinstance(dtype, int) else _dtype_code_from_torch(dtype)
     _check("la_scan_launches",
-           lib.la_scan_launches(ctypes.byref(plan.info), heads, d, d, ctypes.byref(n)))
+           lib.la_scan_launches(ctypes.byref(plan.info), heads, d, d, code, ctypes.byref(n)))
     return n.value
+
+
+def new_workspace(plan, heads, d, dtype, device, stream=None):
+    """A zero-filled workspace of the size the pass needs (the single-launch
+    form needs its header and flags zero before the first pass)."""
+    import torch
+    n = max(workspace_size(plan, heads, d, dtype), 256)
+    if stream is None:
+        return torch.zeros(n, dtype=torch.uint8, device=device)
+    with torch.cuda.stream(stream):
+        return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def scan_status(workspace, clear=False, stream=None):
+    """The sticky status word the kernels left in a workspace (0: none; else
+    LA_ERR_PLAN / LA_ERR_TIMEOUT bits); synchronises the stream."""
+    lib = load_library()
+    st = ctypes.c_int32()
+    _check("la_scan_status",
+           lib.la_scan_status(ctypes.c_void_p(workspace.data_ptr()),
+                              workspace.numel() * workspace.element_size(), ctypes.byref(st),
+                              1 if clear else 0, _stream_ptr(stream, workspace.device)))
+    return st.value
 
 
 def _dtype_code_from_torch(dt):
@@ -334,8 +366,10 @@ def scan_packed(q, k, v, plan, ext_state=None, out=None, final_state=None, works
     la_scan_packed_stages) for profiling; the default runs all of them.  For
     fp32 inputs, split_fp32=True evaluates every product as three bf16 MFMAs
     over hi/lo operand splits (LA_F32_SPLIT) instead of fp32 MFMAs.  `form`
-    forces the two-launch ("two": no prefix launch) or the three-launch
-    ("three") form; None lets the library choose from the pass shape."""
+    forces the single-launch ("one": d 64 bf16 only), two-launch ("two": no
+    prefix launch) or three-launch ("three") form; None lets the library
+    choose.  A caller-given workspace must be zero-filled before its first
+    use (new_workspace)."""
     import torch
     lib = load_library()
     if not (q.is_cuda and k.is_cuda and v.is_cuda):
@@ -368,7 +402,7 @@ def scan_packed(q, k, v, plan, ext_state=None, out=None, final_state=None, works
     if final_state is None:
         final_state = _alloc((info.n_views, H, dk, dv), torch.float32, dev, stream)
     if workspace is None:
-        workspace = _alloc((max(need, 1),), torch.uint8, dev, stream)
+        workspace = new_workspace(plan, H, dk, code, dev, stream)
     ws_bytes = workspace.numel() * workspace.element_size()
     n_ext = 0
     ext_ptr = None

@@ -4,9 +4,9 @@
 
 The host code (pack.cpp: packer and planners; cache.cpp: view-state cache
 directory) is compiled with g++; the kernels and their host entry points
-(scan.hip: the linear-attention scan; attn.hip: the tree-masked softmax
-attention) with hipcc; all are linked into one shared library next to this
-file.  Always recompiles.
+(scan.hip: the linear-attention scan; piece.hip: its d = 64 bf16 path;
+attn.hip: the tree-masked softmax attention) with hipcc; all are linked into
+one shared library next to this file.  Always recompiles.
 """
 import os
 import shutil
@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "liblinattn.so")
 HOST_SOURCES = ["pack.cpp", "cache.cpp"]
-HIP_SOURCES = ["scan.hip", "attn.hip"]
+HIP_SOURCES = ["scan.hip", "piece.hip", "attn.hip"]
 
 HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -18,7 +18,27 @@
 
 namespace {
 
-constexpr int32_t kPlanVersion = 2;
+constexpr int32_t kPlanVersion = 3;
+
+// Piece path (d = 64, bf16): blocks of LA_PIECE_BLOCK_CHUNKS chunks, each cut
+// into pieces of LA_PIECE_CHUNKS chunks, one per wave of a 4-wave workgroup.
+// A branch whose only block is a single piece shares a workgroup with up to
+// three other such branches (one per wave).
+constexpr int32_t kPieceBlockTok = LA_PIECE_BLOCK_CHUNKS * LA_CHUNK;
+constexpr int32_t kPieceTok = LA_PIECE_CHUNKS * LA_CHUNK;
+
+// FNV-1a over the plan words, with the hash word itself taken as zero.
+uint32_t plan_hash(const int32_t* plan, int64_t words) {
+    uint32_t h = 2166136261u;
+    for (int64_t i = 0; i < words; ++i) {
+        const uint32_t w = i == LA_PLAN_HASH_WORD ? 0u : uint32_t(plan[i]);
+        for (int b = 0; b < 4; ++b) {
+            h ^= (w >> (8 * b)) & 0xffu;
+            h *= 16777619u;
+        }
+    }
+    return h;
+}
 
 struct Seg {
     int32_t off, len, parent;
@@ -93,8 +113,30 @@ la_status plan_impl(int32_t n_seg, const int32_t* seg_offsets, const int32_t* br
                 fused_reads += nb * ceil_div(int64_t(seg_offsets[p + 1]) - seg_offsets[p], blk_tok);
         }
     }
+    // Piece path tables: blocks of kPieceBlockTok tokens; a view's blocks all
+    // get a state slot (its total is final_state, its branches start from
+    // it), a branch's all but the last; branches whose only block is a
+    // single piece are packed four to a workgroup, everything else is one
+    // workgroup per block.
+    int64_t p_blocks = 0, p_slots = 0, p_scan = 0, p_block_items = 0, p_packable = 0;
+    for (int32_t s = 0; s < n_seg; ++s) {
+        const bool is_view = branch_parent[s] == -1;
+        const int64_t len = int64_t(seg_offsets[s + 1]) - seg_offsets[s];
+        const int64_t nb = ceil_div(len, kPieceBlockTok);
+        const int64_t nslots = is_view ? nb : nb - 1;
+        p_blocks += nb;
+        p_slots += nslots;
+        if (is_view || nslots >= 1) ++p_scan;
+        if (!is_view && nb == 1 && len <= kPieceTok)
+            ++p_packable;
+        else
+            p_block_items += nb;
+    }
+    const int64_t p_items = p_block_items + ceil_div(p_packable, 4);
     const int64_t words = int64_t(LA_PLAN_HEADER_WORDS) + n_blocks * LA_PLAN_BLOCK_WORDS +
-                          n_delta * LA_PLAN_DELTA_WORDS + n_scan * LA_PLAN_SCAN_WORDS;
+                          n_delta * LA_PLAN_DELTA_WORDS + n_scan * LA_PLAN_SCAN_WORDS +
+                          p_blocks * LA_PLAN_BLOCK_WORDS + p_items * LA_PLAN_ITEM_WORDS +
+                          p_scan * LA_PLAN_SCAN_WORDS;
     if (words > INT32_MAX || n_chunks > INT32_MAX) return LA_ERR_INVALID_ARG;
 
     la_pass_info inf;
@@ -115,6 +157,11 @@ la_status plan_impl(int32_t n_seg, const int32_t* seg_offsets, const int32_t* br
     inf.plan_words = int32_t(words);
     inf.max_seg_tokens = max_len;
     inf.fused_slot_reads = int32_t(std::min<int64_t>(fused_reads, INT32_MAX));
+    inf.piece_blocks = int32_t(p_blocks);
+    inf.piece_items = int32_t(p_items);
+    inf.piece_block_items = int32_t(p_block_items);
+    inf.piece_slots = int32_t(p_slots);
+    inf.piece_scans = int32_t(p_scan);
 
     if (view_ordinal)
         for (int32_t s = 0; s < n_seg; ++s) view_ordinal[s] = ord[size_t(s)];
@@ -123,6 +170,9 @@ la_status plan_impl(int32_t n_seg, const int32_t* seg_offsets, const int32_t* br
         const int32_t off_blocks = LA_PLAN_HEADER_WORDS;
         const int32_t off_delta = off_blocks + int32_t(n_blocks) * LA_PLAN_BLOCK_WORDS;
         const int32_t off_scan = off_delta + int32_t(n_delta) * LA_PLAN_DELTA_WORDS;
+        const int32_t off_pblocks = off_scan + int32_t(n_scan) * LA_PLAN_SCAN_WORDS;
+        const int32_t off_pitems = off_pblocks + int32_t(p_blocks) * LA_PLAN_BLOCK_WORDS;
+        const int32_t off_pscan = off_pitems + int32_t(p_items) * LA_PLAN_ITEM_WORDS;
         int32_t* h = plan;
         std::memset(h, 0, sizeof(int32_t) * LA_PLAN_HEADER_WORDS);
         h[0] = LA_PLAN_MAGIC;
@@ -139,6 +189,14 @@ la_status plan_impl(int32_t n_seg, const int32_t* seg_offsets, const int32_t* br
         h[11] = n_ext;
         h[12] = n_views;
         h[13] = inf.fused_slot_reads;
+        h[15] = int32_t(p_blocks);
+        h[16] = int32_t(p_items);
+        h[17] = int32_t(p_block_items);
+        h[18] = int32_t(p_slots);
+        h[19] = int32_t(p_scan);
+        h[20] = off_pblocks;
+        h[21] = off_pitems;
+        h[22] = off_pscan;
         int32_t* blk = plan + off_blocks;
         int32_t* del = plan + off_delta;
         int32_t* scn = plan + off_scan;
@@ -185,12 +243,97 @@ la_status plan_impl(int32_t n_seg, const int32_t* seg_offsets, const int32_t* br
                 slot += nslots;
             }
         }
+        // Piece path.  Blocks: views (segment order), then branches; each
+        // block {tok0, ntok, slot, seed, seg, slot0, j, final_row}.  Scans:
+        // the views in ordinal order first (a branch finds its view's slots
+        // at pscan[seed]), then branches with slots.  Items: one per
+        // non-packed block in block order, then the packs.
+        int32_t* pb = plan + off_pblocks;
+        int32_t* pit = plan + off_pitems;
+        int32_t* psc = plan + off_pscan;
+        std::vector<int32_t> packable;
+        int32_t pslot = 0, pblock = 0;
+        std::vector<int32_t> view_scan(size_t(n_views > 0 ? n_views : 0), -1);
+        for (int pass = 0; pass < 2; ++pass) {
+            for (int32_t s = 0; s < n_seg; ++s) {
+                const int32_t p = branch_parent[s];
+                const bool is_view = p == -1;
+                if (is_view != (pass == 0)) continue;
+                const int32_t off = seg_offsets[s];
+                const int32_t len = seg_offsets[s + 1] - off;
+                const int32_t nb = int32_t(ceil_div(len, kPieceBlockTok));
+                const int32_t nslots = is_view ? nb : nb - 1;
+                const int32_t seed = is_view ? -1 : (p >= 0 ? ord[size_t(p)] : p);
+                const int32_t slot0 = nslots > 0 ? pslot : -1;
+                const bool pack = !is_view && nb == 1 && len <= kPieceTok;
+                for (int32_t j = 0; j < nb; ++j) {
+                    const int32_t tok0 = off + j * kPieceBlockTok;
+                    const int32_t ntok = std::min(kPieceBlockTok, len - j * kPieceBlockTok);
+                    pb[0] = tok0;
+                    pb[1] = ntok;
+                    pb[2] = j < nslots ? pslot + j : -1;
+                    pb[3] = seed;
+                    pb[4] = s;
+                    pb[5] = slot0;
+                    pb[6] = j;
+                    pb[7] = is_view && j == nb - 1 ? ord[size_t(s)] : -1;
+                    pb += LA_PLAN_BLOCK_WORDS;
+                    if (pack) {
+                        packable.push_back(pblock);
+                    } else {
+                        int32_t* it = pit;
+                        std::memset(it, 0, sizeof(int32_t) * LA_PLAN_ITEM_WORDS);
+                        it[0] = LA_ITEM_BLOCK;
+                        it[1] = 1;
+                        it[2] = pblock;
+                        it[3] = it[4] = it[5] = -1;
+                        pit += LA_PLAN_ITEM_WORDS;
+                    }
+                    ++pblock;
+                }
+                if (is_view || nslots >= 1) {
+                    psc[0] = pslot;
+                    psc[1] = nslots;
+                    psc[2] = is_view ? ord[size_t(s)] : -1;
+                    psc[3] = s;
+                    psc += LA_PLAN_SCAN_WORDS;
+                }
+                pslot += nslots;
+            }
+        }
+        for (size_t i = 0; i < packable.size(); i += 4) {
+            int32_t* it = pit;
+            std::memset(it, 0, sizeof(int32_t) * LA_PLAN_ITEM_WORDS);
+            it[0] = LA_ITEM_PACK;
+            it[1] = int32_t(std::min<size_t>(4, packable.size() - i));
+            for (int w = 0; w < 4; ++w)
+                it[2 + w] = i + size_t(w) < packable.size() ? packable[i + size_t(w)] : -1;
+            pit += LA_PLAN_ITEM_WORDS;
+        }
+        const uint32_t hash = plan_hash(plan, words);
+        h[LA_PLAN_HASH_WORD] = int32_t(hash);
+        inf.plan_hash = int32_t(hash);
     }
+    inf.info_check = int32_t(la_info_checksum(&inf));
     *info = inf;
     return LA_OK;
 }
 
 }  // namespace
+
+// Checksum of an la_pass_info's fields (all but info_check itself): a copy
+// that was edited by hand, or fields mixed from two passes, do not match.
+extern "C" uint32_t la_info_checksum(const la_pass_info* info) {
+    la_pass_info c = *info;
+    c.info_check = 0;
+    const unsigned char* b = reinterpret_cast<const unsigned char*>(&c);
+    uint32_t h = 2166136261u ^ 0x9e3779b9u;
+    for (size_t i = 0; i < sizeof(c); ++i) {
+        h ^= b[i];
+        h *= 16777619u;
+    }
+    return h;
+}
 
 // Work-block size (chunks per block) for a pass of H heads: the largest
 // power of two up to kGroupMaxG whose blocks times H reach kGroupTarget
@@ -296,6 +439,7 @@ extern "C" la_status la_pack_pass_ext(int32_t n_requests, const int32_t* view_le
                              plan, &inf);
     if (st != LA_OK) return st;
     inf.n_requests = n_requests;
+    inf.info_check = int32_t(la_info_checksum(&inf));
     if (seg_offsets) std::memcpy(seg_offsets, off.data(), sizeof(int32_t) * off.size());
     if (branch_parent && n_seg > 0) std::memcpy(branch_parent, par.data(), sizeof(int32_t) * par.size());
     *info = inf;
@@ -372,6 +516,10 @@ extern "C" const char* la_status_string(la_status status) {
         case LA_ERR_UNSUPPORTED: return "unsupported dtype, head dim or chunk size";
         case LA_ERR_WORKSPACE: return "workspace missing or too small";
         case LA_ERR_HIP: return "HIP runtime error";
+        case LA_ERR_PLAN:
+            return "the device plan does not belong to this pass info (rebuild it with the planner)";
+        case LA_ERR_TIMEOUT:
+            return "a wait inside the single-launch scan gave up (its outputs are not valid)";
         case LA_ERR_TOO_LARGE:
             return "the pass needs more workspace than the library's built-in scratch array holds";
         default: return "unknown status";

@@ -1,0 +1,847 @@
+// Piece path of the packed chunked causal linear-attention scan: d = 64,
+// bf16 inputs, gfx950 (MI355X).
+//
+// Source: "Serving 0.88M TPS from Two RTXs and Mac Minis", section "Kernels"
+// (linear attention in 64-token chunks with a few 64x64 matrix products
+// each; one scan covers every view of a pass) and section "Long Requests"
+// (branches start from their view's state).  Per head, fp32 state S (64x64):
+//     S_t = S_{t-1} + k_t^T v_t,     o_t = q_t S_t.
+//
+// Decomposition.  A segment (a view or a branch) is cut into blocks of
+// LA_PIECE_BLOCK_CHUNKS = 8 chunks, a block into up to four pieces of
+// LA_PIECE_CHUNKS = 2 chunks.  One workgroup of four waves takes a block
+// and a head; wave w owns piece w end to end: it loads that piece's k, v
+// and q, keeps the whole 64x64 state in its own registers, and computes
+// every output feature of its tokens, so the chunk loop has no workgroup
+// barrier and no state is published through LDS.  Branches whose only block
+// is one piece are packed four to a workgroup, one per wave.
+//
+// Arithmetic, identical in every form (same device functions, same order):
+//   A_w   = sum over the piece's chunks of K_c^T V_c (MFMA accumulation,
+//           chunk 1 before chunk 0), the piece's own state;
+//   E_w   = 0 + A_0 + ... + A_{w-1} (fp32, left to right), the block's
+//           state before piece w;
+//   A_b   = E_{n-1} + A_{n-1}, the block's own state (n pieces);
+//   own_j = 0 + A_b(0) + ... + A_b(j-1), the segment's state before block j;
+//   S_b   = seed (a branch: its view's total own; a shard branch: ext_state;
+//           a view: 0), then += own_j if j > 0;
+//   S     = S_b + E_w at the start of piece w; within the piece, after its
+//           first chunk, S += K_0^T V_0 (MFMA accumulation into S);
+//   O_c   = tril(Q_c K_c^T) V_c + Q_c S_hi + Q_c S_lo, with S = S_hi + S_lo
+//           split into two bf16 terms (the split keeps the state's fp32
+//           precision in the product at no memory cost).
+//
+// Forms (they differ only in how own_j and the seed reach a workgroup):
+//   three launches  states -> prefix (the shared prefix kernel, in place)
+//                   -> outputs reading own_j and the view total from slots;
+//   two launches    states -> outputs summing the slots themselves;
+//   one launch      each workgroup computes A_b, publishes it, and obtains
+//                   own_j from its predecessors in the same launch (a
+//                   decoupled look-back: the nearest predecessor that has
+//                   published its inclusive prefix, then the aggregates after
+//                   it, added left to right, so the bits do not depend on
+//                   timing), publishes its own inclusive prefix, then
+//                   computes its outputs from the k and v it already holds.
+//                   k and v are read from HBM once per pass.
+//
+// Single-launch coordination.  Workgroups take tickets from a counter in the
+// workspace header, so a workgroup only ever waits for tickets taken before
+// its own (running workgroups): forward progress does not depend on how many
+// workgroups fit on the GPU.  Published states and flags are written and read
+// with device-coherent accesses (sc1), stores are drained (s_waitcnt) before
+// the flag that announces them, and every wait is bounded: past the spin
+// limit the workgroup records LA_ERR_TIMEOUT in the header and carries on,
+// so every wave reaches the end of the kernel.  The last workgroup to retire
+// clears the flags and resets the counters for the next pass.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "linattn.h"
+#include "piece.h"
+#include "tiles.h"
+
+namespace {
+
+constexpr int PD = 64;                       // head dim of this path
+constexpr int PLD = 80;                      // staged row stride (elements): 160-byte rows
+constexpr int kStageElems = kChunk * PLD;    // one 64-row tile
+constexpr int kTiles = 16;                   // 16x16 tiles of a 64x64 state
+constexpr int kStateBytes = PD * PD * 4;     // one state, fp32
+constexpr int kWaitLgkm0 = 0xC07F;           // s_waitcnt lgkmcnt(0), others at max
+constexpr uint64_t kFlagA = 0x7FF44C41464C0001ull;   // aggregate published (NaN payload)
+constexpr uint64_t kFlagP = 0x7FF44C41464C0002ull;   // inclusive prefix published
+constexpr int kAuxCoherent = 16;             // buffer-op cache policy: sc1 (device scope)
+
+enum Mode { kStates = 0, kOut3 = 1, kOut2 = 2, kFused = 3 };
+
+struct PBlock {
+    int tok0, ntok, slot, seed, seg, slot0, j, final_row;
+};
+struct PItem {
+    int kind, n, b[4], pad0, pad1;
+};
+struct PScan {
+    int first_slot, n_slots, final_row, seg;
+};
+
+struct PArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const int32_t* plan;
+    const PBlock* blocks;
+    const PItem* items;
+    const PScan* scans;
+    float* aslots;                 // [slots][H][16 KB] block states
+    float* pslots;                 // [slots][H][16 KB] inclusive prefixes (one launch)
+    uint64_t* flags;               // [slots][H] (one launch)
+    int* hdr;                      // workspace header
+    float* final_state;
+    const float* ext_state;
+    uint16_t* out;
+    int H;
+    int n_work;                    // workgroups of the launch (items x H)
+    int n_flags;                   // slots x H
+    int plan_hash;
+    int spin_limit;
+    int force_timeout;
+};
+
+typedef f32x4 State[kTiles];       // tile t = vb * 4 + kb; lane 16g + c holds
+                                   // S[16 kb + 4 g + j][16 vb + c], j = 0..3
+
+// ---------------------------------------------------------------------------
+// Small helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void zero_state(State& s) {
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) s[t] = zero4();
+}
+
+// One state slot as a 16 KB buffer window; lane l's piece of tile t is the
+// 16 bytes at (t * 64 + l) * 16.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slot_rsrc(const float* base, int slot, int H,
+                                                           int h) {
+    const char* p = reinterpret_cast<const char*>(base) +
+                    (int64_t(slot) * H + h) * int64_t(kStateBytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p), (short)0, kStateBytes,
+                                             0x00020000);
+}
+template <int AUX>
+__device__ __forceinline__ f32x4 slot_load(__amdgpu_buffer_rsrc_t r, int t, int lane) {
+    return __builtin_bit_cast(
+        f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, uint32_t((t * 64 + lane) * 16), 0, AUX));
+}
+template <int AUX>
+__device__ __forceinline__ void slot_store(__amdgpu_buffer_rsrc_t r, int t, int lane, f32x4 x) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, x), r,
+                                           uint32_t((t * 64 + lane) * 16), 0, AUX);
+}
+template <int AUX>
+__device__ __forceinline__ void store_state(const State& s, float* base, int slot, int H, int h,
+                                            int lane) {
+    const auto r = slot_rsrc(base, slot, H, h);
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) slot_store<AUX>(r, t, lane, s[t]);
+}
+
+// Row-major [64][64] state (final_state / ext_state rows) <-> lane layout.
+__device__ __forceinline__ void store_rows_state(const State& s, float* dst, int g, int c16) {
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) {
+        const int kb = t & 3, vb = t >> 2;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dst[(16 * kb + 4 * g + j) * PD + 16 * vb + c16] = s[t][j];
+    }
+}
+__device__ __forceinline__ f32x4 load_rows_tile(const float* src, int t, int g, int c16) {
+    const int kb = t & 3, vb = t >> 2;
+    f32x4 x;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x[j] = src[(16 * kb + 4 * g + j) * PD + 16 * vb + c16];
+    return x;
+}
+
+// Device-coherent flag accesses (sc1), as the single-pass scans of the ROCm
+// primitives library do on gfx942 / gfx950.
+__device__ __forceinline__ uint64_t flag_load(const uint64_t* f) {
+    return __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void flag_store(uint64_t* f, uint64_t x) {
+    __hip_atomic_store(f, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Everything this wave stored has reached the coherence point, and no later
+// memory operation is moved above this point by the compiler.
+__device__ __forceinline__ void drain_stores() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_waitcnt(kWaitVmem0);
+}
+__device__ __forceinline__ void order_after_flag() {
+    __builtin_amdgcn_s_waitcnt(kWaitVmem0);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+// Bounded wait for one flag to say "inclusive prefix published".  On timeout
+// records LA_ERR_TIMEOUT and returns (the caller carries on with whatever
+// the slot holds: in bounds, not valid).
+__device__ void wait_prefix(const PArgs& a, const uint64_t* f) {
+    for (int it = 0;; ++it) {
+        const uint64_t x = a.force_timeout ? 0 : flag_load(f);
+        if (x == kFlagP) break;
+        if (it >= a.spin_limit) {
+            __hip_atomic_fetch_or(a.hdr + piece::kStatusWord, LA_ERR_TIMEOUT, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+            break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+    }
+    order_after_flag();
+}
+
+// The look-back of block j of a segment (slots slot0 .. slot0 + j - 1 hold
+// its predecessors): the nearest predecessor m that has published its
+// inclusive prefix, with every predecessor after it having published at
+// least its aggregate.  The flags of up to 64 predecessors are polled at
+// once, one per lane (lane i: predecessor j - 1 - i).  Block 0 of a segment
+// always publishes its prefix, so the walk ends.  On timeout records
+// LA_ERR_TIMEOUT and returns 0.
+__device__ int find_prefix(const PArgs& a, int slot0, int j, int h, int lane) {
+    for (int base = j - 1;; base -= 64) {
+        const int m = base - lane;
+        for (int it = 0;; ++it) {
+            const uint64_t f = (m >= 0 && !a.force_timeout)
+                                   ? flag_load(a.flags + int64_t(slot0 + m) * a.H + h)
+                                   : 0;
+            const uint64_t bp = __builtin_amdgcn_ballot_w64(m >= 0 && f == kFlagP);
+            const uint64_t br =
+                __builtin_amdgcn_ballot_w64(m < 0 || f == kFlagP || f == kFlagA);
+            if (bp) {
+                const int l = __builtin_ctzll(bp);                 // nearest prefix
+                const uint64_t need = l == 63 ? ~0ull : ((2ull << l) - 1);
+                if ((br & need) == need) {
+                    order_after_flag();
+                    return base - l;
+                }
+            } else if (br == ~0ull && base >= 64) {
+                break;                                             // next window
+            }
+            if (it >= a.spin_limit) {
+                __hip_atomic_fetch_or(a.hdr + piece::kStatusWord, LA_ERR_TIMEOUT,
+                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                order_after_flag();
+                return 0;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Chunk data of one wave: k and v rows as loaded (64 tokens x 64 features
+// each; load i gives lane l token 8 i + l / 8, features 8 (l % 8) .. + 7).
+// ---------------------------------------------------------------------------
+struct ChunkKV {
+    u32x4 k[8], v[8];
+};
+
+__device__ __forceinline__ void load_chunk_kv(ChunkKV& r, const PArgs& a, int64_t tok0, int rows,
+                                              int h, int lane) {
+    const int64_t first = tok0 * a.H * PD;
+    const auto rk = chunk_rsrc(a.k, first, 2, rows, a.H, PD);
+    const auto rv = chunk_rsrc(a.v, first, 2, rows, a.H, PD);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t off = uint32_t((((8 * i + (lane >> 3)) * a.H + h) * PD + 8 * (lane & 7)) * 2);
+        r.k[i] = buf_load16(rk, off);
+        r.v[i] = buf_load16(rv, off);
+    }
+}
+
+// q of a chunk as the B operand of the products over d_k: lane 16 g + c
+// holds token 16 tb + c; loaded as 16 contiguous bytes (features
+// 32 ks + 8 g .. + 7) and regrouped below.
+struct ChunkQ {
+    u32x4 q[4][2];
+};
+__device__ __forceinline__ void load_chunk_q(ChunkQ& r, const PArgs& a, int64_t tok0, int rows,
+                                             int h, int g, int c16) {
+    const auto rq = chunk_rsrc(a.q, tok0 * a.H * PD, 2, rows, a.H, PD);
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+            r.q[tb][ks] =
+                buf_load16(rq, uint32_t((((16 * tb + c16) * a.H + h) * PD + 32 * ks + 8 * g) * 2));
+}
+
+// k-slot order of every product over d_k: in a K = 32 step ks, lane group g
+// holds features 32 ks + 4 g .. + 3 (elements 0..3) and 32 ks + 16 + 4 g ..
+// + 3 (elements 4..7) -- the order in which a state's accumulator tiles
+// (kb = 2 ks, 2 ks + 1) hold their rows, so the state feeds the product
+// straight from registers.  A contiguous 16-byte piece (features 8 g .. + 7
+// of the step) becomes that order with two lane swaps: swapping odd 16-lane
+// rows of the low halves with even rows of the high halves, then the upper
+// 32 lanes of the low halves with the lower 32 of the high halves.
+__device__ __forceinline__ u32x4 to_slot_order(u32x4 x) {
+    const auto r0 = __builtin_amdgcn_permlane16_swap(x[0], x[2], false, false);
+    const auto r1 = __builtin_amdgcn_permlane16_swap(x[1], x[3], false, false);
+    const auto s0 = __builtin_amdgcn_permlane32_swap(r0[0], r0[1], false, false);
+    const auto s1 = __builtin_amdgcn_permlane32_swap(r1[0], r1[1], false, false);
+    return u32x4{s0[0], s1[0], s0[1], s1[1]};
+}
+// The inverse: slot order (features 4 g .. and 16 + 4 g .. of a 32-feature
+// half) back to 16 contiguous bytes (features 8 g .. + 7).
+__device__ __forceinline__ u32x4 from_slot_order(u32x4 x) {
+    const auto s0 = __builtin_amdgcn_permlane32_swap(x[0], x[2], false, false);
+    const auto s1 = __builtin_amdgcn_permlane32_swap(x[1], x[3], false, false);
+    const auto r0 = __builtin_amdgcn_permlane16_swap(s0[0], s0[1], false, false);
+    const auto r1 = __builtin_amdgcn_permlane16_swap(s1[0], s1[1], false, false);
+    return u32x4{r0[0], r1[0], r0[1], r1[1]};
+}
+
+// Registers -> the wave's LDS tiles, row-major (160-byte rows).
+__device__ __forceinline__ void stage_chunk(const ChunkKV& r, uint16_t* sK, uint16_t* sV,
+                                            int lane) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int o = (8 * i + (lane >> 3)) * PLD + 8 * (lane & 7);
+        *reinterpret_cast<u32x4*>(sK + o) = r.k[i];
+        *reinterpret_cast<u32x4*>(sV + o) = r.v[i];
+    }
+    // the wave reads what it wrote: LDS operations of one wave complete in
+    // order, the wait keeps the compiler from moving the reads up
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __builtin_amdgcn_wave_barrier();
+}
+
+// S += K^T V of the staged chunk (accumulator tile (kb, vb)).
+__device__ __forceinline__ void acc_kv(State& S, const uint16_t* sK, const uint16_t* sV, int g,
+                                       int c16) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        u32x4 ak[4], bv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            ak[i] = tr_frag(sK, PLD, 16 * i, ks, g, c16);
+            bv[i] = tr_frag(sV, PLD, 16 * i, ks, g, c16);
+        }
+#pragma unroll
+        for (int vb = 0; vb < 4; ++vb)
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+                S[vb * 4 + kb] = mfma_bf16(ak[kb], bv[vb], S[vb * 4 + kb]);
+    }
+}
+
+// Outputs of one staged chunk for the wave's 64 tokens, all 64 features:
+// O^T = V^T P^T + S_hi^T Q^T + S_lo^T Q^T with P = tril(Q K^T), stored as
+// bf16 (round to nearest even), 16 contiguous bytes per lane and store.
+template <int TB>
+__device__ __forceinline__ void out_tokens(const u32x4 (&kr)[4][2], const u32x4 (&vt)[4][2],
+                                           const u32x4 (&sh)[4][2], const u32x4 (&sl)[4][2],
+                                           const u32x4 (&qt)[2], __amdgpu_buffer_rsrc_t ro,
+                                           int H, int h, int g, int c16) {
+    f32x4 p[TB + 1];
+#pragma unroll
+    for (int ub = 0; ub <= TB; ++ub) {
+        p[ub] = mfma_bf16(kr[ub][0], qt[0], zero4());
+        p[ub] = mfma_bf16(kr[ub][1], qt[1], p[ub]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)   // causal mask of the diagonal tile: key u <= query t
+        if (4 * g + j > c16) p[TB][j] = 0.f;
+    u32x4 pb[TB / 2 + 1];
+#pragma unroll
+    for (int pp = 0; pp <= TB / 2; ++pp) {
+        const f32x4 x = p[2 * pp];
+        const f32x4 y = 2 * pp + 1 <= TB ? p[2 * pp + 1] : zero4();
+        pb[pp] = u32x4{cvt_bf2(x[0], x[1]), cvt_bf2(x[2], x[3]), cvt_bf2(y[0], y[1]),
+                       cvt_bf2(y[2], y[3])};
+    }
+    f32x4 o[4];
+#pragma unroll
+    for (int fb = 0; fb < 4; ++fb) {
+        o[fb] = zero4();
+#pragma unroll
+        for (int pp = 0; pp <= TB / 2; ++pp) o[fb] = mfma_bf16(vt[fb][pp], pb[pp], o[fb]);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            o[fb] = mfma_bf16(sh[fb][ks], qt[ks], o[fb]);
+            o[fb] = mfma_bf16(sl[fb][ks], qt[ks], o[fb]);
+        }
+    }
+    // lane 16 g + c: token 16 TB + c, features 16 fb + 4 g .. + 3 of each tile
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+        const f32x4 x = o[2 * hh], y = o[2 * hh + 1];
+        const u32x4 pc = from_slot_order(u32x4{cvt_bf2(x[0], x[1]), cvt_bf2(x[2], x[3]),
+                                               cvt_bf2(y[0], y[1]), cvt_bf2(y[2], y[3])});
+        buf_store16u(ro, uint32_t((((16 * TB + c16) * H + h) * PD + 32 * hh + 8 * g) * 2), pc);
+    }
+}
+
+__device__ __forceinline__ void chunk_out(const State& S, const uint16_t* sK, const uint16_t* sV,
+                                          const ChunkQ& qraw, const PArgs& a, int64_t tok0,
+                                          int rows, int h, int g, int c16) {
+    // S^T as A operands, split into two bf16 terms
+    u32x4 sh[4][2], sl[4][2];
+#pragma unroll
+    for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const f32x4 x = S[fb * 4 + 2 * ks], y = S[fb * 4 + 2 * ks + 1];
+            const uint32_t h0 = cvt_bf2(x[0], x[1]), h1 = cvt_bf2(x[2], x[3]);
+            const uint32_t h2 = cvt_bf2(y[0], y[1]), h3 = cvt_bf2(y[2], y[3]);
+            sh[fb][ks] = u32x4{h0, h1, h2, h3};
+            sl[fb][ks] = u32x4{cvt_bf2(x[0] - bf_lo(h0), x[1] - bf_hi(h0)),
+                               cvt_bf2(x[2] - bf_lo(h1), x[3] - bf_hi(h1)),
+                               cvt_bf2(y[0] - bf_lo(h2), y[1] - bf_hi(h2)),
+                               cvt_bf2(y[2] - bf_lo(h3), y[3] - bf_hi(h3))};
+        }
+    // K rows in slot order (two 8-byte reads), V^T fragments in token order
+    u32x4 kr[4][2], vt[4][2];
+#pragma unroll
+    for (int ub = 0; ub < 4; ++ub)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const uint16_t* p = sK + (16 * ub + c16) * PLD + 32 * ks + 4 * g;
+            kr[ub][ks] = cat2(lds_u32x2(p), lds_u32x2(p + 16));
+            vt[ub][ks] = tr_frag(sV, PLD, 16 * ub, ks, g, c16);
+        }
+    u32x4 qt[4][2];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) qt[tb][ks] = to_slot_order(qraw.q[tb][ks]);
+    const auto ro = chunk_rsrc(a.out, tok0 * a.H * PD, 2, rows, a.H, PD);
+    out_tokens<0>(kr, vt, sh, sl, qt[0], ro, a.H, h, g, c16);
+    out_tokens<1>(kr, vt, sh, sl, qt[1], ro, a.H, h, g, c16);
+    out_tokens<2>(kr, vt, sh, sl, qt[2], ro, a.H, h, g, c16);
+    out_tokens<3>(kr, vt, sh, sl, qt[3], ro, a.H, h, g, c16);
+}
+
+// One wave's piece (up to two chunks at tok0 .. tok0 + ntok): outputs from
+// state S.  Chunk 0's k / v are already staged when `staged`; chunk 1's are
+// in r1; q of both chunks in q0, q1.
+__device__ __forceinline__ void piece_outputs(State& S, uint16_t* sK, uint16_t* sV,
+                                              const ChunkKV& r0, const ChunkKV& r1,
+                                              const ChunkQ& q0, const ChunkQ& q1, const PArgs& a,
+                                              int64_t tok0, int ntok, bool staged, int h, int g,
+                                              int c16, int lane) {
+    if (ntok <= 0) return;
+    if (!staged) stage_chunk(r0, sK, sV, lane);
+    chunk_out(S, sK, sV, q0, a, tok0, min(ntok, kChunk), h, g, c16);
+    if (ntok > kChunk) {
+        acc_kv(S, sK, sV, g, c16);
+        // every lane's reads of chunk 0 are done before chunk 1 overwrites it
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        __builtin_amdgcn_wave_barrier();
+        stage_chunk(r1, sK, sV, lane);
+        chunk_out(S, sK, sV, q1, a, tok0 + kChunk, ntok - kChunk, h, g, c16);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// State sums split over the four waves: wave w adds tiles 4 w .. 4 w + 3.
+// ---------------------------------------------------------------------------
+// acc += slot tiles of slots first .. first + n - 1, in order.  Loads go out
+// in batches of four slots with the next batch issued before the current one
+// is added, so two batches are in flight.
+template <int AUX>
+__device__ __forceinline__ void add_slots4(f32x4 (&acc)[4], const float* base, int first, int n,
+                                           int H, int h, int w, int lane) {
+    auto load4 = [&](f32x4 (&x)[4][4], int s0) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            // slots past n read an empty window (zeros, not added)
+            const auto r = s0 + b < n ? slot_rsrc(base, first + s0 + b, H, h)
+                                      : __builtin_amdgcn_make_buffer_rsrc(
+                                            const_cast<float*>(base), (short)0, 0, 0x00020000);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[b][i] = slot_load<AUX>(r, 4 * w + i, lane);
+        }
+    };
+    if (n <= 0) return;
+    f32x4 cur[4][4], nxt[4][4];
+    load4(cur, 0);
+    for (int s0 = 0; s0 < n; s0 += 4) {
+        if (s0 + 4 < n) load4(nxt, s0 + 4);
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+            if (s0 + b < n)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i] += cur[b][i];
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) cur[b][i] = nxt[b][i];
+    }
+}
+
+// LDS exchange region: two states in the lane layout.
+struct Xch {
+    f32x4 x[2][kTiles * 64];
+};
+__device__ __forceinline__ void put_state(Xch& X, int b, const State& s, int lane) {
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) X.x[b][t * 64 + lane] = s[t];
+}
+__device__ __forceinline__ void get_state(const Xch& X, int b, State& s, int lane) {
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) s[t] = X.x[b][t * 64 + lane];
+}
+__device__ __forceinline__ void put_tiles4(Xch& X, int b, const f32x4 (&v)[4], int w, int lane) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) X.x[b][(4 * w + i) * 64 + lane] = v[i];
+}
+
+// ---------------------------------------------------------------------------
+// The kernel (all forms).
+// ---------------------------------------------------------------------------
+template <int MODE>
+__global__ __launch_bounds__(kThreads) void piece_kernel(PArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t sStage[4][2][kStageElems];
+    __shared__ Xch X;
+    __shared__ int sB[2];
+    const int tid = threadIdx.x, w = wave_id(), lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+    uint16_t* sK = sStage[w][0];
+    uint16_t* sV = sStage[w][1];
+    const int H = a.H;
+
+    // the plan must be the one the pass info was built with
+    if (a.plan[0] != LA_PLAN_MAGIC || a.plan[LA_PLAN_HASH_WORD] != a.plan_hash) {
+        if (tid == 0)
+            __hip_atomic_fetch_or(a.hdr + piece::kStatusWord, LA_ERR_PLAN, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
+
+    int work;
+    if constexpr (MODE == kFused) {
+        // tickets in launch order of the items: everything a workgroup waits
+        // for belongs to a smaller ticket, held by a running workgroup
+        if (tid == 0)
+            sB[0] = __hip_atomic_fetch_add(a.hdr + piece::kTicketWord, 1, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        work = sB[0];
+    } else {
+        work = blockIdx.x;
+    }
+    if (work < a.n_work) {
+        const int item = work / H, h = work % H;
+        const PItem it = a.items[item];
+        if (it.kind == LA_ITEM_BLOCK) {
+            const PBlock B = a.blocks[it.b[0]];
+            const int np = (B.ntok + 2 * kChunk - 1) / (2 * kChunk);   // pieces
+            const int64_t ptok0 = int64_t(B.tok0) + w * 2 * kChunk;
+            const int pntok = min(2 * kChunk, B.ntok - w * 2 * kChunk);   // <= 0: no piece
+            ChunkKV r0, r1;
+            ChunkQ q0, q1;
+            load_chunk_kv(r0, a, ptok0, pntok, h, lane);
+            load_chunk_kv(r1, a, ptok0 + kChunk, pntok - kChunk, h, lane);
+            if constexpr (MODE != kStates) {
+                load_chunk_q(q0, a, ptok0, pntok, h, g, c16);
+                load_chunk_q(q1, a, ptok0 + kChunk, pntok - kChunk, h, g, c16);
+            }
+
+            // the piece's own state, chunk 1 first so chunk 0 stays staged
+            State A;
+            zero_state(A);
+            if (pntok > kChunk) {
+                stage_chunk(r1, sK, sV, lane);
+                acc_kv(A, sK, sV, g, c16);
+                __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+                __builtin_amdgcn_wave_barrier();
+            }
+            if (pntok > 0) {
+                stage_chunk(r0, sK, sV, lane);
+                acc_kv(A, sK, sV, g, c16);
+            }
+
+            // in-block prefix over the pieces: E_w and A_b (wave np - 1)
+            State E, Ab;
+            zero_state(E);
+            if (w == 0 && np > 1) put_state(X, 0, A, lane);
+            if (w == 2 && np > 3) put_state(X, 1, A, lane);
+            __syncthreads();
+            State T;
+            if (w == 1 && np > 1) {
+                State x;
+                get_state(X, 0, x, lane);
+#pragma unroll
+                for (int t = 0; t < kTiles; ++t) E[t] = zero4() + x[t];
+                if (np > 2) {
+                    State i1;
+#pragma unroll
+                    for (int t = 0; t < kTiles; ++t) i1[t] = E[t] + A[t];
+                    put_state(X, 0, i1, lane);
+                }
+            }
+            if (w == 3 && np > 3) get_state(X, 1, T, lane);
+            __syncthreads();
+            if ((w == 2 && np > 2) || (w == 3 && np > 3)) get_state(X, 0, E, lane);
+            if (w == 3 && np > 3) {
+#pragma unroll
+                for (int t = 0; t < kTiles; ++t) E[t] = E[t] + T[t];
+            }
+            if (w == np - 1) {
+#pragma unroll
+                for (int t = 0; t < kTiles; ++t) Ab[t] = (w == 0 ? zero4() : E[t]) + A[t];
+            }
+            __syncthreads();   // X is reused below
+
+            if constexpr (MODE == kStates) {
+                if (w == np - 1 && B.slot >= 0) store_state<0>(Ab, a.aslots, B.slot, H, h, lane);
+            } else {
+                // own: the segment's state before this block (fold of the
+                // earlier blocks' states), seed: where a branch starts
+                const bool has_seed = B.seed != -1;
+                f32x4 own4[4], sin4[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) own4[i] = zero4();
+                if constexpr (MODE == kFused) {
+                    if (B.slot >= 0 && w == np - 1) {
+                        if (B.j == 0) {
+                            State P;
+#pragma unroll
+                            for (int t = 0; t < kTiles; ++t) P[t] = zero4() + Ab[t];
+                            store_state<kAuxCoherent>(P, a.pslots, B.slot, H, h, lane);
+                            drain_stores();
+                            if (lane == 0) flag_store(a.flags + int64_t(B.slot) * H + h, kFlagP);
+                        } else {
+                            store_state<kAuxCoherent>(Ab, a.aslots, B.slot, H, h, lane);
+                            drain_stores();
+                            if (lane == 0) flag_store(a.flags + int64_t(B.slot) * H + h, kFlagA);
+                        }
+                    }
+                    if (B.j > 0) {
+                        // nearest predecessor with an inclusive prefix, then
+                        // the aggregates after it, left to right
+                        const int m = find_prefix(a, B.slot0, B.j, h, lane);
+                        {
+                            const auto r = slot_rsrc(a.pslots, B.slot0 + m, H, h);
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                own4[i] = slot_load<kAuxCoherent>(r, 4 * w + i, lane);
+                        }
+                        add_slots4<kAuxCoherent>(own4, a.aslots, B.slot0 + m + 1, B.j - 1 - m, H,
+                                                 h, w, lane);
+                    }
+                } else if (B.j > 0) {
+                    if constexpr (MODE == kOut3) {
+                        const auto r = slot_rsrc(a.aslots, B.slot0 + B.j - 1, H, h);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) own4[i] = slot_load<0>(r, 4 * w + i, lane);
+                    } else {
+                        add_slots4<0>(own4, a.aslots, B.slot0, B.j, H, h, w, lane);
+                    }
+                }
+                // seed tiles of this wave
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sin4[i] = zero4();
+                if (B.seed >= 0) {
+                    const PScan vs = a.scans[B.seed];
+                    const int last = vs.first_slot + vs.n_slots - 1;
+                    if constexpr (MODE == kFused) {
+                        wait_prefix(a, a.flags + int64_t(last) * H + h);
+                        const auto r = slot_rsrc(a.pslots, last, H, h);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            sin4[i] = slot_load<kAuxCoherent>(r, 4 * w + i, lane);
+                    } else if constexpr (MODE == kOut3) {
+                        const auto r = slot_rsrc(a.aslots, last, H, h);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) sin4[i] = slot_load<0>(r, 4 * w + i, lane);
+                    } else {
+                        add_slots4<0>(sin4, a.aslots, vs.first_slot, vs.n_slots, H, h, w, lane);
+                    }
+                } else if (B.seed <= -2) {
+                    const float* src = a.ext_state + (int64_t(-B.seed - 2) * H + h) * PD * PD;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) sin4[i] = load_rows_tile(src, 4 * w + i, g, c16);
+                }
+                // S_b = seed (or 0), += own if the block has predecessors
+                if (B.j > 0)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) sin4[i] += own4[i];
+                put_tiles4(X, 0, own4, w, lane);
+                put_tiles4(X, 1, sin4, w, lane);
+                __syncthreads();
+                if (w == np - 1 && (B.slot >= 0 || B.final_row >= 0) &&
+                    (MODE == kFused || MODE == kOut2)) {
+                    // inclusive prefix of this block: own + A_b
+                    State P;
+                    if (B.j > 0) {
+                        get_state(X, 0, P, lane);
+#pragma unroll
+                        for (int t = 0; t < kTiles; ++t) P[t] = P[t] + Ab[t];
+                    } else {
+#pragma unroll
+                        for (int t = 0; t < kTiles; ++t) P[t] = zero4() + Ab[t];
+                    }
+                    if (MODE == kFused && B.slot >= 0 && B.j > 0) {
+                        store_state<kAuxCoherent>(P, a.pslots, B.slot, H, h, lane);
+                        drain_stores();
+                        if (lane == 0) flag_store(a.flags + int64_t(B.slot) * H + h, kFlagP);
+                    }
+                    if (B.final_row >= 0)
+                        store_rows_state(P, a.final_state + (int64_t(B.final_row) * H + h) * PD * PD,
+                                         g, c16);
+                }
+                State S;
+                get_state(X, 1, S, lane);
+                if (!has_seed && B.j == 0) zero_state(S);
+                if (w >= 1)
+#pragma unroll
+                    for (int t = 0; t < kTiles; ++t) S[t] = S[t] + E[t];
+                piece_outputs(S, sK, sV, r0, r1, q0, q1, a, ptok0, pntok, true, h, g, c16, lane);
+            }
+        } else if constexpr (MODE != kStates) {
+            // up to four one-piece branches, one per wave, each from its seed
+            if (w < it.n) {
+                const PBlock B = a.blocks[a.items[item].b[w]];
+                ChunkKV r0, r1;
+                ChunkQ q0, q1;
+                load_chunk_kv(r0, a, B.tok0, B.ntok, h, lane);
+                load_chunk_kv(r1, a, int64_t(B.tok0) + kChunk, B.ntok - kChunk, h, lane);
+                load_chunk_q(q0, a, B.tok0, B.ntok, h, g, c16);
+                load_chunk_q(q1, a, int64_t(B.tok0) + kChunk, B.ntok - kChunk, h, g, c16);
+                State S;
+                zero_state(S);
+                if (B.seed >= 0) {
+                    const PScan vs = a.scans[B.seed];
+                    const int last = vs.first_slot + vs.n_slots - 1;
+                    if constexpr (MODE == kFused) {
+                        wait_prefix(a, a.flags + int64_t(last) * H + h);
+                        const auto r = slot_rsrc(a.pslots, last, H, h);
+#pragma unroll
+                        for (int t = 0; t < kTiles; ++t) S[t] = slot_load<kAuxCoherent>(r, t, lane);
+                    } else if constexpr (MODE == kOut3) {
+                        const auto r = slot_rsrc(a.aslots, last, H, h);
+#pragma unroll
+                        for (int t = 0; t < kTiles; ++t) S[t] = slot_load<0>(r, t, lane);
+                    } else {
+                        // the view's total, summed from zero in slot order
+                        for (int s = 0; s < vs.n_slots; ++s) {
+                            const auto r = slot_rsrc(a.aslots, vs.first_slot + s, H, h);
+#pragma unroll
+                            for (int t = 0; t < kTiles; ++t) S[t] += slot_load<0>(r, t, lane);
+                        }
+                    }
+                } else if (B.seed <= -2) {
+                    const float* src = a.ext_state + (int64_t(-B.seed - 2) * H + h) * PD * PD;
+#pragma unroll
+                    for (int t = 0; t < kTiles; ++t) S[t] = load_rows_tile(src, t, g, c16);
+                }
+                piece_outputs(S, sK, sV, r0, r1, q0, q1, a, B.tok0, B.ntok, false, h, g, c16,
+                              lane);
+            }
+        }
+    }
+
+    if constexpr (MODE == kFused) {
+        // the last workgroup to retire resets the single-launch state
+        __syncthreads();
+        if (tid == 0) {
+            const int r = __hip_atomic_fetch_add(a.hdr + piece::kRetireWord, 1, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+            sB[1] = r == a.n_work - 1;
+        }
+        __syncthreads();
+        if (sB[1]) {
+            for (int i = tid; i < a.n_flags; i += kThreads) flag_store(a.flags + i, 0);
+            if (tid == 0) {
+                __hip_atomic_store(a.hdr + piece::kTicketWord, 0, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(a.hdr + piece::kRetireWord, 0, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+    }
+}
+
+// Layout of the piece path's part of a workspace (after the header).
+struct WsLayout {
+    size_t flags, aslots, pslots, total;
+};
+WsLayout ws_layout(const la_pass_info& info, int32_t H) {
+    WsLayout l;
+    const size_t nsh = size_t(info.piece_slots) * size_t(H);
+    l.flags = piece::kHeaderBytes;
+    l.aslots = (l.flags + nsh * sizeof(uint64_t) + 255) / 256 * 256;
+    l.pslots = l.aslots + nsh * size_t(kStateBytes);
+    l.total = l.pslots + nsh * size_t(kStateBytes);
+    return l;
+}
+
+}  // namespace
+
+namespace piece {
+
+size_t workspace_bytes(const la_pass_info& info, int32_t H) { return ws_layout(info, H).total; }
+
+la_status launch(int32_t stages, int form, const void* q, const void* k, const void* v,
+                 int32_t H, const la_pass_info& info, const int32_t* plan,
+                 const float* ext_state, void* out, float* final_state, void* workspace,
+                 hipStream_t st, int32_t spin_limit, bool force_timeout) {
+    const WsLayout l = ws_layout(info, H);
+    char* ws = static_cast<char*>(workspace);
+    PArgs a;
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k);
+    a.v = static_cast<const uint16_t*>(v);
+    // table offsets from the pass info (the plan itself is device memory)
+    const int64_t off_pblocks = int64_t(LA_PLAN_HEADER_WORDS) +
+                                int64_t(info.n_blocks) * LA_PLAN_BLOCK_WORDS +
+                                int64_t(info.n_delta) * LA_PLAN_DELTA_WORDS +
+                                int64_t(info.n_scan) * LA_PLAN_SCAN_WORDS;
+    const int64_t off_pitems = off_pblocks + int64_t(info.piece_blocks) * LA_PLAN_BLOCK_WORDS;
+    const int64_t off_pscan = off_pitems + int64_t(info.piece_items) * LA_PLAN_ITEM_WORDS;
+    a.plan = plan;
+    a.blocks = reinterpret_cast<const PBlock*>(plan + off_pblocks);
+    a.items = reinterpret_cast<const PItem*>(plan + off_pitems);
+    a.scans = reinterpret_cast<const PScan*>(plan + off_pscan);
+    a.hdr = reinterpret_cast<int*>(ws);
+    a.flags = reinterpret_cast<uint64_t*>(ws + l.flags);
+    a.aslots = reinterpret_cast<float*>(ws + l.aslots);
+    a.pslots = reinterpret_cast<float*>(ws + l.pslots);
+    a.final_state = final_state;
+    a.ext_state = ext_state;
+    a.out = static_cast<uint16_t*>(out);
+    a.H = H;
+    a.n_flags = info.piece_slots * H;
+    a.plan_hash = info.plan_hash;
+    a.spin_limit = spin_limit;
+    a.force_timeout = force_timeout ? 1 : 0;
+    const dim3 blk(kThreads);
+    if (form == 1) {
+        if (!(stages & LA_STAGE_ALL)) return LA_OK;
+        a.n_work = info.piece_items * H;
+        if (a.n_work > 0)
+            hipLaunchKernelGGL(piece_kernel<kFused>, dim3(unsigned(a.n_work)), blk, 0, st, a);
+        return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_HIP;
+    }
+    if ((stages & LA_STAGE_STATES) && info.piece_block_items > 0) {
+        a.n_work = info.piece_block_items * H;
+        hipLaunchKernelGGL(piece_kernel<kStates>, dim3(unsigned(a.n_work)), blk, 0, st, a);
+        if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
+    }
+    if ((stages & LA_STAGE_PREFIX) && form == 3 && info.piece_scans > 0) {
+        const la_status s = launch_prefix(plan + off_pscan, info.piece_scans, a.aslots,
+                                          final_state, H, st, plan, a.hdr, info.plan_hash);
+        if (s != LA_OK) return s;
+    }
+    if ((stages & LA_STAGE_OUTPUT) && info.piece_items > 0) {
+        a.n_work = info.piece_items * H;
+        if (form == 3)
+            hipLaunchKernelGGL(piece_kernel<kOut3>, dim3(unsigned(a.n_work)), blk, 0, st, a);
+        else
+            hipLaunchKernelGGL(piece_kernel<kOut2>, dim3(unsigned(a.n_work)), blk, 0, st, a);
+        if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
+    }
+    return LA_OK;
+}
+
+}  // namespace piece

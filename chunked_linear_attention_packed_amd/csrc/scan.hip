@@ -46,6 +46,7 @@
 #include <type_traits>
 
 #include "linattn.h"
+#include "piece.h"
 #include "tiles.h"
 
 namespace {
@@ -82,6 +83,22 @@ struct ScanDesc {
     int first_slot, n_slots, final_row, seg;
 };
 
+// Every kernel first checks that the device plan is the one its la_pass_info
+// describes (magic word and the planner's hash); on a mismatch it records
+// LA_ERR_PLAN in the workspace header and does no work.
+struct PlanCheck {
+    const int32_t* plan;
+    int* hdr;
+    int hash;
+    __device__ bool ok() const {
+        if (plan[0] == LA_PLAN_MAGIC && plan[LA_PLAN_HASH_WORD] == hash) return true;
+        if (threadIdx.x == 0)
+            __hip_atomic_fetch_or(hdr + piece::kStatusWord, LA_ERR_PLAN, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+        return false;
+    }
+};
+
 // ===========================================================================
 // Launch 1: per delta block and head, sum over chunks of K_c^T V_c.  NP
 // workgroups share a (delta block, head) item, each summing the state
@@ -104,7 +121,9 @@ struct Delta1 {
 template <int D, int NP>
 __global__ __launch_bounds__(kThreads) void delta_kernel_bf16(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const DeltaDesc* __restrict__ deltas, float* __restrict__ ws, int H, int n_items) {
+    const DeltaDesc* __restrict__ deltas, float* __restrict__ ws, int H, int n_items,
+    PlanCheck pc) {
+    if (!pc.ok()) return;
     using D1 = Delta1<D, NP>;
     constexpr int R = D1::R, DVW = D1::DVW, NKB = D1::NKB, NVB = D1::NVB;
     constexpr int VBW = D1::VBW, KBW = D1::KBW, DD = D * D;
@@ -248,7 +267,8 @@ __device__ __forceinline__ void f32_state_update(f32x4 (&S)[D / 64][D / 16], con
 template <int D>
 __global__ __launch_bounds__(kThreads) void delta_kernel_f32(
     const float* __restrict__ k, const float* __restrict__ v,
-    const DeltaDesc* __restrict__ deltas, float* __restrict__ ws, int H) {
+    const DeltaDesc* __restrict__ deltas, float* __restrict__ ws, int H, PlanCheck pc) {
+    if (!pc.ok()) return;
     using TL = F32Tiles<D>;
     constexpr int NKB = D / 16, VBW = D / 64, DD = D * D;
     __shared__ __attribute__((aligned(16))) float sK[kChunk * TL::LD];
@@ -307,11 +327,12 @@ __global__ __launch_bounds__(kThreads) void delta_kernel_f32(
 // ===========================================================================
 constexpr int64_t kPrefixWideGroups = 8192;   // workgroups at one element per thread
 
-template <int D, int EPT, int BATCH>
+template <int D, int EPT, int BATCH, bool REWRITE_FIRST = false>
 __global__ __launch_bounds__(kThreads) void prefix_kernel(const ScanDesc* __restrict__ scans,
                                                           float* __restrict__ ws,
                                                           float* __restrict__ final_state,
-                                                          int H) {
+                                                          int H, PlanCheck pc) {
+    if (!pc.ok()) return;
     static_assert(EPT == 1 || EPT == 4, "one element or one 16-byte piece per thread");
     using V = typename std::conditional<EPT == 4, f32x4, float>::type;
     constexpr int DD = D * D, WPS = DD / (kThreads * EPT);
@@ -334,7 +355,7 @@ __global__ __launch_bounds__(kThreads) void prefix_kernel(const ScanDesc* __rest
         for (int i = 0; i < BATCH; ++i) {
             const int j = j0 + i;
             acc += x[i];
-            if (j >= 1 && j < last_store) p[j * stride] = acc;
+            if ((REWRITE_FIRST || j >= 1) && j < last_store) p[j * stride] = acc;
         }
     }
     if (sd.final_row >= 0) {
@@ -619,7 +640,8 @@ __global__ __launch_bounds__(O3::NT) void output_kernel_bf16(
     const uint16_t* __restrict__ v, const BlockDesc* __restrict__ blocks,
     const ScanDesc* __restrict__ scans, const float* __restrict__ ws,
     float* __restrict__ final_state, const float* __restrict__ ext_state,
-    uint16_t* __restrict__ out, int H, int n_items) {
+    uint16_t* __restrict__ out, int H, int n_items, PlanCheck pc) {
+    if (!pc.ok()) return;
     constexpr int R = O3::R, NT = O3::NT, NP = O3::NP_, DV = O3::DV;
     using ST = Stage<D, R>;
     constexpr int NKB = O3::NKB, NVB = O3::NVB, NKS = O3::NKS, VBH = O3::VBH, TPW = O3::TPW;
@@ -772,7 +794,8 @@ __global__ __launch_bounds__(kThreads) void output_kernel_f32(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const BlockDesc* __restrict__ blocks, const ScanDesc* __restrict__ scans,
     const float* __restrict__ ws, float* __restrict__ final_state,
-    const float* __restrict__ ext_state, float* __restrict__ out, int H) {
+    const float* __restrict__ ext_state, float* __restrict__ out, int H, PlanCheck pc) {
+    if (!pc.ok()) return;
     using TL = F32Tiles<D>;
     constexpr int NKB = D / 16, VBW = D / 64;
     __shared__ __attribute__((aligned(16))) float sQ[kChunk * TL::LD];
@@ -972,7 +995,8 @@ __device__ __forceinline__ f32x4 mfma3(u32x4 ah, u32x4 al, u32x4 bh, u32x4 bl, f
 template <int D>
 __global__ __launch_bounds__(kThreads) void delta_kernel_split(
     const float* __restrict__ k, const float* __restrict__ v,
-    const DeltaDesc* __restrict__ deltas, float* __restrict__ ws, int H) {
+    const DeltaDesc* __restrict__ deltas, float* __restrict__ ws, int H, PlanCheck pc) {
+    if (!pc.ok()) return;
     using D1 = Delta1<D, 1>;
     constexpr int R = D1::R, NKB = D1::NKB, VBW = D1::VBW, KBW = D1::KBW, DD = D * D;
     using ST = Stage<D, R>;
@@ -1098,7 +1122,9 @@ __global__ __launch_bounds__(O3::NT) void output_kernel_split(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const BlockDesc* __restrict__ blocks, const ScanDesc* __restrict__ scans,
     const float* __restrict__ ws, float* __restrict__ final_state,
-    const float* __restrict__ ext_state, float* __restrict__ out, int H, int n_items) {
+    const float* __restrict__ ext_state, float* __restrict__ out, int H, int n_items,
+    PlanCheck pc) {
+    if (!pc.ok()) return;
     constexpr int R = O3::R, NT = O3::NT, NP = O3::NP_, DV = O3::DV;
     using ST = Stage<D, R>;
     constexpr int NKB = O3::NKB, NVB = O3::NVB, NKS = O3::NKS, VBH = O3::VBH, TPW = O3::TPW;
@@ -1236,6 +1262,10 @@ bool supported_dims(int32_t d_k, int32_t d_v) {
 // tokens 79.3 / 77.0 (113 MB); one view of 18,000 with 256 branches
 // 100.9 / 131.1 (1.25 GB).
 constexpr double kTwoLaunchReadBytes = 128.0 * 1024 * 1024;
+// Polls of a single-launch wait before it gives up (each poll is a device-
+// coherent load plus a short sleep: a few tenths of a second in all, four
+// orders of magnitude above a wait in a normal pass).
+constexpr int32_t kSpinLimit = 1 << 18;
 bool two_launch_pays(const la_pass_info& info, int32_t H, int32_t d) {
     return double(info.fused_slot_reads) * H * d * d * 4 <= kTwoLaunchReadBytes;
 }
@@ -1262,7 +1292,7 @@ template <int D>
 la_status launch_all(int32_t stages, bool fused, const void* q, const void* k, const void* v,
                      la_dtype dtype, int32_t H, const la_pass_info& info, const int32_t* plan,
                      const float* ext_state, void* out, float* final_state, float* ws,
-                     hipStream_t st) {
+                     hipStream_t st, PlanCheck pc) {
     const int32_t off_blocks = LA_PLAN_HEADER_WORDS;
     const int32_t off_delta = off_blocks + info.n_blocks * LA_PLAN_BLOCK_WORDS;
     const int32_t off_scan = off_delta + info.n_delta * LA_PLAN_DELTA_WORDS;
@@ -1276,25 +1306,25 @@ la_status launch_all(int32_t stages, bool fused, const void* q, const void* k, c
         if (dtype == LA_BF16)
             hipLaunchKernelGGL((delta_kernel_bf16<D, NP>), dim3(unsigned(split_grid<NP>(items))),
                                blk, 0, st, static_cast<const uint16_t*>(k),
-                               static_cast<const uint16_t*>(v), deltas, ws, H, items);
+                               static_cast<const uint16_t*>(v), deltas, ws, H, items, pc);
         else if (dtype == LA_F32_SPLIT)
             hipLaunchKernelGGL(delta_kernel_split<D>, dim3(unsigned(items)), blk, 0, st,
                                static_cast<const float*>(k), static_cast<const float*>(v),
-                               deltas, ws, H);
+                               deltas, ws, H, pc);
         else
             hipLaunchKernelGGL(delta_kernel_f32<D>, dim3(unsigned(items)), blk, 0, st,
                                static_cast<const float*>(k), static_cast<const float*>(v), deltas,
-                               ws, H);
+                               ws, H, pc);
         if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
     }
     if ((stages & LA_STAGE_PREFIX) && !fused && info.n_scan > 0) {
         const int64_t wgs = int64_t(info.n_scan) * H * (D * D / kThreads);
         if (wgs >= kPrefixWideGroups)
             hipLaunchKernelGGL((prefix_kernel<D, 4, 8>), dim3(unsigned(wgs / 4)), blk, 0, st,
-                               scans, ws, final_state, H);
+                               scans, ws, final_state, H, pc);
         else
             hipLaunchKernelGGL((prefix_kernel<D, 1, 32>), dim3(unsigned(wgs)), blk, 0, st,
-                               scans, ws, final_state, H);
+                               scans, ws, final_state, H, pc);
         if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
     }
     if ((stages & LA_STAGE_OUTPUT) && info.n_blocks > 0) {
@@ -1306,7 +1336,7 @@ la_status launch_all(int32_t stages, bool fused, const void* q, const void* k, c
             hipLaunchKernelGGL(kern, g3, dim3(O3::NT), 0, st, static_cast<const uint16_t*>(q),
                                static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
                                blocks, scans, ws, final_state, ext_state,
-                               static_cast<uint16_t*>(out), H, items);
+                               static_cast<uint16_t*>(out), H, items, pc);
         } else if (dtype == LA_F32_SPLIT) {
             using O3S = typename LaunchCfg<D>::O3S;
             auto kern = fused ? output_kernel_split<D, O3S, true> : output_kernel_split<D, O3S, false>;
@@ -1314,13 +1344,13 @@ la_status launch_all(int32_t stages, bool fused, const void* q, const void* k, c
             hipLaunchKernelGGL(kern, g3s, dim3(O3S::NT), 0, st, static_cast<const float*>(q),
                                static_cast<const float*>(k), static_cast<const float*>(v), blocks,
                                scans, ws, final_state, ext_state, static_cast<float*>(out), H,
-                               items);
+                               items, pc);
         } else {
             auto kern = fused ? output_kernel_f32<D, true> : output_kernel_f32<D, false>;
             hipLaunchKernelGGL(kern, dim3(unsigned(items)), blk, 0, st,
                                static_cast<const float*>(q), static_cast<const float*>(k),
                                static_cast<const float*>(v), blocks, scans, ws, final_state,
-                               ext_state, static_cast<float*>(out), H);
+                               ext_state, static_cast<float*>(out), H, pc);
         }
         if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
     }
@@ -1373,14 +1403,49 @@ la_status scratch_for_current_device(hipStream_t st, void** out) {
     return LA_OK;
 }
 
+// Bytes of the workspace before the old path's block states: the header
+// (status word) every form shares.
+constexpr size_t kWsHeader = piece::kHeaderBytes;
+
+bool info_matches(const la_pass_info& info) {
+    return uint32_t(info.info_check) == la_info_checksum(&info);
+}
+
+}  // namespace
+
+namespace piece {
+// The prefix launch over the piece path's slots (views' totals go to
+// final_state); every slot, the first included, becomes the sum from zero of
+// the slots up to it.
+la_status launch_prefix(const int32_t* scans, int32_t n_scan, float* slots, float* final_state,
+                        int32_t H, hipStream_t st, const int32_t* plan, int* hdr, int hash) {
+    const PlanCheck pc{plan, hdr, hash};
+    const auto* sc = reinterpret_cast<const ScanDesc*>(scans);
+    const int64_t wgs = int64_t(n_scan) * H * (64 * 64 / kThreads);
+    if (wgs >= kPrefixWideGroups)
+        hipLaunchKernelGGL((prefix_kernel<64, 4, 8, true>), dim3(unsigned(wgs / 4)),
+                           dim3(kThreads), 0, st, sc, slots, final_state, H, pc);
+    else
+        hipLaunchKernelGGL((prefix_kernel<64, 1, 32, true>), dim3(unsigned(wgs)), dim3(kThreads),
+                           0, st, sc, slots, final_state, H, pc);
+    return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+}  // namespace piece
+
+namespace {
 }  // namespace
 
 extern "C" la_status la_scan_workspace_size(const la_pass_info* info, int32_t H, int32_t d_k,
                                             int32_t d_v, la_dtype dtype, size_t* bytes) {
-    if (!info || !bytes || H < 1 || info->n_delta < 0) return LA_ERR_INVALID_ARG;
+    if (!info || !bytes || H < 1 || info->n_delta < 0 || info->piece_slots < 0)
+        return LA_ERR_INVALID_ARG;
     if (!supported_dims(d_k, d_v) || (dtype != LA_F32 && dtype != LA_BF16 && dtype != LA_F32_SPLIT))
         return LA_ERR_UNSUPPORTED;
-    *bytes = size_t(info->n_delta) * size_t(H) * size_t(d_k) * size_t(d_v) * sizeof(float);
+    if (piece::applies(d_k, dtype))
+        *bytes = piece::workspace_bytes(*info, H);
+    else
+        *bytes = kWsHeader +
+                 size_t(info->n_delta) * size_t(H) * size_t(d_k) * size_t(d_v) * sizeof(float);
     return LA_OK;
 }
 
@@ -1391,10 +1456,12 @@ extern "C" la_status la_scan_packed_stages(int32_t stages, const void* q, const 
                                            int32_t n_ext, void* out, float* final_state,
                                            void* workspace, size_t workspace_bytes,
                                            void* stream) {
-    if (!info || (stages & ~(LA_STAGE_ALL | LA_FORM_TWO_LAUNCH | LA_FORM_THREE_LAUNCH)) ||
-        !(stages & LA_STAGE_ALL) ||
-        ((stages & LA_FORM_TWO_LAUNCH) && (stages & LA_FORM_THREE_LAUNCH)))
+    constexpr int32_t kForms = LA_FORM_ONE_LAUNCH | LA_FORM_TWO_LAUNCH | LA_FORM_THREE_LAUNCH;
+    if (!info || (stages & ~(LA_STAGE_ALL | kForms | LA_DEBUG_FORCE_TIMEOUT)) ||
+        !(stages & LA_STAGE_ALL) || __builtin_popcount(unsigned(stages & kForms)) > 1)
         return LA_ERR_INVALID_ARG;
+    // an la_pass_info whose fields were edited, or mixed from two passes
+    if (!info_matches(*info)) return LA_ERR_INVALID_ARG;
     if (dtype != LA_F32 && dtype != LA_BF16 && dtype != LA_F32_SPLIT) return LA_ERR_UNSUPPORTED;
     if (!supported_dims(d_k, d_v) || info->chunk != LA_CHUNK) return LA_ERR_UNSUPPORTED;
     if (H < 1 || info->n_tokens < 0 || info->n_blocks < 0 || info->n_delta < 0 ||
@@ -1428,23 +1495,57 @@ extern "C" la_status la_scan_packed_stages(int32_t stages, const void* q, const 
     size_t need = 0;
     la_status stw = la_scan_workspace_size(info, H, d_k, d_v, dtype, &need);
     if (stw != LA_OK) return stw;
-    if (need > 0 && (!workspace || workspace_bytes < need)) return LA_ERR_WORKSPACE;
+    if (!workspace || workspace_bytes < need) return LA_ERR_WORKSPACE;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    float* ws = static_cast<float*>(workspace);
+    if (piece::applies(d_k, dtype)) {
+        const int form = (stages & LA_FORM_TWO_LAUNCH)     ? 2
+                         : (stages & LA_FORM_THREE_LAUNCH) ? 3
+                                                           : 1;
+        const bool force = (stages & LA_DEBUG_FORCE_TIMEOUT) != 0;
+        return piece::launch(stages & LA_STAGE_ALL, form, q, k, v, H, *info, plan, ext_state,
+                             out, final_state, workspace, st, force ? 16 : kSpinLimit, force);
+    }
+    if (stages & (LA_FORM_ONE_LAUNCH | LA_DEBUG_FORCE_TIMEOUT)) return LA_ERR_UNSUPPORTED;
+    int* hdr = static_cast<int*>(workspace);
+    float* ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + kWsHeader);
+    const PlanCheck pc{plan, hdr, info->plan_hash};
     const bool fused = (stages & LA_FORM_TWO_LAUNCH) ||
                        (!(stages & LA_FORM_THREE_LAUNCH) && two_launch_pays(*info, H, d_k));
     if (d_k == 64)
         return launch_all<64>(stages, fused, q, k, v, dtype, H, *info, plan, ext_state, out,
-                              final_state, ws, st);
+                              final_state, ws, st, pc);
     return launch_all<128>(stages, fused, q, k, v, dtype, H, *info, plan, ext_state, out,
-                           final_state, ws, st);
+                           final_state, ws, st, pc);
 }
 
 extern "C" la_status la_scan_launches(const la_pass_info* info, int32_t H, int32_t d_k,
-                                      int32_t d_v, int32_t* n_launches) {
+                                      int32_t d_v, la_dtype dtype, int32_t* n_launches) {
     if (!info || !n_launches || H < 1) return LA_ERR_INVALID_ARG;
     if (!supported_dims(d_k, d_v)) return LA_ERR_UNSUPPORTED;
-    *n_launches = two_launch_pays(*info, H, d_k) ? 2 : 3;
+    if (piece::applies(d_k, dtype))
+        *n_launches = 1;
+    else
+        *n_launches = two_launch_pays(*info, H, d_k) ? 2 : 3;
+    return LA_OK;
+}
+
+extern "C" la_status la_scan_status(const void* workspace, size_t workspace_bytes,
+                                    int32_t* status, int32_t clear, void* stream) {
+    if (!workspace || !status || workspace_bytes < kWsHeader) return LA_ERR_INVALID_ARG;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int32_t v = 0;
+    const int32_t* src = static_cast<const int32_t*>(workspace) + piece::kStatusWord;
+    if (hipMemcpyAsync(&v, src, sizeof(v), hipMemcpyDeviceToHost, st) != hipSuccess)
+        return LA_ERR_HIP;
+    if (hipStreamSynchronize(st) != hipSuccess) return LA_ERR_HIP;
+    if (clear && v != 0) {
+        const int32_t zero = 0;
+        if (hipMemcpyAsync(const_cast<int32_t*>(src), &zero, sizeof(zero), hipMemcpyHostToDevice,
+                           st) != hipSuccess ||
+            hipStreamSynchronize(st) != hipSuccess)
+            return LA_ERR_HIP;
+    }
+    *status = v;
     return LA_OK;
 }
 

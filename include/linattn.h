@@ -55,9 +55,14 @@ enum {
     LA_ERR_UNSUPPORTED = 2,   /* dtype, head dim or chunk size not built   */
     LA_ERR_WORKSPACE = 3,     /* workspace missing or too small            */
     LA_ERR_HIP = 4,           /* a HIP runtime call or launch failed       */
-    LA_ERR_TOO_LARGE = 5      /* the pass needs more scratch memory than the
+    LA_ERR_TOO_LARGE = 5,     /* the pass needs more scratch memory than the
                                  library's built-in array holds
                                  (la_scan_packed_noalloc)                  */
+    LA_ERR_PLAN = 6,          /* the device plan does not belong to the
+                                 la_pass_info given with it (reported by
+                                 the kernels, see la_scan_status)          */
+    LA_ERR_TIMEOUT = 7        /* a bounded wait of the single-launch scan
+                                 gave up (see la_scan_status)              */
 };
 
 typedef int32_t la_dtype;
@@ -76,12 +81,22 @@ enum {
  * page evaluates linear attention in 64-token chunks; only 64 is built. */
 #define LA_CHUNK 64
 
-/* Magic word at plan[0]. */
+/* Magic word at plan[0]; plan[LA_PLAN_HASH_WORD] holds a hash of the whole
+ * plan (taken with that word as zero), also kept in la_pass_info.plan_hash. */
 #define LA_PLAN_MAGIC 0x4C41504E
-#define LA_PLAN_HEADER_WORDS 16
+#define LA_PLAN_HASH_WORD 14
+#define LA_PLAN_HEADER_WORDS 32
 #define LA_PLAN_BLOCK_WORDS 8
 #define LA_PLAN_DELTA_WORDS 4
 #define LA_PLAN_SCAN_WORDS 4
+#define LA_PLAN_ITEM_WORDS 8
+#define LA_ITEM_BLOCK 0
+#define LA_ITEM_PACK 1
+/* The piece path (d = 64, bf16 inputs) cuts every segment into blocks of
+ * LA_PIECE_BLOCK_CHUNKS chunks and every block into pieces of
+ * LA_PIECE_CHUNKS chunks, one piece per wave of a 4-wave workgroup. */
+#define LA_PIECE_CHUNKS 2
+#define LA_PIECE_BLOCK_CHUNKS 8
 
 /* Shape summary of one packed pass, filled by la_pack_pass or
  * la_plan_segments and read by la_scan_workspace_size and la_scan_packed. */
@@ -105,8 +120,21 @@ typedef struct {
                                  launch when it sums the block states itself
                                  (two-launch form, see la_scan_packed),
                                  saturated at INT32_MAX                        */
-    int32_t reserved[8];
+    int32_t piece_blocks;     /* piece path: blocks of LA_PIECE_BLOCK_CHUNKS    */
+    int32_t piece_items;      /* piece path: workgroup items (x H heads)        */
+    int32_t piece_block_items;/* piece path: items holding one block (the
+                                 others hold up to four one-piece branches)    */
+    int32_t piece_slots;      /* piece path: block states kept per head        */
+    int32_t piece_scans;      /* piece path: segments with block states        */
+    int32_t plan_hash;        /* hash of the plan the planner wrote            */
+    int32_t info_check;       /* la_info_checksum of the other fields          */
+    int32_t reserved[1];
 } la_pass_info;
+
+/* Checksum of an la_pass_info, over every field but info_check.  The planners
+ * store it in info_check; la_scan_packed rejects an info whose fields no
+ * longer match it (edited, or mixed from two passes).  Host only. */
+uint32_t la_info_checksum(const la_pass_info* info);
 
 /*
  * la_plan_segments -- build the device work plan of a pass from its segment
@@ -135,9 +163,11 @@ typedef struct {
  * Errors: LA_ERR_INVALID_ARG (bad table), LA_ERR_UNSUPPORTED (chunk).
  *
  * Plan layout (int32 words):
- *   [0..15]   header: magic, version 2, n_blocks, n_delta, n_scan, chunk,
+ *   [0..31]   header: magic, version 3, n_blocks, n_delta, n_scan, chunk,
  *             block_chunks, n_tokens, off_blocks, off_delta, off_scan, n_ext,
- *             n_views, fused_slot_reads, 0, 0
+ *             n_views, fused_slot_reads, plan hash, then for the piece path
+ *             piece_blocks, piece_items, piece_block_items, piece_slots,
+ *             piece_scans, off_pblocks, off_pitems, off_pscan, 0 ...
  *   blocks    n_blocks x 8:
  *             {tok0, ntok, sin_slot, delta_slot, seed, seg, slot0, final_row}
  *             sin_slot   workspace slot holding the segment-local state before
@@ -156,6 +186,15 @@ typedef struct {
  *   scan      n_scan x 4:  {first_slot, n_slots, final_row (-1: branch), seg};
  *             the first n_views entries are the views, in ordinal order (the
  *             two-launch form finds a branch's view slots at scan[seed])
+ *   pblocks   piece_blocks x 8: {tok0, ntok, slot, seed, seg, slot0, j,
+ *             final_row} -- blocks of LA_PIECE_BLOCK_CHUNKS chunks; slot: the
+ *             block's state slot (-1: none needed), slot0: the segment's first
+ *             slot, j: the block's position in its segment
+ *   pitems    piece_items x 8: {kind, n, b0, b1, b2, b3, 0, 0} -- kind
+ *             LA_ITEM_BLOCK: one block b0 (wave w takes its piece w);
+ *             LA_ITEM_PACK: n one-piece branch blocks b0.. (wave w takes
+ *             b_w).  Block items first, in block order, then the packs.
+ *   pscan     piece_scans x 4, as scan, for the piece path's slots
  * View blocks come first (longest work first), then branch blocks.
  */
 la_status la_plan_segments(int32_t n_segments, const int32_t* seg_offsets,
@@ -230,33 +269,44 @@ la_status la_pack_pass_ext(int32_t n_requests, const int32_t* view_len,
 
 /*
  * la_scan_workspace_size -- bytes of device workspace la_scan_packed needs:
- * one fp32 d_k x d_v state per (delta block, head).
+ * a 256-byte header (a sticky status word, see la_scan_status, and the
+ * single-launch form's counters) plus the block states (one fp32 d_k x d_v
+ * state per block and head; the piece path, d = 64 with bf16 inputs, also
+ * keeps a flag and an inclusive prefix per block and head for its
+ * single-launch form).  The same size serves every form of a pass.
  * Errors: LA_ERR_INVALID_ARG (NULL), LA_ERR_UNSUPPORTED (shape/dtype).
  */
 la_status la_scan_workspace_size(const la_pass_info* info, int32_t H, int32_t d_k,
                                  int32_t d_v, la_dtype dtype, size_t* bytes);
 
 /*
- * la_scan_packed -- the scan of one packed pass, in three launches on
- * `stream` (section "Kernels", paragraph "One scan per pass"):
- *   1. per work block and head, the block's state sum_t k_t^T v_t (MFMA);
- *   2. per segment, head and state element, the prefix of those block
- *      states; writes final_state for every view;
- *   3. per work block and head, chunk by chunk: o = q S_in + (causal
- *      (q k^T)) v, carrying S in registers; branch blocks start from their
- *      view's total (the same bits as its final_state row) or from ext_state.
- * For passes whose block states are few (la_pass_info.fused_slot_reads x H
- * x d_k x d_v x 4 bytes up to 128 MiB) launch 2 is left out: each launch-3
- * workgroup sums the block states before it (and a branch those of its view)
- * itself, and each view's last block writes final_state.  Both forms add the
- * states in the same order and give the same bits.
+ * la_scan_packed -- the scan of one packed pass on `stream` (section
+ * "Kernels", paragraph "One scan per pass": one scan covers every view of the
+ * pass).  The arithmetic, per head: the block states sum_t k_t^T v_t (MFMA),
+ * their prefix within each segment (a view's total is final_state), and per
+ * chunk o = q S_in + (causal (q k^T)) v carrying S; branch blocks start from
+ * their view's total (the same bits as its final_state row) or from
+ * ext_state.  It runs in one of three forms, all giving the same bits:
+ *   three launches  block states, prefix, outputs (the page's structure);
+ *   two launches    block states, then outputs whose workgroups sum the
+ *                   states they need themselves (no prefix launch);
+ *   one launch      d = 64 with bf16 inputs only: each workgroup computes
+ *                   its block's state, obtains the prefix from the
+ *                   workgroups before it in the same launch, and computes its
+ *                   outputs from the k and v it has already read, so k and v
+ *                   cross HBM once.
+ * The library picks one launch for d = 64 with bf16 inputs, otherwise two
+ * launches for passes whose block states are few (la_pass_info.
+ * fused_slot_reads x H x d_k x d_v x 4 bytes up to 128 MiB) and three
+ * otherwise; la_scan_launches reports the choice and la_scan_packed_stages
+ * can force a form.
  *
  *   q, k           device [T][H][d_k], dtype
  *   v              device [T][H][d_v], dtype
  *   dtype          LA_F32, LA_F32_SPLIT (both fp32 tensors) or LA_BF16
  *   H              heads >= 1
  *   d_k, d_v       head dims; d_k == d_v, 64 or 128
- *   info           host, from the planner that built `plan`
+ *   info           host, from the planner that built `plan` (unedited)
  *   plan           device [info->plan_words] int32, a copy of the plan
  *   ext_state      device [n_ext][H][d_k][d_v] fp32 or NULL when the pass has
  *                  no shard branches (info->n_ext == 0); must not overlap
@@ -265,7 +315,10 @@ la_status la_scan_workspace_size(const la_pass_info* info, int32_t H, int32_t d_
  *   out            device [T][H][d_v], dtype: fully overwritten
  *   final_state    device [info->n_views][H][d_k][d_v] fp32, row-major
  *                  (d_v fastest): fully overwritten; NULL iff n_views == 0
- *   workspace      device, >= la_scan_workspace_size bytes (NULL if 0)
+ *   workspace      device, >= la_scan_workspace_size bytes, zero-filled
+ *                  before its first use (the single-launch form keeps its
+ *                  counters and flags there and leaves them zero after every
+ *                  pass; fill it with zeros again after an error)
  *   stream         hipStream_t as void*
  * Accumulation is fp32; bf16 outputs are rounded to nearest even.  A pass is
  * idempotent: it reads only its inputs and overwrites all outputs.  Calls
@@ -273,10 +326,14 @@ la_status la_scan_workspace_size(const la_pass_info* info, int32_t H, int32_t d_
  * Errors (all detected on the host before anything is enqueued; outputs are
  * then untouched): LA_ERR_INVALID_ARG for NULL or misaligned pointers (q, k,
  * v, out 16-byte aligned; states and plan 4-byte; workspace 16-byte), H < 1,
- * n_ext < info->n_ext, ext_state overlapping final_state, or sizes past the
- * 32-bit dispatch and buffer limits; LA_ERR_UNSUPPORTED for other dtypes,
- * head dims or chunk sizes; LA_ERR_WORKSPACE for a missing or short
- * workspace; LA_ERR_HIP if a launch fails.
+ * n_ext < info->n_ext, ext_state overlapping final_state, an info whose
+ * fields no longer match its checksum, or sizes past the 32-bit dispatch and
+ * buffer limits; LA_ERR_UNSUPPORTED for other dtypes, head dims or chunk
+ * sizes; LA_ERR_WORKSPACE for a missing or short workspace; LA_ERR_HIP if a
+ * launch fails.  Found on the device (recorded in the workspace's status
+ * word, see la_scan_status): LA_ERR_PLAN when the device plan is not the one
+ * `info` describes (the kernels then do no work), LA_ERR_TIMEOUT when a wait
+ * of the single-launch form gave up (its outputs are then not valid).
  */
 la_status la_scan_packed(const void* q, const void* k, const void* v, la_dtype dtype,
                          int32_t H, int32_t d_k, int32_t d_v, const la_pass_info* info,
@@ -285,23 +342,40 @@ la_status la_scan_packed(const void* q, const void* k, const void* v, la_dtype d
                          size_t workspace_bytes, void* stream);
 
 /*
- * la_scan_launches -- the form la_scan_packed picks for a pass: 2 (no prefix
- * launch) or 3, written to *n_launches.  Host only; no device work.
+ * la_scan_launches -- the form la_scan_packed picks for a pass with these
+ * head dims and dtype: 1, 2 or 3 launches, written to *n_launches.  Host only.
  * Errors: LA_ERR_INVALID_ARG (NULL, H < 1), LA_ERR_UNSUPPORTED (head dims).
  */
 la_status la_scan_launches(const la_pass_info* info, int32_t H, int32_t d_k, int32_t d_v,
-                           int32_t* n_launches);
+                           la_dtype dtype, int32_t* n_launches);
+
+/*
+ * la_scan_status -- reads the sticky status word of a workspace after the
+ * passes enqueued on `stream` (synchronises the stream): LA_OK, or an error
+ * the kernels recorded (LA_ERR_PLAN, LA_ERR_TIMEOUT; several may be or-ed).
+ * clear != 0 resets the word to zero afterwards.
+ * Errors: LA_ERR_INVALID_ARG (NULL, workspace shorter than its header),
+ * LA_ERR_HIP.
+ */
+la_status la_scan_status(const void* workspace, size_t workspace_bytes, int32_t* status,
+                         int32_t clear, void* stream);
 
 /* Launch selection bits for la_scan_packed_stages. */
 #define LA_STAGE_STATES 1     /* launch 1: per-block states          */
 #define LA_STAGE_PREFIX 2     /* launch 2: segmented prefix          */
 #define LA_STAGE_OUTPUT 4     /* launch 3: chunk outputs             */
 #define LA_STAGE_ALL 7
-/* Form of the scan, for la_scan_packed_stages (at most one of the two; with
- * neither the library picks the form from the pass shape). */
+/* Form of the scan, for la_scan_packed_stages (at most one of the three;
+ * with none the library picks the form from the pass shape). */
 #define LA_FORM_TWO_LAUNCH 8    /* no prefix launch: each output workgroup sums
                                    the block states it needs itself        */
 #define LA_FORM_THREE_LAUNCH 16 /* the prefix launch runs between 1 and 3   */
+#define LA_FORM_ONE_LAUNCH 32   /* single launch (d = 64, bf16 only); any
+                                   LA_STAGE_* bit runs the whole pass      */
+/* Test aid for the single-launch form: every wait gives up after a few polls
+ * (LA_ERR_TIMEOUT is recorded, the outputs are not valid, every kernel still
+ * exits normally). */
+#define LA_DEBUG_FORCE_TIMEOUT 64
 
 /*
  * la_scan_packed_stages -- la_scan_packed restricted to the launches whose
@@ -309,14 +383,15 @@ la_status la_scan_launches(const la_pass_info* info, int32_t H, int32_t d_k, int
  * For profiling one launch in isolation.  Launch 2 rewrites the workspace in
  * place, so it must follow a launch 1 on the same buffers; launch 3 only
  * reads the workspace (and ext_state), so after one complete pass it may be
- * repeated alone and produces the same out.  One
- * of LA_FORM_TWO_LAUNCH / LA_FORM_THREE_LAUNCH may be or-ed in to force the
- * form (in the two-launch form the LA_STAGE_PREFIX bit does nothing); every
- * call on one workspace must use the same form.  la_scan_packed(...) is
- * la_scan_packed_stages(LA_STAGE_ALL, ...).
+ * repeated alone and produces the same out.  One of the LA_FORM_* bits may be
+ * or-ed in to force the form (in the two-launch form the LA_STAGE_PREFIX bit
+ * does nothing); every call on one workspace must use the same form.
+ * la_scan_packed(...) is la_scan_packed_stages(LA_STAGE_ALL, ...).
  * Errors: as la_scan_packed (LA_ERR_INVALID_ARG also for ext_state overlapping
- * final_state), plus LA_ERR_INVALID_ARG when no LA_STAGE_* bit
- * is set, an unknown bit is set, or both LA_FORM_* bits are set.
+ * final_state), plus LA_ERR_INVALID_ARG when no LA_STAGE_* bit is set, an
+ * unknown bit is set, or more than one LA_FORM_* bit is set, and
+ * LA_ERR_UNSUPPORTED for LA_FORM_ONE_LAUNCH or LA_DEBUG_FORCE_TIMEOUT outside
+ * the piece path.
  */
 la_status la_scan_packed_stages(int32_t stages, const void* q, const void* k, const void* v,
                                 la_dtype dtype, int32_t H, int32_t d_k, int32_t d_v,

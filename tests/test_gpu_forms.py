@@ -1,8 +1,10 @@
-"""The two forms of the scan on the GPU: three launches (block states, prefix
-launch, outputs) and two launches (the output workgroups sum the block
-states they need themselves; a view's last block writes its final state).
+"""The forms of the scan on the GPU: three launches (block states, prefix
+launch, outputs), two launches (the output workgroups sum the block states
+they need themselves; a view's last block writes its final state) and, on
+the piece path (d = 64, bf16), one launch (each workgroup obtains the prefix
+from the workgroups before it in the same launch).
 
-Both forms add the block states in the same order, so they must agree bit
+All forms add the block states in the same order, so they must agree bit
 for bit, and each must match the fp64 oracle within the tolerance (row-
 normalised max relative error 1e-3 for fp32 inputs, 2e-2 for bf16).
 """
@@ -63,6 +65,9 @@ def test_two_and_three_launch_forms_agree(dtype, d, split, G, case):
     o2, f2 = _run(q, k, v, plan, "two", ext, split)
     assert torch.equal(o2, o3)
     assert torch.equal(f2, f3)
+    if dtype == "bf16" and d == 64:
+        o1, f1 = _run(q, k, v, plan, "one", ext, split)
+        assert torch.equal(o1, o3) and torch.equal(f1, f3)
     ref_o, ref_f = oracle.scan_recurrence(q, k, v, plan.seg_offsets, plan.branch_parent,
                                           ext_state=ext)
     eo, ef = oracle.row_rel_err(o2, ref_o), oracle.state_rel_err(f2, ref_f)
@@ -106,7 +111,9 @@ def test_workload_forms_agree(name):
           f"{la.scan_launches(plan, w.H, w.d)}", flush=True)
     o3, f3 = _run(w.q, w.k, w.v, plan, "three")
     o2, f2 = _run(w.q, w.k, w.v, plan, "two")
+    o1, f1 = _run(w.q, w.k, w.v, plan, "one")
     assert torch.equal(o2, o3) and torch.equal(f2, f3)
+    assert torch.equal(o1, o3) and torch.equal(f1, f3)
     ref_o, ref_f = oracle.scan_recurrence(w.q, w.k, w.v, plan.seg_offsets, plan.branch_parent)
     assert oracle.row_rel_err(o2, ref_o) <= TOL["bf16"]
     assert oracle.state_rel_err(f2, ref_f) <= TOL["bf16"]
@@ -118,8 +125,7 @@ def test_output_launch_alone_repeats_in_two_launch_form():
     w = synth.workload("view7400_br8x48_h16_d64_bf16")
     plan = la.pack(w.view_len, w.branch_count, w.branch_len, heads=w.H)
     qd, kd, vd = (x.to(DEV) for x in (w.q, w.k, w.v))
-    ws = torch.empty(la.workspace_size(plan, w.H, w.d, la.LA_BF16), dtype=torch.uint8,
-                     device=DEV)
+    ws = la.new_workspace(plan, w.H, w.d, la.LA_BF16, DEV)
     o1, f1 = la.scan_packed(qd, kd, vd, plan, workspace=ws, form="two")
     o1 = o1.clone()
     o2 = torch.full_like(o1, float("nan"))
@@ -148,6 +154,9 @@ def test_wide_prefix_launch_agrees(d):
     o3, f3 = _run(q, k, v, plan, "three")
     o2, f2 = _run(q, k, v, plan, "two")
     assert torch.equal(o2, o3) and torch.equal(f2, f3)
+    if d == 64:
+        o1, f1 = _run(q, k, v, plan, "one")
+        assert torch.equal(o1, o3) and torch.equal(f1, f3)
     ref_o, ref_f = oracle.scan_recurrence(q, k, v, plan.seg_offsets, plan.branch_parent)
     eo, ef = oracle.row_rel_err(o3, ref_o), oracle.state_rel_err(f3, ref_f)
     print(f"  wide prefix d={d}: T={T} scans={plan.info.n_scan} out err {eo:.3e} final err {ef:.3e}",
@@ -167,7 +176,7 @@ def test_launches_one_at_a_time_equal_the_full_pass(form):
     q, k, v = synth.draw_qkv(np.random.default_rng(77), T, H, d, "bf16")
     qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
     o_full, f_full = la.scan_packed(qd, kd, vd, plan, form=form)
-    ws = torch.empty(la.workspace_size(plan, H, d, la.LA_BF16), dtype=torch.uint8, device=DEV)
+    ws = la.new_workspace(plan, H, d, la.LA_BF16, DEV)
     out = torch.full_like(o_full, float("nan"))
     fin = torch.full_like(f_full, float("nan"))
     for stage in (la.STAGE_STATES, la.STAGE_PREFIX, la.STAGE_OUTPUT):

@@ -60,9 +60,10 @@ def test_random_scan(i):
     qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
     ed = None if ext is None else ext.to(DEV)
     out, fin = la.scan_packed(qd, kd, vd, plan, ext_state=ed, split_fp32=split)
-    # both forms of the scan (two launches; three with the prefix launch) give
-    # the same bits as the one the library picked
-    for form in ("two", "three"):
+    # every form of the scan (one launch on the piece path; two launches; three
+    # with the prefix launch) gives the same bits as the one the library picked
+    forms = ("one", "two", "three") if (dtype == "bf16" and d == 64) else ("two", "three")
+    for form in forms:
         o_f, f_f = la.scan_packed(qd, kd, vd, plan, ext_state=ed, split_fp32=split, form=form)
         assert torch.equal(o_f, out) and torch.equal(f_f, fin), form
     torch.cuda.synchronize()

@@ -46,19 +46,87 @@ def test_pack_matches_oracle_packer(name):
     _check_plan(plan, so, bp, vo)
 
 
+def _fnv1a(words):
+    h = 2166136261
+    for w in words:
+        w &= 0xFFFFFFFF
+        for b in range(4):
+            h ^= (w >> (8 * b)) & 0xFF
+            h = (h * 16777619) & 0xFFFFFFFF
+    return h
+
+
+def _check_piece_tables(plan, so, bp, vo):
+    """The piece path's tables against the rules they follow: blocks of 8
+    chunks restarting at every segment, a state slot for every view block and
+    every branch block but the last, segments' slots contiguous, branches
+    whose only block is one piece (<= 128 tokens) packed four to an item, every
+    other block one item in block order; and the plan hash and info check."""
+    info, P = plan.info, plan.plan.astype(np.int64)
+    BT, PT = 8 * 64, 2 * 64
+    nb_, ni, nbi, nsl, nsc = (int(x) for x in P[15:20])
+    assert (nb_, ni, nbi, nsl, nsc) == (info.piece_blocks, info.piece_items,
+                                        info.piece_block_items, info.piece_slots,
+                                        info.piece_scans)
+    ob, oi, osc = (int(x) for x in P[20:23])
+    assert oi == ob + 8 * nb_ and osc == oi + 8 * ni and osc + 4 * nsc == info.plan_words
+    blocks = P[ob:ob + 8 * nb_].reshape(-1, 8)
+    items = P[oi:oi + 8 * ni].reshape(-1, 8)
+    scans = P[osc:osc + 4 * nsc].reshape(-1, 4)
+    # expected blocks, views first then branches, in segment order
+    want, slot, view_scan = [], 0, {}
+    packed = []
+    for pass_ in (0, 1):
+        for s in range(len(bp)):
+            is_view = bp[s] == -1
+            if is_view != (pass_ == 0):
+                continue
+            n = int(so[s + 1] - so[s])
+            nb = -(-n // BT)
+            nsl_s = nb if is_view else nb - 1
+            seed = -1 if is_view else (int(vo[bp[s]]) if bp[s] >= 0 else int(bp[s]))
+            for j in range(nb):
+                want.append([int(so[s]) + j * BT, min(BT, n - j * BT),
+                             slot + j if j < nsl_s else -1, seed, s,
+                             slot if nsl_s > 0 else -1, j,
+                             int(vo[s]) if is_view and j == nb - 1 else -1])
+                if not is_view and nb == 1 and n <= PT:
+                    packed.append(len(want) - 1)
+            if is_view:
+                view_scan[int(vo[s])] = (slot, nsl_s)
+            slot += nsl_s
+    assert blocks.tolist() == want and slot == nsl
+    kinds = items[:, 0]
+    assert np.all(kinds[:nbi] == 0) and np.all(kinds[nbi:] == 1)
+    singles = [i for i in range(len(want)) if i not in set(packed)]
+    assert items[:nbi, 2].tolist() == singles and np.all(items[:nbi, 1] == 1)
+    got_packed = []
+    for row in items[nbi:]:
+        assert 1 <= row[1] <= 4 and all(x == -1 for x in row[2 + row[1]:6])
+        got_packed += row[2:2 + row[1]].tolist()
+    assert got_packed == packed
+    for v, (first, n) in view_scan.items():
+        assert scans[v].tolist() == [first, n, v, int(np.flatnonzero((bp == -1) & (vo == v))[0])]
+    ph = P.copy()
+    ph[14] = 0
+    assert _fnv1a(ph.tolist()) == (int(P[14]) & 0xFFFFFFFF) == (info.plan_hash & 0xFFFFFFFF)
+    assert (info.info_check & 0xFFFFFFFF) == la.load_library().la_info_checksum(ctypes.byref(info))
+
+
 def _check_plan(plan, so, bp, vo):
     """Every token in exactly one block; blocks never cross segments; slots of
     a segment are contiguous, the delta list matches the blocks, and the scan
     list covers views plus branches with >= 2 slots."""
     info, P = plan.info, plan.plan
     G, C = info.block_chunks, info.chunk
-    assert P[0] == 0x4C41504E and P[1] == 2
+    assert P[0] == 0x4C41504E and P[1] == 3
     assert (P[2], P[3], P[4]) == (info.n_blocks, info.n_delta, info.n_scan)
     ob, od, osc = P[8], P[9], P[10]
     blocks = P[ob:ob + 8 * info.n_blocks].reshape(-1, 8)
     deltas = P[od:od + 4 * info.n_delta].reshape(-1, 4)
     scans = P[osc:osc + 4 * info.n_scan].reshape(-1, 4)
-    assert osc + 4 * info.n_scan == info.plan_words
+    assert osc + 4 * info.n_scan == P[20]
+    _check_piece_tables(plan, so, bp, vo)
     cover = np.zeros(info.n_tokens, dtype=np.int64)
     seg_blocks = {}
     fused_reads = 0
@@ -180,9 +248,16 @@ def test_unsupported_chunk_and_dims():
                                       ctypes.byref(n)) == la.LA_ERR_UNSUPPORTED
     assert lib.la_scan_workspace_size(ctypes.byref(plan.info), 2, 64, 64, 7,
                                       ctypes.byref(n)) == la.LA_ERR_UNSUPPORTED
+    assert lib.la_scan_workspace_size(ctypes.byref(plan.info), 2, 64, 64, la.LA_F32,
+                                      ctypes.byref(n)) == la.LA_OK
+    # a 256-byte header, then one fp32 state per delta block and head
+    assert n.value == 256 + plan.info.n_delta * 2 * 64 * 64 * 4
     assert lib.la_scan_workspace_size(ctypes.byref(plan.info), 2, 64, 64, la.LA_BF16,
                                       ctypes.byref(n)) == la.LA_OK
-    assert n.value == plan.info.n_delta * 2 * 64 * 64 * 4
+    # piece path: header, a flag per slot and head (rounded to 256 bytes), then
+    # block states and inclusive prefixes
+    nsh = plan.info.piece_slots * 2
+    assert n.value == 256 + -(-nsh * 8 // 256) * 256 + 2 * nsh * 64 * 64 * 4
 
 
 def test_scan_rejects_bad_arguments_before_launch():
@@ -217,6 +292,23 @@ def test_scan_rejects_bad_arguments_before_launch():
     assert call(ws=ctypes.c_void_p(4100)) == la.LA_ERR_INVALID_ARG
     assert call(plan=ctypes.c_void_p(4097)) == la.LA_ERR_INVALID_ARG
     assert call(dtype=la.LA_F32_SPLIT, dk=96, dv=96) == la.LA_ERR_UNSUPPORTED
+
+    def staged(stages, **kw):
+        a = dict(args, **kw)
+        return lib.la_scan_packed_stages(stages, a["q"], a["k"], a["v"], a["dtype"], a["H"],
+                                         a["dk"], a["dv"], ctypes.byref(info), a["plan"],
+                                         a["ext"], a["n_ext"], a["out"], a["fin"], a["ws"],
+                                         a["wsb"], None)
+    assert staged(la.STAGE_ALL | la.FORM_ONE_LAUNCH | la.FORM_TWO_LAUNCH) == la.LA_ERR_INVALID_ARG
+    assert staged(la.FORM_ONE_LAUNCH) == la.LA_ERR_INVALID_ARG        # no stage bit
+    assert staged(la.STAGE_ALL | 128) == la.LA_ERR_INVALID_ARG        # unknown bit
+    need32 = ctypes.c_size_t()
+    lib.la_scan_workspace_size(ctypes.byref(info), 2, 64, 64, la.LA_F32, ctypes.byref(need32))
+    # the single-launch form and its timeout aid exist on the piece path only
+    assert staged(la.STAGE_ALL | la.FORM_ONE_LAUNCH, dtype=la.LA_F32,
+                  wsb=need32.value) == la.LA_ERR_UNSUPPORTED
+    assert staged(la.STAGE_ALL | la.DEBUG_FORCE_TIMEOUT, dtype=la.LA_F32,
+                  wsb=need32.value) == la.LA_ERR_UNSUPPORTED
     shard = la.pack([0], [2], [10, 20], block_chunks=1)
     st = lib.la_scan_packed(fake, fake, fake, la.LA_BF16, 2, 64, 64, ctypes.byref(shard.info),
                             fake, None, 0, fake, None, fake, 1 << 20, None)
@@ -226,8 +318,9 @@ def test_scan_rejects_bad_arguments_before_launch():
 
 
 def test_scan_launches_by_pass_shape():
-    """The two-launch form is taken while the workspace reads it adds stay
-    small (fused_slot_reads x H x d^2 x 4 bytes up to 128 MiB): the 628- and
+    """d = 64 with bf16 inputs runs the single-launch piece path.  Otherwise
+    the two-launch form is taken while the workspace reads it adds stay small
+    (fused_slot_reads x H x d^2 x 4 bytes up to 128 MiB): the 628- and
     7,400-token passes (one view of 15 blocks, 8 one-block branches: 58 MB)
     qualify; the view of 18,000 tokens with 256 branches (each branch reading
     all view slots: 1.25 GB) does not."""
@@ -235,19 +328,40 @@ def test_scan_launches_by_pass_shape():
     p7 = la.pack(*w7, heads=16)
     nb = -(-7400 // (64 * p7.info.block_chunks))
     assert p7.info.fused_slot_reads == nb * (nb - 1) // 2 + 1 + 8 * nb
-    assert la.scan_launches(p7, 16, 64) == 2
+    assert la.scan_launches(p7, 16, 64, la.LA_BF16) == 1
+    assert la.scan_launches(p7, 16, 128, la.LA_BF16) == 3   # 4x the slot bytes at d 128
+    assert la.scan_launches(p7, 16, 64, la.LA_F32) == 2
     w1 = synth.shapes("view500_br4x32_h2_d64_f32")
-    assert la.scan_launches(la.pack(*w1, heads=2), 2, 64) == 2
+    assert la.scan_launches(la.pack(*w1, heads=2), 2, 64, la.LA_F32) == 2
     w4 = synth.shapes("view18000_br256x32-128_h16_d64_bf16")
-    assert la.scan_launches(la.pack(*w4, heads=16), 16, 64) == 3
+    assert la.scan_launches(la.pack(*w4, heads=16), 16, 64, la.LA_F32_SPLIT) == 3
     # a view of two one-chunk blocks: the second block reads the first slot,
     # and its own to write final_state
     p1 = la.pack([100], [0], [], block_chunks=1)
-    assert p1.info.fused_slot_reads == 1 + 1 and la.scan_launches(p1, 1, 64) == 2
+    assert p1.info.fused_slot_reads == 1 + 1 and la.scan_launches(p1, 1, 64, la.LA_F32) == 2
     with pytest.raises(la.LinAttnError):
         la.scan_launches(p1, 0, 64)
     with pytest.raises(la.LinAttnError):
         la.scan_launches(p1, 1, 96)
+
+
+@pytest.mark.parametrize("field", ["n_blocks", "n_tokens", "piece_items", "plan_hash",
+                                   "n_views"])
+def test_edited_pass_info_is_rejected_before_launch(field):
+    """A pass info whose fields no longer match its checksum (edited, or
+    mixed from two passes) is rejected on the host, without device work."""
+    lib = la.load_library()
+    plan = la.pack([300, 90], [2, 1], [10, 20, 70], heads=2)
+    info = la.PassInfo.from_buffer_copy(plan.info)
+    setattr(info, field, getattr(info, field) + 1)
+    fake = ctypes.c_void_p(4096)
+    need = ctypes.c_size_t()
+    lib.la_scan_workspace_size(ctypes.byref(plan.info), 2, 64, 64, la.LA_BF16,
+                               ctypes.byref(need))
+    st = lib.la_scan_packed(fake, fake, fake, la.LA_BF16, 2, 64, 64, ctypes.byref(info), fake,
+                            None, 0, fake, fake, fake, need.value + (1 << 20), None)
+    assert st == la.LA_ERR_INVALID_ARG
+    assert lib.la_info_checksum(ctypes.byref(info)) != (info.info_check & 0xFFFFFFFF)
 
 
 def test_block_size_choice_on_the_workloads():
@@ -286,6 +400,7 @@ def test_stage_and_form_bits_checked_before_any_device_work():
     lib = la.load_library()
     info = la.PassInfo()
     info.chunk = la.CHUNK
+    info.info_check = lib.la_info_checksum(ctypes.byref(info))
 
     def call(stages):
         return lib.la_scan_packed_stages(stages, None, None, None, la.LA_BF16, 1, 64, 64,
@@ -294,8 +409,10 @@ def test_stage_and_form_bits_checked_before_any_device_work():
     assert call(la.STAGE_ALL) == la.LA_OK
     assert call(la.STAGE_ALL | la.FORM_TWO_LAUNCH) == la.LA_OK
     assert call(la.STAGE_OUTPUT | la.FORM_THREE_LAUNCH) == la.LA_OK
+    assert call(la.STAGE_ALL | la.FORM_ONE_LAUNCH) == la.LA_OK
     for bad in (0, la.FORM_TWO_LAUNCH, la.STAGE_ALL | la.FORM_TWO_LAUNCH | la.FORM_THREE_LAUNCH,
-                la.STAGE_ALL | 32, -1):
+                la.STAGE_ALL | la.FORM_ONE_LAUNCH | la.FORM_THREE_LAUNCH, la.STAGE_ALL | 128,
+                -1):
         assert call(bad) == la.LA_ERR_INVALID_ARG, bad
 
 
@@ -323,13 +440,16 @@ def test_noalloc_rejects_passes_beyond_its_scratch():
     array on the host and returns LA_ERR_TOO_LARGE before any device work (so
     this runs without a GPU)."""
     lib = la.load_library()
-    # one view of 2^17 tokens in blocks of one chunk: 2048 block states of
-    # 16 KiB per head, 32 MiB per head, 128 MiB at 4 heads
-    plan = la.pack([1 << 17], [0], [], heads=4, block_chunks=1)
-    need = la.workspace_size(plan, 4, 64, la.LA_BF16)
-    assert need > la.NOALLOC_SCRATCH_BYTES
     fake = ctypes.c_void_p(16)
-    st = lib.la_scan_packed_noalloc(fake, fake, fake, la.LA_BF16, 4, 64, 64,
-                                    ctypes.byref(plan.info), fake, None, 0, fake, fake, None)
-    assert st == la.LA_ERR_TOO_LARGE
-    assert b"scratch" in lib.la_status_string(st)
+    # one view of 2^17 tokens: fp32 in blocks of one chunk (2048 states of
+    # 16 KiB per head, 128 MiB at 4 heads); bf16 on the piece path (256
+    # blocks, a state and a prefix each, 16 heads: 128 MiB)
+    for dtype, H, G in ((la.LA_F32, 4, 1), (la.LA_BF16, 16, 8)):
+        plan = la.pack([1 << 17], [0], [], heads=H, block_chunks=G)
+        need = la.workspace_size(plan, H, 64, dtype)
+        assert need > la.NOALLOC_SCRATCH_BYTES
+        st = lib.la_scan_packed_noalloc(fake, fake, fake, dtype, H, 64, 64,
+                                        ctypes.byref(plan.info), fake, None, 0, fake, fake,
+                                        None)
+        assert st == la.LA_ERR_TOO_LARGE
+        assert b"scratch" in lib.la_status_string(st)

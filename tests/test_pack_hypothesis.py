@@ -27,7 +27,7 @@ def test_pack_matches_oracle_and_plan_properties(reqs, G):
     assert info.n_views == sum(1 for v in vl if v > 0)
     assert info.n_ext == sum(1 for v in vl if v == 0)
     # blocks tile every segment exactly, G chunks at most, in whole chunks
-    blocks = p.plan[16:16 + 8 * info.n_blocks].reshape(-1, 8)
+    blocks = p.plan[p.plan[8]:p.plan[8] + 8 * info.n_blocks].reshape(-1, 8)
     cover = np.zeros(info.n_tokens, dtype=int)
     for tok0, ntok, sin, dslot, seed, seg, _, _ in blocks:
         assert 1 <= ntok <= 64 * G and tok0 >= so[seg] and tok0 + ntok <= so[seg + 1]
@@ -36,6 +36,24 @@ def test_pack_matches_oracle_and_plan_properties(reqs, G):
         if tok0 == so[seg]:
             assert sin == -1           # a segment's first block needs no prefix
     assert (cover == 1).all()
+    # piece path: blocks of at most 8 chunks tile every segment; every block is
+    # in exactly one work item, packs hold only one-piece single-block branches
+    ob, oi = int(p.plan[20]), int(p.plan[21])
+    pblocks = p.plan[ob:ob + 8 * info.piece_blocks].reshape(-1, 8)
+    pitems = p.plan[oi:oi + 8 * info.piece_items].reshape(-1, 8)
+    cover[:] = 0
+    for tok0, ntok, slot, seed, seg, slot0, j, frow in pblocks:
+        assert 1 <= ntok <= 512 and tok0 == so[seg] + 512 * j
+        cover[tok0:tok0 + ntok] += 1
+    assert (cover == 1).all()
+    seen = np.zeros(info.piece_blocks, dtype=int)
+    for kind, n, b0, b1, b2, b3, _, _ in pitems:
+        for b in (b0, b1, b2, b3)[:n]:
+            seen[b] += 1
+            if kind == 1:
+                tok0, ntok, _, seed, seg = pblocks[b][:5]
+                assert seed != -1 and ntok <= 128 and ntok == so[seg + 1] - so[seg]
+    assert (seen == 1).all()
     # attention items cover every query exactly once, in <= 64-token blocks
     ext_len = [11] * info.n_ext
     items = la.attn_plan(so, bp, ext_len).items
