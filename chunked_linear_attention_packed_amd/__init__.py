@@ -42,6 +42,7 @@ LA_ATTN_NO_VIEW, LA_ATTN_PACKED_VIEW, LA_ATTN_EXT_VIEW = 0, 1, 2
 STAGE_STATES, STAGE_PREFIX, STAGE_OUTPUT, STAGE_ALL = 1, 2, 4, 7
 FORM_TWO_LAUNCH, FORM_THREE_LAUNCH, FORM_ONE_LAUNCH = 8, 16, 32
 DEBUG_FORCE_TIMEOUT = 64
+DEBUG_ORDERED = 128
 _FORMS = {None: 0, "auto": 0, "one": FORM_ONE_LAUNCH, "two": FORM_TWO_LAUNCH,
           "three": FORM_THREE_LAUNCH}
 
@@ -190,6 +191,12 @@ def pack(view_len, branch_count, branch_len, heads=16, block_chunks=None, chunk=
     er = None if ext_row is None else _i32(ext_row)
     if er is not None and len(er) != len(vl):
         raise ValueError("ext_row needs one entry per request")
+    # the library reads exactly len(view_len) counts and sum(branch_count)
+    # branch lengths
+    if len(bc) != len(vl):
+        raise ValueError("branch_count needs one entry per request")
+    if len(bl) != int(np.sum(np.maximum(bc, 0), dtype=np.int64)):
+        raise ValueError("branch_len needs sum(branch_count) entries")
     info = PassInfo()
     if block_chunks is None:   # the segment table first, then the library's block size
         _check("la_pack_pass", lib.la_pack_pass_ext(len(vl), _ptr(vl), _ptr(bc), _ptr(bl),

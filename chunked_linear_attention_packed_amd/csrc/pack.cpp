@@ -10,6 +10,7 @@
 // only metadata the device kernels read: one descriptor per work block, per
 // delta block and per scanned segment.
 #include <algorithm>
+#include <array>
 #include <cstdint>
 #include <cstring>
 #include <vector>
@@ -18,14 +19,33 @@
 
 namespace {
 
-constexpr int32_t kPlanVersion = 3;
+constexpr int32_t kPlanVersion = 4;
 
 // Piece path (d = 64, bf16): blocks of LA_PIECE_BLOCK_CHUNKS chunks, each cut
 // into pieces of LA_PIECE_CHUNKS chunks, one per wave of a 4-wave workgroup.
-// A branch whose only block is a single piece shares a workgroup with up to
-// three other such branches (one per wave).
+// Branches whose only block is a single piece are packed into workgroups of
+// their own, four waves of them: two branches of at most one chunk share a
+// wave, a branch of two chunks has one alone.
 constexpr int32_t kPieceBlockTok = LA_PIECE_BLOCK_CHUNKS * LA_CHUNK;
 constexpr int32_t kPieceTok = LA_PIECE_CHUNKS * LA_CHUNK;
+constexpr int kPackWaves = 4;
+
+// Waves of the packs, filled in branch order: a branch of at most one chunk
+// joins the wave of the last such branch if that wave has room, else opens a
+// new wave; a longer branch takes a new wave.
+struct PackWaves {
+    std::vector<std::array<int32_t, 2>> waves;
+    int64_t open = -1;   // wave holding a lone branch of at most one chunk
+    void add(int32_t block, int32_t len) {
+        if (len <= LA_CHUNK && open >= 0) {
+            waves[size_t(open)][1] = block;
+            open = -1;
+            return;
+        }
+        if (len <= LA_CHUNK) open = int64_t(waves.size());
+        waves.push_back({block, -1});
+    }
+};
 
 // FNV-1a over the plan words, with the hash word itself taken as zero.
 uint32_t plan_hash(const int32_t* plan, int64_t words) {
@@ -116,9 +136,10 @@ la_status plan_impl(int32_t n_seg, const int32_t* seg_offsets, const int32_t* br
     // Piece path tables: blocks of kPieceBlockTok tokens; a view's blocks all
     // get a state slot (its total is final_state, its branches start from
     // it), a branch's all but the last; branches whose only block is a
-    // single piece are packed four to a workgroup, everything else is one
-    // workgroup per block.
-    int64_t p_blocks = 0, p_slots = 0, p_scan = 0, p_block_items = 0, p_packable = 0;
+    // single piece are packed (PackWaves), everything else is one workgroup
+    // per block.
+    int64_t p_blocks = 0, p_slots = 0, p_scan = 0, p_block_items = 0;
+    PackWaves pack_count;
     for (int32_t s = 0; s < n_seg; ++s) {
         const bool is_view = branch_parent[s] == -1;
         const int64_t len = int64_t(seg_offsets[s + 1]) - seg_offsets[s];
@@ -128,11 +149,11 @@ la_status plan_impl(int32_t n_seg, const int32_t* seg_offsets, const int32_t* br
         p_slots += nslots;
         if (is_view || nslots >= 1) ++p_scan;
         if (!is_view && nb == 1 && len <= kPieceTok)
-            ++p_packable;
+            pack_count.add(0, int32_t(len));
         else
             p_block_items += nb;
     }
-    const int64_t p_items = p_block_items + ceil_div(p_packable, 4);
+    const int64_t p_items = p_block_items + ceil_div(int64_t(pack_count.waves.size()), kPackWaves);
     const int64_t words = int64_t(LA_PLAN_HEADER_WORDS) + n_blocks * LA_PLAN_BLOCK_WORDS +
                           n_delta * LA_PLAN_DELTA_WORDS + n_scan * LA_PLAN_SCAN_WORDS +
                           p_blocks * LA_PLAN_BLOCK_WORDS + p_items * LA_PLAN_ITEM_WORDS +
@@ -251,7 +272,7 @@ la_status plan_impl(int32_t n_seg, const int32_t* seg_offsets, const int32_t* br
         int32_t* pb = plan + off_pblocks;
         int32_t* pit = plan + off_pitems;
         int32_t* psc = plan + off_pscan;
-        std::vector<int32_t> packable;
+        PackWaves packs;
         int32_t pslot = 0, pblock = 0;
         std::vector<int32_t> view_scan(size_t(n_views > 0 ? n_views : 0), -1);
         for (int pass = 0; pass < 2; ++pass) {
@@ -279,14 +300,14 @@ la_status plan_impl(int32_t n_seg, const int32_t* seg_offsets, const int32_t* br
                     pb[7] = is_view && j == nb - 1 ? ord[size_t(s)] : -1;
                     pb += LA_PLAN_BLOCK_WORDS;
                     if (pack) {
-                        packable.push_back(pblock);
+                        packs.add(pblock, len);
                     } else {
                         int32_t* it = pit;
                         std::memset(it, 0, sizeof(int32_t) * LA_PLAN_ITEM_WORDS);
                         it[0] = LA_ITEM_BLOCK;
                         it[1] = 1;
                         it[2] = pblock;
-                        it[3] = it[4] = it[5] = -1;
+                        for (int b = 1; b < 2 * kPackWaves; ++b) it[2 + b] = -1;
                         pit += LA_PLAN_ITEM_WORDS;
                     }
                     ++pblock;
@@ -301,13 +322,15 @@ la_status plan_impl(int32_t n_seg, const int32_t* seg_offsets, const int32_t* br
                 pslot += nslots;
             }
         }
-        for (size_t i = 0; i < packable.size(); i += 4) {
+        const size_t nw = packs.waves.size();
+        for (size_t i = 0; i < nw; i += kPackWaves) {
             int32_t* it = pit;
             std::memset(it, 0, sizeof(int32_t) * LA_PLAN_ITEM_WORDS);
             it[0] = LA_ITEM_PACK;
-            it[1] = int32_t(std::min<size_t>(4, packable.size() - i));
-            for (int w = 0; w < 4; ++w)
-                it[2 + w] = i + size_t(w) < packable.size() ? packable[i + size_t(w)] : -1;
+            it[1] = int32_t(std::min<size_t>(kPackWaves, nw - i));
+            for (int w = 0; w < kPackWaves; ++w)
+                for (int b = 0; b < 2; ++b)
+                    it[2 + 2 * w + b] = i + size_t(w) < nw ? packs.waves[i + size_t(w)][size_t(b)] : -1;
             pit += LA_PLAN_ITEM_WORDS;
         }
         const uint32_t hash = plan_hash(plan, words);

@@ -31,11 +31,13 @@ size_t workspace_bytes(const la_pass_info& info, int32_t H);
 inline bool applies(int32_t d, la_dtype dtype) { return d == 64 && dtype == LA_BF16; }
 
 // Enqueues the launches of `stages` (LA_STAGE_* bits) in form `form`
-// (1, 2 or 3 launches).  Arguments are validated by the caller.
+// (1, 2 or 3 launches).  Arguments are validated by the caller.  In the
+// single-launch form, `ordered` makes the workgroups take tickets even when
+// the whole launch fits on the device at once.
 la_status launch(int32_t stages, int form, const void* q, const void* k, const void* v,
                  int32_t H, const la_pass_info& info, const int32_t* plan,
                  const float* ext_state, void* out, float* final_state, void* workspace,
-                 hipStream_t stream, int32_t spin_limit, bool force_timeout);
+                 hipStream_t stream, int32_t spin_limit, bool force_timeout, bool ordered);
 
 // The prefix launch of the shared scan code over the piece path's slots
 // (defined in scan.hip, which holds the prefix kernel).

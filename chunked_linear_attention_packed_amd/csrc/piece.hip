@@ -55,6 +55,7 @@
 // clears the flags and resets the counters for the next pass.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
 
 #include "linattn.h"
@@ -72,6 +73,9 @@ constexpr int kWaitLgkm0 = 0xC07F;           // s_waitcnt lgkmcnt(0), others at 
 constexpr uint64_t kFlagA = 0x7FF44C41464C0001ull;   // aggregate published (NaN payload)
 constexpr uint64_t kFlagP = 0x7FF44C41464C0002ull;   // inclusive prefix published
 constexpr int kAuxCoherent = 16;             // buffer-op cache policy: sc1 (device scope)
+constexpr int kAuxL2 = 1;                    // sc0: past the CU's L1, served by the XCD's L2
+constexpr uint64_t kFlagXcd = 0xF00ull;      // flag bits naming the publisher's XCD
+constexpr int kHwRegXccId = (3 << 11) | 20;  // s_getreg operand: XCC_ID bits 3:0
 
 enum Mode { kStates = 0, kOut3 = 1, kOut2 = 2, kFused = 3 };
 
@@ -79,7 +83,7 @@ struct PBlock {
     int tok0, ntok, slot, seed, seg, slot0, j, final_row;
 };
 struct PItem {
-    int kind, n, b[4], pad0, pad1;
+    int kind, n, b[8], pad0, pad1;
 };
 struct PScan {
     int first_slot, n_slots, final_row, seg;
@@ -95,7 +99,7 @@ struct PArgs {
     const PScan* scans;
     float* aslots;                 // [slots][H][16 KB] block states
     float* pslots;                 // [slots][H][16 KB] inclusive prefixes (one launch)
-    uint64_t* flags;               // [slots][H] (one launch)
+    uint64_t* flags;               // [H][slots] (one launch): a head's flags contiguous
     int* hdr;                      // workspace header
     float* final_state;
     const float* ext_state;
@@ -103,9 +107,11 @@ struct PArgs {
     int H;
     int n_work;                    // workgroups of the launch (items x H)
     int n_flags;                   // slots x H
+    int n_slots;                   // slots
     int plan_hash;
     int spin_limit;
     int force_timeout;
+    int ordered;                   // one launch: take tickets (the launch may not fit at once)
 };
 
 typedef f32x4 State[kTiles];       // tile t = vb * 4 + kb; lane 16g + c holds
@@ -182,21 +188,42 @@ __device__ __forceinline__ void order_after_flag() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
-// Bounded wait for one flag to say "inclusive prefix published".  On timeout
-// records LA_ERR_TIMEOUT and returns (the caller carries on with whatever
-// the slot holds: in bounds, not valid).
-__device__ void wait_prefix(const PArgs& a, const uint64_t* f) {
+// Flags carry the XCD of the workgroup that published (bits 8..11).  The
+// XCDs' L2 caches are not coherent with each other, so a state published
+// from another XCD is read with device-coherent loads (sc1, from memory); a
+// state published from the reader's own XCD went through that XCD's L2 with
+// the publisher's stores, so it is read there (sc0: past the CU's L1, which
+// holds no line of it).  The kernel's workgroups of one head run on one XCD
+// when the launch maps them there, which keeps most look-back reads in L2.
+__device__ __forceinline__ uint64_t* flag_ptr(const PArgs& a, int slot, int h) {
+    return a.flags + int64_t(h) * a.n_slots + slot;
+}
+__device__ __forceinline__ uint64_t xcd_tag() {
+    return uint64_t(__builtin_amdgcn_s_getreg(kHwRegXccId) & 15) << 8;
+}
+__device__ __forceinline__ bool is_flag(uint64_t f, uint64_t kind) {
+    return (f & ~kFlagXcd) == kind;
+}
+
+// Bounded wait for one flag to say "inclusive prefix published"; returns
+// whether the publisher ran on this XCD (tag).  On timeout records
+// LA_ERR_TIMEOUT and returns false (the caller carries on with whatever the
+// slot holds: in bounds, not valid).
+__device__ bool wait_prefix(const PArgs& a, const uint64_t* f, uint64_t tag) {
+    uint64_t x = 0;
     for (int it = 0;; ++it) {
-        const uint64_t x = a.force_timeout ? 0 : flag_load(f);
-        if (x == kFlagP) break;
+        x = a.force_timeout ? 0 : flag_load(f);
+        if (is_flag(x, kFlagP)) break;
         if (it >= a.spin_limit) {
             __hip_atomic_fetch_or(a.hdr + piece::kStatusWord, LA_ERR_TIMEOUT, __ATOMIC_RELAXED,
                                   __HIP_MEMORY_SCOPE_AGENT);
+            x = 0;
             break;
         }
         __builtin_amdgcn_s_sleep(2);
     }
     order_after_flag();
+    return __builtin_amdgcn_readfirstlane(int(is_flag(x, kFlagP) && (x & kFlagXcd) == tag)) != 0;
 }
 
 // The look-back of block j of a segment (slots slot0 .. slot0 + j - 1 hold
@@ -204,32 +231,40 @@ __device__ void wait_prefix(const PArgs& a, const uint64_t* f) {
 // inclusive prefix, with every predecessor after it having published at
 // least its aggregate.  The flags of up to 64 predecessors are polled at
 // once, one per lane (lane i: predecessor j - 1 - i).  Block 0 of a segment
-// always publishes its prefix, so the walk ends.  On timeout records
-// LA_ERR_TIMEOUT and returns 0.
-__device__ int find_prefix(const PArgs& a, int slot0, int j, int h, int lane) {
+// always publishes its prefix, so the walk ends.  `local` tells whether
+// every state the caller will read (the prefix and the aggregates after it)
+// was published from this XCD (tag).  On timeout records LA_ERR_TIMEOUT and
+// returns 0.
+__device__ int find_prefix(const PArgs& a, int slot0, int j, int h, int lane, uint64_t tag,
+                           bool& local) {
+    bool passed_local = true;   // windows walked past: all their aggregates are read
     for (int base = j - 1;; base -= 64) {
         const int m = base - lane;
         for (int it = 0;; ++it) {
             const uint64_t f = (m >= 0 && !a.force_timeout)
-                                   ? flag_load(a.flags + int64_t(slot0 + m) * a.H + h)
+                                   ? flag_load(flag_ptr(a, slot0 + m, h))
                                    : 0;
-            const uint64_t bp = __builtin_amdgcn_ballot_w64(m >= 0 && f == kFlagP);
-            const uint64_t br =
-                __builtin_amdgcn_ballot_w64(m < 0 || f == kFlagP || f == kFlagA);
+            const uint64_t bp = __builtin_amdgcn_ballot_w64(m >= 0 && is_flag(f, kFlagP));
+            const uint64_t br = __builtin_amdgcn_ballot_w64(m < 0 || is_flag(f, kFlagP) ||
+                                                            is_flag(f, kFlagA));
+            const uint64_t bl = __builtin_amdgcn_ballot_w64(m < 0 || (f & kFlagXcd) == tag);
             if (bp) {
                 const int l = __builtin_ctzll(bp);                 // nearest prefix
                 const uint64_t need = l == 63 ? ~0ull : ((2ull << l) - 1);
                 if ((br & need) == need) {
                     order_after_flag();
+                    local = passed_local && (bl & need) == need;
                     return base - l;
                 }
             } else if (br == ~0ull && base >= 64) {
+                passed_local = passed_local && bl == ~0ull;
                 break;                                             // next window
             }
             if (it >= a.spin_limit) {
                 __hip_atomic_fetch_or(a.hdr + piece::kStatusWord, LA_ERR_TIMEOUT,
                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 order_after_flag();
+                local = false;
                 return 0;
             }
             __builtin_amdgcn_s_sleep(2);
@@ -334,14 +369,65 @@ __device__ __forceinline__ void acc_kv(State& S, const uint16_t* sK, const uint1
     }
 }
 
-// Outputs of one staged chunk for the wave's 64 tokens, all 64 features:
-// O^T = V^T P^T + S_hi^T Q^T + S_lo^T Q^T with P = tril(Q K^T), stored as
-// bf16 (round to nearest even), 16 contiguous bytes per lane and store.
-template <int TB>
-__device__ __forceinline__ void out_tokens(const u32x4 (&kr)[4][2], const u32x4 (&vt)[4][2],
-                                           const u32x4 (&sh)[4][2], const u32x4 (&sl)[4][2],
-                                           const u32x4 (&qt)[2], __amdgpu_buffer_rsrc_t ro,
-                                           int H, int h, int g, int c16) {
+// Outputs of a chunk are built in two parts: the part local to the piece,
+//   O_loc = tril(Q K^T) V + Q S_loc   (S_loc: the piece's own state before
+//                                      the chunk, from inside its block),
+// which needs nothing from other workgroups, and the part of the state the
+// block starts from, O += Q S_b, added once S_b is known.  O^T is kept in
+// fp32 MFMA accumulators: tile tb * 4 + fb, lane 16 g + c: token 16 tb + c,
+// features 16 fb + 4 g .. + 3; written as bf16 (round to nearest even).
+typedef f32x4 OTiles[16];
+
+// q of a chunk in k-slot order (the B operand of the products over d_k).
+struct QSlots {
+    u32x4 q[4][2];
+};
+__device__ __forceinline__ void q_slots(const ChunkQ& raw, QSlots& qs) {
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) qs.q[tb][ks] = to_slot_order(raw.q[tb][ks]);
+}
+
+// S^T as A operands, split into two bf16 terms S = hi + lo (the split keeps
+// the fp32 state's precision in the bf16 product).
+struct SSplit {
+    u32x4 hi[4][2], lo[4][2];
+};
+__device__ __forceinline__ void split_state(const State& S, SSplit& sp) {
+#pragma unroll
+    for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const f32x4 x = S[fb * 4 + 2 * ks], y = S[fb * 4 + 2 * ks + 1];
+            const uint32_t h0 = cvt_bf2(x[0], x[1]), h1 = cvt_bf2(x[2], x[3]);
+            const uint32_t h2 = cvt_bf2(y[0], y[1]), h3 = cvt_bf2(y[2], y[3]);
+            sp.hi[fb][ks] = u32x4{h0, h1, h2, h3};
+            sp.lo[fb][ks] = u32x4{cvt_bf2(x[0] - bf_lo(h0), x[1] - bf_hi(h0)),
+                                  cvt_bf2(x[2] - bf_lo(h1), x[3] - bf_hi(h1)),
+                                  cvt_bf2(y[0] - bf_lo(h2), y[1] - bf_hi(h2)),
+                                  cvt_bf2(y[2] - bf_lo(h3), y[3] - bf_hi(h3))};
+        }
+}
+
+// O += Q S for the chunk's 64 tokens (both terms of S, hi first).
+__device__ __forceinline__ void add_qs(OTiles& O, const SSplit& sp, const QSlots& qs) {
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                O[tb * 4 + fb] = mfma_bf16(sp.hi[fb][ks], qs.q[tb][ks], O[tb * 4 + fb]);
+                O[tb * 4 + fb] = mfma_bf16(sp.lo[fb][ks], qs.q[tb][ks], O[tb * 4 + fb]);
+            }
+}
+
+// Local outputs of tokens 16 TB .. 16 TB + 15 of the staged chunk.
+template <int TB, bool WITH_S>
+__device__ __forceinline__ void local_tokens(OTiles& O, const u32x4 (&kr)[4][2],
+                                             const u32x4 (&vt)[4][2], const SSplit& sp,
+                                             const u32x4 (&qt)[2], int g, int c16) {
     f32x4 p[TB + 1];
 #pragma unroll
     for (int ub = 0; ub <= TB; ++ub) {
@@ -359,46 +445,29 @@ __device__ __forceinline__ void out_tokens(const u32x4 (&kr)[4][2], const u32x4 
         pb[pp] = u32x4{cvt_bf2(x[0], x[1]), cvt_bf2(x[2], x[3]), cvt_bf2(y[0], y[1]),
                        cvt_bf2(y[2], y[3])};
     }
-    f32x4 o[4];
 #pragma unroll
     for (int fb = 0; fb < 4; ++fb) {
-        o[fb] = zero4();
+        f32x4 o = zero4();
 #pragma unroll
-        for (int pp = 0; pp <= TB / 2; ++pp) o[fb] = mfma_bf16(vt[fb][pp], pb[pp], o[fb]);
+        for (int pp = 0; pp <= TB / 2; ++pp) o = mfma_bf16(vt[fb][pp], pb[pp], o);
+        if constexpr (WITH_S) {
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            o[fb] = mfma_bf16(sh[fb][ks], qt[ks], o[fb]);
-            o[fb] = mfma_bf16(sl[fb][ks], qt[ks], o[fb]);
+            for (int ks = 0; ks < 2; ++ks) {
+                o = mfma_bf16(sp.hi[fb][ks], qt[ks], o);
+                o = mfma_bf16(sp.lo[fb][ks], qt[ks], o);
+            }
         }
-    }
-    // lane 16 g + c: token 16 TB + c, features 16 fb + 4 g .. + 3 of each tile
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-        const f32x4 x = o[2 * hh], y = o[2 * hh + 1];
-        const u32x4 pc = from_slot_order(u32x4{cvt_bf2(x[0], x[1]), cvt_bf2(x[2], x[3]),
-                                               cvt_bf2(y[0], y[1]), cvt_bf2(y[2], y[3])});
-        buf_store16u(ro, uint32_t((((16 * TB + c16) * H + h) * PD + 32 * hh + 8 * g) * 2), pc);
+        O[TB * 4 + fb] = o;
     }
 }
 
-__device__ __forceinline__ void chunk_out(const State& S, const uint16_t* sK, const uint16_t* sV,
-                                          const ChunkQ& qraw, const PArgs& a, int64_t tok0,
-                                          int rows, int h, int g, int c16) {
-    // S^T as A operands, split into two bf16 terms
-    u32x4 sh[4][2], sl[4][2];
-#pragma unroll
-    for (int fb = 0; fb < 4; ++fb)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const f32x4 x = S[fb * 4 + 2 * ks], y = S[fb * 4 + 2 * ks + 1];
-            const uint32_t h0 = cvt_bf2(x[0], x[1]), h1 = cvt_bf2(x[2], x[3]);
-            const uint32_t h2 = cvt_bf2(y[0], y[1]), h3 = cvt_bf2(y[2], y[3]);
-            sh[fb][ks] = u32x4{h0, h1, h2, h3};
-            sl[fb][ks] = u32x4{cvt_bf2(x[0] - bf_lo(h0), x[1] - bf_hi(h0)),
-                               cvt_bf2(x[2] - bf_lo(h1), x[3] - bf_hi(h1)),
-                               cvt_bf2(y[0] - bf_lo(h2), y[1] - bf_hi(h2)),
-                               cvt_bf2(y[2] - bf_lo(h3), y[3] - bf_hi(h3))};
-        }
+// O = tril(Q K^T) V (+ Q S_loc when WITH_S) of the staged chunk.
+template <bool WITH_S>
+__device__ __forceinline__ void chunk_local(OTiles& O, const State& S, const uint16_t* sK,
+                                            const uint16_t* sV, const QSlots& qs, int g,
+                                            int c16) {
+    SSplit sp;
+    if constexpr (WITH_S) split_state(S, sp);
     // K rows in slot order (two 8-byte reads), V^T fragments in token order
     u32x4 kr[4][2], vt[4][2];
 #pragma unroll
@@ -409,36 +478,46 @@ __device__ __forceinline__ void chunk_out(const State& S, const uint16_t* sK, co
             kr[ub][ks] = cat2(lds_u32x2(p), lds_u32x2(p + 16));
             vt[ub][ks] = tr_frag(sV, PLD, 16 * ub, ks, g, c16);
         }
-    u32x4 qt[4][2];
+    local_tokens<0, WITH_S>(O, kr, vt, sp, qs.q[0], g, c16);
+    local_tokens<1, WITH_S>(O, kr, vt, sp, qs.q[1], g, c16);
+    local_tokens<2, WITH_S>(O, kr, vt, sp, qs.q[2], g, c16);
+    local_tokens<3, WITH_S>(O, kr, vt, sp, qs.q[3], g, c16);
+}
+
+// Rows tok0 .. tok0 + rows - 1 of out from O (16 contiguous bytes per lane
+// and store; rows past `rows` fall outside the buffer window).
+__device__ __forceinline__ void store_chunk(const OTiles& O, const PArgs& a, int64_t tok0,
+                                            int rows, int h, int g, int c16) {
+    const auto ro = chunk_rsrc(a.out, tok0 * a.H * PD, 2, rows, a.H, PD);
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) qt[tb][ks] = to_slot_order(qraw.q[tb][ks]);
-    const auto ro = chunk_rsrc(a.out, tok0 * a.H * PD, 2, rows, a.H, PD);
-    out_tokens<0>(kr, vt, sh, sl, qt[0], ro, a.H, h, g, c16);
-    out_tokens<1>(kr, vt, sh, sl, qt[1], ro, a.H, h, g, c16);
-    out_tokens<2>(kr, vt, sh, sl, qt[2], ro, a.H, h, g, c16);
-    out_tokens<3>(kr, vt, sh, sl, qt[3], ro, a.H, h, g, c16);
+        for (int hh = 0; hh < 2; ++hh) {
+            const f32x4 x = O[tb * 4 + 2 * hh], y = O[tb * 4 + 2 * hh + 1];
+            const u32x4 pc = from_slot_order(u32x4{cvt_bf2(x[0], x[1]), cvt_bf2(x[2], x[3]),
+                                                   cvt_bf2(y[0], y[1]), cvt_bf2(y[2], y[3])});
+            buf_store16u(ro, uint32_t((((16 * tb + c16) * a.H + h) * PD + 32 * hh + 8 * g) * 2),
+                         pc);
+        }
 }
 
-// One wave's piece (up to two chunks at tok0 .. tok0 + ntok): outputs from
-// state S.  Chunk 0's k / v are already staged when `staged`; chunk 1's are
-// in r1; q of both chunks in q0, q1.
-__device__ __forceinline__ void piece_outputs(State& S, uint16_t* sK, uint16_t* sV,
-                                              const ChunkKV& r0, const ChunkKV& r1,
-                                              const ChunkQ& q0, const ChunkQ& q1, const PArgs& a,
-                                              int64_t tok0, int ntok, bool staged, int h, int g,
-                                              int c16, int lane) {
+// The local part of one wave's piece (up to two chunks at tok0 ..
+// tok0 + ntok): O0, O1 from the piece's state before it, S (updated: the
+// state after chunk 0 on return).  Chunk 0's k / v are staged on entry,
+// chunk 1's are in r1.
+__device__ __forceinline__ void piece_local(OTiles& O0, OTiles& O1, State& S, uint16_t* sK,
+                                            uint16_t* sV, const ChunkKV& r1, const QSlots& qs0,
+                                            const QSlots& qs1, int ntok, int g, int c16,
+                                            int lane) {
     if (ntok <= 0) return;
-    if (!staged) stage_chunk(r0, sK, sV, lane);
-    chunk_out(S, sK, sV, q0, a, tok0, min(ntok, kChunk), h, g, c16);
+    chunk_local<true>(O0, S, sK, sV, qs0, g, c16);
     if (ntok > kChunk) {
         acc_kv(S, sK, sV, g, c16);
         // every lane's reads of chunk 0 are done before chunk 1 overwrites it
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
         __builtin_amdgcn_wave_barrier();
         stage_chunk(r1, sK, sV, lane);
-        chunk_out(S, sK, sV, q1, a, tok0 + kChunk, ntok - kChunk, h, g, c16);
+        chunk_local<true>(O1, S, sK, sV, qs1, g, c16);
     }
 }
 
@@ -479,6 +558,17 @@ __device__ __forceinline__ void add_slots4(f32x4 (&acc)[4], const float* base, i
     }
 }
 
+// own = P_m + A_{m+1} + ... + A_{j-1} (this wave's four tiles), read with
+// cache policy AUX.
+template <int AUX>
+__device__ __forceinline__ void look_back(f32x4 (&own)[4], const PArgs& a, int slot0, int m,
+                                          int j, int h, int w, int lane) {
+    const auto r = slot_rsrc(a.pslots, slot0 + m, a.H, h);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) own[i] = slot_load<AUX>(r, 4 * w + i, lane);
+    add_slots4<AUX>(own, a.aslots, slot0 + m + 1, j - 1 - m, a.H, h, w, lane);
+}
+
 // LDS exchange region: two states in the lane layout.
 struct Xch {
     f32x4 x[2][kTiles * 64];
@@ -494,6 +584,47 @@ __device__ __forceinline__ void get_state(const Xch& X, int b, State& s, int lan
 __device__ __forceinline__ void put_tiles4(Xch& X, int b, const f32x4 (&v)[4], int w, int lane) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) X.x[b][(4 * w + i) * 64 + lane] = v[i];
+}
+
+// The state a branch starts from (whole, in the lane layout): its view's
+// total (seed >= 0: the view's scan entry), ext_state row -seed - 2
+// (seed <= -2), or zero (seed == -1).  In the single-launch form the view's
+// inclusive prefix is awaited; in the three-launch form the prefix launch
+// left it in the view's last slot; in the two-launch form the view's block
+// states are summed from zero, in slot order.
+template <int MODE>
+__device__ __forceinline__ void load_seed(State& S, const PArgs& a, int seed, int h, int g,
+                                          int c16, int lane) {
+    const int H = a.H;
+    zero_state(S);
+    if (seed >= 0) {
+        const PScan vs = a.scans[seed];
+        const int last = vs.first_slot + vs.n_slots - 1;
+        if constexpr (MODE == kFused) {
+            const auto r = slot_rsrc(a.pslots, last, H, h);
+            if (wait_prefix(a, flag_ptr(a, last, h), xcd_tag())) {
+#pragma unroll
+                for (int t = 0; t < kTiles; ++t) S[t] = slot_load<kAuxL2>(r, t, lane);
+            } else {
+#pragma unroll
+                for (int t = 0; t < kTiles; ++t) S[t] = slot_load<kAuxCoherent>(r, t, lane);
+            }
+        } else if constexpr (MODE == kOut3) {
+            const auto r = slot_rsrc(a.aslots, last, H, h);
+#pragma unroll
+            for (int t = 0; t < kTiles; ++t) S[t] = slot_load<0>(r, t, lane);
+        } else {
+            for (int s = 0; s < vs.n_slots; ++s) {
+                const auto r = slot_rsrc(a.aslots, vs.first_slot + s, H, h);
+#pragma unroll
+                for (int t = 0; t < kTiles; ++t) S[t] += slot_load<0>(r, t, lane);
+            }
+        }
+    } else if (seed <= -2) {
+        const float* src = a.ext_state + (int64_t(-seed - 2) * H + h) * PD * PD;
+#pragma unroll
+        for (int t = 0; t < kTiles; ++t) S[t] = load_rows_tile(src, t, g, c16);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -517,23 +648,22 @@ __global__ __launch_bounds__(kThreads) void piece_kernel(PArgs a) {
         return;
     }
 
-    int work;
-    if constexpr (MODE == kFused) {
+    int work = blockIdx.x;
+    if (MODE == kFused && a.ordered) {
         // tickets in launch order of the items: everything a workgroup waits
-        // for belongs to a smaller ticket, held by a running workgroup
+        // for belongs to a smaller ticket, held by a running workgroup.  (When
+        // every workgroup of the launch is resident at once, waits need no
+        // order and the index is the work.)
         if (tid == 0)
             sB[0] = __hip_atomic_fetch_add(a.hdr + piece::kTicketWord, 1, __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT);
         __syncthreads();
         work = sB[0];
-    } else {
-        work = blockIdx.x;
     }
     if (work < a.n_work) {
         const int item = work / H, h = work % H;
-        const PItem it = a.items[item];
-        if (it.kind == LA_ITEM_BLOCK) {
-            const PBlock B = a.blocks[it.b[0]];
+        if (a.items[item].kind == LA_ITEM_BLOCK) {
+            const PBlock B = a.blocks[a.items[item].b[0]];
             const int np = (B.ntok + 2 * kChunk - 1) / (2 * kChunk);   // pieces
             const int64_t ptok0 = int64_t(B.tok0) + w * 2 * kChunk;
             const int pntok = min(2 * kChunk, B.ntok - w * 2 * kChunk);   // <= 0: no piece
@@ -541,10 +671,6 @@ __global__ __launch_bounds__(kThreads) void piece_kernel(PArgs a) {
             ChunkQ q0, q1;
             load_chunk_kv(r0, a, ptok0, pntok, h, lane);
             load_chunk_kv(r1, a, ptok0 + kChunk, pntok - kChunk, h, lane);
-            if constexpr (MODE != kStates) {
-                load_chunk_q(q0, a, ptok0, pntok, h, g, c16);
-                load_chunk_q(q1, a, ptok0 + kChunk, pntok - kChunk, h, g, c16);
-            }
 
             // the piece's own state, chunk 1 first so chunk 0 stays staged
             State A;
@@ -560,6 +686,13 @@ __global__ __launch_bounds__(kThreads) void piece_kernel(PArgs a) {
                 acc_kv(A, sK, sV, g, c16);
             }
 
+            // q is loaded once k and v are in (they come first: every block
+            // after this one waits for the state they give)
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (MODE != kStates) {
+                load_chunk_q(q0, a, ptok0, pntok, h, g, c16);
+                load_chunk_q(q1, a, ptok0 + kChunk, pntok - kChunk, h, g, c16);
+            }
             // in-block prefix over the pieces: E_w and A_b (wave np - 1)
             State E, Ab;
             zero_state(E);
@@ -609,25 +742,38 @@ __global__ __launch_bounds__(kThreads) void piece_kernel(PArgs a) {
                             for (int t = 0; t < kTiles; ++t) P[t] = zero4() + Ab[t];
                             store_state<kAuxCoherent>(P, a.pslots, B.slot, H, h, lane);
                             drain_stores();
-                            if (lane == 0) flag_store(a.flags + int64_t(B.slot) * H + h, kFlagP);
+                            if (lane == 0)
+                                flag_store(flag_ptr(a, B.slot, h), kFlagP | xcd_tag());
                         } else {
                             store_state<kAuxCoherent>(Ab, a.aslots, B.slot, H, h, lane);
                             drain_stores();
-                            if (lane == 0) flag_store(a.flags + int64_t(B.slot) * H + h, kFlagA);
+                            if (lane == 0)
+                                flag_store(flag_ptr(a, B.slot, h), kFlagA | xcd_tag());
                         }
                     }
+                }
+                // the local part of the outputs (from the piece's state
+                // inside the block) while predecessors finish theirs
+                QSlots qs0, qs1;
+                q_slots(q0, qs0);
+                q_slots(q1, qs1);
+                OTiles O0, O1;
+                {
+                    State S;
+#pragma unroll
+                    for (int t = 0; t < kTiles; ++t) S[t] = E[t];
+                    piece_local(O0, O1, S, sK, sV, r1, qs0, qs1, pntok, g, c16, lane);
+                }
+                if constexpr (MODE == kFused) {
                     if (B.j > 0) {
                         // nearest predecessor with an inclusive prefix, then
                         // the aggregates after it, left to right
-                        const int m = find_prefix(a, B.slot0, B.j, h, lane);
-                        {
-                            const auto r = slot_rsrc(a.pslots, B.slot0 + m, H, h);
-#pragma unroll
-                            for (int i = 0; i < 4; ++i)
-                                own4[i] = slot_load<kAuxCoherent>(r, 4 * w + i, lane);
-                        }
-                        add_slots4<kAuxCoherent>(own4, a.aslots, B.slot0 + m + 1, B.j - 1 - m, H,
-                                                 h, w, lane);
+                        bool local;
+                        const int m = find_prefix(a, B.slot0, B.j, h, lane, xcd_tag(), local);
+                        if (__builtin_amdgcn_readfirstlane(int(local)))
+                            look_back<kAuxL2>(own4, a, B.slot0, m, B.j, h, w, lane);
+                        else
+                            look_back<kAuxCoherent>(own4, a, B.slot0, m, B.j, h, w, lane);
                     }
                 } else if (B.j > 0) {
                     if constexpr (MODE == kOut3) {
@@ -645,11 +791,16 @@ __global__ __launch_bounds__(kThreads) void piece_kernel(PArgs a) {
                     const PScan vs = a.scans[B.seed];
                     const int last = vs.first_slot + vs.n_slots - 1;
                     if constexpr (MODE == kFused) {
-                        wait_prefix(a, a.flags + int64_t(last) * H + h);
                         const auto r = slot_rsrc(a.pslots, last, H, h);
+                        if (wait_prefix(a, flag_ptr(a, last, h), xcd_tag())) {
 #pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            sin4[i] = slot_load<kAuxCoherent>(r, 4 * w + i, lane);
+                            for (int i = 0; i < 4; ++i)
+                                sin4[i] = slot_load<kAuxL2>(r, 4 * w + i, lane);
+                        } else {
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                sin4[i] = slot_load<kAuxCoherent>(r, 4 * w + i, lane);
+                        }
                     } else if constexpr (MODE == kOut3) {
                         const auto r = slot_rsrc(a.aslots, last, H, h);
 #pragma unroll
@@ -684,59 +835,83 @@ __global__ __launch_bounds__(kThreads) void piece_kernel(PArgs a) {
                     if (MODE == kFused && B.slot >= 0 && B.j > 0) {
                         store_state<kAuxCoherent>(P, a.pslots, B.slot, H, h, lane);
                         drain_stores();
-                        if (lane == 0) flag_store(a.flags + int64_t(B.slot) * H + h, kFlagP);
+                        if (lane == 0)
+                            flag_store(flag_ptr(a, B.slot, h), kFlagP | xcd_tag());
                     }
                     if (B.final_row >= 0)
                         store_rows_state(P, a.final_state + (int64_t(B.final_row) * H + h) * PD * PD,
                                          g, c16);
                 }
-                State S;
-                get_state(X, 1, S, lane);
-                if (!has_seed && B.j == 0) zero_state(S);
-                if (w >= 1)
-#pragma unroll
-                    for (int t = 0; t < kTiles; ++t) S[t] = S[t] + E[t];
-                piece_outputs(S, sK, sV, r0, r1, q0, q1, a, ptok0, pntok, true, h, g, c16, lane);
+                // O += Q S_b, S_b the state the block starts from
+                if ((has_seed || B.j > 0) && pntok > 0) {
+                    SSplit sp;
+                    {
+                        State Sb;
+                        get_state(X, 1, Sb, lane);
+                        split_state(Sb, sp);
+                    }
+                    add_qs(O0, sp, qs0);
+                    if (pntok > kChunk) add_qs(O1, sp, qs1);
+                }
+                if (pntok > 0) store_chunk(O0, a, ptok0, min(pntok, kChunk), h, g, c16);
+                if (pntok > kChunk) store_chunk(O1, a, ptok0 + kChunk, pntok - kChunk, h, g, c16);
             }
         } else if constexpr (MODE != kStates) {
-            // up to four one-piece branches, one per wave, each from its seed
-            if (w < it.n) {
-                const PBlock B = a.blocks[a.items[item].b[w]];
+            // packed branches: wave w takes block b_2w and, when there is one,
+            // block b_2w+1 (then both are one chunk long), each from its seed
+            const int b0 = a.items[item].b[2 * w], b1 = a.items[item].b[2 * w + 1];
+            if (b0 >= 0) {
+                const PBlock B = a.blocks[b0];
+                const PBlock B1 = b1 >= 0 ? a.blocks[b1] : B;
+                // chunk 1: the branch's second chunk, or the second branch
+                const int64_t t1 = b1 >= 0 ? int64_t(B1.tok0) : int64_t(B.tok0) + kChunk;
+                const int n1 = b1 >= 0 ? B1.ntok : B.ntok - kChunk;
                 ChunkKV r0, r1;
                 ChunkQ q0, q1;
                 load_chunk_kv(r0, a, B.tok0, B.ntok, h, lane);
-                load_chunk_kv(r1, a, int64_t(B.tok0) + kChunk, B.ntok - kChunk, h, lane);
+                load_chunk_kv(r1, a, t1, n1, h, lane);
                 load_chunk_q(q0, a, B.tok0, B.ntok, h, g, c16);
-                load_chunk_q(q1, a, int64_t(B.tok0) + kChunk, B.ntok - kChunk, h, g, c16);
-                State S;
-                zero_state(S);
-                if (B.seed >= 0) {
-                    const PScan vs = a.scans[B.seed];
-                    const int last = vs.first_slot + vs.n_slots - 1;
-                    if constexpr (MODE == kFused) {
-                        wait_prefix(a, a.flags + int64_t(last) * H + h);
-                        const auto r = slot_rsrc(a.pslots, last, H, h);
-#pragma unroll
-                        for (int t = 0; t < kTiles; ++t) S[t] = slot_load<kAuxCoherent>(r, t, lane);
-                    } else if constexpr (MODE == kOut3) {
-                        const auto r = slot_rsrc(a.aslots, last, H, h);
-#pragma unroll
-                        for (int t = 0; t < kTiles; ++t) S[t] = slot_load<0>(r, t, lane);
-                    } else {
-                        // the view's total, summed from zero in slot order
-                        for (int s = 0; s < vs.n_slots; ++s) {
-                            const auto r = slot_rsrc(a.aslots, vs.first_slot + s, H, h);
-#pragma unroll
-                            for (int t = 0; t < kTiles; ++t) S[t] += slot_load<0>(r, t, lane);
-                        }
+                load_chunk_q(q1, a, t1, n1, h, g, c16);
+                QSlots qs0, qs1;
+                q_slots(q0, qs0);
+                q_slots(q1, qs1);
+                // local parts first (a branch's own tokens, from a zero
+                // state), then each branch's seed
+                OTiles O0, O1;
+                stage_chunk(r0, sK, sV, lane);
+                {
+                    State S;
+                    zero_state(S);
+                    chunk_local<false>(O0, S, sK, sV, qs0, g, c16);
+                    if (n1 > 0) {
+                        if (b1 < 0) acc_kv(S, sK, sV, g, c16);   // the branch's chunk 1
+                        // every lane's reads of chunk 0 are done before chunk 1
+                        // overwrites it
+                        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+                        __builtin_amdgcn_wave_barrier();
+                        stage_chunk(r1, sK, sV, lane);
+                        chunk_local<true>(O1, S, sK, sV, qs1, g, c16);
                     }
-                } else if (B.seed <= -2) {
-                    const float* src = a.ext_state + (int64_t(-B.seed - 2) * H + h) * PD * PD;
-#pragma unroll
-                    for (int t = 0; t < kTiles; ++t) S[t] = load_rows_tile(src, t, g, c16);
                 }
-                piece_outputs(S, sK, sV, r0, r1, q0, q1, a, B.tok0, B.ntok, false, h, g, c16,
-                              lane);
+                {
+                    SSplit sp;
+                    {
+                        State Sb;
+                        load_seed<MODE>(Sb, a, B.seed, h, g, c16, lane);
+                        split_state(Sb, sp);
+                    }
+                    add_qs(O0, sp, qs0);
+                    if (n1 > 0) {
+                        if (b1 >= 0 && B1.seed != B.seed) {
+                            State Sb;
+                            load_seed<MODE>(Sb, a, B1.seed, h, g, c16, lane);
+                            split_state(Sb, sp);
+                        }
+                        add_qs(O1, sp, qs1);
+                    }
+                }
+                store_chunk(O0, a, B.tok0, min(B.ntok, kChunk), h, g, c16);
+                if (n1 > 0) store_chunk(O1, a, t1, n1, h, g, c16);
             }
         }
     }
@@ -776,6 +951,28 @@ WsLayout ws_layout(const la_pass_info& info, int32_t H) {
     return l;
 }
 
+// Workgroups of the single-launch kernel the current device holds at once
+// (0 when unknown).  A launch of at most that many workgroups is resident in
+// full, so its waits need no ordering of the work.
+int resident_capacity() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+    if (dev < 64) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void*>(piece_kernel<kFused>), kThreads, 0) !=
+            hipSuccess)
+        return 0;
+    const int c = cus > 0 && per_cu > 0 ? cus * per_cu : 0;
+    if (dev < 64 && c > 0) cache[dev].store(c, std::memory_order_relaxed);
+    return c;
+}
+
 }  // namespace
 
 namespace piece {
@@ -785,7 +982,7 @@ size_t workspace_bytes(const la_pass_info& info, int32_t H) { return ws_layout(i
 la_status launch(int32_t stages, int form, const void* q, const void* k, const void* v,
                  int32_t H, const la_pass_info& info, const int32_t* plan,
                  const float* ext_state, void* out, float* final_state, void* workspace,
-                 hipStream_t st, int32_t spin_limit, bool force_timeout) {
+                 hipStream_t st, int32_t spin_limit, bool force_timeout, bool ordered) {
     const WsLayout l = ws_layout(info, H);
     char* ws = static_cast<char*>(workspace);
     PArgs a;
@@ -812,13 +1009,19 @@ la_status launch(int32_t stages, int form, const void* q, const void* k, const v
     a.out = static_cast<uint16_t*>(out);
     a.H = H;
     a.n_flags = info.piece_slots * H;
+    a.n_slots = info.piece_slots;
     a.plan_hash = info.plan_hash;
     a.spin_limit = spin_limit;
     a.force_timeout = force_timeout ? 1 : 0;
+    a.ordered = 1;
     const dim3 blk(kThreads);
     if (form == 1) {
         if (!(stages & LA_STAGE_ALL)) return LA_OK;
         a.n_work = info.piece_items * H;
+        if (!ordered) {
+            const int cap = resident_capacity();
+            a.ordered = cap > 0 && a.n_work <= cap ? 0 : 1;
+        }
         if (a.n_work > 0)
             hipLaunchKernelGGL(piece_kernel<kFused>, dim3(unsigned(a.n_work)), blk, 0, st, a);
         return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_HIP;

@@ -1457,7 +1457,7 @@ extern "C" la_status la_scan_packed_stages(int32_t stages, const void* q, const 
                                            void* workspace, size_t workspace_bytes,
                                            void* stream) {
     constexpr int32_t kForms = LA_FORM_ONE_LAUNCH | LA_FORM_TWO_LAUNCH | LA_FORM_THREE_LAUNCH;
-    if (!info || (stages & ~(LA_STAGE_ALL | kForms | LA_DEBUG_FORCE_TIMEOUT)) ||
+    if (!info || (stages & ~(LA_STAGE_ALL | kForms | LA_DEBUG_FORCE_TIMEOUT | LA_DEBUG_ORDERED)) ||
         !(stages & LA_STAGE_ALL) || __builtin_popcount(unsigned(stages & kForms)) > 1)
         return LA_ERR_INVALID_ARG;
     // an la_pass_info whose fields were edited, or mixed from two passes
@@ -1503,9 +1503,11 @@ extern "C" la_status la_scan_packed_stages(int32_t stages, const void* q, const 
                                                            : 1;
         const bool force = (stages & LA_DEBUG_FORCE_TIMEOUT) != 0;
         return piece::launch(stages & LA_STAGE_ALL, form, q, k, v, H, *info, plan, ext_state,
-                             out, final_state, workspace, st, force ? 16 : kSpinLimit, force);
+                             out, final_state, workspace, st, force ? 16 : kSpinLimit, force,
+                             (stages & LA_DEBUG_ORDERED) != 0);
     }
-    if (stages & (LA_FORM_ONE_LAUNCH | LA_DEBUG_FORCE_TIMEOUT)) return LA_ERR_UNSUPPORTED;
+    if (stages & (LA_FORM_ONE_LAUNCH | LA_DEBUG_FORCE_TIMEOUT | LA_DEBUG_ORDERED))
+        return LA_ERR_UNSUPPORTED;
     int* hdr = static_cast<int*>(workspace);
     float* ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + kWsHeader);
     const PlanCheck pc{plan, hdr, info->plan_hash};

@@ -89,7 +89,7 @@ enum {
 #define LA_PLAN_BLOCK_WORDS 8
 #define LA_PLAN_DELTA_WORDS 4
 #define LA_PLAN_SCAN_WORDS 4
-#define LA_PLAN_ITEM_WORDS 8
+#define LA_PLAN_ITEM_WORDS 12
 #define LA_ITEM_BLOCK 0
 #define LA_ITEM_PACK 1
 /* The piece path (d = 64, bf16 inputs) cuts every segment into blocks of
@@ -190,10 +190,13 @@ uint32_t la_info_checksum(const la_pass_info* info);
  *             final_row} -- blocks of LA_PIECE_BLOCK_CHUNKS chunks; slot: the
  *             block's state slot (-1: none needed), slot0: the segment's first
  *             slot, j: the block's position in its segment
- *   pitems    piece_items x 8: {kind, n, b0, b1, b2, b3, 0, 0} -- kind
- *             LA_ITEM_BLOCK: one block b0 (wave w takes its piece w);
- *             LA_ITEM_PACK: n one-piece branch blocks b0.. (wave w takes
- *             b_w).  Block items first, in block order, then the packs.
+ *   pitems    piece_items x 12: {kind, n, b0, .., b7, 0, 0} -- kind
+ *             LA_ITEM_BLOCK: one block b0 (wave w takes its piece w), n = 1,
+ *             b1.. = -1; LA_ITEM_PACK: branches whose only block is one piece,
+ *             n waves of them: wave w takes block b_2w and, when b_2w+1 is
+ *             not -1, block b_2w+1 after it (two branches of at most one
+ *             chunk each share a wave; a branch of two chunks has one alone).
+ *             Block items first, in block order, then the packs.
  *   pscan     piece_scans x 4, as scan, for the piece path's slots
  * View blocks come first (longest work first), then branch blocks.
  */
@@ -376,6 +379,10 @@ la_status la_scan_status(const void* workspace, size_t workspace_bytes, int32_t*
  * (LA_ERR_TIMEOUT is recorded, the outputs are not valid, every kernel still
  * exits normally). */
 #define LA_DEBUG_FORCE_TIMEOUT 64
+/* Test aid for the single-launch form: workgroups take their work in ticket
+ * order even when the whole launch fits on the GPU at once (the library
+ * takes tickets only when it does not). */
+#define LA_DEBUG_ORDERED 128
 
 /*
  * la_scan_packed_stages -- la_scan_packed restricted to the launches whose
@@ -390,8 +397,8 @@ la_status la_scan_status(const void* workspace, size_t workspace_bytes, int32_t*
  * Errors: as la_scan_packed (LA_ERR_INVALID_ARG also for ext_state overlapping
  * final_state), plus LA_ERR_INVALID_ARG when no LA_STAGE_* bit is set, an
  * unknown bit is set, or more than one LA_FORM_* bit is set, and
- * LA_ERR_UNSUPPORTED for LA_FORM_ONE_LAUNCH or LA_DEBUG_FORCE_TIMEOUT outside
- * the piece path.
+ * LA_ERR_UNSUPPORTED for LA_FORM_ONE_LAUNCH, LA_DEBUG_FORCE_TIMEOUT or
+ * LA_DEBUG_ORDERED outside the piece path.
  */
 la_status la_scan_packed_stages(int32_t stages, const void* q, const void* k, const void* v,
                                 la_dtype dtype, int32_t H, int32_t d_k, int32_t d_v,

@@ -86,3 +86,16 @@ def test_allocation_follows_the_given_stream(monkeypatch):
     assert entered == [marker] and t.shape == (3, 4)
     la._alloc((2,), torch.float32, "cpu", None)
     assert entered == [marker]
+
+
+def test_pack_rejects_mismatched_request_arrays():
+    """The library reads one branch count per request and sum(branch_count)
+    branch lengths: shorter arrays would be read past their end, longer ones
+    silently cut, so the binding refuses both."""
+    la.pack([100, 50], [1, 2], [10, 20, 30])
+    with pytest.raises(ValueError):
+        la.pack([100, 50], [1, 2], [10, 20])
+    with pytest.raises(ValueError):
+        la.pack([100, 50], [1, 2], [10, 20, 30, 40])
+    with pytest.raises(ValueError):
+        la.pack([100, 50], [1], [10])

@@ -176,3 +176,88 @@ def test_single_launch_is_deterministic():
     for _ in range(9):
         o, f = la.scan_packed(qd, kd, vd, plan, workspace=ws, form="one")
         assert torch.equal(o, o0) and torch.equal(f, f0)
+
+
+def test_ordered_tickets_match_index_order():
+    """The single launch with the work taken in ticket order (forced; the
+    library takes tickets only when the launch does not fit on the device at
+    once) gives the bits of the launch that uses the workgroup index, on the
+    7,400-token pass (256 workgroups) and on a pass larger than the device."""
+    for name in ("view7400_br8x48_h16_d64_bf16", None):
+        if name:
+            w = synth.workload(name)
+            plan = la.pack(w.view_len, w.branch_count, w.branch_len, heads=w.H)
+            q, k, v, H = w.q, w.k, w.v, w.H
+        else:
+            H = 16
+            plan, q, k, v = _inputs([20000, 3000], [6, 3], [48, 64, 1, 130, 500, 2, 64, 64, 9],
+                                    H, 41)
+        qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+        ws = la.new_workspace(plan, H, 64, la.LA_BF16, DEV)
+        print(f"ordered vs index: workgroups={plan.info.piece_items * H}", flush=True)
+        o1, f1 = la.scan_packed(qd, kd, vd, plan, workspace=ws, form="one")
+        o1, f1 = o1.clone(), f1.clone()
+        o2, f2 = la.scan_packed(qd, kd, vd, plan, workspace=ws, form="one",
+                                stages=la.STAGE_ALL | la.DEBUG_ORDERED)
+        o3, f3 = la.scan_packed(qd, kd, vd, plan, form="three")
+        assert la.scan_status(ws) == 0
+        assert torch.equal(o1, o2) and torch.equal(f1, f2)
+        assert torch.equal(o1, o3) and torch.equal(f1, f3)
+        assert _header_words(ws, 4) == [0, 0, 0, 0]
+
+
+def test_packed_short_branches_share_waves():
+    """Branches of at most one chunk are packed two to a wave, with seeds
+    from different views and from ext_state rows in one wave (the second
+    branch reloads its own seed), next to branches of two chunks that take a
+    wave alone: all forms bit-identical, oracle within tolerance."""
+    vl = [300, 0, 700, 64, 0]
+    bc = [3, 2, 4, 2, 2]
+    bl = [10, 64, 1, 33, 128, 5, 100, 64, 63, 2, 65, 17, 40]
+    H = 3
+    plan = la.pack(vl, bc, bl, heads=H)
+    P = plan.plan
+    oi = int(P[21])
+    nbi, ni = plan.info.piece_block_items, plan.info.piece_items
+    items = P[oi:oi + 12 * ni].reshape(-1, 12)
+    pairs = sum(1 for row in items[nbi:] for w in range(row[1]) if row[3 + 2 * w] != -1)
+    assert pairs >= 3
+    T = plan.info.n_tokens
+    q, k, v = synth.draw_qkv(np.random.default_rng(57), T, H, 64, "bf16")
+    ext = torch.from_numpy(np.random.default_rng(58).standard_normal(
+        (plan.info.n_ext, H, 64, 64)).astype(np.float32))
+    qd, kd, vd, ed = q.to(DEV), k.to(DEV), v.to(DEV), ext.to(DEV)
+    outs = {f: la.scan_packed(qd, kd, vd, plan, ext_state=ed, form=f)
+            for f in ("one", "two", "three")}
+    for f in ("one", "two"):
+        assert torch.equal(outs[f][0], outs["three"][0]), f
+        assert torch.equal(outs[f][1], outs["three"][1]), f
+    ref_o, ref_f = oracle.scan_recurrence(q, k, v, plan.seg_offsets, plan.branch_parent,
+                                          ext_state=ext)
+    eo = oracle.row_rel_err(outs["one"][0].cpu(), ref_o)
+    ef = oracle.state_rel_err(outs["one"][1].cpu(), ref_f)
+    print(f"packed short branches: pairs={pairs} out err {eo:.2e} final {ef:.2e}", flush=True)
+    assert eo <= TOL and ef <= TOL
+
+
+def test_alternating_inputs_on_one_workspace():
+    """Passes over two different input sets, alternating on one workspace:
+    every state slot is rewritten with other values at the same address each
+    pass, so a look-back that read a stale cached copy of a slot (from the
+    pass before) would change the bits.  Each pass must equal the three-
+    launch form on its own inputs."""
+    w = synth.workload("view7400_br8x48_h16_d64_bf16")
+    plan = la.pack(w.view_len, w.branch_count, w.branch_len, heads=w.H)
+    sets = []
+    for seed in (71, 72):
+        q, k, v = synth.draw_qkv(np.random.default_rng(seed), plan.info.n_tokens, w.H, 64,
+                                 "bf16")
+        qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+        ref = la.scan_packed(qd, kd, vd, plan, form="three")
+        sets.append((qd, kd, vd, ref))
+    ws = la.new_workspace(plan, w.H, 64, la.LA_BF16, DEV)
+    for i in range(8):
+        qd, kd, vd, (ro, rf) = sets[i % 2]
+        o, f = la.scan_packed(qd, kd, vd, plan, workspace=ws, form="one")
+        assert torch.equal(o, ro) and torch.equal(f, rf), i
+    assert la.scan_status(ws) == 0

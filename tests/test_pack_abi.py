@@ -60,8 +60,10 @@ def _check_piece_tables(plan, so, bp, vo):
     """The piece path's tables against the rules they follow: blocks of 8
     chunks restarting at every segment, a state slot for every view block and
     every branch block but the last, segments' slots contiguous, branches
-    whose only block is one piece (<= 128 tokens) packed four to an item, every
-    other block one item in block order; and the plan hash and info check."""
+    whose only block is one piece (<= 128 tokens) packed into items of four
+    waves (two branches of <= 64 tokens share a wave, a longer one has a wave
+    alone, as few waves as that allows, in branch order), every other block
+    one item in block order; and the plan hash and info check."""
     info, P = plan.info, plan.plan.astype(np.int64)
     BT, PT = 8 * 64, 2 * 64
     nb_, ni, nbi, nsl, nsc = (int(x) for x in P[15:20])
@@ -69,9 +71,10 @@ def _check_piece_tables(plan, so, bp, vo):
                                         info.piece_block_items, info.piece_slots,
                                         info.piece_scans)
     ob, oi, osc = (int(x) for x in P[20:23])
-    assert oi == ob + 8 * nb_ and osc == oi + 8 * ni and osc + 4 * nsc == info.plan_words
+    IW = 12
+    assert oi == ob + 8 * nb_ and osc == oi + IW * ni and osc + 4 * nsc == info.plan_words
     blocks = P[ob:ob + 8 * nb_].reshape(-1, 8)
-    items = P[oi:oi + 8 * ni].reshape(-1, 8)
+    items = P[oi:oi + IW * ni].reshape(-1, IW)
     scans = P[osc:osc + 4 * nsc].reshape(-1, 4)
     # expected blocks, views first then branches, in segment order
     want, slot, view_scan = [], 0, {}
@@ -100,11 +103,23 @@ def _check_piece_tables(plan, so, bp, vo):
     assert np.all(kinds[:nbi] == 0) and np.all(kinds[nbi:] == 1)
     singles = [i for i in range(len(want)) if i not in set(packed)]
     assert items[:nbi, 2].tolist() == singles and np.all(items[:nbi, 1] == 1)
-    got_packed = []
-    for row in items[nbi:]:
-        assert 1 <= row[1] <= 4 and all(x == -1 for x in row[2 + row[1]:6])
-        got_packed += row[2:2 + row[1]].tolist()
-    assert got_packed == packed
+    assert np.all(items[:nbi, 3:10] == -1) and np.all(items[:, 10:] == 0)
+    waves = []
+    for r, row in enumerate(items[nbi:]):
+        nw = int(row[1])
+        assert 1 <= nw <= 4 and (nw == 4 or r == ni - nbi - 1)
+        assert np.all(row[2 + 2 * nw:10] == -1)
+        waves += [(int(row[2 + 2 * w]), int(row[3 + 2 * w])) for w in range(nw)]
+    ntok = {b: want[b][1] for b in packed}
+    got = [b for w in waves for b in w if b != -1]
+    assert sorted(got) == packed and len(set(got)) == len(got)
+    for b0, b1 in waves:
+        assert b0 in ntok
+        if b1 != -1:   # two short branches, in branch order
+            assert ntok[b0] <= 64 and ntok[b1] <= 64 and b0 < b1
+    assert [w[0] for w in waves] == sorted(w[0] for w in waves)
+    n_short = sum(1 for b in packed if ntok[b] <= 64)
+    assert len(waves) == len(packed) - n_short + -(-n_short // 2)
     for v, (first, n) in view_scan.items():
         assert scans[v].tolist() == [first, n, v, int(np.flatnonzero((bp == -1) & (vo == v))[0])]
     ph = P.copy()
@@ -119,7 +134,7 @@ def _check_plan(plan, so, bp, vo):
     list covers views plus branches with >= 2 slots."""
     info, P = plan.info, plan.plan
     G, C = info.block_chunks, info.chunk
-    assert P[0] == 0x4C41504E and P[1] == 3
+    assert P[0] == 0x4C41504E and P[1] == 4
     assert (P[2], P[3], P[4]) == (info.n_blocks, info.n_delta, info.n_scan)
     ob, od, osc = P[8], P[9], P[10]
     blocks = P[ob:ob + 8 * info.n_blocks].reshape(-1, 8)
@@ -301,13 +316,15 @@ def test_scan_rejects_bad_arguments_before_launch():
                                          a["wsb"], None)
     assert staged(la.STAGE_ALL | la.FORM_ONE_LAUNCH | la.FORM_TWO_LAUNCH) == la.LA_ERR_INVALID_ARG
     assert staged(la.FORM_ONE_LAUNCH) == la.LA_ERR_INVALID_ARG        # no stage bit
-    assert staged(la.STAGE_ALL | 128) == la.LA_ERR_INVALID_ARG        # unknown bit
+    assert staged(la.STAGE_ALL | 256) == la.LA_ERR_INVALID_ARG        # unknown bit
     need32 = ctypes.c_size_t()
     lib.la_scan_workspace_size(ctypes.byref(info), 2, 64, 64, la.LA_F32, ctypes.byref(need32))
     # the single-launch form and its timeout aid exist on the piece path only
     assert staged(la.STAGE_ALL | la.FORM_ONE_LAUNCH, dtype=la.LA_F32,
                   wsb=need32.value) == la.LA_ERR_UNSUPPORTED
     assert staged(la.STAGE_ALL | la.DEBUG_FORCE_TIMEOUT, dtype=la.LA_F32,
+                  wsb=need32.value) == la.LA_ERR_UNSUPPORTED
+    assert staged(la.STAGE_ALL | la.DEBUG_ORDERED, dtype=la.LA_F32,
                   wsb=need32.value) == la.LA_ERR_UNSUPPORTED
     shard = la.pack([0], [2], [10, 20], block_chunks=1)
     st = lib.la_scan_packed(fake, fake, fake, la.LA_BF16, 2, 64, 64, ctypes.byref(shard.info),
@@ -410,8 +427,9 @@ def test_stage_and_form_bits_checked_before_any_device_work():
     assert call(la.STAGE_ALL | la.FORM_TWO_LAUNCH) == la.LA_OK
     assert call(la.STAGE_OUTPUT | la.FORM_THREE_LAUNCH) == la.LA_OK
     assert call(la.STAGE_ALL | la.FORM_ONE_LAUNCH) == la.LA_OK
+    assert call(la.STAGE_ALL | la.FORM_ONE_LAUNCH | la.DEBUG_ORDERED) == la.LA_OK
     for bad in (0, la.FORM_TWO_LAUNCH, la.STAGE_ALL | la.FORM_TWO_LAUNCH | la.FORM_THREE_LAUNCH,
-                la.STAGE_ALL | la.FORM_ONE_LAUNCH | la.FORM_THREE_LAUNCH, la.STAGE_ALL | 128,
+                la.STAGE_ALL | la.FORM_ONE_LAUNCH | la.FORM_THREE_LAUNCH, la.STAGE_ALL | 256,
                 -1):
         assert call(bad) == la.LA_ERR_INVALID_ARG, bad
 

@@ -40,19 +40,25 @@ def test_pack_matches_oracle_and_plan_properties(reqs, G):
     # in exactly one work item, packs hold only one-piece single-block branches
     ob, oi = int(p.plan[20]), int(p.plan[21])
     pblocks = p.plan[ob:ob + 8 * info.piece_blocks].reshape(-1, 8)
-    pitems = p.plan[oi:oi + 8 * info.piece_items].reshape(-1, 8)
+    pitems = p.plan[oi:oi + 12 * info.piece_items].reshape(-1, 12)
     cover[:] = 0
     for tok0, ntok, slot, seed, seg, slot0, j, frow in pblocks:
         assert 1 <= ntok <= 512 and tok0 == so[seg] + 512 * j
         cover[tok0:tok0 + ntok] += 1
     assert (cover == 1).all()
     seen = np.zeros(info.piece_blocks, dtype=int)
-    for kind, n, b0, b1, b2, b3, _, _ in pitems:
-        for b in (b0, b1, b2, b3)[:n]:
+    for row in pitems:
+        kind, n, bs = row[0], row[1], row[2:10]
+        members = [b for b in (bs[:1] if kind == 0 else bs[:2 * n]) if b != -1]
+        for b in members:
             seen[b] += 1
             if kind == 1:
                 tok0, ntok, _, seed, seg = pblocks[b][:5]
                 assert seed != -1 and ntok <= 128 and ntok == so[seg + 1] - so[seg]
+        if kind == 1:   # a wave holds one branch, or two of at most one chunk
+            for w in range(n):
+                if bs[2 * w + 1] != -1:
+                    assert pblocks[bs[2 * w]][1] <= 64 and pblocks[bs[2 * w + 1]][1] <= 64
     assert (seen == 1).all()
     # attention items cover every query exactly once, in <= 64-token blocks
     ext_len = [11] * info.n_ext
