@@ -1,8 +1,8 @@
 """Benchmark: linear-attention layer tokens/s per packed pass on one MI355X.
 
-One step = one packed pass through la_scan_packed (all its launches: two or
-three, the form the library picks for the pass, or --form) over
-one batch of synthetic input already resident in HBM.  The default workload
+One step = one packed pass through la_scan_packed (all its launches: one for
+d = 64 bf16 passes, else two or three, the form the library picks for the
+pass, or --form) over one batch of synthetic input already resident in HBM.  The default workload
 is one 7,400-token view with 8 branches of 48 tokens, H = 16, d = 64, bf16
 (the pass size of the page "Serving 0.88M TPS from Two RTXs and Mac Minis",
 section "Kernels", paragraph "One scan per pass").
@@ -10,10 +10,13 @@ section "Kernels", paragraph "One scan per pass").
 Timing: W warm-up passes, then exactly K passes, both replayed as HIP graphs
 on one stream and bracketed by torch.cuda.synchronize().  Inputs rotate over
 enough copies (>= 1 GiB in total) that each pass reads its q/k/v from HBM
-rather than from the 256 MB Infinity Cache.  The dominant kernel (launch 3,
-the chunk outputs) is timed alone with HIP events on the same stream for the
-roofline line.  The fp64 CPU oracle is timed on the host cores on the same
-workload (cpu_baseline).
+rather than from the 256 MB Infinity Cache.  The roofline line is the whole
+pass (its algorithmic bytes over the pass time from HIP events on the
+stream the launches run on; in the single-launch form the pass is one
+kernel); multi-launch forms also report launch 3 alone.  HBM traffic and MFMA
+busy cycles come from committed rocprofv3 counter summaries (profiles/),
+used only when they were taken on the current kernel sources.  The fp64 CPU
+oracle is timed on the host cores on the same workload (cpu_baseline).
 
 Prints one JSON line.
 """
@@ -169,6 +172,7 @@ def cpu_baseline(w, so, bp, target_s):
     except OSError:
         pass
     return {"value": w.n_tokens / wall, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "host_cores": os.cpu_count(), "affinity_cores": len(os.sched_getaffinity(0)),
             "sample": f"whole pass ({w.n_tokens} tokens x {w.H} heads), {len(walls)} repeats, "
                       f"median wall {wall:.3f} s, {cpu:.1f} s CPU work, {model}"}
 
@@ -450,19 +454,6 @@ def cost_model_bench(a):
     }), flush=True)
 
 
-def traffic_from_profiles(kernel_tag, workload, src_hash):
-    """HBM bytes per launch of the dominant kernel from committed rocprofv3
-    --pmc summaries, only if they were taken on the current kernel source."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel_tag}_{workload}.json")
-    if not os.path.exists(path):
-        return None
-    with open(path) as f:
-        rec = json.load(f)
-    if rec.get("source_sha256") != src_hash:
-        return None
-    return rec.get("bytes_per_launch")
-
-
 def main():
     a = parse()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -621,25 +612,28 @@ def main():
                      "inputs": "one set reused (cache-warm)"}
         del gw
 
-    # launch 3 alone (reads what the last full pass left in ws / final_state)
-    out_only = make_graph(a.steps, la.STAGE_OUTPUT)
-    with torch.cuda.stream(stream):
-        out_only()
-    torch.cuda.synchronize()
-    e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(stream):
-        e2.record(stream)
-        out_only()
-        e3.record(stream)
-    torch.cuda.synchronize()
-    l3_us = e2.elapsed_time(e3) * 1e3 / a.steps
+    # launch 3 alone (reads what the last full pass left in ws / final_state);
+    # the single-launch form has no separate output launch
+    l3_us = None
+    if n_launches > 1:
+        out_only = make_graph(a.steps, la.STAGE_OUTPUT)
+        with torch.cuda.stream(stream):
+            out_only()
+        torch.cuda.synchronize()
+        e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            e2.record(stream)
+            out_only()
+            e3.record(stream)
+        torch.cuda.synchronize()
+        l3_us = e2.elapsed_time(e3) * 1e3 / a.steps
 
     # algorithmic bytes: q, k, v read once and out written once per token-head;
     # final states written once per view and head
     per_token_head = d * (3 * s_el + s_el)
     l3_bytes = T * H * per_token_head
     pass_bytes = l3_bytes + info.n_views * H * d * d * 4
-    achieved = l3_bytes / (l3_us * 1e-6) / 1e9
+    achieved = l3_bytes / (l3_us * 1e-6) / 1e9 if l3_us else None
     # algorithmic matrix work per chunk of c tokens and head: q.S (2 c d^2),
     # the causal scores and weighted values (c (c + 1) 2d), and the chunk's
     # own state K^T V (2 c d^2) where a later chunk needs it (every chunk but
@@ -653,12 +647,15 @@ def main():
         flops += sum(2 * c * d * d + c * (c + 1) * 2 * d for c in sizes)
         flops += sum(2 * c * d * d for c in sizes[:-1])
     flops *= H
-    src = os.path.join(ROOT, "chunked_linear_attention_packed_amd", "csrc", "scan.hip")
-    with open(src, "rb") as f:
-        src_hash = hashlib.sha256(f.read()).hexdigest()
-    traffic = traffic_from_profiles("output_kernel_split" if a.split_fp32 else "output_kernel",
-                                    a.workload, src_hash)
+    from chunked_linear_attention_packed_amd.profile_summary import (kernel_source_hash,
+                                                                     profile_record)
+    src_hash = kernel_source_hash()
+    form_tag = {1: "one", 2: "two", 3: "three"}[n_launches] + ("_split" if a.split_fp32 else "")
+    tr = profile_record("traffic", a.workload, form_tag, src_hash)
+    traffic = tr["bytes_per_pass"] if tr else None
+    sq = profile_record("counters", a.workload, form_tag, src_hash)
     pass_us = gpu_ms * 1e3 / a.steps
+    pass_achieved = pass_bytes / (pass_us * 1e-6) / 1e9
 
     # spread of single passes: each of `steps` eager passes bracketed by its own
     # events on the stream (eager launches add host submission gaps, so these
@@ -709,7 +706,7 @@ def main():
             "pass_algorithmic_flops": flops,
             "pass_mfma_frac": flops / (pass_us * 1e-6) / (
                 2.5e15 if (w.dtype == "bf16" or a.split_fp32) else 157.3e12),
-            "output_kernel_us": l3_us,
+            "mfma_busy_frac_counters": (sq or {}).get("mfma_busy_frac"),
             "single_pass_us_eager": {"p10": float(np.percentile(singles, 10)),
                                      "median": float(np.median(singles)),
                                      "p90": float(np.percentile(singles, 90))},
@@ -718,15 +715,22 @@ def main():
             "warm_same_inputs": warm_same,
         },
         "roofline": {
-            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-            "kernel": ("output_kernel (launch 3; in the two-launch form it also sums the "
-                       "block states before its block)" if n_launches == 2
-                       else "output_kernel (launch 3)"),
-            "bytes_per_launch": l3_bytes,
+            "bound": "hbm", "achieved": pass_achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": pass_achieved / HBM_PEAK_GBS, "traffic": traffic,
+            "kernel": ("piece_kernel, single launch: the whole pass" if n_launches == 1
+                       else f"the whole pass ({n_launches} launches)"),
+            "bytes_per_pass": pass_bytes,
+            "traffic_source": tr.get("source") if tr else None,
         },
         "cpu_baseline": cpu,
     }
+    if n_launches > 1:
+        rec["launch3_roofline"] = {
+            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS, "us": l3_us, "bytes_per_launch": l3_bytes,
+            "kernel": ("output launch (in the two-launch form it also sums the block states "
+                       "before its block)" if n_launches == 2 else "output launch"),
+        }
     print(json.dumps(rec), flush=True)
 
 

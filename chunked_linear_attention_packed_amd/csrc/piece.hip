@@ -11,10 +11,11 @@
 // LA_PIECE_BLOCK_CHUNKS = 8 chunks, a block into up to four pieces of
 // LA_PIECE_CHUNKS = 2 chunks.  One workgroup of four waves takes a block
 // and a head; wave w owns piece w end to end: it loads that piece's k, v
-// and q, keeps the whole 64x64 state in its own registers, and computes
-// every output feature of its tokens, so the chunk loop has no workgroup
-// barrier and no state is published through LDS.  Branches whose only block
-// is one piece are packed four to a workgroup, one per wave.
+// and q, keeps whole 64x64 states in its own registers, and computes every
+// output feature of its tokens, so the chunk loop has no workgroup barrier.
+// Branches whose only block is one piece are packed into workgroups of their
+// own, four waves of them: two branches of at most one chunk share a wave,
+// a branch of two chunks has one alone.
 //
 // Arithmetic, identical in every form (same device functions, same order):
 //   A_w   = sum over the piece's chunks of K_c^T V_c (MFMA accumulation,
@@ -25,11 +26,15 @@
 //   own_j = 0 + A_b(0) + ... + A_b(j-1), the segment's state before block j;
 //   S_b   = seed (a branch: its view's total own; a shard branch: ext_state;
 //           a view: 0), then += own_j if j > 0;
-//   S     = S_b + E_w at the start of piece w; within the piece, after its
-//           first chunk, S += K_0^T V_0 (MFMA accumulation into S);
-//   O_c   = tril(Q_c K_c^T) V_c + Q_c S_hi + Q_c S_lo, with S = S_hi + S_lo
-//           split into two bf16 terms (the split keeps the state's fp32
+//   S     = S_b + E_w, the state piece w starts from;
+//   O_0   = tril(Q_0 K_0^T) V_0 + Q_0 S,
+//   O_1   = tril(Q_1 K_1^T) V_1 + (Q_1 K_0^T) V_0 + Q_1 S  (MFMA accumulation
+//           in that order; scores enter the value products as bf16, S as
+//           S_hi + S_lo, two bf16 terms, which keeps the state's fp32
 //           precision in the product at no memory cost).
+// The terms without S need only the piece's own q, k, v: a workgroup
+// computes them while the blocks before it publish their states, and adds
+// Q S once S_b is known.
 //
 // Forms (they differ only in how own_j and the seed reach a workgroup):
 //   three launches  states -> prefix (the shared prefix kernel, in place)
@@ -44,15 +49,19 @@
 //                   computes its outputs from the k and v it already holds.
 //                   k and v are read from HBM once per pass.
 //
-// Single-launch coordination.  Workgroups take tickets from a counter in the
-// workspace header, so a workgroup only ever waits for tickets taken before
-// its own (running workgroups): forward progress does not depend on how many
-// workgroups fit on the GPU.  Published states and flags are written and read
-// with device-coherent accesses (sc1), stores are drained (s_waitcnt) before
-// the flag that announces them, and every wait is bounded: past the spin
-// limit the workgroup records LA_ERR_TIMEOUT in the header and carries on,
-// so every wave reaches the end of the kernel.  The last workgroup to retire
-// clears the flags and resets the counters for the next pass.
+// Single-launch coordination.  A workgroup only waits for work that comes
+// before its own.  When the whole grid is resident on the device at once
+// (the launch checks the occupancy), the workgroup index is the work;
+// otherwise workgroups take tickets from a counter in the workspace header,
+// so a workgroup only ever waits for tickets taken before its own (running
+// workgroups): forward progress never depends on the dispatch order.
+// Published states and flags are written and read with device-coherent
+// accesses (sc1; a state published from the reader's own XCD is read through
+// that XCD's L2), stores are drained (s_waitcnt) before the flag that
+// announces them, and every wait is bounded: past the spin limit the
+// workgroup records LA_ERR_TIMEOUT in the header and carries on, so every
+// wave reaches the end of the kernel.  The last workgroup to retire clears
+// the flags and resets the counters for the next pass.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -293,38 +302,6 @@ __device__ __forceinline__ void load_chunk_kv(ChunkKV& r, const PArgs& a, int64_
     }
 }
 
-// q of a chunk as the B operand of the products over d_k: lane 16 g + c
-// holds token 16 tb + c; loaded as 16 contiguous bytes (features
-// 32 ks + 8 g .. + 7) and regrouped below.
-struct ChunkQ {
-    u32x4 q[4][2];
-};
-__device__ __forceinline__ void load_chunk_q(ChunkQ& r, const PArgs& a, int64_t tok0, int rows,
-                                             int h, int g, int c16) {
-    const auto rq = chunk_rsrc(a.q, tok0 * a.H * PD, 2, rows, a.H, PD);
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-            r.q[tb][ks] =
-                buf_load16(rq, uint32_t((((16 * tb + c16) * a.H + h) * PD + 32 * ks + 8 * g) * 2));
-}
-
-// k-slot order of every product over d_k: in a K = 32 step ks, lane group g
-// holds features 32 ks + 4 g .. + 3 (elements 0..3) and 32 ks + 16 + 4 g ..
-// + 3 (elements 4..7) -- the order in which a state's accumulator tiles
-// (kb = 2 ks, 2 ks + 1) hold their rows, so the state feeds the product
-// straight from registers.  A contiguous 16-byte piece (features 8 g .. + 7
-// of the step) becomes that order with two lane swaps: swapping odd 16-lane
-// rows of the low halves with even rows of the high halves, then the upper
-// 32 lanes of the low halves with the lower 32 of the high halves.
-__device__ __forceinline__ u32x4 to_slot_order(u32x4 x) {
-    const auto r0 = __builtin_amdgcn_permlane16_swap(x[0], x[2], false, false);
-    const auto r1 = __builtin_amdgcn_permlane16_swap(x[1], x[3], false, false);
-    const auto s0 = __builtin_amdgcn_permlane32_swap(r0[0], r0[1], false, false);
-    const auto s1 = __builtin_amdgcn_permlane32_swap(r1[0], r1[1], false, false);
-    return u32x4{s0[0], s1[0], s0[1], s1[1]};
-}
 // The inverse: slot order (features 4 g .. and 16 + 4 g .. of a 32-feature
 // half) back to 16 contiguous bytes (features 8 g .. + 7).
 __device__ __forceinline__ u32x4 from_slot_order(u32x4 x) {
@@ -369,24 +346,43 @@ __device__ __forceinline__ void acc_kv(State& S, const uint16_t* sK, const uint1
     }
 }
 
-// Outputs of a chunk are built in two parts: the part local to the piece,
-//   O_loc = tril(Q K^T) V + Q S_loc   (S_loc: the piece's own state before
-//                                      the chunk, from inside its block),
-// which needs nothing from other workgroups, and the part of the state the
-// block starts from, O += Q S_b, added once S_b is known.  O^T is kept in
-// fp32 MFMA accumulators: tile tb * 4 + fb, lane 16 g + c: token 16 tb + c,
-// features 16 fb + 4 g .. + 3; written as bf16 (round to nearest even).
+// Outputs of a piece are built in two parts.  The part within the piece,
+//   O_c = tril(Q_c K_c^T) V_c               (each chunk c),
+//   O_1 += (Q_1 K_0^T) V_0                   (chunk 1 sees all of chunk 0),
+// needs nothing but the piece's own q, k and v, so it is computed while the
+// workgroups before it publish their states.  The state the piece starts
+// from, S = S_b + E_p (the block's starting state plus the pieces before it
+// in the block), enters once the look-back has S_b: O_c += Q_c S.  O^T is kept
+// in fp32 MFMA accumulators: tile tb * 4 + fb, lane 16 g + c: token 16 tb + c,
+// features 16 fb + 4 g .. + 3; written as bf16 (round to nearest even).  The
+// scores P = Q K^T of a chunk and across the two chunks enter their products
+// as bf16 (round to nearest even), the state as two bf16 terms.
 typedef f32x4 OTiles[16];
 
-// q of a chunk in k-slot order (the B operand of the products over d_k).
+// q of a chunk as the B operand of the products over d_k, in k-slot order:
+// lane 16 g + c holds token 16 tb + c; in a K = 32 step ks, features
+// 32 ks + 4 g .. + 3 (elements 0..3) and 32 ks + 16 + 4 g .. + 3 (elements
+// 4..7) -- the order in which a state's accumulator tiles (kb = 2 ks,
+// 2 ks + 1) hold their rows, so a state feeds the products straight from
+// registers.  Loaded as two 8-byte pieces per step.
 struct QSlots {
     u32x4 q[4][2];
 };
-__device__ __forceinline__ void q_slots(const ChunkQ& raw, QSlots& qs) {
+__device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+__device__ __forceinline__ void load_q_slots(QSlots& qs, const PArgs& a, int64_t tok0, int rows,
+                                             int h, int g, int c16) {
+    const auto rq = chunk_rsrc(a.q, tok0 * a.H * PD, 2, rows, a.H, PD);
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) qs.q[tb][ks] = to_slot_order(raw.q[tb][ks]);
+        for (int ks = 0; ks < 2; ++ks) {
+            const uint32_t off =
+                uint32_t((((16 * tb + c16) * a.H + h) * PD + 32 * ks + 4 * g) * 2);
+            const u32x2 x = buf_load8(rq, off), y = buf_load8(rq, off + 32);
+            qs.q[tb][ks] = u32x4{x[0], x[1], y[0], y[1]};
+        }
 }
 
 // S^T as A operands, split into two bf16 terms S = hi + lo (the split keeps
@@ -423,53 +419,69 @@ __device__ __forceinline__ void add_qs(OTiles& O, const SSplit& sp, const QSlots
             }
 }
 
-// Local outputs of tokens 16 TB .. 16 TB + 15 of the staged chunk.
-template <int TB, bool WITH_S>
-__device__ __forceinline__ void local_tokens(OTiles& O, const u32x4 (&kr)[4][2],
-                                             const u32x4 (&vt)[4][2], const SSplit& sp,
-                                             const u32x4 (&qt)[2], int g, int c16) {
-    f32x4 p[TB + 1];
+// Scores of 16 queries (slot-order q, B operand) against the 4 key tiles
+// of a chunk (K rows in slot order, A operands) -> P^T as bf16 B operands of
+// the value product: pb[pp] covers key tiles 2 pp, 2 pp + 1.  Key tiles past
+// NK - 1 are not computed (zero); with DIAG the last one is masked causally
+// (key u <= query t).
+template <int NK, bool DIAG>
+__device__ __forceinline__ void score_tiles(u32x4 (&pb)[2], const u32x4 (&kr)[4][2],
+                                            const u32x4 (&qt)[2], int g, int c16) {
+    f32x4 p[NK];
 #pragma unroll
-    for (int ub = 0; ub <= TB; ++ub) {
+    for (int ub = 0; ub < NK; ++ub) {
         p[ub] = mfma_bf16(kr[ub][0], qt[0], zero4());
         p[ub] = mfma_bf16(kr[ub][1], qt[1], p[ub]);
     }
+    if constexpr (DIAG) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)   // causal mask of the diagonal tile: key u <= query t
-        if (4 * g + j > c16) p[TB][j] = 0.f;
-    u32x4 pb[TB / 2 + 1];
+        for (int j = 0; j < 4; ++j)
+            if (4 * g + j > c16) p[NK - 1][j] = 0.f;
+    }
 #pragma unroll
-    for (int pp = 0; pp <= TB / 2; ++pp) {
+    for (int pp = 0; pp < (NK + 1) / 2; ++pp) {
         const f32x4 x = p[2 * pp];
-        const f32x4 y = 2 * pp + 1 <= TB ? p[2 * pp + 1] : zero4();
+        const f32x4 y = 2 * pp + 1 < NK ? p[2 * pp + 1] : zero4();
         pb[pp] = u32x4{cvt_bf2(x[0], x[1]), cvt_bf2(x[2], x[3]), cvt_bf2(y[0], y[1]),
                        cvt_bf2(y[2], y[3])};
     }
+}
+
+// O (tokens 16 TB ..) = tril(Q K^T) V within the staged chunk.
+template <int TB>
+__device__ __forceinline__ void intra_tokens(OTiles& O, const u32x4 (&kr)[4][2],
+                                             const u32x4 (&vt)[4][2], const u32x4 (&qt)[2],
+                                             int g, int c16) {
+    u32x4 pb[2];
+    score_tiles<TB + 1, true>(pb, kr, qt, g, c16);
 #pragma unroll
     for (int fb = 0; fb < 4; ++fb) {
         f32x4 o = zero4();
 #pragma unroll
         for (int pp = 0; pp <= TB / 2; ++pp) o = mfma_bf16(vt[fb][pp], pb[pp], o);
-        if constexpr (WITH_S) {
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                o = mfma_bf16(sp.hi[fb][ks], qt[ks], o);
-                o = mfma_bf16(sp.lo[fb][ks], qt[ks], o);
-            }
-        }
         O[TB * 4 + fb] = o;
     }
 }
 
-// O = tril(Q K^T) V (+ Q S_loc when WITH_S) of the staged chunk.
-template <bool WITH_S>
-__device__ __forceinline__ void chunk_local(OTiles& O, const State& S, const uint16_t* sK,
-                                            const uint16_t* sV, const QSlots& qs, int g,
-                                            int c16) {
-    SSplit sp;
-    if constexpr (WITH_S) split_state(S, sp);
-    // K rows in slot order (two 8-byte reads), V^T fragments in token order
-    u32x4 kr[4][2], vt[4][2];
+// O (tokens 16 TB .. of chunk 1) += (Q_1 K_0^T) V_0: every key of chunk 0.
+template <int TB>
+__device__ __forceinline__ void cross_tokens(OTiles& O, const u32x4 (&kr0)[4][2],
+                                             const u32x4 (&vt0)[4][2], const u32x4 (&qt)[2],
+                                             int g, int c16) {
+    u32x4 pb[2];
+    score_tiles<4, false>(pb, kr0, qt, g, c16);
+#pragma unroll
+    for (int fb = 0; fb < 4; ++fb) {
+        O[TB * 4 + fb] = mfma_bf16(vt0[fb][0], pb[0], O[TB * 4 + fb]);
+        O[TB * 4 + fb] = mfma_bf16(vt0[fb][1], pb[1], O[TB * 4 + fb]);
+    }
+}
+
+// K rows in slot order (two 8-byte reads) and V^T fragments in token order
+// of the staged chunk: the operands of its score and value products.
+__device__ __forceinline__ void chunk_operands(u32x4 (&kr)[4][2], u32x4 (&vt)[4][2],
+                                               const uint16_t* sK, const uint16_t* sV, int g,
+                                               int c16) {
 #pragma unroll
     for (int ub = 0; ub < 4; ++ub)
 #pragma unroll
@@ -478,10 +490,25 @@ __device__ __forceinline__ void chunk_local(OTiles& O, const State& S, const uin
             kr[ub][ks] = cat2(lds_u32x2(p), lds_u32x2(p + 16));
             vt[ub][ks] = tr_frag(sV, PLD, 16 * ub, ks, g, c16);
         }
-    local_tokens<0, WITH_S>(O, kr, vt, sp, qs.q[0], g, c16);
-    local_tokens<1, WITH_S>(O, kr, vt, sp, qs.q[1], g, c16);
-    local_tokens<2, WITH_S>(O, kr, vt, sp, qs.q[2], g, c16);
-    local_tokens<3, WITH_S>(O, kr, vt, sp, qs.q[3], g, c16);
+}
+
+// O = tril(Q K^T) V of the staged chunk; its operands are left in kr, vt.
+__device__ __forceinline__ void chunk_intra(OTiles& O, u32x4 (&kr)[4][2], u32x4 (&vt)[4][2],
+                                            const uint16_t* sK, const uint16_t* sV,
+                                            const QSlots& qs, int g, int c16) {
+    chunk_operands(kr, vt, sK, sV, g, c16);
+    intra_tokens<0>(O, kr, vt, qs.q[0], g, c16);
+    intra_tokens<1>(O, kr, vt, qs.q[1], g, c16);
+    intra_tokens<2>(O, kr, vt, qs.q[2], g, c16);
+    intra_tokens<3>(O, kr, vt, qs.q[3], g, c16);
+}
+__device__ __forceinline__ void chunk_cross(OTiles& O, const u32x4 (&kr0)[4][2],
+                                            const u32x4 (&vt0)[4][2], const QSlots& qs, int g,
+                                            int c16) {
+    cross_tokens<0>(O, kr0, vt0, qs.q[0], g, c16);
+    cross_tokens<1>(O, kr0, vt0, qs.q[1], g, c16);
+    cross_tokens<2>(O, kr0, vt0, qs.q[2], g, c16);
+    cross_tokens<3>(O, kr0, vt0, qs.q[3], g, c16);
 }
 
 // Rows tok0 .. tok0 + rows - 1 of out from O (16 contiguous bytes per lane
@@ -501,23 +528,26 @@ __device__ __forceinline__ void store_chunk(const OTiles& O, const PArgs& a, int
         }
 }
 
-// The local part of one wave's piece (up to two chunks at tok0 ..
-// tok0 + ntok): O0, O1 from the piece's state before it, S (updated: the
-// state after chunk 0 on return).  Chunk 0's k / v are staged on entry,
-// chunk 1's are in r1.
-__device__ __forceinline__ void piece_local(OTiles& O0, OTiles& O1, State& S, uint16_t* sK,
-                                            uint16_t* sV, const ChunkKV& r1, const QSlots& qs0,
-                                            const QSlots& qs1, int ntok, int g, int c16,
-                                            int lane) {
-    if (ntok <= 0) return;
-    chunk_local<true>(O0, S, sK, sV, qs0, g, c16);
-    if (ntok > kChunk) {
-        acc_kv(S, sK, sV, g, c16);
+// The part of one wave's piece (up to two chunks) within the piece: O0, O1.
+// Chunk 0's k / v are staged on entry; chunk 1's are in r1 (`same` false:
+// chunk 1 belongs to another branch and sees nothing of chunk 0).
+__device__ __forceinline__ void piece_intra(OTiles& O0, OTiles& O1, uint16_t* sK, uint16_t* sV,
+                                            const ChunkKV& r1, const QSlots& qs0,
+                                            const QSlots& qs1, int n0, int n1, bool same, int g,
+                                            int c16, int lane) {
+    if (n0 <= 0) return;
+    u32x4 kr0[4][2], vt0[4][2];
+    chunk_intra(O0, kr0, vt0, sK, sV, qs0, g, c16);
+    if (n1 > 0) {
         // every lane's reads of chunk 0 are done before chunk 1 overwrites it
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
         __builtin_amdgcn_wave_barrier();
         stage_chunk(r1, sK, sV, lane);
-        chunk_local<true>(O1, S, sK, sV, qs1, g, c16);
+        {
+            u32x4 kr1[4][2], vt1[4][2];
+            chunk_intra(O1, kr1, vt1, sK, sV, qs1, g, c16);
+        }
+        if (same) chunk_cross(O1, kr0, vt0, qs1, g, c16);
     }
 }
 
@@ -668,7 +698,7 @@ __global__ __launch_bounds__(kThreads) void piece_kernel(PArgs a) {
             const int64_t ptok0 = int64_t(B.tok0) + w * 2 * kChunk;
             const int pntok = min(2 * kChunk, B.ntok - w * 2 * kChunk);   // <= 0: no piece
             ChunkKV r0, r1;
-            ChunkQ q0, q1;
+            QSlots qs0, qs1;
             load_chunk_kv(r0, a, ptok0, pntok, h, lane);
             load_chunk_kv(r1, a, ptok0 + kChunk, pntok - kChunk, h, lane);
 
@@ -690,8 +720,8 @@ __global__ __launch_bounds__(kThreads) void piece_kernel(PArgs a) {
             // after this one waits for the state they give)
             __builtin_amdgcn_sched_barrier(0);
             if constexpr (MODE != kStates) {
-                load_chunk_q(q0, a, ptok0, pntok, h, g, c16);
-                load_chunk_q(q1, a, ptok0 + kChunk, pntok - kChunk, h, g, c16);
+                load_q_slots(qs0, a, ptok0, pntok, h, g, c16);
+                load_q_slots(qs1, a, ptok0 + kChunk, pntok - kChunk, h, g, c16);
             }
             // in-block prefix over the pieces: E_w and A_b (wave np - 1)
             State E, Ab;
@@ -752,18 +782,11 @@ __global__ __launch_bounds__(kThreads) void piece_kernel(PArgs a) {
                         }
                     }
                 }
-                // the local part of the outputs (from the piece's state
-                // inside the block) while predecessors finish theirs
-                QSlots qs0, qs1;
-                q_slots(q0, qs0);
-                q_slots(q1, qs1);
+                // the part of the outputs within each piece, computed while
+                // the blocks before finish publishing
                 OTiles O0, O1;
-                {
-                    State S;
-#pragma unroll
-                    for (int t = 0; t < kTiles; ++t) S[t] = E[t];
-                    piece_local(O0, O1, S, sK, sV, r1, qs0, qs1, pntok, g, c16, lane);
-                }
+                piece_intra(O0, O1, sK, sV, r1, qs0, qs1, pntok, pntok - kChunk, true, g, c16,
+                            lane);
                 if constexpr (MODE == kFused) {
                     if (B.j > 0) {
                         // nearest predecessor with an inclusive prefix, then
@@ -822,15 +845,25 @@ __global__ __launch_bounds__(kThreads) void piece_kernel(PArgs a) {
                 __syncthreads();
                 if (w == np - 1 && (B.slot >= 0 || B.final_row >= 0) &&
                     (MODE == kFused || MODE == kOut2)) {
-                    // inclusive prefix of this block: own + A_b
+                    // inclusive prefix of this block: own + A_b.  A_b is read
+                    // back from its slot (this wave published it in one
+                    // launch; the states launch wrote it in the two-launch
+                    // form), which frees its registers for the products
                     State P;
-                    if (B.j > 0) {
-                        get_state(X, 0, P, lane);
+                    {
+                        const float* ab = MODE == kFused && B.j == 0 ? a.pslots : a.aslots;
+                        const auto r = slot_rsrc(ab, B.slot, H, h);
 #pragma unroll
-                        for (int t = 0; t < kTiles; ++t) P[t] = P[t] + Ab[t];
+                        for (int t = 0; t < kTiles; ++t) P[t] = slot_load<kAuxCoherent>(r, t, lane);
+                    }
+                    if (B.j > 0) {
+                        State own;
+                        get_state(X, 0, own, lane);
+#pragma unroll
+                        for (int t = 0; t < kTiles; ++t) P[t] = own[t] + P[t];
                     } else {
 #pragma unroll
-                        for (int t = 0; t < kTiles; ++t) P[t] = zero4() + Ab[t];
+                        for (int t = 0; t < kTiles; ++t) P[t] = zero4() + P[t];
                     }
                     if (MODE == kFused && B.slot >= 0 && B.j > 0) {
                         store_state<kAuxCoherent>(P, a.pslots, B.slot, H, h, lane);
@@ -842,13 +875,18 @@ __global__ __launch_bounds__(kThreads) void piece_kernel(PArgs a) {
                         store_rows_state(P, a.final_state + (int64_t(B.final_row) * H + h) * PD * PD,
                                          g, c16);
                 }
-                // O += Q S_b, S_b the state the block starts from
-                if ((has_seed || B.j > 0) && pntok > 0) {
+                // O += Q S, S = S_b + E_p: the block's starting state and the
+                // pieces before this one in the block
+                if (pntok > 0 && (has_seed || B.j > 0 || w >= 1)) {
                     SSplit sp;
                     {
-                        State Sb;
-                        get_state(X, 1, Sb, lane);
-                        split_state(Sb, sp);
+                        State S;
+                        get_state(X, 1, S, lane);
+                        if (!has_seed && B.j == 0) zero_state(S);
+                        if (w >= 1)
+#pragma unroll
+                            for (int t = 0; t < kTiles; ++t) S[t] = S[t] + E[t];
+                        split_state(S, sp);
                     }
                     add_qs(O0, sp, qs0);
                     if (pntok > kChunk) add_qs(O1, sp, qs1);
@@ -867,32 +905,17 @@ __global__ __launch_bounds__(kThreads) void piece_kernel(PArgs a) {
                 const int64_t t1 = b1 >= 0 ? int64_t(B1.tok0) : int64_t(B.tok0) + kChunk;
                 const int n1 = b1 >= 0 ? B1.ntok : B.ntok - kChunk;
                 ChunkKV r0, r1;
-                ChunkQ q0, q1;
+                QSlots qs0, qs1;
                 load_chunk_kv(r0, a, B.tok0, B.ntok, h, lane);
                 load_chunk_kv(r1, a, t1, n1, h, lane);
-                load_chunk_q(q0, a, B.tok0, B.ntok, h, g, c16);
-                load_chunk_q(q1, a, t1, n1, h, g, c16);
-                QSlots qs0, qs1;
-                q_slots(q0, qs0);
-                q_slots(q1, qs1);
+                load_q_slots(qs0, a, B.tok0, B.ntok, h, g, c16);
+                load_q_slots(qs1, a, t1, n1, h, g, c16);
                 // local parts first (a branch's own tokens, from a zero
                 // state), then each branch's seed
                 OTiles O0, O1;
                 stage_chunk(r0, sK, sV, lane);
-                {
-                    State S;
-                    zero_state(S);
-                    chunk_local<false>(O0, S, sK, sV, qs0, g, c16);
-                    if (n1 > 0) {
-                        if (b1 < 0) acc_kv(S, sK, sV, g, c16);   // the branch's chunk 1
-                        // every lane's reads of chunk 0 are done before chunk 1
-                        // overwrites it
-                        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-                        __builtin_amdgcn_wave_barrier();
-                        stage_chunk(r1, sK, sV, lane);
-                        chunk_local<true>(O1, S, sK, sV, qs1, g, c16);
-                    }
-                }
+                piece_intra(O0, O1, sK, sV, r1, qs0, qs1, min(B.ntok, kChunk), n1, b1 < 0, g, c16,
+                            lane);
                 {
                     SSplit sp;
                     {
