@@ -865,7 +865,14 @@ __global__ __launch_bounds__(kThreads) void piece_kernel(PArgs a) {
 #pragma unroll
                         for (int t = 0; t < kTiles; ++t) P[t] = zero4() + P[t];
                     }
-                    if (MODE == kFused && B.slot >= 0 && B.j > 0) {
+                    // published where a look-back can use it: a view's total
+                    // (branches' seed), and every block when the work comes by
+                    // ticket (later blocks may start after this one ends); when
+                    // the whole grid runs at once every look-back runs while
+                    // its predecessors' prefixes are still being formed, and
+                    // finds its segment's first block
+                    if (MODE == kFused && B.slot >= 0 && B.j > 0 &&
+                        (a.ordered || B.final_row >= 0)) {
                         store_state<kAuxCoherent>(P, a.pslots, B.slot, H, h, lane);
                         drain_stores();
                         if (lane == 0)
