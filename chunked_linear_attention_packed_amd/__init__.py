@@ -121,6 +121,10 @@ def load_library():
     lib.la_cache_count.argtypes = [ctypes.c_void_p, _I32P]
     lib.la_attn_plan.argtypes = [ctypes.c_int32, _I32P, _I32P, ctypes.c_int32, _I32P, _I32P,
                                  _I32P]
+    lib.la_attn_plan_ext.argtypes = [ctypes.c_int32, _I32P, _I32P, ctypes.c_int32, _I32P, _I32P,
+                                     ctypes.c_int32, _I32P, _I32P]
+    lib.la_export_view_kv.argtypes = [_P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                      ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P, _P]
     lib.la_attn_packed.argtypes = [_P, _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                    ctypes.c_int32, ctypes.c_float, _P, ctypes.c_int32,
                                    ctypes.c_int32, _P, _P, ctypes.c_int32, _P, _P]
@@ -131,7 +135,7 @@ def load_library():
                "la_scan_packed_noalloc", "la_scan_status",
                "la_scan_launches", "la_choose_block_chunks", "la_export_view_state", "la_cache_create", "la_cache_destroy",
                "la_cache_lookup", "la_cache_reserve", "la_cache_erase", "la_cache_count",
-               "la_attn_plan", "la_attn_packed"):
+               "la_attn_plan", "la_attn_plan_ext", "la_attn_packed", "la_export_view_kv"):
         getattr(lib, fn).restype = ctypes.c_int32
     _lib = lib
     return lib
@@ -447,14 +451,41 @@ def export_view_state(final_state, view_row, dst=None, stream=None):
     return dst
 
 
-class ViewStateCache:
-    """Device pool of view states [capacity, H, d, d] fp32 with the library's
-    least-recently-used directory (la_cache_*), for branch shards that start
-    from a cached view (section "Long Requests").  `pool` is the ext_state of
-    shard passes; `lookup` gives the row to pass as ext_row.  Device copies go
-    on the caller's stream; not thread-safe."""
+def export_view_kv(k, v, tok0, n_tok, dst_k, dst_v, stream=None):
+    """Copy tokens tok0 .. tok0 + n_tok - 1 of k and v ([T, H, d]) into
+    dst_k, dst_v ([n_tok, H, d], e.g. a K/V pool row's region) on the device."""
+    lib = load_library()
+    if k.dim() != 3 or v.shape != k.shape or k.dtype != v.dtype:
+        raise ValueError("k, v: [T, H, d] of one dtype")
+    T, H, d = k.shape
+    if not (k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("k, v must be contiguous")
+    for name, t in (("dst_k", dst_k), ("dst_v", dst_v)):
+        _check_tensor(name, t, (n_tok, H, d), k.dtype, k.device)
+    _check("la_export_view_kv",
+           lib.la_export_view_kv(ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
+                                 _dtype_code(k), T, H, d, tok0, n_tok,
+                                 ctypes.c_void_p(dst_k.data_ptr()),
+                                 ctypes.c_void_p(dst_v.data_ptr()), _stream_ptr(stream, k.device)))
 
-    def __init__(self, capacity, heads, d, device="cuda"):
+
+class ViewStateCache:
+    """The view cache of a node (section "Long Requests"): for each cached view,
+    its linear-attention state and, when kv_tokens > 0, the K/V of its softmax
+    layers, in device pools with the library's least-recently-used directory
+    (la_cache_*), so branch shards skip their view.
+
+    pool   [capacity, H, d, d] fp32: the ext_state of shard passes (lookup
+           gives the row to pass as ext_row);
+    kv_k, kv_v   [kv_layers, capacity * kv_tokens, H, d]: row r of the
+           directory owns token rows r * kv_tokens .. of each layer; a shard's
+           attention names them with kv_extent (ext_start / ext_len of
+           attn_plan, ext_tokens = capacity * kv_tokens).
+
+    Device copies go on the caller's stream; not thread-safe."""
+
+    def __init__(self, capacity, heads, d, device="cuda", kv_tokens=0, kv_layers=1,
+                 kv_dtype=None):
         import torch
         lib = load_library()
         self._lib = lib
@@ -462,6 +493,18 @@ class ViewStateCache:
         _check("la_cache_create", lib.la_cache_create(capacity, ctypes.byref(self._h)))
         self.capacity, self.heads, self.d = capacity, heads, d
         self.pool = torch.empty((capacity, heads, d, d), dtype=torch.float32, device=device)
+        self.kv_tokens, self.kv_layers = int(kv_tokens), int(kv_layers)
+        self.kv_k = self.kv_v = None
+        if self.kv_tokens > 0:
+            shape = (self.kv_layers, capacity * self.kv_tokens, heads, d)
+            dt = torch.bfloat16 if kv_dtype is None else kv_dtype
+            self.kv_k = torch.empty(shape, dtype=dt, device=device)
+            self.kv_v = torch.empty(shape, dtype=dt, device=device)
+
+    @property
+    def _kv_len(self):
+        """row -> tokens of K/V held in that row's region."""
+        return self.__dict__.setdefault("_kv_rows", {})
 
     def lookup(self, view_id):
         """Pool row holding view_id's state (now most recent), or None."""
@@ -475,19 +518,54 @@ class ViewStateCache:
         _check("la_cache_reserve", self._lib.la_cache_reserve(self._h, view_id,
                                                               ctypes.byref(row),
                                                               ctypes.byref(ev)))
+        self._kv_len.pop(row.value, None)   # the row's K/V, if any, are not view_id's
         return row.value, (None if ev.value < 0 else ev.value)
 
-    def store(self, view_id, final_state, view_row, stream=None):
+    def store(self, view_id, final_state, view_row, stream=None, kv=None, view_tok0=0,
+              view_tokens=0):
         """Copy final_state[view_row] into view_id's pool row (evicting the
-        least recently used view if the pool is full); returns the row."""
+        least recently used view if the pool is full); with kv = [(k, v) per
+        softmax layer] ([T, H, d] of the pass that scored the view), also
+        copy the view's tokens view_tok0 .. view_tok0 + view_tokens - 1 of
+        each layer into the row's K/V region.  Returns the row."""
         if final_state.shape[1:] != self.pool.shape[1:]:
             raise ValueError("final_state rows must be [H, d, d] of this cache")
+        if kv is not None:
+            if self.kv_k is None:
+                raise ValueError("this cache holds no K/V (kv_tokens = 0)")
+            if len(kv) != self.kv_layers:
+                raise ValueError(f"kv needs {self.kv_layers} (k, v) pairs")
+            if not 1 <= view_tokens <= self.kv_tokens:
+                raise ValueError(f"view_tokens must be 1 .. {self.kv_tokens}")
         row, _ = self.reserve(view_id)
         export_view_state(final_state, view_row, self.pool[row], stream=stream)
+        if kv is not None:
+            a = row * self.kv_tokens
+            for layer, (k, v) in enumerate(kv):
+                export_view_kv(k, v, view_tok0, view_tokens,
+                               self.kv_k[layer, a:a + view_tokens],
+                               self.kv_v[layer, a:a + view_tokens], stream=stream)
+            self._kv_len[row] = int(view_tokens)
         return row
 
+    def kv_extent(self, view_id):
+        """(row, first token row, tokens) of view_id's cached K/V in kv_k /
+        kv_v, or None (not cached, or cached without K/V).  Marks the view
+        most recent."""
+        row = self.lookup(view_id)
+        if row is None or row not in self._kv_len:
+            return None
+        return row, row * self.kv_tokens, self._kv_len[row]
+
+    @property
+    def kv_pool_tokens(self):
+        return self.capacity * self.kv_tokens
+
     def erase(self, view_id):
+        row = self.lookup(view_id)
         _check("la_cache_erase", self._lib.la_cache_erase(self._h, view_id))
+        if row is not None:
+            self._kv_len.pop(row, None)
 
     def __len__(self):
         n = ctypes.c_int32()
@@ -523,19 +601,28 @@ class AttnPlan:
         return self._dev[key]
 
 
-def attn_plan(seg_offsets, branch_parent, ext_len=None):
+def attn_plan(seg_offsets, branch_parent, ext_len=None, ext_start=None, ext_tokens=None):
     """Segment table (parents >= 0 are views, -2 - e external view e of
-    ext_len[e] tokens) -> AttnPlan."""
+    ext_len[e] tokens) -> AttnPlan.  External views are concatenated in
+    ext_k / ext_v, or, with ext_start, view e starts at token row
+    ext_start[e] of arrays of ext_tokens rows (a K/V cache pool)."""
     lib = load_library()
     so, bp = _i32(seg_offsets), _i32(branch_parent)
     el = _i32([] if ext_len is None else ext_len)
+    if ext_start is None:
+        st, n_rows = None, int(el.sum())
+    else:
+        st = _i32(ext_start)
+        if len(st) != len(el) or ext_tokens is None:
+            raise ValueError("ext_start needs one entry per external view, and ext_tokens")
+        n_rows = int(ext_tokens)
     n = ctypes.c_int32()
-    _check("la_attn_plan", lib.la_attn_plan(len(bp), _ptr(so), _ptr(bp), len(el), _ptr(el),
-                                            None, ctypes.byref(n)))
+    _check("la_attn_plan", lib.la_attn_plan_ext(len(bp), _ptr(so), _ptr(bp), len(el), _ptr(el),
+                                                _ptr(st), n_rows, None, ctypes.byref(n)))
     items = np.zeros((n.value, 8), dtype=np.int32)
-    _check("la_attn_plan", lib.la_attn_plan(len(bp), _ptr(so), _ptr(bp), len(el), _ptr(el),
-                                            _ptr(items), ctypes.byref(n)))
-    return AttnPlan(int(so[-1]) if len(so) else 0, int(el.sum()), items)
+    _check("la_attn_plan", lib.la_attn_plan_ext(len(bp), _ptr(so), _ptr(bp), len(el), _ptr(el),
+                                                _ptr(st), n_rows, _ptr(items), ctypes.byref(n)))
+    return AttnPlan(int(so[-1]) if len(so) else 0, n_rows, items)
 
 
 def attn_packed(q, k, v, plan, scale, ext_k=None, ext_v=None, out=None, stream=None):

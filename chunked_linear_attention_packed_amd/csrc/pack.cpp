@@ -478,21 +478,28 @@ extern "C" la_status la_pack_pass(int32_t n_requests, const int32_t* view_len,
                             block_chunks, seg_offsets, branch_parent, view_ordinal, plan, info);
 }
 
-extern "C" la_status la_attn_plan(int32_t n_segments, const int32_t* seg_offsets,
-                                  const int32_t* branch_parent, int32_t n_ext,
-                                  const int32_t* ext_len, int32_t* items, int32_t* n_items) {
-    if (!n_items || n_segments < 0 || n_ext < 0) return LA_ERR_INVALID_ARG;
+extern "C" la_status la_attn_plan_ext(int32_t n_segments, const int32_t* seg_offsets,
+                                      const int32_t* branch_parent, int32_t n_ext,
+                                      const int32_t* ext_len, const int32_t* ext_start,
+                                      int32_t ext_tokens, int32_t* items, int32_t* n_items) {
+    if (!n_items || n_segments < 0 || n_ext < 0 || ext_tokens < 0) return LA_ERR_INVALID_ARG;
     if (n_segments > 0 && (!seg_offsets || !branch_parent)) return LA_ERR_INVALID_ARG;
     if (n_ext > 0 && !ext_len) return LA_ERR_INVALID_ARG;
     if (n_segments > 0 && seg_offsets[0] != 0) return LA_ERR_INVALID_ARG;
     for (int32_t s = 0; s < n_segments; ++s)
         if (seg_offsets[s + 1] <= seg_offsets[s]) return LA_ERR_INVALID_ARG;
-    // external views, concatenated: view e is tokens [ext_off[e], ext_off[e] + ext_len[e])
+    // external view e is tokens [ext_off[e], ext_off[e] + ext_len[e]) of ext_k / ext_v:
+    // at ext_start[e], or concatenated in order when ext_start is NULL; every
+    // view lies inside the ext_tokens rows the arrays hold
     std::vector<int64_t> ext_off(size_t(n_ext) + 1, 0);
     for (int32_t e = 0; e < n_ext; ++e) {
         if (ext_len[e] < 1) return LA_ERR_INVALID_ARG;
-        ext_off[e + 1] = ext_off[e] + ext_len[e];
-        if (ext_off[e + 1] > INT32_MAX) return LA_ERR_INVALID_ARG;
+        if (ext_start) {
+            if (ext_start[e] < 0) return LA_ERR_INVALID_ARG;
+            ext_off[e] = ext_start[e];
+        }
+        if (ext_off[e] + ext_len[e] > ext_tokens) return LA_ERR_INVALID_ARG;
+        if (!ext_start) ext_off[e + 1] = ext_off[e] + ext_len[e];
     }
     struct Item {
         int32_t w[8];
@@ -530,6 +537,20 @@ extern "C" la_status la_attn_plan(int32_t n_segments, const int32_t* seg_offsets
             std::memcpy(items + i * LA_ATTN_ITEM_WORDS, out[i].w, sizeof(out[i].w));
     *n_items = int32_t(out.size());
     return LA_OK;
+}
+
+extern "C" la_status la_attn_plan(int32_t n_segments, const int32_t* seg_offsets,
+                                  const int32_t* branch_parent, int32_t n_ext,
+                                  const int32_t* ext_len, int32_t* items, int32_t* n_items) {
+    if (n_ext < 0 || (n_ext > 0 && !ext_len)) return LA_ERR_INVALID_ARG;
+    int64_t total = 0;
+    for (int32_t e = 0; e < n_ext; ++e) {
+        if (ext_len[e] < 1) return LA_ERR_INVALID_ARG;
+        total += ext_len[e];
+        if (total > INT32_MAX) return LA_ERR_INVALID_ARG;
+    }
+    return la_attn_plan_ext(n_segments, seg_offsets, branch_parent, n_ext, ext_len, nullptr,
+                            int32_t(total), items, n_items);
 }
 
 extern "C" const char* la_status_string(la_status status) {

@@ -1238,7 +1238,7 @@ __global__ __launch_bounds__(O3::NT) void output_kernel_split(
 }
 
 // ===========================================================================
-// View-state export: plain vectorised copy of H*d_k*d_v floats.
+// View-state and view K/V export: plain vectorised copy of 16-byte pieces.
 // ===========================================================================
 __global__ __launch_bounds__(kThreads) void copy_kernel(const f32x4* __restrict__ src,
                                                         f32x4* __restrict__ dst, int64_t n4) {
@@ -1576,6 +1576,38 @@ extern "C" la_status la_export_view_state(const float* final_state, int32_t view
     hipLaunchKernelGGL(copy_kernel, dim3(grid), dim3(kThreads), 0,
                        static_cast<hipStream_t>(stream), reinterpret_cast<const f32x4*>(src),
                        reinterpret_cast<f32x4*>(dst), n4);
+    if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
+    return LA_OK;
+}
+
+extern "C" la_status la_export_view_kv(const void* k, const void* v, la_dtype dtype,
+                                       int32_t n_tokens, int32_t H, int32_t d, int32_t tok0,
+                                       int32_t n_tok, void* dst_k, void* dst_v, void* stream) {
+    if (!k || !v || !dst_k || !dst_v || H < 1 || n_tokens < 1 || tok0 < 0 || n_tok < 1 ||
+        int64_t(tok0) + n_tok > n_tokens)
+        return LA_ERR_INVALID_ARG;
+    if (dtype != LA_BF16 && dtype != LA_F32) return LA_ERR_UNSUPPORTED;
+    if (d != 64 && d != 128) return LA_ERR_UNSUPPORTED;
+    if (!aligned16(k) || !aligned16(v) || !aligned16(dst_k) || !aligned16(dst_v))
+        return LA_ERR_INVALID_ARG;
+    const int64_t row = int64_t(H) * d * (dtype == LA_BF16 ? 2 : 4);   // bytes per token
+    const int64_t bytes = row * n_tok;
+    const char* sk = static_cast<const char*>(k) + row * tok0;
+    const char* sv = static_cast<const char*>(v) + row * tok0;
+    char* dk = static_cast<char*>(dst_k);
+    char* dv = static_cast<char*>(dst_v);
+    auto overlap = [bytes](const char* a, const char* b) { return a < b + bytes && b < a + bytes; };
+    if (overlap(sk, dk) || overlap(sk, dv) || overlap(sv, dk) || overlap(sv, dv) ||
+        overlap(dk, dv))
+        return LA_ERR_INVALID_ARG;
+    const int64_t n4 = bytes / 16;
+    if ((n4 + kThreads - 1) / kThreads > int64_t(UINT32_MAX)) return LA_ERR_INVALID_ARG;
+    const unsigned grid = unsigned((n4 + kThreads - 1) / kThreads);
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    hipLaunchKernelGGL(copy_kernel, dim3(grid), dim3(kThreads), 0, st,
+                       reinterpret_cast<const f32x4*>(sk), reinterpret_cast<f32x4*>(dk), n4);
+    hipLaunchKernelGGL(copy_kernel, dim3(grid), dim3(kThreads), 0, st,
+                       reinterpret_cast<const f32x4*>(sv), reinterpret_cast<f32x4*>(dv), n4);
     if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
     return LA_OK;
 }

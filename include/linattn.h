@@ -421,6 +421,21 @@ la_status la_export_view_state(const float* final_state, int32_t view_row,
                                float* dst, void* stream);
 
 /*
+ * la_export_view_kv -- copy a view's keys and values (tokens tok0 ..
+ * tok0 + n_tok - 1 of a pass) into a cache pool, for the softmax-attention
+ * layers of later branch shards (section "Long Requests": nodes cache the
+ * view's linear-attention state and the K/V of its softmax layers).
+ *   k, v           device [n_tokens][H][d] (dtype LA_BF16 or LA_F32)
+ *   dst_k, dst_v   device [n_tok][H][d] each (e.g. a pool row's region); none
+ *                  of the four ranges may overlap another
+ * Errors: LA_ERR_INVALID_ARG (range, NULL, alignment, overlap),
+ * LA_ERR_UNSUPPORTED (dtype, d), LA_ERR_HIP.
+ */
+la_status la_export_view_kv(const void* k, const void* v, la_dtype dtype, int32_t n_tokens,
+                            int32_t H, int32_t d, int32_t tok0, int32_t n_tok, void* dst_k,
+                            void* dst_v, void* stream);
+
+/*
  * Tree-masked softmax attention over a packed pass -- the other layer type of
  * the pass (section "The Workload": Span-1 is mostly linear attention with a
  * few softmax-attention layers; branches attend to their view, never to each
@@ -450,6 +465,15 @@ la_status la_export_view_state(const float* final_state, int32_t view_row,
  * (LA_ATTN_NO_VIEW).  Items are ordered longest key range first.
  * Errors: LA_ERR_INVALID_ARG (bad table, parent or length).
  *
+ * la_attn_plan_ext -- la_attn_plan where external view e is tokens
+ * ext_start[e] .. ext_start[e] + ext_len[e] - 1 of arrays holding ext_tokens
+ * token rows (for a pool of cached view K/V: one region per cache row), or,
+ * with ext_start NULL, concatenated in order from row 0.
+ *   ext_start      host [n_ext] (>= 0) or NULL
+ *   ext_tokens     token rows of ext_k / ext_v; every view must lie inside
+ * Errors: as la_attn_plan, and LA_ERR_INVALID_ARG for a view outside
+ * ext_tokens.  la_attn_packed's n_ext_tokens is then ext_tokens.
+ *
  * la_attn_packed -- device: the attention of the pass on `stream`, one
  * workgroup per (item, head): online softmax over 64-key blocks (bf16 MFMA
  * for q.k and p.v, fp32 scores, running max and sums), out rounded to bf16.
@@ -472,6 +496,10 @@ la_status la_export_view_state(const float* final_state, int32_t view_row,
 la_status la_attn_plan(int32_t n_segments, const int32_t* seg_offsets,
                        const int32_t* branch_parent, int32_t n_ext, const int32_t* ext_len,
                        int32_t* items, int32_t* n_items);
+la_status la_attn_plan_ext(int32_t n_segments, const int32_t* seg_offsets,
+                           const int32_t* branch_parent, int32_t n_ext, const int32_t* ext_len,
+                           const int32_t* ext_start, int32_t ext_tokens, int32_t* items,
+                           int32_t* n_items);
 la_status la_attn_packed(const void* q, const void* k, const void* v, la_dtype dtype, int32_t H,
                          int32_t d_k, int32_t d_v, float scale, const int32_t* items,
                          int32_t n_items, int32_t n_tokens, const void* ext_k,

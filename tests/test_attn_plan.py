@@ -59,3 +59,33 @@ def test_plan_rejects_bad_tables(so, bp, ext):
         return
     with pytest.raises(la.LinAttnError):
         la.attn_plan(so, bp, ext)
+
+
+def test_plan_external_views_at_given_starts():
+    """la_attn_plan_ext: external view e at token row ext_start[e] of arrays
+    of ext_tokens rows (a K/V cache pool with one region per cache row); the
+    items equal the concatenated plan's except for each view's first row."""
+    so, bp, ext = [0, 30, 130, 200, 201], [-4, -1, 1, -2], [70, 5, 200]
+    starts = [1000, 3000, 0]
+    p = la.attn_plan(so, bp, ext, ext_start=starts, ext_tokens=4000)
+    want = _expected(so, bp, ext)
+    offs = np.concatenate([[0], np.cumsum(ext)])
+    for row in want:
+        if row[5] == la.LA_ATTN_EXT_VIEW:
+            e = int(np.flatnonzero(offs[:-1] == row[3])[0])
+            row[3] = starts[e]
+    assert np.array_equal(p.items, want)
+    assert p.n_ext_tokens == 4000
+    # concatenated starts give la_attn_plan's items exactly
+    q = la.attn_plan(so, bp, ext, ext_start=offs[:-1], ext_tokens=int(offs[-1]))
+    assert np.array_equal(q.items, la.attn_plan(so, bp, ext).items)
+
+
+@pytest.mark.parametrize("starts,rows", [([1000, 3000, 3801], 4000),   # view 2 past the end
+                                         ([-1, 0, 500], 4000),          # negative start
+                                         ([0, 0, 0], 199)])             # all past 199 rows
+def test_plan_external_starts_checked(starts, rows):
+    so, bp, ext = [0, 30, 130, 200, 201], [-4, -1, 1, -2], [70, 5, 200]
+    with pytest.raises(la.LinAttnError) as e:
+        la.attn_plan(so, bp, ext, ext_start=starts, ext_tokens=rows)
+    assert e.value.status == la.LA_ERR_INVALID_ARG

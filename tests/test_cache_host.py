@@ -125,3 +125,26 @@ def test_pack_ext_rows_of_view_requests_are_ignored():
     p = la.pack([10, 0], [1, 1], [3, 4], heads=1, ext_row=[-7, 5])
     assert list(p.branch_parent) == [-1, 0, -7]
     assert p.info.n_ext == 6
+
+
+def test_kv_extents_follow_the_rows():
+    """The K/V extent a cache row holds belongs to the view that stored it:
+    reserving the row for another view (eviction or a direct reserve) or
+    erasing the view forgets it, so a shard never reads another view's K/V."""
+    c = la.ViewStateCache.__new__(la.ViewStateCache)   # directory only, no device pool
+    lib = la.load_library()
+    c._lib = lib
+    c._h = la.ctypes.c_void_p()
+    assert lib.la_cache_create(2, la.ctypes.byref(c._h)) == la.LA_OK
+    c.capacity, c.kv_tokens = 2, 100
+    ra, _ = c.reserve(1)
+    c._kv_len[ra] = 40                       # as store(..., kv=...) records it
+    rb, _ = c.reserve(2)
+    c._kv_len[rb] = 70
+    assert c.kv_extent(1) == (ra, ra * 100, 40) and c.kv_extent(2) == (rb, rb * 100, 70)
+    rc, ev = c.reserve(3)                    # evicts the least recent: view 1
+    assert ev == 1 and rc == ra and c.kv_extent(3) is None and c.kv_extent(1) is None
+    assert c.kv_extent(2) == (rb, rb * 100, 70)
+    c.erase(2)
+    assert c.kv_extent(2) is None and rb not in c._kv_len
+    c.close()
