@@ -107,16 +107,54 @@ __global__ __launch_bounds__(64 * (4 / QT)) void attn_kernel_bf16(
         if (b >= nkb) rows = 0;                       // past the end: empty window
         if (from_ext && ext_k == nullptr) rows = 0;   // no external arrays given
     };
+    // This thread's share of a key block's staging, the same for every block:
+    // piece i is R tokens x 8 features of K or of V (wave-uniform choice), at
+    // byte goff[i] of the block's window (+ one head row per token) and at
+    // element loff[i] of its LDS tile (+ one tile row per token).
+    using KS = KVStage<D, D, R, NT>;
     BlkR<R> kv[NPER];
+    uint32_t goff[NPER];
+    int loff[NPER];
+    bool isv[NPER];
+    {
+        const int wbase = w * 64;
+#pragma unroll
+        for (int i = 0; i < NPER; ++i) {
+            const int b0 = wbase + i * NT;   // wave-uniform
+            isv[i] = b0 >= KS::NBK;
+            const int wb = (isv[i] ? b0 - KS::NBK : b0) + lane;
+            const int rg = wb / KS::NCGK, cg = wb % KS::NCGK;
+            goff[i] = uint32_t((((rg * R) * H + h) * D + cg * 8) * 2);
+            loff[i] = (rg * R) * (isv[i] ? LDV : LDR) + cg * 8;
+        }
+    }
+    const uint32_t row_bytes = uint32_t(H) * D * 2;
     auto load = [&](int b) {
         int64_t tok;
         int rows;
         bool fe;
         block_src(b, tok, rows, fe);
-        const uint16_t* kb = fe ? ext_k : k;
-        const uint16_t* vb = fe ? ext_v : v;
-        load_kv<D, D, R, NT, NPER>(kv, chunk_rsrc(kb, tok * row_elems, 2, rows, H, D),
-                                   chunk_rsrc(vb, tok * row_elems, 2, rows, H, D), 0, H, h);
+        const auto rk = chunk_rsrc(fe ? ext_k : k, tok * row_elems, 2, rows, H, D);
+        const auto rv = chunk_rsrc(fe ? ext_v : v, tok * row_elems, 2, rows, H, D);
+#pragma unroll
+        for (int i = 0; i < NPER; ++i) {
+            if constexpr (NPER * NT > KS::NBK + KS::NBV)
+                if (w * 64 + i * NT >= KS::NBK + KS::NBV) break;
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                kv[i].r[r] = buf_load16(isv[i] ? rv : rk, goff[i] + uint32_t(r) * row_bytes);
+        }
+    };
+    auto stage = [&]() {
+#pragma unroll
+        for (int i = 0; i < NPER; ++i) {
+            if constexpr (NPER * NT > KS::NBK + KS::NBV)
+                if (w * 64 + i * NT >= KS::NBK + KS::NBV) break;
+            uint16_t* dst = (isv[i] ? sV : sK) + loff[i];
+            const int ld = isv[i] ? LDV : LDR;
+#pragma unroll
+            for (int r = 0; r < R; ++r) *reinterpret_cast<u32x4*>(dst + r * ld) = kv[i].r[r];
+        }
     };
 
     // Online softmax with a lazily moved reference maximum: a lane's weights
@@ -246,14 +284,14 @@ __global__ __launch_bounds__(64 * (4 / QT)) void attn_kernel_bf16(
     load(order(0));
     int i = 0;
     for (; i < n_full; ++i) {
-        stage_kv_rows<D, D, R, NT, NPER>(kv, sK, sV);
+        stage();
         __syncthreads();
         load(order(i + 1));
         block(kChunk, false, std::false_type{});
         __syncthreads();
     }
     for (; i < nkb; ++i) {
-        stage_kv_rows<D, D, R, NT, NPER>(kv, sK, sV);
+        stage();
         __syncthreads();
         load(order(i + 1));
         const int b = order(i);
