@@ -45,9 +45,15 @@
 //                   decoupled look-back: the nearest predecessor that has
 //                   published its inclusive prefix, then the aggregates after
 //                   it, added left to right, so the bits do not depend on
-//                   timing), publishes its own inclusive prefix, then
-//                   computes its outputs from the k and v it already holds.
-//                   k and v are read from HBM once per pass.
+//                   timing), publishes its own inclusive prefix where a
+//                   later workgroup reads it (a view's total; every block
+//                   when the work comes by ticket), then computes its
+//                   outputs from the k and v it already holds.  A branch's
+//                   seed is its view's total, read once the view's last
+//                   block has published it, or, when the whole grid is
+//                   resident, summed by the branch's workgroup itself from
+//                   the view's block states (the same fold, so the same
+//                   bits).  k and v are read from HBM once per pass.
 //
 // Single-launch coordination.  A workgroup only waits for work that comes
 // before its own.  When the whole grid is resident on the device at once
@@ -560,10 +566,11 @@ __device__ __forceinline__ void piece_intra(OTiles& O0, OTiles& O1, uint16_t* sK
 template <int AUX>
 __device__ __forceinline__ void add_slots4(f32x4 (&acc)[4], const float* base, int first, int n,
                                            int H, int h, int w, int lane) {
+    // batch of 4 slots from s0; slots past n read an empty window (zeros,
+    // no memory access)
     auto load4 = [&](f32x4 (&x)[4][4], int s0) {
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-            // slots past n read an empty window (zeros, not added)
             const auto r = s0 + b < n ? slot_rsrc(base, first + s0 + b, H, h)
                                       : __builtin_amdgcn_make_buffer_rsrc(
                                             const_cast<float*>(base), (short)0, 0, 0x00020000);
@@ -571,20 +578,23 @@ __device__ __forceinline__ void add_slots4(f32x4 (&acc)[4], const float* base, i
             for (int i = 0; i < 4; ++i) x[b][i] = slot_load<AUX>(r, 4 * w + i, lane);
         }
     };
-    if (n <= 0) return;
-    f32x4 cur[4][4], nxt[4][4];
-    load4(cur, 0);
-    for (int s0 = 0; s0 < n; s0 += 4) {
-        if (s0 + 4 < n) load4(nxt, s0 + 4);
+    auto add4 = [&](const f32x4 (&x)[4][4], int s0) {
 #pragma unroll
         for (int b = 0; b < 4; ++b)
             if (s0 + b < n)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] += cur[b][i];
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) cur[b][i] = nxt[b][i];
+                for (int i = 0; i < 4; ++i) acc[i] += x[b][i];
+    };
+    if (n <= 0) return;
+    // two batches in flight, alternating buffers: each add waits only for
+    // its own batch (loads complete in order), while the next is loading
+    f32x4 xa[4][4], xb[4][4];
+    load4(xa, 0);
+    for (int s0 = 0; s0 < n; s0 += 8) {
+        load4(xb, s0 + 4);
+        add4(xa, s0);
+        load4(xa, s0 + 8);
+        add4(xb, s0 + 4);
     }
 }
 
@@ -717,11 +727,17 @@ __global__ __launch_bounds__(kThreads) void piece_kernel(PArgs a) {
             }
 
             // q is loaded once k and v are in (they come first: every block
-            // after this one waits for the state they give)
+            // after this one waits for the state they give).  The wave that
+            // publishes the block's state loads its q after the publication:
+            // the wait before the flag covers every load the wave has in
+            // flight, q included
             __builtin_amdgcn_sched_barrier(0);
+            const bool publisher = MODE == kFused && B.slot >= 0 && w == np - 1;
             if constexpr (MODE != kStates) {
-                load_q_slots(qs0, a, ptok0, pntok, h, g, c16);
-                load_q_slots(qs1, a, ptok0 + kChunk, pntok - kChunk, h, g, c16);
+                if (!publisher) {
+                    load_q_slots(qs0, a, ptok0, pntok, h, g, c16);
+                    load_q_slots(qs1, a, ptok0 + kChunk, pntok - kChunk, h, g, c16);
+                }
             }
             // in-block prefix over the pieces: E_w and A_b (wave np - 1)
             State E, Ab;
@@ -782,6 +798,10 @@ __global__ __launch_bounds__(kThreads) void piece_kernel(PArgs a) {
                         }
                     }
                 }
+                if (publisher) {
+                    load_q_slots(qs0, a, ptok0, pntok, h, g, c16);
+                    load_q_slots(qs1, a, ptok0 + kChunk, pntok - kChunk, h, g, c16);
+                }
                 // the part of the outputs within each piece, computed while
                 // the blocks before finish publishing
                 OTiles O0, O1;
@@ -813,7 +833,18 @@ __global__ __launch_bounds__(kThreads) void piece_kernel(PArgs a) {
                 if (B.seed >= 0) {
                     const PScan vs = a.scans[B.seed];
                     const int last = vs.first_slot + vs.n_slots - 1;
-                    if constexpr (MODE == kFused) {
+                    if (MODE == kFused && !a.ordered) {
+                        // every block of the view is running: sum its
+                        // states here rather than wait for its last block
+                        bool local;
+                        const int m = find_prefix(a, vs.first_slot, vs.n_slots, h, lane, xcd_tag(),
+                                                  local);
+                        if (__builtin_amdgcn_readfirstlane(int(local)))
+                            look_back<kAuxL2>(sin4, a, vs.first_slot, m, vs.n_slots, h, w, lane);
+                        else
+                            look_back<kAuxCoherent>(sin4, a, vs.first_slot, m, vs.n_slots, h, w,
+                                                    lane);
+                    } else if constexpr (MODE == kFused) {
                         const auto r = slot_rsrc(a.pslots, last, H, h);
                         if (wait_prefix(a, flag_ptr(a, last, h), xcd_tag())) {
 #pragma unroll
@@ -843,18 +874,22 @@ __global__ __launch_bounds__(kThreads) void piece_kernel(PArgs a) {
                 put_tiles4(X, 0, own4, w, lane);
                 put_tiles4(X, 1, sin4, w, lane);
                 __syncthreads();
-                if (w == np - 1 && (B.slot >= 0 || B.final_row >= 0) &&
-                    (MODE == kFused || MODE == kOut2)) {
-                    // inclusive prefix of this block: own + A_b.  A_b is read
-                    // back from its slot (this wave published it in one
-                    // launch; the states launch wrote it in the two-launch
-                    // form), which frees its registers for the products
+                // the block's inclusive prefix, where it is needed: a view's
+                // total (final_state), and the prefix later look-backs use
+                // when the work comes by ticket
+                const bool need_p = B.final_row >= 0 ||
+                                    (MODE == kFused && a.ordered && B.slot >= 0 && B.j > 0);
+                if (w == np - 1 && need_p && (MODE == kFused || MODE == kOut2)) {
+                    // own + A_b.  A_b is read back from its slot (this wave
+                    // published it in one launch; the states launch wrote it
+                    // in the two-launch form), which frees its registers for
+                    // the products
                     State P;
                     {
                         const float* ab = MODE == kFused && B.j == 0 ? a.pslots : a.aslots;
                         const auto r = slot_rsrc(ab, B.slot, H, h);
 #pragma unroll
-                        for (int t = 0; t < kTiles; ++t) P[t] = slot_load<kAuxCoherent>(r, t, lane);
+                        for (int t = 0; t < kTiles; ++t) P[t] = slot_load<kAuxL2>(r, t, lane);
                     }
                     if (B.j > 0) {
                         State own;
@@ -904,41 +939,78 @@ __global__ __launch_bounds__(kThreads) void piece_kernel(PArgs a) {
         } else if constexpr (MODE != kStates) {
             // packed branches: wave w takes block b_2w and, when there is one,
             // block b_2w+1 (then both are one chunk long), each from its seed
-            const int b0 = a.items[item].b[2 * w], b1 = a.items[item].b[2 * w + 1];
+            const PItem& it = a.items[item];
+            const int b0 = it.b[2 * w], b1 = it.b[2 * w + 1];
+            // when every branch of the pack starts from one view's total and
+            // the whole grid is resident, the four waves sum the view's
+            // states themselves (four tiles each) instead of waiting for the
+            // view's last block to publish it
+            int shared = -1;
+            if (MODE == kFused && !a.ordered) {
+                int sd = -1;
+                bool same = true;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int b = it.b[i];
+                    if (b >= 0) {
+                        const int x = a.blocks[b].seed;
+                        if (sd == -1) sd = x;
+                        same = same && x == sd && x >= 0;
+                    }
+                }
+                shared = same ? sd : -1;
+            }
+            const PBlock B = a.blocks[b0 >= 0 ? b0 : 0];
+            const PBlock B1 = b1 >= 0 ? a.blocks[b1] : B;
+            // chunk 1: the branch's second chunk, or the second branch
+            const int64_t t1 = b1 >= 0 ? int64_t(B1.tok0) : int64_t(B.tok0) + kChunk;
+            const int n1 = b1 >= 0 ? B1.ntok : B.ntok - kChunk;
+            OTiles O0, O1;
+            QSlots qs0, qs1;
             if (b0 >= 0) {
-                const PBlock B = a.blocks[b0];
-                const PBlock B1 = b1 >= 0 ? a.blocks[b1] : B;
-                // chunk 1: the branch's second chunk, or the second branch
-                const int64_t t1 = b1 >= 0 ? int64_t(B1.tok0) : int64_t(B.tok0) + kChunk;
-                const int n1 = b1 >= 0 ? B1.ntok : B.ntok - kChunk;
                 ChunkKV r0, r1;
-                QSlots qs0, qs1;
                 load_chunk_kv(r0, a, B.tok0, B.ntok, h, lane);
                 load_chunk_kv(r1, a, t1, n1, h, lane);
                 load_q_slots(qs0, a, B.tok0, B.ntok, h, g, c16);
                 load_q_slots(qs1, a, t1, n1, h, g, c16);
                 // local parts first (a branch's own tokens, from a zero
                 // state), then each branch's seed
-                OTiles O0, O1;
                 stage_chunk(r0, sK, sV, lane);
                 piece_intra(O0, O1, sK, sV, r1, qs0, qs1, min(B.ntok, kChunk), n1, b1 < 0, g, c16,
                             lane);
+            }
+            if (shared >= 0) {
+                const PScan vs = a.scans[shared];
+                f32x4 tot4[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) tot4[i] = zero4();
+                bool local;
+                const int m = find_prefix(a, vs.first_slot, vs.n_slots, h, lane, xcd_tag(), local);
+                if (__builtin_amdgcn_readfirstlane(int(local)))
+                    look_back<kAuxL2>(tot4, a, vs.first_slot, m, vs.n_slots, h, w, lane);
+                else
+                    look_back<kAuxCoherent>(tot4, a, vs.first_slot, m, vs.n_slots, h, w, lane);
+                put_tiles4(X, 0, tot4, w, lane);
+                __syncthreads();
+            }
+            if (b0 >= 0) {
+                SSplit sp;
                 {
-                    SSplit sp;
-                    {
-                        State Sb;
+                    State Sb;
+                    if (shared >= 0)
+                        get_state(X, 0, Sb, lane);
+                    else
                         load_seed<MODE>(Sb, a, B.seed, h, g, c16, lane);
+                    split_state(Sb, sp);
+                }
+                add_qs(O0, sp, qs0);
+                if (n1 > 0) {
+                    if (b1 >= 0 && B1.seed != B.seed) {
+                        State Sb;
+                        load_seed<MODE>(Sb, a, B1.seed, h, g, c16, lane);
                         split_state(Sb, sp);
                     }
-                    add_qs(O0, sp, qs0);
-                    if (n1 > 0) {
-                        if (b1 >= 0 && B1.seed != B.seed) {
-                            State Sb;
-                            load_seed<MODE>(Sb, a, B1.seed, h, g, c16, lane);
-                            split_state(Sb, sp);
-                        }
-                        add_qs(O1, sp, qs1);
-                    }
+                    add_qs(O1, sp, qs1);
                 }
                 store_chunk(O0, a, B.tok0, min(B.ntok, kChunk), h, g, c16);
                 if (n1 > 0) store_chunk(O1, a, t1, n1, h, g, c16);
