@@ -19,7 +19,7 @@
 
 namespace {
 
-constexpr int32_t kPlanVersion = 4;
+constexpr int32_t kPlanVersion = 5;
 
 // Piece path (d = 64, bf16): blocks of LA_PIECE_BLOCK_CHUNKS chunks, each cut
 // into pieces of LA_PIECE_CHUNKS chunks, one per wave of a 4-wave workgroup.
@@ -302,12 +302,15 @@ la_status plan_impl(int32_t n_seg, const int32_t* seg_offsets, const int32_t* br
                     if (pack) {
                         packs.add(pblock, len);
                     } else {
+                        // a block item carries a copy of its block, so a
+                        // workgroup reads one record before its first load
                         int32_t* it = pit;
-                        std::memset(it, 0, sizeof(int32_t) * LA_PLAN_ITEM_WORDS);
                         it[0] = LA_ITEM_BLOCK;
                         it[1] = 1;
                         it[2] = pblock;
-                        for (int b = 1; b < 2 * kPackWaves; ++b) it[2 + b] = -1;
+                        it[3] = -1;
+                        std::memcpy(it + 4, pb - LA_PLAN_BLOCK_WORDS,
+                                    sizeof(int32_t) * LA_PLAN_BLOCK_WORDS);
                         pit += LA_PLAN_ITEM_WORDS;
                     }
                     ++pblock;

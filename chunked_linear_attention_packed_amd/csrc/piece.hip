@@ -100,6 +100,11 @@ struct PBlock {
 struct PItem {
     int kind, n, b[8], pad0, pad1;
 };
+struct PItemBlock {                // a block item: its block copied in
+    int kind, n, b0, unused;
+    PBlock blk;
+};
+static_assert(sizeof(PItem) == sizeof(PItemBlock), "one item size");
 struct PScan {
     int first_slot, n_slots, final_row, seg;
 };
@@ -680,16 +685,29 @@ __global__ __launch_bounds__(kThreads) void piece_kernel(PArgs a) {
     uint16_t* sV = sStage[w][1];
     const int H = a.H;
 
-    // the plan must be the one the pass info was built with
-    if (a.plan[0] != LA_PLAN_MAGIC || a.plan[LA_PLAN_HASH_WORD] != a.plan_hash) {
+    // In index mode the work's item is known at once: its record (inside
+    // the plan's info->plan_words words) is read together with the plan
+    // check, and nothing of it is used unless the check passes.
+    int work = blockIdx.x;
+    const bool by_index = !(MODE == kFused && a.ordered);
+    PItemBlock ib = reinterpret_cast<const PItemBlock*>(
+        a.items)[by_index ? min(work, a.n_work - 1) / H : 0];   // n_work >= 1
+
+    // the plan must be the one the pass info was built with (both words are
+    // read before either is tested, and the item's with them: the empty asm
+    // takes the item's words, so their loads are not moved past the test)
+    const int magic = a.plan[0], hash = a.plan[LA_PLAN_HASH_WORD];
+    asm volatile("" ::"s"(ib.kind), "s"(ib.n), "s"(ib.b0), "s"(ib.unused), "s"(ib.blk.tok0),
+                 "s"(ib.blk.ntok), "s"(ib.blk.slot), "s"(ib.blk.seed), "s"(ib.blk.seg),
+                 "s"(ib.blk.slot0), "s"(ib.blk.j), "s"(ib.blk.final_row), "s"(magic), "s"(hash));
+    if ((magic != LA_PLAN_MAGIC) | (hash != a.plan_hash)) {
         if (tid == 0)
             __hip_atomic_fetch_or(a.hdr + piece::kStatusWord, LA_ERR_PLAN, __ATOMIC_RELAXED,
                                   __HIP_MEMORY_SCOPE_AGENT);
         return;
     }
 
-    int work = blockIdx.x;
-    if (MODE == kFused && a.ordered) {
+    if (!by_index) {
         // tickets in launch order of the items: everything a workgroup waits
         // for belongs to a smaller ticket, held by a running workgroup.  (When
         // every workgroup of the launch is resident at once, waits need no
@@ -699,11 +717,14 @@ __global__ __launch_bounds__(kThreads) void piece_kernel(PArgs a) {
                                            __HIP_MEMORY_SCOPE_AGENT);
         __syncthreads();
         work = sB[0];
+        if (work < a.n_work)
+            ib = reinterpret_cast<const PItemBlock*>(
+                a.items)[__builtin_amdgcn_readfirstlane(work / H)];
     }
     if (work < a.n_work) {
         const int item = work / H, h = work % H;
-        if (a.items[item].kind == LA_ITEM_BLOCK) {
-            const PBlock B = a.blocks[a.items[item].b[0]];
+        if (ib.kind == LA_ITEM_BLOCK) {
+            const PBlock B = ib.blk;
             const int np = (B.ntok + 2 * kChunk - 1) / (2 * kChunk);   // pieces
             const int64_t ptok0 = int64_t(B.tok0) + w * 2 * kChunk;
             const int pntok = min(2 * kChunk, B.ntok - w * 2 * kChunk);   // <= 0: no piece
@@ -939,7 +960,7 @@ __global__ __launch_bounds__(kThreads) void piece_kernel(PArgs a) {
         } else if constexpr (MODE != kStates) {
             // packed branches: wave w takes block b_2w and, when there is one,
             // block b_2w+1 (then both are one chunk long), each from its seed
-            const PItem& it = a.items[item];
+            const PItem it = __builtin_bit_cast(PItem, ib);
             const int b0 = it.b[2 * w], b1 = it.b[2 * w + 1];
             // when every branch of the pack starts from one view's total and
             // the whole grid is resident, the four waves sum the view's

@@ -163,7 +163,7 @@ uint32_t la_info_checksum(const la_pass_info* info);
  * Errors: LA_ERR_INVALID_ARG (bad table), LA_ERR_UNSUPPORTED (chunk).
  *
  * Plan layout (int32 words):
- *   [0..31]   header: magic, version 3, n_blocks, n_delta, n_scan, chunk,
+ *   [0..31]   header: magic, version 5, n_blocks, n_delta, n_scan, chunk,
  *             block_chunks, n_tokens, off_blocks, off_delta, off_scan, n_ext,
  *             n_views, fused_slot_reads, plan hash, then for the piece path
  *             piece_blocks, piece_items, piece_block_items, piece_slots,
@@ -190,9 +190,10 @@ uint32_t la_info_checksum(const la_pass_info* info);
  *             final_row} -- blocks of LA_PIECE_BLOCK_CHUNKS chunks; slot: the
  *             block's state slot (-1: none needed), slot0: the segment's first
  *             slot, j: the block's position in its segment
- *   pitems    piece_items x 12: {kind, n, b0, .., b7, 0, 0} -- kind
- *             LA_ITEM_BLOCK: one block b0 (wave w takes its piece w), n = 1,
- *             b1.. = -1; LA_ITEM_PACK: branches whose only block is one piece,
+ *   pitems    piece_items x 12 -- kind LA_ITEM_BLOCK: {kind, 1, b0, -1,
+ *             pblocks[b0]} (one block, its 8 words copied into the item;
+ *             wave w takes its piece w); kind LA_ITEM_PACK: {kind, n, b0, ..,
+ *             b7, 0, 0}, branches whose only block is one piece,
  *             n waves of them: wave w takes block b_2w and, when b_2w+1 is
  *             not -1, block b_2w+1 after it (two branches of at most one
  *             chunk each share a wave; a branch of two chunks has one alone).
@@ -310,7 +311,10 @@ la_status la_scan_workspace_size(const la_pass_info* info, int32_t H, int32_t d_
  *   H              heads >= 1
  *   d_k, d_v       head dims; d_k == d_v, 64 or 128
  *   info           host, from the planner that built `plan` (unedited)
- *   plan           device [info->plan_words] int32, a copy of the plan
+ *   plan           device [info->plan_words] int32, a copy of the plan (a
+ *                  kernel may read its work record together with the
+ *                  header check, so all info->plan_words words must be
+ *                  readable even when the plan is another pass's)
  *   ext_state      device [n_ext][H][d_k][d_v] fp32 or NULL when the pass has
  *                  no shard branches (info->n_ext == 0); must not overlap
  *                  final_state

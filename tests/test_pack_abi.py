@@ -63,7 +63,8 @@ def _check_piece_tables(plan, so, bp, vo):
     whose only block is one piece (<= 128 tokens) packed into items of four
     waves (two branches of <= 64 tokens share a wave, a longer one has a wave
     alone, as few waves as that allows, in branch order), every other block
-    one item in block order; and the plan hash and info check."""
+    one item in block order carrying a copy of its block; and the plan hash
+    and info check."""
     info, P = plan.info, plan.plan.astype(np.int64)
     BT, PT = 8 * 64, 2 * 64
     nb_, ni, nbi, nsl, nsc = (int(x) for x in P[15:20])
@@ -103,7 +104,10 @@ def _check_piece_tables(plan, so, bp, vo):
     assert np.all(kinds[:nbi] == 0) and np.all(kinds[nbi:] == 1)
     singles = [i for i in range(len(want)) if i not in set(packed)]
     assert items[:nbi, 2].tolist() == singles and np.all(items[:nbi, 1] == 1)
-    assert np.all(items[:nbi, 3:10] == -1) and np.all(items[:, 10:] == 0)
+    # a block item carries a copy of its block's 8 words
+    assert np.all(items[:nbi, 3] == -1)
+    assert items[:nbi, 4:12].tolist() == [want[b] for b in singles]
+    assert np.all(items[nbi:, 10:] == 0)
     waves = []
     for r, row in enumerate(items[nbi:]):
         nw = int(row[1])
@@ -134,7 +138,7 @@ def _check_plan(plan, so, bp, vo):
     list covers views plus branches with >= 2 slots."""
     info, P = plan.info, plan.plan
     G, C = info.block_chunks, info.chunk
-    assert P[0] == 0x4C41504E and P[1] == 4
+    assert P[0] == 0x4C41504E and P[1] == 5
     assert (P[2], P[3], P[4]) == (info.n_blocks, info.n_delta, info.n_scan)
     ob, od, osc = P[8], P[9], P[10]
     blocks = P[ob:ob + 8 * info.n_blocks].reshape(-1, 8)
