@@ -676,7 +676,12 @@ __device__ __forceinline__ void load_seed(State& S, const PArgs& a, int seed, in
 // The kernel (all forms).
 // ---------------------------------------------------------------------------
 template <int MODE>
-__global__ __launch_bounds__(kThreads) void piece_kernel(PArgs a) {
+// The first arguments repeat what the kernel reads before its first load,
+// so that they arrive in registers (kernel argument preloading) rather than
+// through a load of the argument block.
+__global__ __launch_bounds__(kThreads) void piece_kernel(const int32_t* plan, const PItem* items,
+                                                         int n_work, int H_, int plan_hash,
+                                                         int ordered, PArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t sStage[4][2][kStageElems];
     __shared__ Xch X;
     __shared__ int sB[2];
@@ -689,18 +694,18 @@ __global__ __launch_bounds__(kThreads) void piece_kernel(PArgs a) {
     // the plan's info->plan_words words) is read together with the plan
     // check, and nothing of it is used unless the check passes.
     int work = blockIdx.x;
-    const bool by_index = !(MODE == kFused && a.ordered);
+    const bool by_index = !(MODE == kFused && ordered);
     PItemBlock ib = reinterpret_cast<const PItemBlock*>(
-        a.items)[by_index ? min(work, a.n_work - 1) / H : 0];   // n_work >= 1
+        items)[by_index ? min(work, n_work - 1) / H_ : 0];   // n_work >= 1
 
     // the plan must be the one the pass info was built with (both words are
     // read before either is tested, and the item's with them: the empty asm
     // takes the item's words, so their loads are not moved past the test)
-    const int magic = a.plan[0], hash = a.plan[LA_PLAN_HASH_WORD];
+    const int magic = plan[0], hash = plan[LA_PLAN_HASH_WORD];
     asm volatile("" ::"s"(ib.kind), "s"(ib.n), "s"(ib.b0), "s"(ib.unused), "s"(ib.blk.tok0),
                  "s"(ib.blk.ntok), "s"(ib.blk.slot), "s"(ib.blk.seed), "s"(ib.blk.seg),
                  "s"(ib.blk.slot0), "s"(ib.blk.j), "s"(ib.blk.final_row), "s"(magic), "s"(hash));
-    if ((magic != LA_PLAN_MAGIC) | (hash != a.plan_hash)) {
+    if ((magic != LA_PLAN_MAGIC) | (hash != plan_hash)) {
         if (tid == 0)
             __hip_atomic_fetch_or(a.hdr + piece::kStatusWord, LA_ERR_PLAN, __ATOMIC_RELAXED,
                                   __HIP_MEMORY_SCOPE_AGENT);
@@ -1146,12 +1151,14 @@ la_status launch(int32_t stages, int form, const void* q, const void* k, const v
             a.ordered = cap > 0 && a.n_work <= cap ? 0 : 1;
         }
         if (a.n_work > 0)
-            hipLaunchKernelGGL(piece_kernel<kFused>, dim3(unsigned(a.n_work)), blk, 0, st, a);
+            hipLaunchKernelGGL(piece_kernel<kFused>, dim3(unsigned(a.n_work)), blk, 0, st, a.plan,
+                           a.items, a.n_work, a.H, a.plan_hash, a.ordered, a);
         return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_HIP;
     }
     if ((stages & LA_STAGE_STATES) && info.piece_block_items > 0) {
         a.n_work = info.piece_block_items * H;
-        hipLaunchKernelGGL(piece_kernel<kStates>, dim3(unsigned(a.n_work)), blk, 0, st, a);
+        hipLaunchKernelGGL(piece_kernel<kStates>, dim3(unsigned(a.n_work)), blk, 0, st, a.plan,
+                           a.items, a.n_work, a.H, a.plan_hash, a.ordered, a);
         if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
     }
     if ((stages & LA_STAGE_PREFIX) && form == 3 && info.piece_scans > 0) {
@@ -1162,9 +1169,11 @@ la_status launch(int32_t stages, int form, const void* q, const void* k, const v
     if ((stages & LA_STAGE_OUTPUT) && info.piece_items > 0) {
         a.n_work = info.piece_items * H;
         if (form == 3)
-            hipLaunchKernelGGL(piece_kernel<kOut3>, dim3(unsigned(a.n_work)), blk, 0, st, a);
+            hipLaunchKernelGGL(piece_kernel<kOut3>, dim3(unsigned(a.n_work)), blk, 0, st, a.plan,
+                           a.items, a.n_work, a.H, a.plan_hash, a.ordered, a);
         else
-            hipLaunchKernelGGL(piece_kernel<kOut2>, dim3(unsigned(a.n_work)), blk, 0, st, a);
+            hipLaunchKernelGGL(piece_kernel<kOut2>, dim3(unsigned(a.n_work)), blk, 0, st, a.plan,
+                           a.items, a.n_work, a.H, a.plan_hash, a.ordered, a);
         if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
     }
     return LA_OK;
