@@ -563,6 +563,23 @@ __device__ __forceinline__ int out_row(int f) {
     return 32 * (f >> 5) + 16 * ((f >> 2) & 1) + 4 * ((f >> 3) & 3) + (f & 3);
 }
 
+// LDS rows of the bf16 output launch's K and S^T tiles.  d = 64: the common
+// 160-byte rows with the scol swizzle.  d = 128: 288-byte rows, and rows with
+// bit 4 set keep the two 8-element halves of each 16-element group swapped;
+// in a 64-bank model this leaves no bank conflicts in the 8-byte S^T
+// publication stores (their 16 lanes hit rows r and r + 16), the 16-byte
+// S^T and K fragment reads, the transposed K reads of the carry and the K
+// staging stores (272-byte rows without the swizzle: two-way conflicts in
+// the publication and the transposed reads).
+template <int D>
+struct OutLds {
+    static constexpr int LDR = D == 128 ? D + 16 : Stage<D, 4>::LDR;
+    __device__ static int col(int row, int k) {
+        if constexpr (D == 128) return k ^ ((row & 16) >> 1);
+        return scol<D>(row, k);
+    }
+};
+
 // The outputs of one wave for one chunk: its 16 tokens (token block TB), the
 // 64 output features of feature half hv of the workgroup in the order above.  Specialised per
 // TB so that the causal structure (TB + 1 score tiles, TB / 2 + 1
@@ -575,7 +592,7 @@ __device__ __forceinline__ void out_tiles(const uint16_t* sK, const uint16_t* sV
                                           f32x4 (&acc)[VBH]) {
     static_assert(VBH == 4, "one wave covers the 64 output features of its workgroup");
     constexpr int NKS = D / 32;
-    constexpr int LDR = Stage<D, 4>::LDR;
+    constexpr int LDR = OutLds<D>::LDR;
     // P^T tiles (ub, TB), ub <= TB: P^T[u][t] = sum_d K[u][d] Q[t][d]
     f32x4 p[TB + 1];
 #pragma unroll
@@ -607,7 +624,7 @@ __device__ __forceinline__ void out_tiles(const uint16_t* sK, const uint16_t* sV
 #pragma unroll
         for (int x = 0; x < VBH; ++x) {
             const int row = hv * 64 + x * 16 + c16;
-            const int o = row * LDR + scol<D>(row, ks * 32 + 8 * g);
+            const int o = row * LDR + OutLds<D>::col(row, ks * 32 + 8 * g);
             ah[x] = lds_u32x4(sSh + o);
             al[x] = lds_u32x4(sSl + o);
         }
@@ -647,7 +664,7 @@ __global__ __launch_bounds__(O3::NT) void output_kernel_bf16(
     constexpr int NKB = O3::NKB, NVB = O3::NVB, NKS = O3::NKS, VBH = O3::VBH, TPW = O3::TPW;
     constexpr int DD = D * D;
     constexpr int NPER = KVStage<D, DV, R, NT>::NPER;
-    constexpr int LDR = ST::LDR;
+    constexpr int LDR = OutLds<D>::LDR;
     // V rows of 192 bytes: the permuted V^T fragment reads of out_tiles (8-byte
     // pieces 16 bytes apart on four rows) and the carry's reads both hit every
     // LDS bank at most once per 128 bytes
@@ -717,11 +734,11 @@ __global__ __launch_bounds__(O3::NT) void output_kernel_bf16(
             const uint32_t l23 = cvt_bf2(s[2] - bf_lo(h23), s[3] - bf_hi(h23));
             const int f = vbo * 16 + c16;   // feature within the part
             const int row = (f & ~63) + out_row(f & 63);
-            const int off = row * LDR + scol<D>(row, (kbo + i) * 16 + 4 * g);
+            const int off = row * LDR + OutLds<D>::col(row, (kbo + i) * 16 + 4 * g);
             *reinterpret_cast<u32x2*>(sSh + off) = u32x2{h01, h23};
             *reinterpret_cast<u32x2*>(sSl + off) = u32x2{l01, l23};
         }
-        stage_kv_rows<D, DV, R, NT, NPER, LDV>(kv, sK, sV);
+        stage_kv_rows<D, DV, R, NT, NPER, LDV, LDR>(kv, sK, sV);
     };
     // The loop is rotated: chunk c + 1 is staged (and its q moved to qf) at
     // the end of iteration c, right after chunk c's output stores.  Its loads

@@ -280,7 +280,7 @@ __device__ __forceinline__ void load_kv(BlkR<R> (&pre)[NPER], __amdgpu_buffer_rs
 // workgroup's DVW features of V into sV (stride LDR of a DVW-wide tile);
 // transposed operands are then read with tr_frag.
 template <int D, int DVW, int R, int NT, int NPER,
-          int LDVS = Stage<D, R>::template LDV<DVW>>
+          int LDVS = Stage<D, R>::template LDV<DVW>, int LDKS = Stage<D, R>::LDR>
 __device__ __forceinline__ void stage_kv_rows(const BlkR<R> (&pre)[NPER], uint16_t* sK,
                                               uint16_t* sV) {
     using KS = KVStage<D, DVW, R, NT>;
@@ -296,7 +296,7 @@ __device__ __forceinline__ void stage_kv_rows(const BlkR<R> (&pre)[NPER], uint16
             store_rows<R>(sV, pre[i], wv / KS::NCGV, wv % KS::NCGV, LDVS);
         } else {
             const int wk = b0 + lane;
-            store_rows<R>(sK, pre[i], wk / KS::NCGK, wk % KS::NCGK, Stage<D, R>::LDR);
+            store_rows<R>(sK, pre[i], wk / KS::NCGK, wk % KS::NCGK, LDKS);
         }
     }
 }
