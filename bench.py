@@ -399,7 +399,11 @@ def cost_model_bench(a):
     log-uniform in [500, 18000] tokens, 1-64 branches of 24-128 tokens per
     request (the page's ranges), H = 16, d = 64, bf16 -- seed 2024.  Each
     pass is timed as `steps` graph-replayed passes after its warm-up.  The
-    fit uses the even-numbered shapes; the odd ones are predicted (hold-out)."""
+    fit uses the even-numbered shapes; the odd ones are predicted (hold-out).
+    The structural variant (ours) is fitted the same way from each pass's
+    plan: tokens and rounds of workgroups (the single launch holds one
+    workgroup per CU: its LDS); the longest view's 512-token block count is
+    recorded with each sample."""
     import numpy as np
     import torch
     import chunked_linear_attention_packed_amd as la
@@ -409,7 +413,8 @@ def cost_model_bench(a):
     H, d = 16, 64
     dev = torch.device("cuda:0")
     stream = torch.cuda.Stream(dev)
-    rows = []
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    rows, struct = [], []
     for i in range(a.cost_model):
         r = int(rng.integers(1, 9))
         vl = np.round(np.exp(rng.uniform(np.log(500), np.log(18000), size=r))).astype(np.int32)
@@ -426,11 +431,16 @@ def cost_model_bench(a):
                                     stream=stream)
         us = _graph_us(fn, a.steps, a.warmup, stream, a.eager)
         rows.append((vl.tolist(), bc.tolist(), int(bl.sum()), T, us))
+        work = plan.info.piece_items * H
+        chain = -(-int(vl.max()) // 512)
+        struct.append({"work_items": int(work), "chain_blocks": int(chain)})
         print(f"pass {i}: requests {r} tokens {T} branches {int(bc.sum())} "
               f"block_chunks {plan.info.block_chunks} {us:.1f} us", file=sys.stderr, flush=True)
         del q, k, v, out, fin, ws
     X = np.array([cm.features(vl, bc) for vl, bc, _, _, _ in rows])
     Xt = np.array([[1.0, float(np.sum(vl)), float(bt)] for vl, _, bt, _, _ in rows])
+    Xs = np.array([cm.features_structural(T, st["work_items"], cus)
+                   for (_, _, _, T, _), st in zip(rows, struct)])
     t = np.array([us for *_, us in rows])
     tr, te = np.arange(0, len(t), 2), np.arange(1, len(t), 2)
 
@@ -449,8 +459,12 @@ def cost_model_bench(a):
         "fit_all": cm.fit(X, t), "fit_even_holdout_odd": holdout(X),
         "variant_branch_tokens": {"model": "t_us = c0 + c1 * sum(view) + c2 * sum(branch tokens)",
                                   "fit_all": cm.fit(Xt, t), "fit_even_holdout_odd": holdout(Xt)},
+        "variant_structural": {"model": "t_us = c0 + c1 * tokens + c2 * ceil(workgroups / CUs)",
+                               "cus": cus,
+                               "fit_all": cm.fit(Xs, t), "fit_even_holdout_odd": holdout(Xs)},
         "samples": [{"view_len": vl, "branches": int(np.sum(bc)), "branch_tokens": bt,
-                     "tokens": T, "us": us} for vl, bc, bt, T, us in rows],
+                     "tokens": T, "us": us, **st}
+                    for (vl, bc, bt, T, us), st in zip(rows, struct)],
     }), flush=True)
 
 

@@ -57,3 +57,34 @@ def test_needs_three_passes():
     m.update([1, 2, 3], 1.0)
     with pytest.raises(ValueError):
         m.coefficients()
+    with pytest.raises(ValueError):
+        m.update([1, 2, 3, 4], 1.0)
+    m4 = cm.CostModel(4)
+    for _ in range(3):
+        m4.update([1, 2, 3, 4], 1.0)
+    with pytest.raises(ValueError):
+        m4.coefficients()
+
+
+def test_structural_features():
+    # 7,784 tokens, 16 items x 16 heads on 256 resident workgroups
+    assert list(cm.features_structural(7784, 256, 256)) == [1.0, 7784.0, 1.0]
+    assert cm.features_structural(100, 257, 256)[2] == 2.0
+    assert cm.features_structural(100, 0, 256)[2] == 0.0
+
+
+def test_structural_constants_are_recovered():
+    rng = np.random.default_rng(6)
+    X = []
+    for _ in range(40):
+        T = int(rng.integers(600, 150000))
+        items = int(rng.integers(1, 400)) * 16
+        X.append(cm.features_structural(T, items, 256))
+    X = np.array(X)
+    c = np.array([9.0, 2.5e-3, 6.0])
+    r = cm.fit(X, X @ c)
+    assert np.allclose(r["c"], c, rtol=1e-7) and r["rel_max"] < 1e-9
+    m = cm.CostModel(3)
+    for x, y in zip(X, X @ c):
+        m.update(x, y)
+    assert m.predict(X[3]) == pytest.approx(float(X[3] @ c), rel=1e-9)
