@@ -6,9 +6,12 @@ The host code (pack.cpp: packer and planners; cache.cpp: view-state cache
 directory) is compiled with g++; the kernels and their host entry points
 (scan.hip: the linear-attention scan; piece.hip: its d = 64 bf16 path;
 attn.hip: the tree-masked softmax attention) with hipcc; all are linked into
-one shared library next to this file.  Always recompiles.
+one shared library next to this file.  Always recompiles.  Every kernel is
+designed to fit its registers: a kernel that needs scratch memory (register
+spills, or a private array) fails the build.
 """
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -51,6 +54,21 @@ def _run(cmd, verbose):
         raise RuntimeError(f"build step failed ({res.returncode}): {' '.join(cmd)}\n{out}")
     if verbose and out.strip():
         print(out, flush=True)
+    return out
+
+
+def _scratch_kernels(remarks):
+    """(kernel, bytes per lane) of every kernel with scratch memory, from
+    the compiler's kernel-resource-usage remarks."""
+    found, name = [], None
+    for line in remarks.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and name and int(m.group(1)) > 0:
+            found.append((name, int(m.group(1))))
+    return found
 
 
 def build(verbose=False):
@@ -65,8 +83,12 @@ def build(verbose=False):
         dev_o = []
         for name in HIP_SOURCES:
             obj = os.path.join(tmp, name.replace(".hip", ".o"))
-            _run([hipcc] + HIP_FLAGS + ["-I", INCLUDE, "-c", os.path.join(CSRC, name),
-                                        "-o", obj], verbose)
+            out = _run([hipcc] + HIP_FLAGS + ["-Rpass-analysis=kernel-resource-usage", "-I",
+                                              INCLUDE, "-c", os.path.join(CSRC, name), "-o", obj],
+                       False)
+            spills = _scratch_kernels(out)
+            if spills:
+                raise RuntimeError(f"{name}: kernels using scratch memory: {spills}")
             dev_o.append(obj)
         tmp_lib = LIB + ".tmp"
         _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC"] + host_o + dev_o +

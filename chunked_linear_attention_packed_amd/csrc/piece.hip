@@ -966,7 +966,10 @@ __global__ __launch_bounds__(kThreads) void piece_kernel(const int32_t* plan, co
             // packed branches: wave w takes block b_2w and, when there is one,
             // block b_2w+1 (then both are one chunk long), each from its seed
             const PItem it = __builtin_bit_cast(PItem, ib);
-            const int b0 = it.b[2 * w], b1 = it.b[2 * w + 1];
+            // this wave's pair, selected (an index into the record would put
+            // it on the stack)
+            const int b0 = w == 0 ? it.b[0] : w == 1 ? it.b[2] : w == 2 ? it.b[4] : it.b[6];
+            const int b1 = w == 0 ? it.b[1] : w == 1 ? it.b[3] : w == 2 ? it.b[5] : it.b[7];
             // when every branch of the pack starts from one view's total and
             // the whole grid is resident, the four waves sum the view's
             // states themselves (four tiles each) instead of waiting for the

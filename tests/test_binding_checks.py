@@ -99,3 +99,15 @@ def test_pack_rejects_mismatched_request_arrays():
         la.pack([100, 50], [1, 2], [10, 20, 30, 40])
     with pytest.raises(ValueError):
         la.pack([100, 50], [1], [10])
+
+
+def test_build_refuses_kernels_with_scratch():
+    """The build reads the compiler's resource remarks and names every kernel
+    that needs scratch memory (the kernels are designed without)."""
+    from chunked_linear_attention_packed_amd import build as b
+    remarks = ("x.hip:1:1: remark: Function Name: k_ok [-Rpass-analysis=kernel-resource-usage]\n"
+               "x.hip:1:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]\n"
+               "x.hip:9:1: remark: Function Name: k_spill [-Rpass-analysis=kernel-resource-usage]\n"
+               "x.hip:9:1: remark:     ScratchSize [bytes/lane]: 52 [-Rpass-analysis=kernel-resource-usage]\n")
+    assert b._scratch_kernels(remarks) == [("k_spill", 52)]
+    assert b._scratch_kernels(remarks.replace("52", "0")) == []
