@@ -66,8 +66,9 @@
 // that XCD's L2), stores are drained (s_waitcnt) before the flag that
 // announces them, and every wait is bounded: past the spin limit the
 // workgroup records LA_ERR_TIMEOUT in the header and carries on, so every
-// wave reaches the end of the kernel.  The last workgroup to retire clears
-// the flags and resets the counters for the next pass.
+// wave reaches the end of the kernel.  A workgroup is counted out as soon
+// as it is done with the flags (before its outputs); the last one counted
+// clears the flags and resets the counters for the next pass.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -244,6 +245,29 @@ __device__ bool wait_prefix(const PArgs& a, const uint64_t* f, uint64_t tag) {
     }
     order_after_flag();
     return __builtin_amdgcn_readfirstlane(int(is_flag(x, kFlagP) && (x & kFlagXcd) == tag)) != 0;
+}
+
+// A workgroup that is done with the flags (its waits are over and its
+// states are published) is counted out by one of its waves -- the only wave
+// of the workgroup that stores flags, or any wave when none does -- which
+// first waits for its own stores.  The last workgroup counted clears the
+// flags and the counters for the next pass: every reader of a flag has been
+// counted before it, so no wait can see the clearing.
+__device__ void retire(const PArgs& a, int lane) {
+    drain_stores();
+    int r = 0;
+    if (lane == 0)
+        r = __hip_atomic_fetch_add(a.hdr + piece::kRetireWord, 1, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+    if (__builtin_amdgcn_readfirstlane(r) == a.n_work - 1) {
+        for (int i = lane; i < a.n_flags; i += 64) flag_store(a.flags + i, 0);
+        if (lane == 0) {
+            __hip_atomic_store(a.hdr + piece::kTicketWord, 0, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(a.hdr + piece::kRetireWord, 0, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
 }
 
 // The look-back of block j of a segment (slots slot0 .. slot0 + j - 1 hold
@@ -943,6 +967,9 @@ __global__ __launch_bounds__(kThreads) void piece_kernel(const int32_t* plan, co
                         store_rows_state(P, a.final_state + (int64_t(B.final_row) * H + h) * PD * PD,
                                          g, c16);
                 }
+                // the flags are done with: the publishing wave counts the
+                // workgroup out before its outputs
+                if (MODE == kFused && w == np - 1) retire(a, lane);
                 // O += Q S, S = S_b + E_p: the block's starting state and the
                 // pieces before this one in the block
                 if (pntok > 0 && (has_seed || B.j > 0 || w >= 1)) {
@@ -1021,6 +1048,7 @@ __global__ __launch_bounds__(kThreads) void piece_kernel(const int32_t* plan, co
                     look_back<kAuxCoherent>(tot4, a, vs.first_slot, m, vs.n_slots, h, w, lane);
                 put_tiles4(X, 0, tot4, w, lane);
                 __syncthreads();
+                if (MODE == kFused && w == 0) retire(a, lane);
             }
             if (b0 >= 0) {
                 SSplit sp;
@@ -1044,28 +1072,15 @@ __global__ __launch_bounds__(kThreads) void piece_kernel(const int32_t* plan, co
                 store_chunk(O0, a, B.tok0, min(B.ntok, kChunk), h, g, c16);
                 if (n1 > 0) store_chunk(O1, a, t1, n1, h, g, c16);
             }
-        }
-    }
-
-    if constexpr (MODE == kFused) {
-        // the last workgroup to retire resets the single-launch state
-        __syncthreads();
-        if (tid == 0) {
-            const int r = __hip_atomic_fetch_add(a.hdr + piece::kRetireWord, 1, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-            sB[1] = r == a.n_work - 1;
-        }
-        __syncthreads();
-        if (sB[1]) {
-            for (int i = tid; i < a.n_flags; i += kThreads) flag_store(a.flags + i, 0);
-            if (tid == 0) {
-                __hip_atomic_store(a.hdr + piece::kTicketWord, 0, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(a.hdr + piece::kRetireWord, 0, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+            if (MODE == kFused && shared < 0) {
+                __syncthreads();   // every wave's seed wait is over
+                if (w == 0) retire(a, lane);
             }
         }
+    } else if (MODE == kFused && w == 0) {
+        retire(a, lane);   // no work (not launched so: the grid is the work)
     }
+
 }
 
 // Layout of the piece path's part of a workspace (after the header).
