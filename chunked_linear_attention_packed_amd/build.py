@@ -33,7 +33,7 @@ HIP_FLAGS = [
     "-mllvm", "-amdgpu-mfma-vgpr-form",
     # the first kernel arguments arrive in SGPRs at wave launch (no load)
     "-mllvm", "-amdgpu-kernarg-preload-count=16",
-    "-Wall", "-Wno-unused-function",
+    "-Wall", "-Wextra", "-Wno-unused-function",
 ]
 
 

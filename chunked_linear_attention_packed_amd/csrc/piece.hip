@@ -751,7 +751,7 @@ __global__ __launch_bounds__(kThreads) void piece_kernel(const int32_t* plan, co
                 a.items)[__builtin_amdgcn_readfirstlane(work / H)];
     }
     if (work < a.n_work) {
-        const int item = work / H, h = work % H;
+        const int h = work % H;
         if (ib.kind == LA_ITEM_BLOCK) {
             const PBlock B = ib.blk;
             const int np = (B.ntok + 2 * kChunk - 1) / (2 * kChunk);   // pieces

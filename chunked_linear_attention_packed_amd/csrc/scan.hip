@@ -660,9 +660,7 @@ __global__ __launch_bounds__(O3::NT) void output_kernel_bf16(
     uint16_t* __restrict__ out, int H, int n_items, PlanCheck pc) {
     if (!pc.ok()) return;
     constexpr int R = O3::R, NT = O3::NT, NP = O3::NP_, DV = O3::DV;
-    using ST = Stage<D, R>;
     constexpr int NKB = O3::NKB, NVB = O3::NVB, NKS = O3::NKS, VBH = O3::VBH, TPW = O3::TPW;
-    constexpr int DD = D * D;
     constexpr int NPER = KVStage<D, DV, R, NT>::NPER;
     constexpr int LDR = OutLds<D>::LDR;
     // V rows of 192 bytes: the permuted V^T fragment reads of out_tiles (8-byte
@@ -1145,7 +1143,6 @@ __global__ __launch_bounds__(O3::NT) void output_kernel_split(
     constexpr int R = O3::R, NT = O3::NT, NP = O3::NP_, DV = O3::DV;
     using ST = Stage<D, R>;
     constexpr int NKB = O3::NKB, NVB = O3::NVB, NKS = O3::NKS, VBH = O3::VBH, TPW = O3::TPW;
-    constexpr int DD = D * D;
     constexpr int NPER = KVStage<D, DV, R, NT>::NPER;
     constexpr int LDR = ST::LDR, LDT = ST::LDT;
     __shared__ __attribute__((aligned(16))) uint16_t sKh[kChunk * LDR];
