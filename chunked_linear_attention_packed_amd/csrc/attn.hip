@@ -321,7 +321,7 @@ __global__ __launch_bounds__(64 * (4 / QT)) void attn_kernel_bf16(
 #define LA_ATTN_QT_64 1
 #endif
 #ifndef LA_ATTN_QT_128
-#define LA_ATTN_QT_128 2
+#define LA_ATTN_QT_128 1
 #endif
 
 }  // namespace
