@@ -13,6 +13,7 @@
 #include <array>
 #include <cstdint>
 #include <cstring>
+#include <unordered_map>
 #include <vector>
 
 #include "linattn.h"
@@ -507,6 +508,8 @@ extern "C" la_status la_attn_plan_ext(int32_t n_segments, const int32_t* seg_off
     struct Item {
         int32_t w[8];
         int64_t keys;
+        int64_t group;   // the segment whose keys the item reads first (its view, or itself)
+        int64_t gkeys;   // the longest key range of the group
     };
     std::vector<Item> out;
     for (int32_t s = 0; s < n_segments; ++s) {
@@ -527,13 +530,27 @@ extern "C" la_status la_attn_plan_ext(int32_t n_segments, const int32_t* seg_off
         const int32_t a = seg_offsets[s], b = seg_offsets[s + 1];
         for (int32_t q0 = a; q0 < b; q0 += LA_CHUNK) {
             const int32_t nq = std::min(LA_CHUNK, b - q0);
-            Item it{{q0, nq, a, view0, view_len, src, 0, 0}, int64_t(view_len) + (q0 + nq - a)};
+            Item it{{q0, nq, a, view0, view_len, src, 0, 0}, int64_t(view_len) + (q0 + nq - a),
+                    p >= 0 ? int64_t(p) : p <= -2 ? int64_t(n_segments) - p : int64_t(s), 0};
             out.push_back(it);
         }
     }
-    // longest key range first, so the long items start before the short ones
-    std::stable_sort(out.begin(), out.end(),
-                     [](const Item& x, const Item& y) { return x.keys > y.keys; });
+    // Items that read the same view's keys (the view's own query blocks and
+    // its branches') are consecutive: workgroups dispatched together then
+    // stream the same key blocks and share them in the L2, which a view's
+    // keys at d = 128 (up to 8 MB per head) do not fit otherwise.  Groups
+    // with the longest key range go first, and within a group the longest
+    // items, so the long items start before the short ones.
+    {
+        std::unordered_map<int64_t, int64_t> gk;
+        for (const Item& x : out) gk[x.group] = std::max(gk[x.group], x.keys);
+        for (Item& x : out) x.gkeys = gk[x.group];
+    }
+    std::stable_sort(out.begin(), out.end(), [](const Item& x, const Item& y) {
+        if (x.gkeys != y.gkeys) return x.gkeys > y.gkeys;
+        if (x.group != y.group) return x.group < y.group;
+        return x.keys > y.keys;
+    });
     if (out.size() > size_t(INT32_MAX / LA_ATTN_ITEM_WORDS)) return LA_ERR_INVALID_ARG;
     if (items)
         for (size_t i = 0; i < out.size(); ++i)

@@ -1,5 +1,6 @@
 """Host planner of the softmax attention (la_attn_plan): one item per
-(segment, 64-token query block), longest key range first; CPU only."""
+(segment, 64-token query block), grouped by the view whose keys they read,
+groups and items within a group longest key range first; CPU only."""
 import numpy as np
 import pytest
 
@@ -18,10 +19,17 @@ def _expected(so, bp, ext_len):
             view = (int(offs[-p - 2]), int(ext_len[-p - 2]), la.LA_ATTN_EXT_VIEW)
         else:
             view = (0, 0, la.LA_ATTN_NO_VIEW)
+        # group: the view segment, an external view (after every segment),
+        # or the segment itself
+        group = p if p >= 0 else (len(bp) - p if p <= -2 else s)
         for q0 in range(a, b, 64):
             nq = min(64, b - q0)
-            items.append(((q0, nq, a) + view + (0, 0), view[1] + q0 + nq - a))
-    items.sort(key=lambda it: -it[1])          # stable: ties keep table order
+            items.append(((q0, nq, a) + view + (0, 0), view[1] + q0 + nq - a, group))
+    longest = {}
+    for _, keys, group in items:
+        longest[group] = max(longest.get(group, 0), keys)
+    # stable: ties keep table order
+    items.sort(key=lambda it: (-longest[it[2]], it[2], -it[1]))
     return np.array([it[0] for it in items], dtype=np.int32).reshape(-1, 8)
 
 
