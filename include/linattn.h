@@ -467,11 +467,11 @@ la_status la_export_view_kv(const void* k, const void* v, la_dtype dtype, int32_
  * extra keys are tokens view0 .. view0+view_len-1 of the pass (view_src
  * LA_ATTN_PACKED_VIEW), of ext_k / ext_v (LA_ATTN_EXT_VIEW), or none
  * (LA_ATTN_NO_VIEW).  Items are grouped by the view whose keys they read
- * (a view's query blocks with its branches'; a segment without a view is a
- * group of its own); groups go in order of their longest key range (view
- * tokens plus own tokens up to the block's end), ties by the group's first
- * segment, external views after the pass's segments, and items within a
- * group longest key range first (ties in table order).
+ * (a view's query blocks with those of its branches; the branches of one
+ * external view form one group); groups go in order of their longest key
+ * range (view tokens plus own tokens up to the block's end), ties by the
+ * view's segment index, external views after the pass's views, and items
+ * within a group longest key range first (ties in table order).
  * Errors: LA_ERR_INVALID_ARG (bad table, parent or length).
  *
  * la_attn_plan_ext -- la_attn_plan where external view e is tokens
