@@ -546,21 +546,39 @@ __device__ __forceinline__ void chunk_cross(OTiles& O, const u32x4 (&kr0)[4][2],
     cross_tokens<3>(O, kr0, vt0, qs.q[3], g, c16);
 }
 
-// Rows tok0 .. tok0 + rows - 1 of out from O (16 contiguous bytes per lane
-// and store; rows past `rows` fall outside the buffer window).
+// Rows tok0 .. tok0 + rows - 1 of out from O (rows past `rows` fall outside
+// the buffer window).  Lane (g, c16) holds 16 contiguous bytes of token
+// 16 tb + c16 in each feature half hh (features 32 hh + 8 g ..); neighbouring
+// tokens' lanes (c16, c16 ^ 1) swap one piece, so that each store writes
+// whole 128-byte rows (8 lanes per token): the even tokens' rows, then the
+// odd tokens'.  The outputs are nontemporal stores, which go to memory as
+// they are written: whole rows make whole lines.
 __device__ __forceinline__ void store_chunk(const OTiles& O, const PArgs& a, int64_t tok0,
                                             int rows, int h, int g, int c16) {
     const auto ro = chunk_rsrc(a.out, tok0 * a.H * PD, 2, rows, a.H, PD);
+    const bool odd = (c16 & 1) != 0;
+    const uint32_t row_bytes = uint32_t(a.H * PD * 2);
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
+    for (int tb = 0; tb < 4; ++tb) {
+        u32x4 pc[2];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             const f32x4 x = O[tb * 4 + 2 * hh], y = O[tb * 4 + 2 * hh + 1];
-            const u32x4 pc = from_slot_order(u32x4{cvt_bf2(x[0], x[1]), cvt_bf2(x[2], x[3]),
-                                                   cvt_bf2(y[0], y[1]), cvt_bf2(y[2], y[3])});
-            buf_store16u(ro, uint32_t((((16 * tb + c16) * a.H + h) * PD + 32 * hh + 8 * g) * 2),
-                         pc);
+            pc[hh] = from_slot_order(u32x4{cvt_bf2(x[0], x[1]), cvt_bf2(x[2], x[3]),
+                                           cvt_bf2(y[0], y[1]), cvt_bf2(y[2], y[3])});
         }
+        const u32x4 give = odd ? pc[0] : pc[1];
+        u32x4 got;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)   // quad_perm [1, 0, 3, 2]: lane c16 ^ 1
+            got[i] = __builtin_amdgcn_mov_dpp(int(give[i]), 0xB1, 0xF, 0xF, false);
+        // lane's own token row and feature-half offsets
+        const uint32_t own = uint32_t(((16 * tb + c16) * a.H + h) * PD * 2) + 16 * g;
+        // even token rows: even lanes their half 0, odd lanes the even token's half 1
+        buf_store16u(ro, odd ? own - row_bytes + 64 : own, odd ? got : pc[0]);
+        // odd token rows: even lanes the odd token's half 0, odd lanes their half 1
+        buf_store16u(ro, odd ? own + 64 : own + row_bytes, odd ? pc[1] : got);
+    }
 }
 
 // The part of one wave's piece (up to two chunks) within the piece: O0, O1.
