@@ -14,12 +14,17 @@
 // the block's keys in 64-key blocks -- first the parent view's (from the pass
 // or from the external K/V arrays), then its own segment's up to and
 // including the query block -- keeping for every query a running maximum, a
-// running sum and the unnormalised output (the usual online softmax).  Wave w
-// owns queries w*16 .. w*16+15.  MFMA orientation, as in the scan's output
-// kernel: scores are computed transposed, S^T = K Q^T (A = K rows from LDS,
-// B = Q^T fragments held in registers), so each lane owns one query (its
-// column) and 16 keys of the block; exponentiated scores, packed to bf16,
-// are the B operand of O^T += V^T P^T directly from the accumulator layout.
+// running sum and the unnormalised output (the usual online softmax).  The
+// four waves split each 64 x 64 (queries x keys) block into 2 x 2 tiles:
+// wave w owns queries 32 (w % 2) .. + 31 against keys 32 (w / 2) .. + 31 of
+// every key block, with a running maximum and sum of its own; the two key
+// halves of a query are merged after the last block (the softmax of a union
+// of key sets from the parts' maxima and sums).  MFMA orientation, as in the
+// scan's output kernel: scores are computed transposed, S^T = K Q^T (A = K
+// rows from LDS, B = Q^T fragments held in registers), so each lane owns one
+// query of a tile (its column) and 8 keys of its half; exponentiated scores,
+// packed to bf16, are the B operand of O^T += V^T P^T directly from the
+// accumulator layout.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -48,28 +53,43 @@ __device__ __forceinline__ float max_over_groups(float x) {
     return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
-// QT query tiles of 16 per wave (4 / QT waves per 64-query item): every K
-// and V fragment a wave reads from LDS feeds QT MFMAs.
-template <int D, int QT>
-__global__ __launch_bounds__(64 * (4 / QT)) void attn_kernel_bf16(
+// QT query tiles of 16 per wave; KH key parts per 64-key block.  With
+// KH = 1 a wave takes 16 QT queries against every key (4 / QT waves per
+// 64-query item); with KH = 2 the four waves form 2 x 2 tiles of 32 queries
+// x 32 keys: a wave reads half of each K and V block from LDS for twice the
+// queries, keeps its own running maximum and sums over its keys, and the two
+// key halves of a query are merged once, after the last block.  Every K and
+// V fragment a wave reads from LDS feeds QT MFMAs.
+template <int D, int QT, int KH>
+__global__ __launch_bounds__(64 * KH * (4 / QT))
+__attribute__((amdgpu_waves_per_eu(KH == 2 && D == 64 ? 4 : 1))) void attn_kernel_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ ext_k,
     const uint16_t* __restrict__ ext_v, const AttnItem* __restrict__ items,
     uint16_t* __restrict__ out, int H, float scale_log2) {
-    constexpr int NT = 64 * (4 / QT);
+    static_assert(KH == 1 || (KH == 2 && QT == 2), "key halves pair with 32-query waves");
+    constexpr int NQG = 4 / QT;          // query groups (waves per key part)
+    constexpr int NT = 64 * KH * NQG;
+    constexpr int NUB = 4 / KH;          // 16-key tiles of a block per wave
     constexpr int R = 4, NKS = D / 32, NVB = D / 16;
     using ST = Stage<D, R>;
     constexpr int NPER = KVStage<D, D, R, NT>::NPER;
     constexpr int LDR = ST::LDR;
-    __shared__ __attribute__((aligned(16))) uint16_t sK[kChunk * LDR];   // K block, row-major
     constexpr int LDV = ST::template LDV<D>;
-    __shared__ __attribute__((aligned(16))) uint16_t sV[kChunk * LDV];   // V block, row-major
+    // K block then V block, both row-major; after the last block the key
+    // halves' partial results are merged through the same memory
+    constexpr int kMergeFloats = NQG * (QT * NVB * 64 * 4 + 2 * QT * 64);
+    static_assert(KH == 1 || kMergeFloats * 4 <= kChunk * (LDR + LDV) * 2, "merge fits");
+    __shared__ __attribute__((aligned(16))) uint16_t sKV[kChunk * (LDR + LDV)];
+    uint16_t* sK = sKV;
+    uint16_t* sV = sKV + kChunk * LDR;
 
     const int h = blockIdx.x % H;
     const AttnItem it = items[blockIdx.x / H];
     const int w = wave_id(), lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
+    const int qg = w % NQG, kh = w / NQG;   // query group, key part (wave-uniform)
     // this lane's queries within the block: tile t holds trow0 + 16 t
-    const int trow0 = w * 16 * QT + c16;
+    const int trow0 = qg * 16 * QT + c16;
     const int64_t row_elems = int64_t(H) * D;
 
     // key blocks: the parent view's, then the segment's own up to the query
@@ -184,21 +204,23 @@ __global__ __launch_bounds__(64 * (4 / QT)) void attn_kernel_bf16(
     auto block = [&](int rows, bool diag, auto masked) {
         constexpr bool MASKED = decltype(masked)::value;
         // S^T tiles (ub = key tile): lane holds s[u = ub*16 + 4g + j][trow]
-        f32x4 s[QT][4];
+        // (this wave's key tiles: kh * NUB + ub)
+        f32x4 s[QT][NUB];
 #pragma unroll
         for (int t = 0; t < QT; ++t)
 #pragma unroll
-            for (int ub = 0; ub < 4; ++ub) s[t][ub] = zero4();
+            for (int ub = 0; ub < NUB; ++ub) s[t][ub] = zero4();
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
-            u32x4 kf[4];
+            u32x4 kf[NUB];
 #pragma unroll
-            for (int ub = 0; ub < 4; ++ub)
-                kf[ub] = lds_u32x4(sK + (ub * 16 + c16) * LDR + ks * 32 + 8 * g);
+            for (int ub = 0; ub < NUB; ++ub)
+                kf[ub] = lds_u32x4(sK + ((kh * NUB + ub) * 16 + c16) * LDR + ks * 32 + 8 * g);
 #pragma unroll
             for (int t = 0; t < QT; ++t)
 #pragma unroll
-                for (int ub = 0; ub < 4; ++ub) s[t][ub] = mfma_bf16(kf[ub], qf[t][ks], s[t][ub]);
+                for (int ub = 0; ub < NUB; ++ub)
+                    s[t][ub] = mfma_bf16(kf[ub], qf[t][ks], s[t][ub]);
         }
         bool any_raise = false;
         float bm[QT];
@@ -206,11 +228,11 @@ __global__ __launch_bounds__(64 * (4 / QT)) void attn_kernel_bf16(
         for (int t = 0; t < QT; ++t) {
             float mx = -INFINITY;
 #pragma unroll
-            for (int ub = 0; ub < 4; ++ub)
+            for (int ub = 0; ub < NUB; ++ub)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     if constexpr (MASKED) {
-                        const int u = ub * 16 + 4 * g + j;
+                        const int u = (kh * NUB + ub) * 16 + 4 * g + j;
                         if (!(u < rows && (!diag || u <= trow0 + 16 * t))) s[t][ub][j] = -INFINITY;
                     }
                     mx = fmaxf(mx, s[t][ub][j]);
@@ -238,12 +260,12 @@ __global__ __launch_bounds__(64 * (4 / QT)) void attn_kernel_bf16(
         }
         // a query sees a key in every block it visits, so m is finite here
         // (the guard keeps a row that is masked so far from producing NaNs)
-        u32x2 pb[QT][4];
+        u32x2 pb[QT][NUB];
 #pragma unroll
         for (int t = 0; t < QT; ++t) {
             const float nb = m[t] == -INFINITY ? 0.f : -m[t] * scale_log2;
 #pragma unroll
-            for (int ub = 0; ub < 4; ++ub) {
+            for (int ub = 0; ub < NUB; ++ub) {
                 float p[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j)   // exp2(-inf) = 0
@@ -253,11 +275,11 @@ __global__ __launch_bounds__(64 * (4 / QT)) void attn_kernel_bf16(
         }
         // O^T += V^T P^T; k-slots (g, i) -> key u = (2pp + i/4)*16 + 4g + i%4
 #pragma unroll
-        for (int pp = 0; pp < 2; ++pp) {
+        for (int pp = 0; pp < NUB / 2; ++pp) {
             u32x4 av[NVB];
 #pragma unroll
             for (int x = 0; x < NVB; ++x)
-                av[x] = tr_frag(sV, LDV, x * 16, pp, g, c16);
+                av[x] = tr_frag(sV, LDV, x * 16, kh * (NUB / 2) + pp, g, c16);
 #pragma unroll
             for (int t = 0; t < QT; ++t) {
                 const u32x4 bp = cat2(pb[t][2 * pp], pb[t][2 * pp + 1]);
@@ -302,6 +324,40 @@ __global__ __launch_bounds__(64 * (4 / QT)) void attn_kernel_bf16(
         block(rows, b == nkb - 1, std::true_type{});
         __syncthreads();
     }
+    if constexpr (KH == 2) {
+        // merge the key halves: the second half's waves leave their reference
+        // maxima, sums and unnormalised outputs in LDS (the loop ended with a
+        // barrier, so the K / V tiles are free); the first half's waves
+        // rescale both to the larger reference and add
+        float* mg = reinterpret_cast<float*>(sKV) + qg * (QT * NVB * 64 * 4 + 2 * QT * 64);
+        f32x4* macc = reinterpret_cast<f32x4*>(mg);
+        float* mm = mg + QT * NVB * 64 * 4;
+        float* ml = mm + QT * 64;
+        if (kh == 1) {
+#pragma unroll
+            for (int t = 0; t < QT; ++t) {
+#pragma unroll
+                for (int x = 0; x < NVB; ++x) macc[(t * NVB + x) * 64 + lane] = acc[t][x];
+                mm[t * 64 + lane] = m[t];
+                ml[t * 64 + lane] = accl[t][0];
+            }
+        }
+        __syncthreads();
+        if (kh == 1) return;
+#pragma unroll
+        for (int t = 0; t < QT; ++t) {
+            // the first half holds a key of every query (the diagonal
+            // block's first key), so its reference is finite
+            const float m1 = mm[t * 64 + lane];
+            const float mn = fmaxf(m[t], m1);
+            const float a0 = __builtin_amdgcn_exp2f((m[t] - mn) * scale_log2);
+            const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m1 - mn) * scale_log2);
+            accl[t][0] = a0 * accl[t][0] + a1 * ml[t * 64 + lane];
+#pragma unroll
+            for (int x = 0; x < NVB; ++x)
+                acc[t][x] = a0 * acc[t][x] + a1 * macc[(t * NVB + x) * 64 + lane];
+        }
+    }
     const auto ro = chunk_rsrc(out, int64_t(it.q0) * row_elems, 2, it.nq, H, D);
 #pragma unroll
     for (int t = 0; t < QT; ++t) {
@@ -316,12 +372,19 @@ __global__ __launch_bounds__(64 * (4 / QT)) void attn_kernel_bf16(
     }
 }
 
-// Query tiles per wave, chosen by measurement on MI355X.
+// Query tiles per wave and key parts per block, chosen by measurement on
+// MI355X.
 #ifndef LA_ATTN_QT_64
-#define LA_ATTN_QT_64 1
+#define LA_ATTN_QT_64 2
+#endif
+#ifndef LA_ATTN_KH_64
+#define LA_ATTN_KH_64 2
 #endif
 #ifndef LA_ATTN_QT_128
-#define LA_ATTN_QT_128 1
+#define LA_ATTN_QT_128 2
+#endif
+#ifndef LA_ATTN_KH_128
+#define LA_ATTN_KH_128 2
 #endif
 
 }  // namespace
@@ -361,12 +424,13 @@ extern "C" la_status la_attn_packed(const void* q, const void* k, const void* v,
     const auto* ev = static_cast<const uint16_t*>(ext_v);
     auto* oo = static_cast<uint16_t*>(out);
     if (d_k == 64)
-        hipLaunchKernelGGL((attn_kernel_bf16<64, LA_ATTN_QT_64>), grid, dim3(64 * (4 / LA_ATTN_QT_64)),
-                           0, st, qq, kk, vv, ek, ev, its, oo, H, scale_log2);
+        hipLaunchKernelGGL((attn_kernel_bf16<64, LA_ATTN_QT_64, LA_ATTN_KH_64>), grid,
+                           dim3(64 * LA_ATTN_KH_64 * (4 / LA_ATTN_QT_64)), 0, st, qq, kk, vv, ek,
+                           ev, its, oo, H, scale_log2);
     else
-        hipLaunchKernelGGL((attn_kernel_bf16<128, LA_ATTN_QT_128>), grid,
-                           dim3(64 * (4 / LA_ATTN_QT_128)), 0, st, qq, kk, vv, ek, ev, its, oo, H,
-                           scale_log2);
+        hipLaunchKernelGGL((attn_kernel_bf16<128, LA_ATTN_QT_128, LA_ATTN_KH_128>), grid,
+                           dim3(64 * LA_ATTN_KH_128 * (4 / LA_ATTN_QT_128)), 0, st, qq, kk, vv, ek,
+                           ev, its, oo, H, scale_log2);
     if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
     return LA_OK;
 }

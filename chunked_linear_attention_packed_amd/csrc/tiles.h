@@ -93,19 +93,25 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rsrc(const void* base, i
 __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
-// Output stores are nontemporal (cache policy nt): the outputs are written
-// once and not read again by the pass, and streaming them past the L2 leaves
-// no dirty output lines for the write-back at the end of the kernel (the
-// 7,400-token pass: 24.1 -> 21.9 us).
+// Stores of whole 128-byte output rows per instruction (buf_store16u, used
+// by the row writers of the bf16 scan kernels) are nontemporal (cache policy
+// nt): the outputs are written once and not read again by the pass, and
+// streaming them past the L2 leaves no dirty output lines for the write-back
+// at the end of the kernel (the 7,400-token pass: 24.1 -> 21.9 us).  Stores
+// that write parts of lines (buf_store16, buf_store8) keep the default
+// policy, so that the L2 merges a line's parts before it goes to memory: as
+// nontemporal 8-byte stores, the attention kernel's output wrote 5.3 GB of
+// HBM for 2.2 GB of output at the 272k-token pass.
 constexpr int kAuxStream = 2;   // buffer-op cache policy: nt
 __device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 x) {
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, x), r, off, 0, kAuxStream);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, x), r, off, 0, 0);
 }
 __device__ __forceinline__ void buf_store16u(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 x) {
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, x), r, off, 0, kAuxStream);
 }
+
 __device__ __forceinline__ void buf_store8(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x2 x) {
-    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, x), r, off, 0, kAuxStream);
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, x), r, off, 0, 0);
 }
 
 // ---------------------------------------------------------------------------
