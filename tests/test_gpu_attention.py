@@ -186,6 +186,34 @@ def test_hand_worked_example_on_the_gpu():
     assert torch.all(out[:, 0, 1:] == 0)
 
 
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("first_half_high", [True, False])
+def test_attention_key_halves_far_apart(d, first_half_high):
+    """Keys whose scores differ by about 24 between the first and the second
+    32 positions of every 64-key block: each query's two key halves (kept
+    apart until the end of the walk) have maxima far apart, so combining them
+    rescales one side to almost nothing -- the first half or the second."""
+    H = 2
+    so, bp, _ = oracle.pack_segments([300], [2], [40, 90])
+    T = int(so[-1])
+    rng = np.random.default_rng(47 + d + int(first_half_high))
+    qn = rng.standard_normal((T, H, d)).astype(np.float32) * 0.1 + 1.0
+    pos = np.arange(T) - np.repeat(so[:-1], np.diff(so))   # position in its segment
+    sign = np.where((pos % 64) < 32, 1.0, -1.0).astype(np.float32)
+    if not first_half_high:
+        sign = -sign
+    kn = rng.standard_normal((T, H, d)).astype(np.float32) * 0.05 + \
+        sign[:, None, None] * (12.0 / d)
+    vn = rng.standard_normal((T, H, d)).astype(np.float32)
+    q, k, v = (torch.from_numpy(x).to(torch.bfloat16) for x in (qn, kn, vn))
+    out = _run(q, k, v, so, bp, 1.0)
+    ref = oracle.attention_dense(q, k, v, so, bp, 1.0)
+    err = oracle.row_rel_err(out, ref)
+    print(f"key halves apart d={d} first_high={first_half_high}: err {err:.2e}", flush=True)
+    assert torch.isfinite(out.float()).all()
+    assert err <= TOL
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_attention_rising_scores_rescale_every_block(d):
     """Scores that grow along the keys, so that nearly every key block raises
