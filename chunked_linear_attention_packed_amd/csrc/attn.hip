@@ -182,9 +182,14 @@ __attribute__((amdgpu_waves_per_eu(KH == 2 && D == 64 ? 4 : 1))) void attn_kerne
     // only when a block's maximum exceeds it by more than 2^kLazy in weight
     // (then the running sums are rescaled); otherwise weights up to 2^kLazy
     // are accumulated as they are.  The final division by the running sum
-    // cancels the reference, so the result is the softmax for any m.
+    // cancels the reference, so the result is the softmax for any m.  The
+    // reference is kept in the exponent's units (score * scale_log2) and
+    // starts at kNoRef, a finite value below any scaled score: the first
+    // block with a key raises it, a lane with no key so far gets weights
+    // exp2(-inf) = 0, and no test for "no reference yet" is needed.
     constexpr float kLazy = 8.f;
-    float m[QT];           // reference maximum of each of this lane's queries (raw scores)
+    constexpr float kNoRef = -1e30f;
+    float m[QT];           // reference of each of this lane's queries (log2 units)
     f32x4 acc[QT][NVB];    // O^T tiles: lane holds O[trow][x*16 + 4g + j]
     // running sums of the weights, as one more O^T tile whose A operand is
     // all ones: every row of it holds the sum for the lane's query (column),
@@ -192,7 +197,7 @@ __attribute__((amdgpu_waves_per_eu(KH == 2 && D == 64 ? 4 : 1))) void attn_kerne
     f32x4 accl[QT];
 #pragma unroll
     for (int t = 0; t < QT; ++t) {
-        m[t] = -INFINITY;
+        m[t] = kNoRef;
         accl[t] = zero4();
 #pragma unroll
         for (int x = 0; x < NVB; ++x) acc[t][x] = zero4();
@@ -239,31 +244,29 @@ __attribute__((amdgpu_waves_per_eu(KH == 2 && D == 64 ? 4 : 1))) void attn_kerne
                 }
             bm[t] = max_over_groups(mx);
             // raise the reference where the block's maximum is more than
-            // 2^kLazy above it in weight (always from -inf); scale > 0, so
-            // comparing raw scores is comparing scaled ones
-            any_raise |= m[t] == -INFINITY ? bm[t] != -INFINITY
-                                           : (bm[t] - m[t]) * scale_log2 > kLazy;
+            // 2^kLazy above it in weight (always from kNoRef; never for a
+            // block with no key of this query, whose maximum is -inf)
+            any_raise |= fmaf(bm[t], scale_log2, -m[t]) > kLazy;
         }
         if (__builtin_amdgcn_ballot_w64(any_raise) != 0) {   // wave-uniform
 #pragma unroll
             for (int t = 0; t < QT; ++t) {
-                const bool raise = m[t] == -INFINITY ? bm[t] != -INFINITY
-                                                     : (bm[t] - m[t]) * scale_log2 > kLazy;
-                const float mn = raise ? bm[t] : m[t];
-                const float alpha =
-                    m[t] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m[t] - mn) * scale_log2);
+                const bool raise = fmaf(bm[t], scale_log2, -m[t]) > kLazy;
+                const float mn = raise ? bm[t] * scale_log2 : m[t];
+                // from kNoRef: exp2(-huge) = 0, and the sums are zero anyway
+                const float alpha = __builtin_amdgcn_exp2f(m[t] - mn);
 #pragma unroll
                 for (int x = 0; x < NVB; ++x) acc[t][x] *= alpha;
                 accl[t][0] *= alpha;
                 m[t] = mn;
             }
         }
-        // a query sees a key in every block it visits, so m is finite here
-        // (the guard keeps a row that is masked so far from producing NaNs)
+        // weights exp2(score * scale_log2 - m): at most 2^kLazy, and 0 for
+        // masked scores (-inf) whatever the reference
         u32x2 pb[QT][NUB];
 #pragma unroll
         for (int t = 0; t < QT; ++t) {
-            const float nb = m[t] == -INFINITY ? 0.f : -m[t] * scale_log2;
+            const float nb = -m[t];
 #pragma unroll
             for (int ub = 0; ub < NUB; ++ub) {
                 float p[4];
@@ -324,6 +327,12 @@ __attribute__((amdgpu_waves_per_eu(KH == 2 && D == 64 ? 4 : 1))) void attn_kerne
         block(rows, b == nkb - 1, std::true_type{});
         __syncthreads();
     }
+    // the lane's position again, opaque to the compiler, so that the offsets
+    // below are recomputed here rather than kept in registers over the loops
+    int lane_e = int(threadIdx.x);
+    asm volatile("" : "+v"(lane_e));
+    lane_e &= 63;
+    const int trow_e = qg * 16 * QT + (lane_e & 15), g_e = lane_e >> 4;
     if constexpr (KH == 2) {
         // merge the key halves: the second half's waves leave their reference
         // maxima, sums and unnormalised outputs in LDS (the loop ended with a
@@ -337,9 +346,9 @@ __attribute__((amdgpu_waves_per_eu(KH == 2 && D == 64 ? 4 : 1))) void attn_kerne
 #pragma unroll
             for (int t = 0; t < QT; ++t) {
 #pragma unroll
-                for (int x = 0; x < NVB; ++x) macc[(t * NVB + x) * 64 + lane] = acc[t][x];
-                mm[t * 64 + lane] = m[t];
-                ml[t * 64 + lane] = accl[t][0];
+                for (int x = 0; x < NVB; ++x) macc[(t * NVB + x) * 64 + lane_e] = acc[t][x];
+                mm[t * 64 + lane_e] = m[t];
+                ml[t * 64 + lane_e] = accl[t][0];
             }
         }
         __syncthreads();
@@ -347,15 +356,16 @@ __attribute__((amdgpu_waves_per_eu(KH == 2 && D == 64 ? 4 : 1))) void attn_kerne
 #pragma unroll
         for (int t = 0; t < QT; ++t) {
             // the first half holds a key of every query (the diagonal
-            // block's first key), so its reference is finite
-            const float m1 = mm[t * 64 + lane];
+            // block's first key), so its reference is a real score; a second
+            // half with no key kept kNoRef and weighs exp2(-huge) = 0
+            const float m1 = mm[t * 64 + lane_e];
             const float mn = fmaxf(m[t], m1);
-            const float a0 = __builtin_amdgcn_exp2f((m[t] - mn) * scale_log2);
-            const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m1 - mn) * scale_log2);
-            accl[t][0] = a0 * accl[t][0] + a1 * ml[t * 64 + lane];
+            const float a0 = __builtin_amdgcn_exp2f(m[t] - mn);
+            const float a1 = __builtin_amdgcn_exp2f(m1 - mn);
+            accl[t][0] = a0 * accl[t][0] + a1 * ml[t * 64 + lane_e];
 #pragma unroll
             for (int x = 0; x < NVB; ++x)
-                acc[t][x] = a0 * acc[t][x] + a1 * macc[(t * NVB + x) * 64 + lane];
+                acc[t][x] = a0 * acc[t][x] + a1 * macc[(t * NVB + x) * 64 + lane_e];
         }
     }
     const auto ro = chunk_rsrc(out, int64_t(it.q0) * row_elems, 2, it.nq, H, D);
@@ -363,7 +373,7 @@ __attribute__((amdgpu_waves_per_eu(KH == 2 && D == 64 ? 4 : 1))) void attn_kerne
     for (int t = 0; t < QT; ++t) {
         // every row of accl holds the lane's query's sum
         const float inv = 1.f / accl[t][0];
-        const uint32_t ooff = uint32_t((((trow0 + 16 * t) * H + h) * D + 4 * g) * 2);
+        const uint32_t ooff = uint32_t((((trow_e + 16 * t) * H + h) * D + 4 * g_e) * 2);
 #pragma unroll
         for (int x = 0; x < NVB; ++x)
             buf_store8(ro, ooff + x * 32,
